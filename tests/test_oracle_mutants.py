@@ -1,0 +1,164 @@
+"""Each pin must catch a plausible mistake planted in a copy of the oracle (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.phase_quant as pq
+import pins
+
+
+def fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_split_sign_error_caught():
+    def bad(R):
+        U, W = oracle.split(R)
+        return np.conj(U), W                 # Im U = (R12 - R21)/2
+    fails(pins.check_split_identity, bad)
+    fails(pins.check_split_hand, bad)
+
+
+def test_split_swapped_blocks_caught():
+    def bad(R):
+        n, m = R.shape[0] // 2, R.shape[1] // 2
+        R2 = np.array(R, copy=True)
+        R2[:n, m:], R2[n:, :m] = R[n:, :m], R[:n, m:]     # R12 <-> R21
+        return oracle.split(R2)
+    fails(pins.check_split_identity, bad)
+
+
+def test_split_conj_on_wrong_matrix_caught():
+    def bad(R):
+        U, W = oracle.split(R)
+        return U, np.conj(W)
+    fails(pins.check_split_identity, bad)
+
+
+def test_projection_last_tie_caught():
+    def bad(a, b):
+        s = np.stack([a, b, -a, -b], axis=0)[::-1]
+        return (3 - np.argmax(s, axis=0)).astype(np.uint8)     # last maximum wins
+    fails(pins.check_project_bruteforce, bad)
+    fails(pins.check_project_golden, bad)
+
+
+def test_projection_sign_error_caught():
+    def bad(a, b):
+        return np.argmax(np.stack([a, -b, -a, b], axis=0), axis=0).astype(np.uint8)  # i <-> -i
+    fails(pins.check_project_bruteforce, bad)
+    fails(pins.check_project_angle, bad)
+
+
+def test_sequential_sum_order_caught():
+    def bad(v):
+        out = np.zeros(v.shape[0])
+        for j in range(v.shape[1]):
+            out = out + v[:, j]
+        return out
+    fails(pins.check_ordered_sum_golden, bad)
+
+
+def test_scale_mean_over_all_entries_caught(monkeypatch):
+    real_stage = pq._stage
+
+    def bad_stage(r_re, r_im):
+        k, s_re, s_im, _, _ = real_stage(r_re, r_im)
+        m = r_re.shape[1]
+        on_re = (k == 0) | (k == 2)
+        s_re = pq.ordered_row_sum(np.where(on_re, np.abs(r_re), 0.0)) / m
+        s_im = pq.ordered_row_sum(np.where(~on_re, np.abs(r_im), 0.0)) / m
+        new_re = np.where(k == 0, r_re - s_re[:, None], np.where(k == 2, r_re + s_re[:, None], r_re))
+        new_im = np.where(k == 1, r_im - s_im[:, None], np.where(k == 3, r_im + s_im[:, None], r_im))
+        return k, s_re, s_im, new_re, new_im
+
+    monkeypatch.setattr(pq, "_stage", bad_stage)
+    fails(pins.check_ls_identity, oracle.quantize, oracle.split, oracle.dequantize)
+    fails(pins.check_quantize_hand, oracle.quantize, oracle.unsplit)
+
+
+def test_residual_sign_error_caught(monkeypatch):
+    real_stage = pq._stage
+
+    def bad_stage(r_re, r_im):
+        k, s_re, s_im, _, _ = real_stage(r_re, r_im)
+        new_re = np.where(k == 0, r_re + s_re[:, None], np.where(k == 2, r_re - s_re[:, None], r_re))
+        new_im = np.where(k == 1, r_im - s_im[:, None], np.where(k == 3, r_im + s_im[:, None], r_im))
+        return k, s_re, s_im, new_re, new_im
+
+    monkeypatch.setattr(pq, "_stage", bad_stage)
+    fails(pins.check_norm_nonincreasing, oracle.quantize)
+    fails(pins.check_quantize_hand, oracle.quantize, oracle.unsplit)
+
+
+def test_scale_wrong_component_caught(monkeypatch):
+    real_stage = pq._stage
+
+    def bad_stage(r_re, r_im):
+        k, s_re, s_im, _, _ = real_stage(r_re, r_im)
+        on_re = (k == 0) | (k == 2)
+        n_re = np.maximum(on_re.sum(axis=1), 1)
+        s_re = pq.ordered_row_sum(np.where(on_re, np.abs(r_im), 0.0)) / n_re   # |Im| on the real axis
+        new_re = np.where(k == 0, r_re - s_re[:, None], np.where(k == 2, r_re + s_re[:, None], r_re))
+        new_im = np.where(k == 1, r_im - s_im[:, None], np.where(k == 3, r_im + s_im[:, None], r_im))
+        return k, s_re, s_im, new_re, new_im
+
+    monkeypatch.setattr(pq, "_stage", bad_stage)
+    fails(pins.check_ls_identity, oracle.quantize, oracle.split, oracle.dequantize)
+
+
+def test_pack_msb_first_caught():
+    def bad_pack(codes):
+        T, _, n, m = codes.shape
+        out = np.zeros((n, T, 2, m // 4), dtype=np.uint8)
+        for t in range(T):
+            for M in range(2):
+                c = codes[t, M].astype(np.uint32).reshape(n, m // 4, 4)
+                out[:, t, M] = (c[..., 3] | c[..., 2] << 2 | c[..., 1] << 4 | c[..., 0] << 6).astype(np.uint8)
+        return out
+    fails(pins.check_pack_golden, bad_pack, oracle.unpack)
+
+
+def test_gemv_conj_on_u_caught():
+    def bad(codes, scales, x, stages=None):
+        m = codes.shape[3]
+        x = np.asarray(x, dtype=np.float64).copy()
+        x[:, m:] = -x[:, m:]                 # conj(x) fed to both U and W
+        y = oracle.gemv_ref(codes, scales, x, stages)
+        return y
+    fails(pins.check_gemv_hand, bad)
+    fails(pins.check_gemv_routes, bad, oracle.gemv_ref_real)
+
+
+def test_gemv_dropped_stage_caught():
+    def bad(codes, scales, x, stages=None):
+        return oracle.gemv_ref(codes[:1], scales[:, :1], x, None if stages is None else [0])
+    fails(pins.check_gemv_hand, bad)
+
+
+def test_act_quant_half_away_caught():
+    def bad(x):
+        q, d = oracle.act_quant_ref(x)
+        x = np.asarray(x, dtype=np.float64)
+        for t in range(x.shape[0]):
+            if d[t] != 0:
+                r = (x[t] / float(d[t])).astype(np.float32).astype(np.float64)
+                q[t] = np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -127, 127).astype(np.int8)
+        return q, d
+    fails(pins.check_act_quant_golden, bad)
+
+
+def test_gemm_epilogue_sign_error_caught():
+    def bad(P, scales, delta):
+        P = np.array(P, copy=True)
+        P[:, 1, 1, 1] = -P[:, 1, 1, 1]       # W imaginary-axis b term with the wrong sign
+        return oracle.gemm_epilogue_ref(P, scales, delta)
+    fails(pins.check_gemm_epilogue, oracle.gemm_int_ref, bad, oracle.gemv_ref)
+
+
+def test_gemm_transposed_plane_caught():
+    def bad(codes, q):
+        P = oracle.gemm_int_ref(codes, q)
+        return P[:, :, ::-1]                   # B_re and B_im swapped
+    fails(pins.check_gemm_routes, bad, oracle.gemm_int_ref_loops)
