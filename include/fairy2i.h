@@ -1,0 +1,154 @@
+/*
+ * fairy2i.h -- C ABI of libfairy2i.so, the MI355X (gfx950) hot path of Fairy2i-style
+ * 2-bit widely-linear layers.
+ *
+ * What the library computes (sources are the pages this method is described on):
+ *   - A real layer R (2n x 2m) is rewritten as y = U x + W conj(x) with U, W complex n x m
+ *     (zhichai.net reading note "Fairy2i: Ultra-Low-Bit LLM Quantization Using Complex
+ *     Weights {+-1, +-i}", "Step 1", Theorem 1 and its block closed form; ModelScope card
+ *     "Fairy2i-W2", "Method", widely-linear transform).
+ *   - Each of U, W is approximated by T residual stages of codes in {+1, i, -1, -i} with a
+ *     real-axis and an imaginary-axis scale ("Step 2" projection and dequantization;
+ *     "Step 3" residual recursion; card "Method").
+ *   - The layer is applied without multiplying by weights: every code adds, subtracts or
+ *     swaps real and imaginary parts ("Industry implications: multiplication-free
+ *     inference"; 36Kr article, parallel stages).
+ *
+ * Conventions used by every call:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless stated.
+ *   - Each call checks its arguments on the host, enqueues its kernels on `stream` and
+ *     returns; results are valid once the stream has reached that point.  The library never
+ *     allocates device memory, keeps no pointer after returning and has no global state
+ *     except a thread-local error message.
+ *   - R x~ layout: R is fp32 row-major [2n][2m] (like nn.Linear.weight [out][in]);
+ *     x~ = [Re x; Im x] and y~ = [Re y; Im y], i.e. a real vector of length 2m (2n) whose
+ *     first half is the real part.  R's four quadrants are the blocks R11, R12, R21, R22.
+ *   - Code k in {0,1,2,3} stands for i**k = (1, i, -1, -i).  Bit 0 is the axis (0 real,
+ *     1 imaginary), bit 1 the sign.
+ *   - packed: uint8 [n][T][2][m/4] = (row i, stage t, matrix M = 0 for U, 1 for W), m/16
+ *     little-endian 32-bit words per (i, t, M).  Word w holds codes j = 16w..16w+15; code
+ *     16w+p sits in bits 8*(p%4) + 2*(p/4) .. +1, so byte b holds codes b, b+4, b+8, b+12.
+ *     (One shift and one mask then spread four codes into four bytes in j order.)  Four codes
+ *     per byte: T*n*m/2 bytes per layer, i.e. T bits per real parameter of R.
+ *   - scales: fp32 [n][T][2][2] = [row][stage][matrix][axis], axis 0 = real, 1 = imaginary.
+ *   - Requirements: n >= 1, m >= 64 and m % 64 == 0, 1 <= T <= 4; pointers to packed, x, y,
+ *     codes and workspaces 16-byte aligned; pointers to scales 4-byte aligned (8 for fp64).
+ *   - Every call returns a fairy2i_status.  Nothing aborts or throws across the ABI.  Checks
+ *     run in the order null -> dtype -> stages -> shape -> alignment -> workspace; launch
+ *     failures return FAIRY2I_ERR_HIP.  fairy2i_last_error() gives the detail.
+ *     Data-dependent preconditions (finite inputs, codes <= 3) are not checked.
+ */
+#ifndef FAIRY2I_H
+#define FAIRY2I_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FAIRY2I_ABI_VERSION 1
+
+typedef enum {
+  FAIRY2I_OK = 0,
+  FAIRY2I_ERR_NULL = 1,       /* a required pointer is NULL */
+  FAIRY2I_ERR_SHAPE = 2,      /* n, m, batch or token count out of range */
+  FAIRY2I_ERR_STAGES = 3,     /* T outside [1, 4] */
+  FAIRY2I_ERR_DTYPE = 4,      /* unsupported dtype (or algorithm) combination */
+  FAIRY2I_ERR_ALIGN = 5,      /* pointer not aligned as required */
+  FAIRY2I_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than the *_workspace_bytes call */
+  FAIRY2I_ERR_HIP = 7         /* a HIP runtime call or kernel launch failed */
+} fairy2i_status;
+
+typedef enum {
+  FAIRY2I_F32 = 0,
+  FAIRY2I_BF16 = 1,
+  FAIRY2I_I8 = 2,
+  FAIRY2I_I32 = 3
+} fairy2i_dtype;
+
+/* GEMV kernels.  AUTO picks MFMA for bf16 x (when a large enough workspace is given) and
+ * VALU otherwise.  VALU: exact fp32 add/sub/swap accumulation, any x dtype.  MFMA: codes are
+ * decoded to fp4 {+-2, 0} planes and x (bf16 only) is split exactly into two fp8 e4m3 limbs
+ * with per-32-element power-of-two scales; products run on the scaled fp4 x fp8 MFMA. */
+typedef enum {
+  FAIRY2I_GEMV_AUTO = 0,
+  FAIRY2I_GEMV_VALU = 1,
+  FAIRY2I_GEMV_MFMA = 2
+} fairy2i_gemv_algo;
+
+/* Quantize a real layer.  Widely-linear split (Theorem 1, "Step 1"), then for t < T:
+ * projection to the nearest of {1, i, -1, -i} (first in that order on ties), per-row
+ * per-stage per-matrix axis scales s = mean |Re r| (|Im r|) over the entries coded on that
+ * axis (0 if none), residual r <- r - (s_re b_re + i s_im b_im) ("Step 2", "Step 3").
+ * All arithmetic is fp64; the scale sums use a fixed order (256 partial sums over
+ * j = l, l+256, ..., then a halving tree), so results do not depend on the launch.
+ *   R        fp32 [two_n][two_m], read only.
+ *   packed   out, uint8 [n][T][2][m/4].
+ *   scales   out, fp32 [n][T][2][2] (round-to-nearest-even of the fp64 scales).
+ *   scales64 optional out (NULL skips), fp64 [n][T][2][2].
+ *   codes    optional out (NULL skips), uint8 [T][2][n][m], one code per byte.
+ * Extra requirement: 2*T*m <= 65536 (codes of one row are staged on chip). */
+int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T,
+                     uint8_t* packed, float* scales, double* scales64, uint8_t* codes,
+                     hipStream_t stream);
+
+/* Pack one-byte codes uint8 [T][2][n][m] (values 0..3; higher bits are ignored) into the
+ * packed layout above (ModelScope card "Model details": 2 bits per real parameter at T=2). */
+int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* packed,
+                 hipStream_t stream);
+
+/* Workspace for fairy2i_gemv with the MFMA kernel (0 for the VALU kernel). */
+size_t fairy2i_gemv_workspace_bytes(int64_t m, int64_t B, int algo);
+
+/* Decode GEMV: y~[b] = sum_t U~(t) x[b] + W~(t) conj(x[b]) for b < B, every code an add,
+ * subtract or real/imaginary swap with sign; one fp32 accumulator per (stage, matrix,
+ * axis) so each scale multiplies an accumulated sum, not a weight.
+ *   packed, scales  as produced by fairy2i_quantize.
+ *   x       [B][2m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16.  1 <= B <= 16.
+ *   y       out, [B][2n], y_dtype FAIRY2I_F32 or FAIRY2I_BF16 (round to nearest even).
+ *   algo    fairy2i_gemv_algo.  MFMA requires x_dtype BF16 and a workspace of
+ *           fairy2i_gemv_workspace_bytes(m, B, MFMA) bytes (16-byte aligned).
+ *   workspace, workspace_bytes  may be NULL / 0 for the VALU kernel. */
+int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
+                 const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Per-token int8 activations: delta[tok] = fl32(max_j |x~_j| / 127),
+ * q = clamp(round_half_even(fl32(x~ / delta)), -127, 127); delta == 0 gives q = 0.
+ *   x      [N][two_m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16.  q out int8 [N][two_m],
+ *   delta  out fp32 [N]. */
+int fairy2i_act_quant(const void* x, int x_dtype, int64_t N, int64_t two_m, int8_t* q,
+                      float* delta, hipStream_t stream);
+
+/* Workspace for fairy2i_gemm: int8 activations and their scales when x is not already int8. */
+size_t fairy2i_gemm_workspace_bytes(int64_t n, int64_t m, int T, int64_t N, int x_dtype);
+
+/* Prefill GEMM over N tokens.  Codes are decoded on chip into int8 planes B_re, B_im in
+ * {-1, 0, 1} ("Industry implications"); int8 matrix cores accumulate
+ * P[t][M][plane][comp][tok][i] = sum_j B_plane[i][j] * q[tok][comp*m + j] exactly in int32.
+ *   x        [N][2m]; x_dtype BF16 / F32 (quantized per token inside, see fairy2i_act_quant)
+ *            or I8 (already quantized).
+ *   x_scale  delta [N] fp32: output when x is BF16/F32 (may be NULL), input when x is I8.
+ *   y        y_dtype F32 / BF16: y~ [N][2n] = delta * the widely-linear combination of P
+ *            with the fp32 scales.  y_dtype I32: the raw accumulators, int32
+ *            [T][2][2][2][N][n] = [stage][matrix][plane][comp (0: Re x, 1: Im x)][tok][row].
+ *   workspace  fairy2i_gemm_workspace_bytes(...) bytes, 16-byte aligned (NULL allowed if 0).
+ *   1 <= N <= 1048576. */
+int fairy2i_gemm(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
+                 const void* x, int x_dtype, float* x_scale, int64_t N,
+                 void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+const char* fairy2i_status_string(int status);
+const char* fairy2i_last_error(void);   /* thread-local detail of the last non-OK return */
+int fairy2i_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAIRY2I_H */

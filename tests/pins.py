@@ -245,17 +245,19 @@ def check_empty_axis(quantize, unsplit):
 
 def check_pack_golden(pack, unpack):
     rows = golden_io.pack_bytes()
-    codes = np.array([r[:4] for r in rows], dtype=np.uint8).reshape(1, 1, len(rows), 4)
+    codes = np.array([r[:16] for r in rows], dtype=np.uint8).reshape(1, 1, len(rows), 16)
     codes = np.concatenate([codes, codes], axis=1)           # U and W
     p = pack(codes)
-    assert p.shape == (len(rows), 1, 2, 1)
-    assert [int(v) for v in p[:, 0, 0, 0]] == [r[4] for r in rows]
+    assert p.shape == (len(rows), 1, 2, 4)
+    for i, r in enumerate(rows):
+        assert [int(v) for v in p[i, 0, 0]] == list(r[16:]), (i, p[i, 0, 0])
+        assert [int(v) for v in p[i, 0, 1]] == list(r[16:])
     assert np.array_equal(unpack(p), codes)
 
 
 def check_pack_roundtrip(pack, unpack, packed_nbytes, seed=7):
     rng = np.random.default_rng(seed)
-    for T, n, m in ((1, 3, 64), (2, 5, 128), (3, 2, 256), (4, 1, 4)):
+    for T, n, m in ((1, 3, 64), (2, 5, 128), (3, 2, 256), (4, 1, 16)):
         c = rng.integers(0, 4, size=(T, 2, n, m), dtype=np.uint8)
         p = pack(c)
         assert p.nbytes == packed_nbytes(n, m, T)

@@ -108,15 +108,24 @@ def test_scale_wrong_component_caught(monkeypatch):
     fails(pins.check_ls_identity, oracle.quantize, oracle.split, oracle.dequantize)
 
 
-def test_pack_msb_first_caught():
+def test_pack_consecutive_codes_per_byte_caught():
     def bad_pack(codes):
         T, _, n, m = codes.shape
         out = np.zeros((n, T, 2, m // 4), dtype=np.uint8)
         for t in range(T):
             for M in range(2):
                 c = codes[t, M].astype(np.uint32).reshape(n, m // 4, 4)
-                out[:, t, M] = (c[..., 3] | c[..., 2] << 2 | c[..., 1] << 4 | c[..., 0] << 6).astype(np.uint8)
+                out[:, t, M] = (c[..., 0] | c[..., 1] << 2 | c[..., 2] << 4 | c[..., 3] << 6).astype(np.uint8)
         return out
+    fails(pins.check_pack_golden, bad_pack, oracle.unpack)
+
+
+def test_pack_msb_first_caught():
+    def bad_pack(codes):
+        p = oracle.pack(codes)
+        b = p.astype(np.uint32)
+        rev = ((b & 3) << 6) | ((b & 12) << 2) | ((b & 48) >> 2) | ((b & 192) >> 6)
+        return rev.astype(np.uint8)
     fails(pins.check_pack_golden, bad_pack, oracle.unpack)
 
 

@@ -1,0 +1,206 @@
+// Quantizer: widely-linear split, phase projection, axis scales, residual stages, packing.
+//
+// Sources: zhichai.net reading note "Fairy2i: Ultra-Low-Bit LLM Quantization Using Complex
+// Weights {+-1, +-i}" -- "Step 1" (Theorem 1, block closed form for U and W), "Step 2"
+// (b(w) = argmax_s Re(w conj(s)), axis-wise scales, dequantization), "Step 3" (residual of
+// the next stage = residual minus the dequantized term); ModelScope card "Fairy2i-W2",
+// "Method" and "Model details" (T = 2 stages, 2 bits per real parameter).
+//
+// One workgroup of 256 threads owns one complex output row i.  Thread l handles columns
+// j = l, l+256, ...; it reads R[i][j], R[i][m+j], R[n+i][j], R[n+i][m+j] (coalesced across
+// the workgroup), forms U[i][j] and W[i][j] in fp64 registers and runs every stage on both.
+// The scale sums of a stage are the 256 per-thread partial sums (each in j order) reduced by
+// a halving tree, so the fp64 scales -- and therefore every later stage's codes -- do not
+// depend on the launch.  Codes of the row are kept in LDS (one byte each) and written out
+// packed four to a byte at the end.  Instead of keeping fp64 residuals for every j, each stage
+// recomputes r from the fp32 inputs and subtracts the earlier stages' terms in stage order,
+// which reproduces the same fp64 values bit for bit.
+#include "common.hpp"
+
+namespace f2i {
+
+constexpr int kQThreads = 256;
+
+// First index of the maximum of (re, im, -re, -im): the codeword of {1, i, -1, -i} with the
+// largest Re(w conj(s)); ties go to the earlier codeword.
+__device__ __forceinline__ int project4(double re, double im) {
+  int k = 0;
+  double best = re;
+  if (im > best) { best = im; k = 1; }
+  if (-re > best) { best = -re; k = 2; }
+  if (-im > best) { k = 3; }
+  return k;
+}
+
+// Theorem 1 closed form for one block entry (A, B, C, D) = (R11, R12, R21, R22)[i][j].
+__device__ __forceinline__ void split_entry(int M, float A, float B, float C, float D,
+                                            double& re, double& im) {
+  const double a = A, b = B, c = C, d = D;
+  if (M == 0) { re = (a + d) * 0.5; im = (c - b) * 0.5; }
+  else        { re = (a - d) * 0.5; im = (b + c) * 0.5; }
+}
+
+// Four one-byte codes (low two bits of each byte) -> one packed byte, least significant first.
+__device__ __forceinline__ uint32_t pack4(uint32_t w) {
+  return (w & 3u) | ((w >> 6) & 0xCu) | ((w >> 12) & 0x30u) | ((w >> 18) & 0xC0u);
+}
+__device__ __forceinline__ uint32_t pack16(uint4 w) {
+  return pack4(w.x) | (pack4(w.y) << 8) | (pack4(w.z) << 16) | (pack4(w.w) << 24);
+}
+
+// MAXC > 0: the row's fp32 inputs stay in registers (m <= 256 * MAXC).  MAXC == 0: they are
+// re-read from memory each stage (any m).
+template <int MAXC>
+__global__ __launch_bounds__(kQThreads) void k_quantize(
+    const float* __restrict__ R, int n, int m, int T, uint8_t* __restrict__ packed,
+    float* __restrict__ scales, double* __restrict__ scales64, uint8_t* __restrict__ codes_out) {
+  extern __shared__ __align__(16) uint8_t s_codes[];        // [T][2][m], one code per byte
+  __shared__ double s_part[4][kQThreads];                   // [U re, U im, W re, W im][thread]
+  __shared__ int s_cnt[2][kQThreads / kWave];               // real-axis counts per wave
+  __shared__ double s_scale[4][2][2];                       // fp64 scales [t][M][axis]
+
+  const int i = blockIdx.x;
+  const int l = threadIdx.x;
+  const int64_t ld = 2 * (int64_t)m;
+  const float* __restrict__ r0 = R + (int64_t)i * ld;          // row i of R
+  const float* __restrict__ r1 = R + (int64_t)(n + i) * ld;    // row n+i of R
+  const int nch = (m + kQThreads - 1) / kQThreads;
+
+  constexpr int NR = MAXC > 0 ? MAXC : 1;
+  float qa[NR], qb[NR], qc[NR], qd[NR];
+  if constexpr (MAXC > 0) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int j = l + c * kQThreads;
+      if (j < m) { qa[c] = r0[j]; qb[c] = r0[m + j]; qc[c] = r1[j]; qd[c] = r1[m + j]; }
+      else { qa[c] = qb[c] = qc[c] = qd[c] = 0.f; }
+    }
+  }
+
+  for (int t = 0; t < T; ++t) {
+    double sre[2] = {0.0, 0.0}, sim[2] = {0.0, 0.0};
+    int nre[2] = {0, 0};
+    auto body = [&](int j, float A, float B, float C, float D) {
+#pragma unroll
+      for (int M = 0; M < 2; ++M) {
+        double re, im;
+        split_entry(M, A, B, C, D, re, im);
+        for (int tp = 0; tp < t; ++tp) {                  // earlier stages, in order
+          const int kp = s_codes[(tp * 2 + M) * m + j];
+          if (kp == 0) re = re - s_scale[tp][M][0];
+          else if (kp == 2) re = re + s_scale[tp][M][0];
+          else if (kp == 1) im = im - s_scale[tp][M][1];
+          else im = im + s_scale[tp][M][1];
+        }
+        const int k = project4(re, im);
+        s_codes[(t * 2 + M) * m + j] = (uint8_t)k;
+        if ((k & 1) == 0) { sre[M] += fabs(re); nre[M] += 1; }
+        else { sim[M] += fabs(im); }
+      }
+    };
+    if constexpr (MAXC > 0) {
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int j = l + c * kQThreads;
+        if (j < m) body(j, qa[c], qb[c], qc[c], qd[c]);
+      }
+    } else {
+      for (int c = 0; c < nch; ++c) {
+        const int j = l + c * kQThreads;
+        if (j < m) body(j, r0[j], r0[m + j], r1[j], r1[m + j]);
+      }
+    }
+
+    s_part[0][l] = sre[0];
+    s_part[1][l] = sim[0];
+    s_part[2][l] = sre[1];
+    s_part[3][l] = sim[1];
+    const int cu = wave_sum(nre[0]);
+    const int cw = wave_sum(nre[1]);
+    if ((l & (kWave - 1)) == 0) { s_cnt[0][l / kWave] = cu; s_cnt[1][l / kWave] = cw; }
+    __syncthreads();
+    if (l < kWave) {
+      double v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)   // halving steps 128 and 64 of the tree
+        v[q] = (s_part[q][l] + s_part[q][l + 128]) + (s_part[q][l + 64] + s_part[q][l + 192]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {   // steps 32..1; lane 0 ends with the sum
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = v[q] + __shfl_xor(v[q], off);
+      }
+      if (l == 0) {
+#pragma unroll
+        for (int M = 0; M < 2; ++M) {
+          const int n_re = s_cnt[M][0] + s_cnt[M][1] + s_cnt[M][2] + s_cnt[M][3];
+          const int n_im = m - n_re;
+          const double s_re = n_re > 0 ? v[2 * M] / (double)n_re : 0.0;
+          const double s_im = n_im > 0 ? v[2 * M + 1] / (double)n_im : 0.0;
+          s_scale[t][M][0] = s_re;
+          s_scale[t][M][1] = s_im;
+          const int64_t o = (((int64_t)i * T + t) * 2 + M) * 2;
+          scales[o] = (float)s_re;
+          scales[o + 1] = (float)s_im;
+          if (scales64) { scales64[o] = s_re; scales64[o + 1] = s_im; }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // packed row i: [t][M][m/4] bytes, i.e. the LDS code bytes four to one.
+  const int dw_row = T * m / 8;
+  uint32_t* __restrict__ prow = reinterpret_cast<uint32_t*>(packed + (int64_t)i * T * (m / 2));
+  const uint4* sc4 = reinterpret_cast<const uint4*>(s_codes);
+  for (int q = l; q < dw_row; q += kQThreads) prow[q] = pack16(sc4[q]);
+
+  if (codes_out) {   // [T][2][n][m]
+    const int dw_plane = m / 4;
+    for (int p = 0; p < 2 * T; ++p) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(codes_out + ((int64_t)p * n + i) * m);
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(s_codes + (int64_t)p * m);
+      for (int q = l; q < dw_plane; q += kQThreads) dst[q] = src[q];
+    }
+  }
+}
+
+// codes uint8 [T][2][n][m] -> packed [n][T][2][m/4]; one thread per packed dword (16 codes).
+__global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ codes, int n, int m,
+                                              int T, uint8_t* __restrict__ packed) {
+  const int dw_plane = m / 16;
+  const int dw_row = 2 * T * dw_plane;
+  const int64_t total = (int64_t)n * dw_row;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int i = (int)(idx / dw_row);
+  const int q = (int)(idx % dw_row);
+  const int p = q / dw_plane;        // t * 2 + M
+  const int qq = q % dw_plane;
+  const uint4 w = *reinterpret_cast<const uint4*>(codes + ((int64_t)p * n + i) * m + 16 * qq);
+  reinterpret_cast<uint32_t*>(packed)[idx] = pack16(w);
+}
+
+hipError_t launch_quantize(const float* R, int n, int m, int T, uint8_t* packed, float* scales,
+                           double* scales64, uint8_t* codes, hipStream_t s) {
+  const size_t lds = (size_t)2 * T * m;
+  const int nch = (m + kQThreads - 1) / kQThreads;
+  const dim3 grid(n), block(kQThreads);
+  if (nch <= 1)
+    hipLaunchKernelGGL(k_quantize<1>, grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+  else if (nch <= 8)
+    hipLaunchKernelGGL(k_quantize<8>, grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+  else if (nch <= 24)
+    hipLaunchKernelGGL(k_quantize<24>, grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+  else
+    hipLaunchKernelGGL(k_quantize<0>, grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t* codes, int n, int m, int T, uint8_t* packed, hipStream_t s) {
+  const int64_t total = (int64_t)n * 2 * T * (m / 16);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(256), 0, s, codes, n, m, T, packed);
+  return hipGetLastError();
+}
+
+}  // namespace f2i
