@@ -1,0 +1,228 @@
+"""Benchmark of the Fairy2i widely-linear hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile-steps]
+
+Workload: the LLaMA-2 7B attention projection (R 4096 x 4096 -> U, W 2048 x 2048 complex),
+T = 2 residual stages, bf16 activations, all inputs synthetic and seeded (workloads.py).
+
+One step is one pass of every stage of the path over one batch of inputs:
+  1. quantize + pack the layer (split, projection, axis scales, residual stages, packing);
+  2. decode GEMV at batch 1 over a pool of P distinct copies of the packed layer (P * 4 MB
+     >= 512 MB, more than the 256 MB Infinity Cache, so every launch streams from HBM);
+  3. the same GEMV at batch 4 and batch 16 over the pool;
+  4. prefill: per-token int8 activation quantization of 2048 tokens and the int8-MFMA GEMM.
+Every kernel runs on torch's current HIP stream; each segment is bracketed by HIP events on
+that stream, inputs are resident in HBM before the timed region starts.
+
+`value` is the headline metric: algorithmic HBM bytes of the batch-1 GEMV launches divided by
+their time (GB/s).  The JSON line also carries the roofline of that kernel, the other legs
+(GB/s, TOPS, params/s) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+METRIC = "packed 2-bit widely-linear GEMV HBM GB/s (% peak) + prefill GEMM int8 TOPS"
+POOL_BYTES = 512 * 2 ** 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 256 MiB device copy (counter calibration for profiles)")
+    return ap.parse_args()
+
+
+def gemv_bytes(n, m, T, B, x_bytes=2, y_bytes=4):
+    """Algorithmic bytes of one GEMV: codes + fp32 scales + x + y."""
+    return T * n * m // 2 + n * T * 2 * 2 * 4 + B * 2 * m * x_bytes + B * 2 * n * y_bytes
+
+
+def cpu_baseline(R, T, x1, budget_s):
+    """The oracle (float64 NumPy) on the GPU machine's host: the batch-1 GEMV of the same layer,
+    repeated until the time budget is spent; plus the quantizer on a row sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:                                      # pragma: no cover
+        cores = os.cpu_count() or 1
+    n, m = R.shape[0] // 2, R.shape[1] // 2
+    rows = np.arange(128)
+    sub = np.concatenate([R[rows], R[n + rows]])
+    t0 = time.perf_counter()
+    codes_s, _, _, _ = oracle.quantize(sub, T)
+    tq = time.perf_counter() - t0
+    codes, s32, _, _ = oracle.quantize(R, T)               # setup, not timed
+    reps, t_gemv = 0, 0.0
+    while t_gemv < budget_s or reps == 0:
+        t0 = time.perf_counter()
+        oracle.gemv_ref(codes, s32, x1)
+        t_gemv += time.perf_counter() - t0
+        reps += 1
+    per = t_gemv / reps
+    return {
+        "value": gemv_bytes(n, m, T, 1) / per / 1e9, "unit": "GB/s", "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{reps} x oracle gemv_ref of the full {2*n}x{2*m} layer at batch 1 "
+                  f"({per*1e3:.1f} ms each); quantizer on {len(rows)} of {n} complex rows "
+                  f"took {tq:.3f} s ({len(rows)*m*4/tq/1e6:.2f} M real params/s)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no "
+              f"multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import widely_linear_gemv_amd as f2
+    from widely_linear_gemv_amd import build as _build
+
+    if not os.path.exists(f2.LIB_PATH):
+        _build.build()
+    f2.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    layer = workloads.ATTN
+    n, m, T = layer.n, layer.m, 2
+    R_np = layer.weight()
+    R = torch.from_numpy(R_np).to(dev)
+    q0 = f2.fairy2i_quantize(R, T)
+    layer_bytes = q0["packed"].numel()
+    P = max(1, -(-POOL_BYTES // layer_bytes))
+    pool = q0["packed"].unsqueeze(0).repeat(P, 1, 1, 1, 1).contiguous()
+    spool = q0["scales"].unsqueeze(0).repeat(P, 1, 1, 1, 1).contiguous()
+    xs = {}
+    for B in (1, 4, 16):
+        a = workloads.activations(B, 2 * m, workloads.ATTN_X_SEEDS[B])
+        xs[B] = torch.from_numpy(a.bf16_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    ys = {B: torch.empty((B, 2 * n), dtype=torch.float32, device=dev) for B in xs}
+    Ntok = workloads.PREFILL_TOKENS
+    xp_np = workloads.activations(Ntok, 2 * m, workloads.PREFILL_X_SEED)
+    xp = torch.from_numpy(xp_np.bf16_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qp = torch.empty((Ntok, 2 * m), dtype=torch.int8, device=dev)
+    dp = torch.empty((Ntok,), dtype=torch.float32, device=dev)
+    yp = torch.empty((Ntok, 2 * n), dtype=torch.float32, device=dev)
+    qout = {"packed": torch.empty_like(q0["packed"]), "scales": torch.empty_like(q0["scales"])}
+
+    if args.calib_copy:
+        a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step():
+        e = [ev()]
+        f2.fairy2i_quantize(R, T, packed=qout["packed"], scales=qout["scales"])
+        e.append(ev())
+        for B in (1, 4, 16):
+            for p in range(P):
+                f2.fairy2i_gemv(pool[p], spool[p], xs[B], y=ys[B], algo=f2.GEMV_MFMA)
+            e.append(ev())
+        f2.fairy2i_act_quant(xp, q=qp, delta=dp)
+        e.append(ev())
+        f2.fairy2i_gemm(q0["packed"], q0["scales"], qp, x_scale=dp, y=yp)
+        e.append(ev())
+        return e
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    seg = np.zeros(6)
+    t0 = time.perf_counter()
+    all_events = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e in all_events:
+        seg += np.array([e[k].elapsed_time(e[k + 1]) for k in range(6)])   # ms
+    seg /= args.steps
+    ms_step = float(np.sum(seg))
+
+    bytes_b = {B: gemv_bytes(n, m, T, B) for B in (1, 4, 16)}
+    gemv_ms = {1: seg[1], 4: seg[2], 16: seg[3]}
+    gbs = {B: P * bytes_b[B] / (gemv_ms[B] * 1e-3) / 1e9 for B in (1, 4, 16)}
+    per_launch_us = {B: gemv_ms[B] * 1e3 / P for B in (1, 4, 16)}
+    issued_ops = 16 * T * n * m * Ntok
+    gemm_tops = issued_ops / (seg[5] * 1e-3) / 1e12
+    quant_params = 4 * n * m
+    quant_read = quant_params * 4 + layer_bytes + n * T * 4 * 4
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs[1], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "LLaMA-2 7B attention projection R 4096x4096 -> U,W 2048x2048, T=2; "
+                        "decode GEMV batch 1 (value), 4, 16 over a pool of distinct layer copies; "
+                        "quantize+pack; prefill act-quant + int8 GEMM over 2048 tokens",
+            "rows": 2 * n, "cols": 2 * m, "T": T, "batch": 1, "pool_layers": P,
+            "x_dtype": "bf16", "y_dtype": "f32", "gemv_kernel": "mfma (bf16 code planes x bf16 x)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(bytes_b[1] / (per_launch_us[1] * 1e-6) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(bytes_b[1] / (per_launch_us[1] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "legs": {
+            "gemv_b1": {"GB/s": round(gbs[1], 2), "us_per_launch": round(per_launch_us[1], 3),
+                        "bytes_per_launch": bytes_b[1]},
+            "gemv_b4": {"GB/s": round(gbs[4], 2), "us_per_launch": round(per_launch_us[4], 3),
+                        "bytes_per_launch": bytes_b[4]},
+            "gemv_b16": {"GB/s": round(gbs[16], 2), "us_per_launch": round(per_launch_us[16], 3),
+                         "bytes_per_launch": bytes_b[16]},
+            "quantize": {"us": round(seg[0] * 1e3, 2),
+                         "real_params_per_s": round(quant_params / (seg[0] * 1e-3), 1),
+                         "GB/s": round(quant_read / (seg[0] * 1e-3) / 1e9, 2)},
+            "act_quant": {"us": round(seg[4] * 1e3, 2),
+                          "GB/s": round((Ntok * 2 * m * 3 + Ntok * 4) / (seg[4] * 1e-3) / 1e9, 2)},
+            "gemm": {"us": round(seg[5] * 1e3, 2), "issued_TOPS": round(gemm_tops, 2),
+                     "useful_TOPS": round(gemm_tops / 2, 2),
+                     "frac_of_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "issued_ops": issued_ops},
+            "wall_s": round(wall, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        x1 = workloads.activations(1, 2 * m, workloads.ATTN_X_SEEDS[1]).values
+        out["cpu_baseline"] = cpu_baseline(R_np, T, x1, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,10 +70,10 @@ typedef enum {
   FAIRY2I_I32 = 3
 } fairy2i_dtype;
 
-/* GEMV kernels.  AUTO picks MFMA for bf16 x (when a large enough workspace is given) and
- * VALU otherwise.  VALU: exact fp32 add/sub/swap accumulation, any x dtype.  MFMA: codes are
- * decoded to fp4 {+-2, 0} planes and x (bf16 only) is split exactly into two fp8 e4m3 limbs
- * with per-32-element power-of-two scales; products run on the scaled fp4 x fp8 MFMA. */
+/* GEMV kernels.  AUTO picks MFMA for bf16 x and VALU for fp32 x.  VALU: fp32 add/sub/swap
+ * accumulation on the vector ALUs, any x dtype.  MFMA: codes are decoded in registers to bf16
+ * planes {+-2, 0} and multiplied with the unchanged bf16 x on v_mfma_f32_16x16x32_bf16; every
+ * product is exact and the sums are fp32 (bf16 x only). */
 typedef enum {
   FAIRY2I_GEMV_AUTO = 0,
   FAIRY2I_GEMV_VALU = 1,
@@ -101,21 +101,17 @@ int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T,
 int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* packed,
                  hipStream_t stream);
 
-/* Workspace for fairy2i_gemv with the MFMA kernel (0 for the VALU kernel). */
-size_t fairy2i_gemv_workspace_bytes(int64_t m, int64_t B, int algo);
-
 /* Decode GEMV: y~[b] = sum_t U~(t) x[b] + W~(t) conj(x[b]) for b < B, every code an add,
  * subtract or real/imaginary swap with sign; one fp32 accumulator per (stage, matrix,
  * axis) so each scale multiplies an accumulated sum, not a weight.
  *   packed, scales  as produced by fairy2i_quantize.
  *   x       [B][2m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16.  1 <= B <= 16.
  *   y       out, [B][2n], y_dtype FAIRY2I_F32 or FAIRY2I_BF16 (round to nearest even).
- *   algo    fairy2i_gemv_algo.  MFMA requires x_dtype BF16 and a workspace of
- *           fairy2i_gemv_workspace_bytes(m, B, MFMA) bytes (16-byte aligned).
- *   workspace, workspace_bytes  may be NULL / 0 for the VALU kernel. */
+ *   algo    fairy2i_gemv_algo; MFMA requires x_dtype BF16.
+ * Uses no workspace. */
 int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+                 hipStream_t stream);
 
 /* Per-token int8 activations: delta[tok] = fl32(max_j |x~_j| / 127),
  * q = clamp(round_half_even(fl32(x~ / delta)), -127, 127); delta == 0 gives q = 0.

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the header declares,
+and every argument error returns its documented status (checks run before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import widely_linear_gemv_amd as f2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fairy2i.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(f2.LIB_PATH):
+        from widely_linear_gemv_amd import build
+        build.build()
+    return f2.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fairy2i_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("fairy2i_quantize", "fairy2i_pack", "fairy2i_gemv", "fairy2i_gemm",
+                 "fairy2i_act_quant", "fairy2i_last_error", "fairy2i_status_string"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(f2.SIGNATURES)
+
+
+def test_version_and_status_strings(L):
+    assert f2.fairy2i_abi_version() == 1
+    for s in range(8):
+        assert f2.fairy2i_status_string(s) not in ("", "unknown status")
+    assert f2.fairy2i_status_string(99) == "unknown status"
+
+
+FAKE = 1 << 20          # a 16-byte aligned, never dereferenced address
+FAKE_ODD = FAKE + 2     # misaligned
+NULL = None
+S = None                # default stream
+
+
+def last():
+    return f2.fairy2i_last_error()
+
+
+def test_quantize_errors(L):
+    q = L.fairy2i_quantize
+    assert q(NULL, 256, 256, 2, FAKE, FAKE, NULL, NULL, S) == 1
+    assert q(FAKE, 256, 256, 0, FAKE, FAKE, NULL, NULL, S) == 3
+    assert q(FAKE, 256, 256, 5, FAKE, FAKE, NULL, NULL, S) == 3
+    assert q(FAKE, 255, 256, 2, FAKE, FAKE, NULL, NULL, S) == 2
+    assert q(FAKE, 256, 200, 2, FAKE, FAKE, NULL, NULL, S) == 2         # m = 100
+    assert q(FAKE, 256, 2 * 16384 + 128, 2, FAKE, FAKE, NULL, NULL, S) == 2   # 2*T*m too big
+    assert "65536" in last()
+    assert q(FAKE, 256, 256, 2, FAKE_ODD, FAKE, NULL, NULL, S) == 5
+    assert q(FAKE, 256, 256, 2, FAKE, FAKE, FAKE + 4, NULL, S) == 5     # scales64 needs 8
+
+
+def test_pack_errors(L):
+    p = L.fairy2i_pack
+    assert p(NULL, 4, 64, 2, FAKE, S) == 1
+    assert p(FAKE, 4, 64, 9, FAKE, S) == 3
+    assert p(FAKE, 0, 64, 2, FAKE, S) == 2
+    assert p(FAKE, 4, 96, 2, FAKE, S) == 2
+    assert p(FAKE, 4, 64, 2, FAKE_ODD, S) == 5
+
+
+def test_gemv_errors(L):
+    g = L.fairy2i_gemv
+    ok = dict(packed=FAKE, scales=FAKE, n=8, m=64, T=2, x=FAKE, xd=f2.BF16, B=1, y=FAKE,
+              yd=f2.F32, algo=f2.GEMV_VALU)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["packed"], a["scales"], a["n"], a["m"], a["T"], a["x"], a["xd"], a["B"], a["y"],
+                 a["yd"], a["algo"], S)
+
+    assert call(x=NULL) == 1
+    assert call(xd=f2.I8) == 4
+    assert call(yd=f2.I32) == 4
+    assert call(algo=7) == 4
+    assert call(algo=f2.GEMV_MFMA, xd=f2.F32) == 4
+    assert call(T=0) == 3
+    assert call(B=0) == 2 and call(B=17) == 2
+    assert call(m=32) == 2 and call(n=0) == 2
+    assert call(x=FAKE_ODD) == 5
+    assert call(y=FAKE + 8) == 5
+
+
+def test_act_quant_errors(L):
+    a = L.fairy2i_act_quant
+    assert a(NULL, f2.BF16, 4, 128, FAKE, FAKE, S) == 1
+    assert a(FAKE, f2.I8, 4, 128, FAKE, FAKE, S) == 4
+    assert a(FAKE, f2.BF16, 0, 128, FAKE, FAKE, S) == 2
+    assert a(FAKE, f2.BF16, 4, 12, FAKE, FAKE, S) == 2
+    assert a(FAKE_ODD, f2.BF16, 4, 128, FAKE, FAKE, S) == 5
+
+
+def test_gemm_errors(L):
+    g = L.fairy2i_gemm
+    base = [FAKE, FAKE, 8, 64, 2, FAKE, f2.I8, FAKE, 16, FAKE, f2.F32, NULL, 0, S]
+
+    def call(idx_vals):
+        a = list(base)
+        for i, v in idx_vals.items():
+            a[i] = v
+        return g(*a)
+
+    assert call({7: NULL}) == 1                   # int8 x needs delta
+    assert call({6: f2.I32}) == 4
+    assert call({10: f2.I8}) == 4
+    assert call({4: 5}) == 3
+    assert call({8: 0}) == 2
+    assert call({3: 65}) == 2
+    assert call({9: FAKE_ODD}) == 5
+    need = L.fairy2i_gemm_workspace_bytes(8, 64, 2, 16, f2.BF16)
+    assert need >= 16 * 128 + 16 * 4
+    assert call({6: f2.BF16, 11: FAKE, 12: need - 1}) == 6
+    assert L.fairy2i_gemm_workspace_bytes(8, 64, 2, 16, f2.I8) == 0
+
+
+def test_python_binding_raises_with_message(L):
+    import torch
+    with pytest.raises(f2.Fairy2iError) as e:
+        f2._check(L.fairy2i_pack(NULL, 4, 64, 2, FAKE, S))
+    assert "ERR_NULL" in str(e.value) and "required" in str(e.value)
+    assert torch is not None

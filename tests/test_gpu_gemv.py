@@ -1,0 +1,117 @@
+"""GPU parity: fairy2i_gemv (VALU and MFMA kernels) against the oracle GEMV.
+
+fp32 output: relative L2 <= 1e-5 against the fp64 oracle; bf16 output: <= 2e-3.  Inputs are
+oracle-quantized layers (tiny, attention) or seeded random codes and scales (MLP shapes),
+packed by the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL_F32, announce, check_bf16, device, down, rel_l2, up, x_to_dev
+
+import widely_linear_gemv_amd as f2
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = {"valu": f2.GEMV_VALU, "mfma": f2.GEMV_MFMA}
+
+
+def run(dev, codes, scales, act, algo, y_dtype):
+    packed = up(oracle.pack(codes), dev)
+    s = up(scales.astype(np.float32), dev)
+    x = x_to_dev(act, dev)
+    y = f2.fairy2i_gemv(packed, s, x, algo=algo, y_dtype=y_dtype)
+    return down(y)
+
+
+def check(dev, codes, scales, act, algo, label):
+    want = oracle.gemv_ref(codes, scales.astype(np.float32), act.values)
+    announce("gemv", label, algo, "f32 out")
+    got = run(dev, codes, scales, act, ALGOS[algo], torch.float32)
+    err = rel_l2(got, want)
+    assert err <= TOL_F32, (label, algo, "f32", err)
+    announce("gemv", label, algo, "bf16 out")
+    check_bf16(run(dev, codes, scales, act, ALGOS[algo], torch.bfloat16), want, (label, algo))
+
+
+_ATTN = {}
+
+
+def attention_layer():
+    if not _ATTN:
+        codes, s32, _, _ = oracle.quantize(workloads.ATTN.weight(), 2)
+        _ATTN["v"] = (codes, s32)
+    return _ATTN["v"]
+
+
+def test_tiny_fp32_x():
+    dev = device()
+    codes, s32, _, _ = oracle.quantize(workloads.TINY.weight(), 2)
+    act = workloads.activations(1, 256, workloads.TINY_X_SEED, "f32")
+    check(dev, codes, s32, act, "valu", "tiny")
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+@pytest.mark.parametrize("algo", ["valu", "mfma"])
+def test_attention(B, algo):
+    dev = device()
+    codes, s32 = attention_layer()
+    act = workloads.activations(B, 4096, workloads.ATTN_X_SEEDS[B])
+    check(dev, codes, s32, act, algo, f"attention B={B}")
+
+
+@pytest.mark.parametrize("shape", ["gate_up", "down"])
+@pytest.mark.parametrize("T", [2, 3])
+@pytest.mark.parametrize("B", [1, 8])
+def test_mlp_shapes(shape, T, B):
+    dev = device()
+    layer = workloads.MLP_GATE_UP if shape == "gate_up" else workloads.MLP_DOWN
+    n, m = layer.n, layer.m
+    codes = workloads.random_codes(T, n, m, seed=layer.seed + T)
+    scales = workloads.random_scales(n, T, seed=layer.seed + 10 * T)
+    act = workloads.activations(B, 2 * m, workloads.MLP_X_SEEDS[shape] + B)
+    for algo in ("mfma", "valu"):
+        check(dev, codes, scales, act, algo, f"{shape} T={T} B={B}")
+
+
+@pytest.mark.parametrize("n,m,T,B", [(1, 64, 1, 1), (17, 192, 2, 3), (33, 128, 4, 5), (5, 320, 3, 16),
+                                     (16, 64, 2, 2), (100, 1024, 2, 7)])
+@pytest.mark.parametrize("algo", ["valu", "mfma"])
+def test_ragged_and_small(n, m, T, B, algo):
+    """Ragged row tiles, m not a multiple of 128 (half-empty last MFMA step), every T, odd B."""
+    dev = device()
+    codes = workloads.random_codes(T, n, m, seed=n + m + T + B)
+    scales = workloads.random_scales(n, T, seed=n * 3 + B)
+    act = workloads.activations(B, 2 * m, seed=m + B)
+    check(dev, codes, scales, act, algo, f"n={n} m={m} T={T} B={B}")
+
+
+@pytest.mark.parametrize("algo", ["valu", "mfma"])
+def test_zero_and_wide_range_x(algo):
+    """x with exact zeros and magnitudes spread over 2^-6 .. 2^8 inside each 32-column block."""
+    dev = device()
+    n, m, T, B = 64, 512, 2, 4
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((B, 2 * m)).astype(np.float32)
+    v *= np.float32(2.0) ** rng.integers(-6, 8, size=v.shape).astype(np.float32)
+    v[rng.random(v.shape) < 0.1] = 0.0
+    bits = workloads.f32_to_bf16_bits(v)
+    act = workloads.Activations(values=workloads.bf16_bits_to_f32(bits), dtype="bf16", bf16_bits=bits)
+    codes = workloads.random_codes(T, n, m, seed=4)
+    scales = workloads.random_scales(n, T, seed=5)
+    check(dev, codes, scales, act, algo, "wide-range x")
+
+
+def test_stage_independence_on_gpu():
+    """The T stage terms are independent and summed: the T-stage result equals the sum of the
+    single-stage results (each computed by the GPU from the same codes)."""
+    dev = device()
+    codes, s32 = attention_layer()
+    act = workloads.activations(4, 4096, 203)
+    announce("gemv stage independence")
+    full = run(dev, codes, s32, act, f2.GEMV_MFMA, torch.float32)
+    parts = sum(run(dev, codes[t:t + 1], np.ascontiguousarray(s32[:, t:t + 1]), act, f2.GEMV_MFMA,
+                    torch.float32) for t in range(2))
+    assert rel_l2(full, parts) <= TOL_F32

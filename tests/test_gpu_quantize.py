@@ -1,0 +1,125 @@
+"""GPU parity: fairy2i_quantize and fairy2i_pack against the oracle, bit for bit.
+
+Codes, packed bytes and the fp64 scales must match exactly; the fp32 scales are their
+round-to-nearest-even.  Full matrices are compared where the oracle finishes in seconds;
+the LLaMA-2 MLP shapes are compared on a sample of complex rows (each row i depends only on
+rows i and n+i of R, so the oracle runs on that sub-matrix)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import announce, device, down, up
+
+import widely_linear_gemv_amd as f2
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_quantize(R, T, dev):
+    out = f2.fairy2i_quantize(up(R, dev), T, want_scales64=True, want_codes=True)
+    return {k: down(v) for k, v in out.items()}
+
+
+def assert_rows_match(R, T, rows, got, label):
+    n = R.shape[0] // 2
+    rows = np.asarray(rows)
+    sub = np.concatenate([R[rows], R[n + rows]], axis=0)
+    codes, s32, s64, _ = oracle.quantize(sub, T)
+    packed = oracle.pack(codes)
+    assert np.array_equal(got["codes"][:, :, rows], codes), label + ": codes"
+    assert np.array_equal(got["packed"][rows], packed), label + ": packed"
+    assert np.array_equal(got["scales64"][rows].view(np.uint64), s64.view(np.uint64)), label + ": scales64"
+    assert np.array_equal(got["scales"][rows].view(np.uint32), s32.view(np.uint32)), label + ": scales"
+
+
+def test_tiny_full():
+    dev = device()
+    R = workloads.TINY.weight()
+    announce("quantize tiny 256x256 T=2")
+    got = gpu_quantize(R, 2, dev)
+    assert_rows_match(R, 2, np.arange(128), got, "tiny")
+
+
+def test_attention_full():
+    dev = device()
+    R = workloads.ATTN.weight()
+    announce("quantize 4096x4096 T=2")
+    got = gpu_quantize(R, 2, dev)
+    codes, s32, s64, _ = oracle.quantize(R, 2)
+    assert np.array_equal(got["codes"], codes)
+    assert np.array_equal(got["packed"], oracle.pack(codes))
+    assert np.array_equal(got["scales64"].view(np.uint64), s64.view(np.uint64))
+    assert np.array_equal(got["scales"].view(np.uint32), s32.view(np.uint32))
+
+
+@pytest.mark.parametrize("layer", [workloads.MLP_GATE_UP, workloads.MLP_DOWN], ids=["gate_up", "down"])
+@pytest.mark.parametrize("T", [2, 3])
+def test_mlp_sampled_rows(layer, T):
+    dev = device()
+    R = layer.weight()
+    announce("quantize", layer.name, "T =", T)
+    got = gpu_quantize(R, T, dev)
+    n = layer.n
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, n - 1], rng.choice(n, 93, replace=False)]))
+    assert_rows_match(R, T, rows, got, layer.name)
+    # codes and packed agree everywhere (the packed bytes are the codes, four to a byte)
+    assert np.array_equal(oracle.unpack(got["packed"]), got["codes"])
+
+
+def constructed_edge_matrix(n, m, seed):
+    """Dyadic R whose U and W rows hit every special case: exact ties |Re| = |Im|, zeros,
+    all-real rows (empty imaginary axis), all-imaginary rows, rows already in the codebook
+    times a per-row scale (exact recovery), and random dyadic rows."""
+    rng = np.random.default_rng(seed)
+    Z = []
+    for M in range(2):
+        a = rng.integers(-8, 9, size=(n, m)).astype(np.float64) / 8.0
+        b = rng.integers(-8, 9, size=(n, m)).astype(np.float64) / 8.0
+        tie = rng.random((n, m)) < 0.3
+        b = np.where(tie, np.where(rng.random((n, m)) < 0.5, a, -a), b)
+        zero = rng.random((n, m)) < 0.05
+        a[zero] = 0.0
+        b[zero] = 0.0
+        z = a + 1j * b
+        z[0] = np.abs(a[0]) + 0.125                 # every code 0: empty imaginary axis
+        z[1 % n] = 1j * (-np.abs(b[1 % n]) - 0.25)  # every code 3: empty real axis
+        if n > 2:
+            k = rng.integers(0, 4, size=m)
+            z[2] = np.where(k == 0, 0.5, np.where(k == 2, -0.5, np.where(k == 1, 0.25j, -0.25j)))
+        if n > 3:
+            z[3] = 0.0                              # all zero
+        Z.append(z)
+    return oracle.unsplit(Z[0], Z[1]).astype(np.float32)
+
+
+@pytest.mark.parametrize("n,m,T", [(4, 64, 2), (7, 320, 3), (33, 512, 1), (5, 2048, 4),
+                                   (9, 5504, 2), (3, 6208, 2), (2, 64, 4)])
+def test_edge_cases(n, m, T):
+    """Ties, zeros, empty axes, exact recovery, ragged m (not a multiple of 256), the
+    register-resident and the re-reading (m > 6144) kernel variants, T = 1..4."""
+    dev = device()
+    R = constructed_edge_matrix(n, m, seed=n * 1000 + m + T)
+    announce("quantize edge", n, m, T)
+    got = gpu_quantize(R, T, dev)
+    assert_rows_match(R, T, np.arange(n), got, f"edge n={n} m={m} T={T}")
+
+
+def test_random_fp32_ragged():
+    dev = device()
+    R = workloads.weight(2 * 37, 2 * 704, seed=55)
+    announce("quantize random 74x1408 T=3")
+    got = gpu_quantize(R, 3, dev)
+    assert_rows_match(R, 3, np.arange(37), got, "ragged")
+
+
+@pytest.mark.parametrize("T,n,m", [(1, 3, 64), (2, 17, 128), (3, 5, 192), (4, 2, 1024), (2, 2048, 2048)])
+def test_pack_matches_oracle(T, n, m):
+    dev = device()
+    codes = workloads.random_codes(T, n, m, seed=T * 100 + n)
+    noisy = codes | (np.random.default_rng(1).integers(0, 64, size=codes.shape, dtype=np.uint8) << 2)
+    announce("pack", T, n, m)
+    got = down(f2.fairy2i_pack(up(noisy, dev)))
+    assert np.array_equal(got, oracle.pack(codes))     # bits above the code are ignored

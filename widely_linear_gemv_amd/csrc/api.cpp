@@ -1,0 +1,188 @@
+// C ABI of libfairy2i.so: argument checks, status codes, dispatch to the HIP launchers.
+// The operations themselves are specified in include/fairy2i.h.
+#include "fairy2i.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return FAIRY2I_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FAIRY2I_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxRows = int64_t(1) << 28;   // complex rows n
+constexpr int64_t kMaxCols = int64_t(1) << 22;   // complex columns m
+constexpr int64_t kMaxTokens = int64_t(1) << 20;
+
+int check_stages(int T) {
+  if (T < 1 || T > 4) return fail(FAIRY2I_ERR_STAGES, "T = %d, must be in [1, 4]", T);
+  return FAIRY2I_OK;
+}
+
+int check_nm(int64_t n, int64_t m) {
+  if (n < 1 || n > kMaxRows) return fail(FAIRY2I_ERR_SHAPE, "n = %lld out of range", (long long)n);
+  if (m < 64 || m > kMaxCols || m % 64 != 0)
+    return fail(FAIRY2I_ERR_SHAPE, "m = %lld: need m >= 64 and m %% 64 == 0", (long long)m);
+  return FAIRY2I_OK;
+}
+
+size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
+
+}  // namespace
+
+extern "C" {
+
+int fairy2i_abi_version(void) { return FAIRY2I_ABI_VERSION; }
+
+const char* fairy2i_last_error(void) { return g_err; }
+
+const char* fairy2i_status_string(int status) {
+  switch (status) {
+    case FAIRY2I_OK: return "ok";
+    case FAIRY2I_ERR_NULL: return "null pointer";
+    case FAIRY2I_ERR_SHAPE: return "bad shape";
+    case FAIRY2I_ERR_STAGES: return "bad stage count";
+    case FAIRY2I_ERR_DTYPE: return "bad dtype";
+    case FAIRY2I_ERR_ALIGN: return "misaligned pointer";
+    case FAIRY2I_ERR_WORKSPACE: return "workspace too small";
+    case FAIRY2I_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T, uint8_t* packed,
+                     float* scales, double* scales64, uint8_t* codes, hipStream_t stream) {
+  if (!R || !packed || !scales) return fail(FAIRY2I_ERR_NULL, "R, packed and scales are required");
+  if (int s = check_stages(T)) return s;
+  if (two_n < 2 || two_n % 2 || two_m < 2 || two_m % 2)
+    return fail(FAIRY2I_ERR_SHAPE, "R is %lld x %lld; both sizes must be even",
+                (long long)two_n, (long long)two_m);
+  const int64_t n = two_n / 2, m = two_m / 2;
+  if (int s = check_nm(n, m)) return s;
+  if (2 * T * m > 65536)
+    return fail(FAIRY2I_ERR_SHAPE, "2*T*m = %lld exceeds 65536", (long long)(2 * T * m));
+  if (!aligned(R, 4) || !aligned(packed, 16) || !aligned(scales, 4) ||
+      (scales64 && !aligned(scales64, 8)) || (codes && !aligned(codes, 16)))
+    return fail(FAIRY2I_ERR_ALIGN, "R/scales need 4, scales64 8, packed/codes 16-byte alignment");
+  return hip_status(f2i::launch_quantize(R, (int)n, (int)m, T, packed, scales, scales64, codes, stream),
+                    "quantize launch");
+}
+
+int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* packed,
+                 hipStream_t stream) {
+  if (!codes || !packed) return fail(FAIRY2I_ERR_NULL, "codes and packed are required");
+  if (int s = check_stages(T)) return s;
+  if (int s = check_nm(n, m)) return s;
+  if (!aligned(codes, 16) || !aligned(packed, 16))
+    return fail(FAIRY2I_ERR_ALIGN, "codes and packed need 16-byte alignment");
+  return hip_status(f2i::launch_pack(codes, (int)n, (int)m, T, packed, stream), "pack launch");
+}
+
+int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
+                 const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,
+                 hipStream_t stream) {
+  if (!packed || !scales || !x || !y) return fail(FAIRY2I_ERR_NULL, "packed, scales, x and y are required");
+  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32 or BF16", x_dtype);
+  if (y_dtype != FAIRY2I_F32 && y_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "y_dtype %d: need F32 or BF16", y_dtype);
+  if (algo != FAIRY2I_GEMV_AUTO && algo != FAIRY2I_GEMV_VALU && algo != FAIRY2I_GEMV_MFMA)
+    return fail(FAIRY2I_ERR_DTYPE, "unknown GEMV algorithm %d", algo);
+  if (algo == FAIRY2I_GEMV_MFMA && x_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "the MFMA GEMV takes bf16 x only");
+  if (int s = check_stages(T)) return s;
+  if (int s = check_nm(n, m)) return s;
+  if (B < 1 || B > 16) return fail(FAIRY2I_ERR_SHAPE, "B = %lld: need 1 <= B <= 16", (long long)B);
+  if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(scales, 4))
+    return fail(FAIRY2I_ERR_ALIGN, "packed, x and y need 16-byte alignment, scales 4");
+  const bool use_mfma = algo == FAIRY2I_GEMV_MFMA || (algo == FAIRY2I_GEMV_AUTO && x_dtype == FAIRY2I_BF16);
+  if (use_mfma)
+    return hip_status(f2i::launch_gemv_mfma(packed, scales, (int)n, (int)m, T, x, (int)B, y,
+                                            y_dtype == FAIRY2I_BF16, nullptr, stream),
+                      "gemv (mfma) launch");
+  return hip_status(f2i::launch_gemv_valu(packed, scales, (int)n, (int)m, T, x,
+                                          x_dtype == FAIRY2I_BF16, (int)B, y,
+                                          y_dtype == FAIRY2I_BF16, stream),
+                    "gemv (valu) launch");
+}
+
+int fairy2i_act_quant(const void* x, int x_dtype, int64_t N, int64_t two_m, int8_t* q,
+                      float* delta, hipStream_t stream) {
+  if (!x || !q || !delta) return fail(FAIRY2I_ERR_NULL, "x, q and delta are required");
+  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32 or BF16", x_dtype);
+  if (N < 1 || N > kMaxTokens) return fail(FAIRY2I_ERR_SHAPE, "N = %lld out of range", (long long)N);
+  if (two_m < 8 || two_m % 8 || two_m > 2 * kMaxCols)
+    return fail(FAIRY2I_ERR_SHAPE, "row length %lld: need a positive multiple of 8", (long long)two_m);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(delta, 4))
+    return fail(FAIRY2I_ERR_ALIGN, "x and q need 16-byte alignment, delta 4");
+  return hip_status(f2i::launch_act_quant(x, x_dtype == FAIRY2I_BF16, (int)N, (int)two_m, q, delta, stream),
+                    "act_quant launch");
+}
+
+size_t fairy2i_gemm_workspace_bytes(int64_t n, int64_t m, int T, int64_t N, int x_dtype) {
+  (void)n;
+  (void)T;
+  if (x_dtype == FAIRY2I_I8 || N < 1 || m < 1) return 0;
+  return align16((size_t)N * 2 * (size_t)m) + align16((size_t)N * 4);
+}
+
+int fairy2i_gemm(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
+                 const void* x, int x_dtype, float* x_scale, int64_t N, void* y, int y_dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!packed || !scales || !x || !y) return fail(FAIRY2I_ERR_NULL, "packed, scales, x and y are required");
+  if (x_dtype == FAIRY2I_I8 && !x_scale)
+    return fail(FAIRY2I_ERR_NULL, "x_scale (delta) is required with int8 x");
+  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16 && x_dtype != FAIRY2I_I8)
+    return fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32, BF16 or I8", x_dtype);
+  if (y_dtype != FAIRY2I_F32 && y_dtype != FAIRY2I_BF16 && y_dtype != FAIRY2I_I32)
+    return fail(FAIRY2I_ERR_DTYPE, "y_dtype %d: need F32, BF16 or I32", y_dtype);
+  if (int s = check_stages(T)) return s;
+  if (int s = check_nm(n, m)) return s;
+  if (N < 1 || N > kMaxTokens) return fail(FAIRY2I_ERR_SHAPE, "N = %lld out of range", (long long)N);
+  if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(scales, 4) ||
+      (x_scale && !aligned(x_scale, 4)) || (workspace && !aligned(workspace, 16)))
+    return fail(FAIRY2I_ERR_ALIGN, "packed, x, y, workspace need 16-byte alignment; scales, x_scale 4");
+  const size_t need = fairy2i_gemm_workspace_bytes(n, m, T, N, x_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FAIRY2I_ERR_WORKSPACE, "GEMM needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : size_t(0));
+  const int8_t* q = static_cast<const int8_t*>(x);
+  const float* delta = x_scale;
+  if (x_dtype != FAIRY2I_I8) {
+    int8_t* qw = static_cast<int8_t*>(workspace);
+    float* dw = x_scale ? x_scale
+                        : reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                   align16((size_t)N * 2 * (size_t)m));
+    hipError_t e = f2i::launch_act_quant(x, x_dtype == FAIRY2I_BF16, (int)N, (int)(2 * m), qw, dw, stream);
+    if (e != hipSuccess) return hip_status(e, "act_quant launch");
+    q = qw;
+    delta = dw;
+  }
+  const int mode = y_dtype == FAIRY2I_F32 ? 0 : (y_dtype == FAIRY2I_BF16 ? 1 : 2);
+  return hip_status(f2i::launch_gemm(packed, scales, (int)n, (int)m, T, q, delta, (int)N, y, mode, stream),
+                    "gemm launch");
+}
+
+}  // extern "C"

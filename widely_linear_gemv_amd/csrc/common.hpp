@@ -40,9 +40,8 @@ hipError_t launch_quantize(const float* R, int n, int m, int T, uint8_t* packed,
 hipError_t launch_pack(const uint8_t* codes, int n, int m, int T, uint8_t* packed, hipStream_t s);
 hipError_t launch_gemv_valu(const uint8_t* packed, const float* scales, int n, int m, int T,
                             const void* x, int x_bf16, int B, void* y, int y_bf16, hipStream_t s);
-size_t gemv_mfma_workspace_bytes(int m, int B);
 hipError_t launch_gemv_mfma(const uint8_t* packed, const float* scales, int n, int m, int T,
-                            const void* x, int B, void* y, int y_bf16, void* ws, hipStream_t s);
+                            const void* x, int B, void* y, int y_bf16, void* unused, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int x_bf16, int N, int two_m, int8_t* q, float* delta,
                             hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* scales, int n, int m, int T,

@@ -7,8 +7,9 @@
 // imaginary parts with a sign flip); 36Kr article, parallel stages (the T terms are data
 // independent and summed).
 //
-// One wave per complex row.  Lane l reads packed dwords l, l+64, ... of each (stage, matrix)
-// plane -- 16 codes each, coalesced -- and the 16 matching x values.  For each code it negates
+// One wave per complex row.  Lane l reads packed words l, l+64, ... of each (stage, matrix)
+// plane -- 16 codes each (code p of a word in bits 8*(p%4) + 2*(p/4)), coalesced -- and the
+// 16 matching x values.  For each code it negates
 // the (a, b) pair when the sign bit is set and adds it to the real-axis or imaginary-axis
 // accumulator; the scales of that plane multiply the accumulated sums once per lane, and the
 // wave reduces the per-lane outputs with cross-lane adds at the end.  All sums are fp32.
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const uint8_t* __restrict__ p
             XLoad<XT>::load16(x + bb * xs + m + j0, xb);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const uint32_t k = (w >> (2 * r)) & 3u;
+              const uint32_t k = (w >> (8 * (r & 3) + 2 * (r >> 2))) & 3u;   // code j0 + r
               const uint32_t sgn = (k & 2u) << 30;          // code 2 or 3: negate
               const float va = __uint_as_float(__float_as_uint(xa[r]) ^ sgn);
               const float vb = __uint_as_float(__float_as_uint(xb[r]) ^ sgn);

@@ -12,8 +12,8 @@
 // The scale sums of a stage are the 256 per-thread partial sums (each in j order) reduced by
 // a halving tree, so the fp64 scales -- and therefore every later stage's codes -- do not
 // depend on the launch.  Codes of the row are kept in LDS (one byte each) and written out
-// packed four to a byte at the end.  Instead of keeping fp64 residuals for every j, each stage
-// recomputes r from the fp32 inputs and subtracts the earlier stages' terms in stage order,
+// packed sixteen to a 32-bit word at the end.  Instead of keeping fp64 residuals for every j, each
+// stage recomputes r from the fp32 inputs and subtracts the earlier stages' terms in stage order,
 // which reproduces the same fp64 values bit for bit.
 #include "common.hpp"
 
@@ -40,12 +40,11 @@ __device__ __forceinline__ void split_entry(int M, float A, float B, float C, fl
   else        { re = (a - d) * 0.5; im = (b + c) * 0.5; }
 }
 
-// Four one-byte codes (low two bits of each byte) -> one packed byte, least significant first.
-__device__ __forceinline__ uint32_t pack4(uint32_t w) {
-  return (w & 3u) | ((w >> 6) & 0xCu) | ((w >> 12) & 0x30u) | ((w >> 18) & 0xC0u);
-}
+// Sixteen one-byte codes c0..c15 (low two bits of each byte used) -> one packed 32-bit word:
+// byte b = c[b] | c[b+4] << 2 | c[b+8] << 4 | c[b+12] << 6.
 __device__ __forceinline__ uint32_t pack16(uint4 w) {
-  return pack4(w.x) | (pack4(w.y) << 8) | (pack4(w.z) << 16) | (pack4(w.w) << 24);
+  constexpr uint32_t lo2 = 0x03030303u;
+  return (w.x & lo2) | ((w.y & lo2) << 2) | ((w.z & lo2) << 4) | ((w.w & lo2) << 6);
 }
 
 // MAXC > 0: the row's fp32 inputs stay in registers (m <= 256 * MAXC).  MAXC == 0: they are
@@ -148,7 +147,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     __syncthreads();
   }
 
-  // packed row i: [t][M][m/4] bytes, i.e. the LDS code bytes four to one.
+  // packed row i: [t][M][m/4] bytes, the LDS code bytes sixteen to a word.
   const int dw_row = T * m / 8;
   uint32_t* __restrict__ prow = reinterpret_cast<uint32_t*>(packed + (int64_t)i * T * (m / 2));
   const uint4* sc4 = reinterpret_cast<const uint4*>(s_codes);
