@@ -70,14 +70,22 @@ typedef enum {
   FAIRY2I_I32 = 3
 } fairy2i_dtype;
 
-/* GEMV kernels.  AUTO picks MFMA for bf16 x and VALU for fp32 x.  VALU: fp32 add/sub/swap
- * accumulation on the vector ALUs, any x dtype.  MFMA: codes are decoded in registers to bf16
- * planes {+-2, 0} and multiplied with the unchanged bf16 x on v_mfma_f32_16x16x32_bf16; every
- * product is exact and the sums are fp32 (bf16 x only). */
+/* GEMV kernels.  AUTO picks MFMA for bf16 x and VALU for fp32 x; MFMA means MFMA_BF16 (the
+ * faster of the two matrix-core kernels on gfx950 at every batch size; MFMA_I8 is kept as the
+ * exact-integer variant).
+ *   VALU       fp32 add/sub/swap accumulation on the vector ALUs; fp32 or bf16 x.
+ *   MFMA_BF16  codes decoded in registers to bf16 planes {+-2, 0}, multiplied with the unchanged
+ *              bf16 x on v_mfma_f32_16x16x32_bf16: exact products, fp32 sums.  bf16 x.
+ *   MFMA_I8    codes decoded to int8 planes {-1, 0, 1}; each bf16 column of x is scaled by one
+ *              power of two and rounded to a 23-bit integer (exact unless a value is more than
+ *              2^14 below the column maximum) held as three int8 digits; exact int32 sums on
+ *              v_mfma_i32_16x16x64_i8.  bf16 x, B <= 2. */
 typedef enum {
   FAIRY2I_GEMV_AUTO = 0,
   FAIRY2I_GEMV_VALU = 1,
-  FAIRY2I_GEMV_MFMA = 2
+  FAIRY2I_GEMV_MFMA = 2,
+  FAIRY2I_GEMV_MFMA_BF16 = 3,
+  FAIRY2I_GEMV_MFMA_I8 = 4
 } fairy2i_gemv_algo;
 
 /* Quantize a real layer.  Widely-linear split (Theorem 1, "Step 1"), then for t < T:
@@ -107,11 +115,30 @@ int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* pac
  *   packed, scales  as produced by fairy2i_quantize.
  *   x       [B][2m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16.  1 <= B <= 16.
  *   y       out, [B][2n], y_dtype FAIRY2I_F32 or FAIRY2I_BF16 (round to nearest even).
- *   algo    fairy2i_gemv_algo; MFMA requires x_dtype BF16.
+ *   algo    fairy2i_gemv_algo; the MFMA kernels require x_dtype BF16, MFMA_I8 also B <= 2.
  * Uses no workspace. */
 int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,
                  hipStream_t stream);
+
+/* One GEMV of a grouped call.  packed, scales, x, y as for fairy2i_gemv; n complex rows. */
+typedef struct {
+  const uint8_t* packed;
+  const float* scales;
+  const void* x;
+  void* y;
+  int64_t n;
+} fairy2i_gemv_item;
+
+/* Grouped decode GEMV: `count` independent GEMVs that share m, T, B and the dtypes (for example
+ * the q, k and v projections, which also share x; ModelScope card "Method": every linear layer
+ * becomes a widely-linear layer).  The MFMA kernels cover all items' row tiles in one grid of
+ * up to 48 items per launch, so a small layer does not pay a launch ramp and tail of its own;
+ * VALU and MFMA_I8 run the items one after another.
+ *   items   HOST array of `count` items (read during the call only; the pointers in it are
+ *           device pointers).  Each item is checked like a fairy2i_gemv call. */
+int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, int T, int x_dtype,
+                         int64_t B, int y_dtype, int algo, hipStream_t stream);
 
 /* Per-token int8 activations: delta[tok] = fl32(max_j |x~_j| / 127),
  * q = clamp(round_half_even(fl32(x~ / delta)), -127, 127); delta == 0 gives q = 0.

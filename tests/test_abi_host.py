@@ -91,13 +91,33 @@ def test_gemv_errors(L):
     assert call(x=NULL) == 1
     assert call(xd=f2.I8) == 4
     assert call(yd=f2.I32) == 4
-    assert call(algo=7) == 4
+    assert call(algo=7) == 4 and call(algo=-1) == 4
     assert call(algo=f2.GEMV_MFMA, xd=f2.F32) == 4
+    assert call(algo=f2.GEMV_MFMA_I8, xd=f2.F32) == 4
+    assert call(algo=f2.GEMV_MFMA_I8, B=3) == 2
     assert call(T=0) == 3
     assert call(B=0) == 2 and call(B=17) == 2
     assert call(m=32) == 2 and call(n=0) == 2
     assert call(x=FAKE_ODD) == 5
     assert call(y=FAKE + 8) == 5
+
+
+def test_gemv_grouped_errors(L):
+    g = L.fairy2i_gemv_grouped
+    It = f2.GemvItem
+    good = (It * 2)(It(FAKE, FAKE, FAKE, FAKE, 8), It(FAKE, FAKE, FAKE, FAKE, 24))
+    assert g(None, 2, 64, 2, f2.BF16, 1, f2.F32, f2.GEMV_MFMA, S) == 1
+    assert g(good, 0, 64, 2, f2.BF16, 1, f2.F32, f2.GEMV_MFMA, S) == 2
+    bad = (It * 2)(It(FAKE, FAKE, FAKE, FAKE, 8), It(FAKE, None, FAKE, FAKE, 24))
+    assert g(bad, 2, 64, 2, f2.BF16, 1, f2.F32, f2.GEMV_MFMA, S) == 1
+    assert "item 1" in last()
+    assert g(good, 2, 64, 2, f2.F32, 1, f2.F32, f2.GEMV_MFMA, S) == 4
+    assert g(good, 2, 64, 0, f2.BF16, 1, f2.F32, f2.GEMV_MFMA, S) == 3
+    assert g(good, 2, 96, 2, f2.BF16, 1, f2.F32, f2.GEMV_MFMA, S) == 2
+    badn = (It * 1)(It(FAKE, FAKE, FAKE, FAKE, 0))
+    assert g(badn, 1, 64, 2, f2.BF16, 1, f2.F32, f2.GEMV_MFMA, S) == 2
+    odd = (It * 1)(It(FAKE, FAKE, FAKE_ODD, FAKE, 8))
+    assert g(odd, 1, 64, 2, f2.BF16, 1, f2.F32, f2.GEMV_MFMA, S) == 5
 
 
 def test_act_quant_errors(L):

@@ -15,7 +15,7 @@ import widely_linear_gemv_amd as f2
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = {"valu": f2.GEMV_VALU, "mfma": f2.GEMV_MFMA}
+ALGOS = {"valu": f2.GEMV_VALU, "mfma": f2.GEMV_MFMA, "bf16": f2.GEMV_MFMA_BF16, "i8": f2.GEMV_MFMA_I8}
 
 
 def run(dev, codes, scales, act, algo, y_dtype):
@@ -53,8 +53,8 @@ def test_tiny_fp32_x():
     check(dev, codes, s32, act, "valu", "tiny")
 
 
-@pytest.mark.parametrize("B", [1, 4, 16])
-@pytest.mark.parametrize("algo", ["valu", "mfma"])
+@pytest.mark.parametrize("B,algo", [(1, "valu"), (4, "valu"), (16, "valu"), (1, "bf16"), (4, "bf16"),
+                                    (16, "bf16"), (1, "i8"), (1, "mfma"), (4, "mfma"), (16, "mfma")])
 def test_attention(B, algo):
     dev = device()
     codes, s32 = attention_layer()
@@ -72,14 +72,16 @@ def test_mlp_shapes(shape, T, B):
     codes = workloads.random_codes(T, n, m, seed=layer.seed + T)
     scales = workloads.random_scales(n, T, seed=layer.seed + 10 * T)
     act = workloads.activations(B, 2 * m, workloads.MLP_X_SEEDS[shape] + B)
-    for algo in ("mfma", "valu"):
+    for algo in ("mfma", "valu", "bf16") + (("i8",) if B <= 2 else ()):
         check(dev, codes, scales, act, algo, f"{shape} T={T} B={B}")
 
 
 @pytest.mark.parametrize("n,m,T,B", [(1, 64, 1, 1), (17, 192, 2, 3), (33, 128, 4, 5), (5, 320, 3, 16),
-                                     (16, 64, 2, 2), (100, 1024, 2, 7)])
-@pytest.mark.parametrize("algo", ["valu", "mfma"])
+                                     (16, 64, 2, 2), (100, 1024, 2, 7), (19, 5504, 3, 2), (40, 6208, 2, 1)])
+@pytest.mark.parametrize("algo", ["valu", "bf16", "i8"])
 def test_ragged_and_small(n, m, T, B, algo):
+    if algo == "i8" and B > 2:
+        pytest.skip("the int8 kernel takes B <= 2")
     """Ragged row tiles, m not a multiple of 128 (half-empty last MFMA step), every T, odd B."""
     dev = device()
     codes = workloads.random_codes(T, n, m, seed=n + m + T + B)
@@ -88,11 +90,11 @@ def test_ragged_and_small(n, m, T, B, algo):
     check(dev, codes, scales, act, algo, f"n={n} m={m} T={T} B={B}")
 
 
-@pytest.mark.parametrize("algo", ["valu", "mfma"])
-def test_zero_and_wide_range_x(algo):
+@pytest.mark.parametrize("algo,B", [("valu", 4), ("bf16", 4), ("i8", 2)])
+def test_zero_and_wide_range_x(algo, B):
     """x with exact zeros and magnitudes spread over 2^-6 .. 2^8 inside each 32-column block."""
     dev = device()
-    n, m, T, B = 64, 512, 2, 4
+    n, m, T = 64, 512, 2
     rng = np.random.default_rng(3)
     v = rng.standard_normal((B, 2 * m)).astype(np.float32)
     v *= np.float32(2.0) ** rng.integers(-6, 8, size=v.shape).astype(np.float32)
@@ -115,3 +117,67 @@ def test_stage_independence_on_gpu():
     parts = sum(run(dev, codes[t:t + 1], np.ascontiguousarray(s32[:, t:t + 1]), act, f2.GEMV_MFMA,
                     torch.float32) for t in range(2))
     assert rel_l2(full, parts) <= TOL_F32
+
+
+def test_graph_replay_matches_eager():
+    """A captured sequence of GEMV launches replays to the eager result, every time, with eager
+    work and synchronizations between replays."""
+    dev = device()
+    codes, s32 = attention_layer()
+    packed = up(oracle.pack(codes), dev)
+    s = up(s32, dev)
+    outs = {}
+    for B in (1, 4, 16):
+        act = workloads.activations(B, 4096, workloads.ATTN_X_SEEDS[B])
+        x = x_to_dev(act, dev)
+        announce("graph replay B =", B)
+        eager = f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA)
+        eager_valu = f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_VALU)
+        torch.cuda.synchronize()
+        y = torch.empty_like(eager)
+        yv = torch.empty_like(eager)
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cap):
+            f2.fairy2i_gemv(packed, s, x, y=y, algo=f2.GEMV_MFMA)
+            f2.fairy2i_gemv(packed, s, x, y=yv, algo=f2.GEMV_VALU)
+        for rep in range(3):
+            y.fill_(float("nan"))
+            yv.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, eager), (B, rep)
+            assert torch.equal(yv, eager_valu), (B, rep)
+            f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_VALU)     # eager work between replays
+            torch.cuda.synchronize()
+        outs[B] = eager
+
+
+@pytest.mark.parametrize("algo", ["mfma", "valu"])
+def test_grouped_matches_single_and_oracle(algo):
+    """A grouped call over items of different n (and more items than one launch holds) gives,
+    item by item, exactly the single-call result, within tolerance of the oracle."""
+    dev = device()
+    m, T, B = 512, 2, 3
+    ns = [16, 33, 1, 200, 64] * 11              # 55 items -> two launches of the grouped kernel
+    rng = np.random.default_rng(17)
+    act = workloads.activations(B, 2 * m, seed=21)
+    x = x_to_dev(act, dev)
+    items, singles, refs = [], [], []
+    for k, n in enumerate(ns):
+        codes = workloads.random_codes(T, n, m, seed=1000 + k)
+        scales = workloads.random_scales(n, T, seed=2000 + k)
+        packed = up(oracle.pack(codes), dev)
+        s = up(scales, dev)
+        y = torch.full((B, 2 * n), float("nan"), dtype=torch.float32, device=dev)
+        items.append((packed, s, x, y))
+        singles.append(f2.fairy2i_gemv(packed, s, x, algo=ALGOS[algo]))
+        if k < 10:
+            refs.append(oracle.gemv_ref(codes, scales, act.values))
+    announce("grouped gemv", algo, len(items), "items")
+    f2.fairy2i_gemv_grouped(items, algo=ALGOS[algo])
+    torch.cuda.synchronize()
+    for k, it in enumerate(items):
+        assert torch.equal(it[3], singles[k]), k
+        if k < 10:
+            assert rel_l2(down(it[3]), refs[k]) <= TOL_F32, k

@@ -21,7 +21,7 @@ FAIRY2I_OK = 0
 STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_STAGES", 4: "ERR_DTYPE",
                 5: "ERR_ALIGN", 6: "ERR_WORKSPACE", 7: "ERR_HIP"}
 F32, BF16, I8, I32 = 0, 1, 2, 3
-GEMV_AUTO, GEMV_VALU, GEMV_MFMA = 0, 1, 2
+GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_MFMA_BF16, GEMV_MFMA_I8 = 0, 1, 2, 3, 4
 
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.int32: I32}
 
@@ -41,6 +41,16 @@ SIGNATURES = {
     "fairy2i_last_error": (ctypes.c_char_p, []),
     "fairy2i_abi_version": (_INT, []),
 }
+
+
+
+class GemvItem(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+SIGNATURES["fairy2i_gemv_grouped"] = (_INT, [ctypes.POINTER(GemvItem), _INT, _I64, _INT, _INT, _I64,
+                                              _INT, _INT, _P])
 
 _lib = None
 
@@ -132,6 +142,20 @@ def fairy2i_gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, *,
     _check(lib().fairy2i_gemv(_ptr(packed), _ptr(scales), n, m, T, _ptr(x), _DTYPE[x.dtype], B,
                               _ptr(y), _DTYPE[y.dtype], algo, _stream(stream)))
     return y
+
+
+def fairy2i_gemv_grouped(items, *, algo: int = GEMV_AUTO, stream=None):
+    """items: sequence of (packed, scales, x, y) tensor tuples sharing m, T, B and dtypes; each y
+    [B][2n] is preallocated by the caller.  Returns the list of y."""
+    items = list(items)
+    arr = (GemvItem * len(items))()
+    for k, (packed, scales, x, y) in enumerate(items):
+        arr[k] = GemvItem(packed.data_ptr(), scales.data_ptr(), x.data_ptr(), y.data_ptr(), packed.shape[0])
+    packed0, _, x0, y0 = items[0]
+    _, T, _, q = packed0.shape
+    _check(lib().fairy2i_gemv_grouped(arr, len(items), 4 * q, T, _DTYPE[x0.dtype], x0.shape[0],
+                                      _DTYPE[y0.dtype], algo, _stream(stream)))
+    return [it[3] for it in items]
 
 
 def fairy2i_act_quant(x: torch.Tensor, q=None, delta=None, stream=None):

@@ -36,6 +36,7 @@ SOURCES = {
     "quantize.hip": ["-ffp-contract=off"],
     "gemv_valu.hip": [],
     "gemv_mfma.hip": [],
+    "gemv_i8.hip": [],
     "prefill.hip": ["-ffp-contract=off"],
     "api.cpp": ["-x", "hip"],
 }

@@ -107,24 +107,84 @@ int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t 
     return fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32 or BF16", x_dtype);
   if (y_dtype != FAIRY2I_F32 && y_dtype != FAIRY2I_BF16)
     return fail(FAIRY2I_ERR_DTYPE, "y_dtype %d: need F32 or BF16", y_dtype);
-  if (algo != FAIRY2I_GEMV_AUTO && algo != FAIRY2I_GEMV_VALU && algo != FAIRY2I_GEMV_MFMA)
+  if (algo < FAIRY2I_GEMV_AUTO || algo > FAIRY2I_GEMV_MFMA_I8)
     return fail(FAIRY2I_ERR_DTYPE, "unknown GEMV algorithm %d", algo);
-  if (algo == FAIRY2I_GEMV_MFMA && x_dtype != FAIRY2I_BF16)
-    return fail(FAIRY2I_ERR_DTYPE, "the MFMA GEMV takes bf16 x only");
+  if (algo >= FAIRY2I_GEMV_MFMA && x_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "the MFMA GEMV kernels take bf16 x only");
   if (int s = check_stages(T)) return s;
   if (int s = check_nm(n, m)) return s;
   if (B < 1 || B > 16) return fail(FAIRY2I_ERR_SHAPE, "B = %lld: need 1 <= B <= 16", (long long)B);
+  if (algo == FAIRY2I_GEMV_MFMA_I8 && B > 2)
+    return fail(FAIRY2I_ERR_SHAPE, "B = %lld: the int8 MFMA GEMV takes B <= 2", (long long)B);
   if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(scales, 4))
     return fail(FAIRY2I_ERR_ALIGN, "packed, x and y need 16-byte alignment, scales 4");
-  const bool use_mfma = algo == FAIRY2I_GEMV_MFMA || (algo == FAIRY2I_GEMV_AUTO && x_dtype == FAIRY2I_BF16);
-  if (use_mfma)
+  int kernel = algo;
+  if (kernel == FAIRY2I_GEMV_AUTO) kernel = x_dtype == FAIRY2I_BF16 ? FAIRY2I_GEMV_MFMA : FAIRY2I_GEMV_VALU;
+  if (kernel == FAIRY2I_GEMV_MFMA) kernel = FAIRY2I_GEMV_MFMA_BF16;
+  if (kernel == FAIRY2I_GEMV_MFMA_I8)
+    return hip_status(f2i::launch_gemv_i8(packed, scales, (int)n, (int)m, T, x, (int)B, y,
+                                          y_dtype == FAIRY2I_BF16, stream),
+                      "gemv (int8 mfma) launch");
+  if (kernel == FAIRY2I_GEMV_MFMA_BF16)
     return hip_status(f2i::launch_gemv_mfma(packed, scales, (int)n, (int)m, T, x, (int)B, y,
                                             y_dtype == FAIRY2I_BF16, nullptr, stream),
-                      "gemv (mfma) launch");
+                      "gemv (bf16 mfma) launch");
   return hip_status(f2i::launch_gemv_valu(packed, scales, (int)n, (int)m, T, x,
                                           x_dtype == FAIRY2I_BF16, (int)B, y,
                                           y_dtype == FAIRY2I_BF16, stream),
                     "gemv (valu) launch");
+}
+
+int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, int T, int x_dtype,
+                         int64_t B, int y_dtype, int algo, hipStream_t stream) {
+  if (!items) return fail(FAIRY2I_ERR_NULL, "items is required");
+  if (count < 1) return fail(FAIRY2I_ERR_SHAPE, "count = %d: need at least one item", count);
+  for (int k = 0; k < count; ++k)
+    if (!items[k].packed || !items[k].scales || !items[k].x || !items[k].y)
+      return fail(FAIRY2I_ERR_NULL, "item %d: packed, scales, x and y are required", k);
+  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32 or BF16", x_dtype);
+  if (y_dtype != FAIRY2I_F32 && y_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "y_dtype %d: need F32 or BF16", y_dtype);
+  if (algo < FAIRY2I_GEMV_AUTO || algo > FAIRY2I_GEMV_MFMA_I8)
+    return fail(FAIRY2I_ERR_DTYPE, "unknown GEMV algorithm %d", algo);
+  if (algo >= FAIRY2I_GEMV_MFMA && x_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "the MFMA GEMV kernels take bf16 x only");
+  if (int s = check_stages(T)) return s;
+  for (int k = 0; k < count; ++k)
+    if (int s = check_nm(items[k].n, m)) return s;
+  if (B < 1 || B > 16) return fail(FAIRY2I_ERR_SHAPE, "B = %lld: need 1 <= B <= 16", (long long)B);
+  if (algo == FAIRY2I_GEMV_MFMA_I8 && B > 2)
+    return fail(FAIRY2I_ERR_SHAPE, "B = %lld: the int8 MFMA GEMV takes B <= 2", (long long)B);
+  for (int k = 0; k < count; ++k)
+    if (!aligned(items[k].packed, 16) || !aligned(items[k].x, 16) || !aligned(items[k].y, 16) ||
+        !aligned(items[k].scales, 4))
+      return fail(FAIRY2I_ERR_ALIGN, "item %d: packed, x and y need 16-byte alignment, scales 4", k);
+  const bool grouped = algo == FAIRY2I_GEMV_MFMA_BF16 || algo == FAIRY2I_GEMV_MFMA ||
+                       (algo == FAIRY2I_GEMV_AUTO && x_dtype == FAIRY2I_BF16);
+  if (!grouped) {
+    for (int k = 0; k < count; ++k) {
+      const fairy2i_gemv_item& it = items[k];
+      int s = fairy2i_gemv(it.packed, it.scales, it.n, m, T, it.x, x_dtype, B, it.y, y_dtype, algo, stream);
+      if (s != FAIRY2I_OK) return s;
+    }
+    return ok();
+  }
+  for (int k0 = 0; k0 < count; k0 += f2i::kMaxGroup) {
+    f2i::GemvGroup grp;
+    grp.count = count - k0 < f2i::kMaxGroup ? count - k0 : f2i::kMaxGroup;
+    int tiles = 0;
+    for (int k = 0; k < grp.count; ++k) {
+      const fairy2i_gemv_item& it = items[k0 + k];
+      grp.tile_start[k] = tiles;
+      grp.items[k] = f2i::GemvItem{it.packed, it.scales, it.x, it.y, (int)it.n};
+      tiles += (int)((it.n + 15) / 16);
+    }
+    grp.tile_start[grp.count] = tiles;
+    hipError_t e = f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, y_dtype == FAIRY2I_BF16, stream);
+    if (e != hipSuccess) return hip_status(e, "gemv (grouped bf16 mfma) launch");
+  }
+  return ok();
 }
 
 int fairy2i_act_quant(const void* x, int x_dtype, int64_t N, int64_t two_m, int8_t* q,

@@ -35,6 +35,21 @@ __device__ __forceinline__ void store_out(uint16_t* y, int64_t idx, float v) { y
 
 // ---- internal launchers (host side), implemented in the .hip files ----
 namespace f2i {
+// One GEMV of a grouped launch (all items share m, T, B and the dtypes).
+struct GemvItem {
+  const void* packed;
+  const float* scales;
+  const void* x;
+  void* y;
+  int n;
+};
+constexpr int kMaxGroup = 48;   // items per launch; the table travels in the kernel arguments
+struct GemvGroup {
+  int count;
+  int tile_start[kMaxGroup + 1];   // first 16-row tile of each item; [count] = total tiles
+  GemvItem items[kMaxGroup];
+};
+hipError_t launch_gemv_mfma_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
 hipError_t launch_quantize(const float* R, int n, int m, int T, uint8_t* packed, float* scales,
                            double* scales64, uint8_t* codes, hipStream_t s);
 hipError_t launch_pack(const uint8_t* codes, int n, int m, int T, uint8_t* packed, hipStream_t s);
@@ -42,6 +57,8 @@ hipError_t launch_gemv_valu(const uint8_t* packed, const float* scales, int n, i
                             const void* x, int x_bf16, int B, void* y, int y_bf16, hipStream_t s);
 hipError_t launch_gemv_mfma(const uint8_t* packed, const float* scales, int n, int m, int T,
                             const void* x, int B, void* y, int y_bf16, void* unused, hipStream_t s);
+hipError_t launch_gemv_i8(const uint8_t* packed, const float* scales, int n, int m, int T,
+                          const void* x, int B, void* y, int y_bf16, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int x_bf16, int N, int two_m, int8_t* q, float* delta,
                             hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* scales, int n, int m, int T,
