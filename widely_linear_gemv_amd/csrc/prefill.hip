@@ -8,11 +8,11 @@
 // cores, and its rounding is fixed exactly (see the header).
 //
 // GEMM: output rows are (complex row i, stage t, matrix M, plane), output columns are
-// (token, component a = Re x or b = Im x).  Each wave owns 16 complex rows and 8*NF tokens.
-// Per 64-column step a lane reads one 32-bit code word per (t, M) -- 16 codes of its row --
-// spreads the codes into bytes with a shift and a mask (the packed layout puts codes
-// b, b+4, b+8, b+12 in byte b), and maps each byte through a 4-entry table with v_perm_b32
-// into the int8 planes B_re and B_im.  Each plane and 16-column activation fragment feeds one
+// (token, component a = Re x or b = Im x).  A workgroup owns 16 complex rows and 8 waves of 8*NF
+// tokens.  Per 64-column step the workgroup decodes the tile's code words once: a shift and a
+// mask spread four codes into four bytes (the packed layout puts codes b, b+4, b+8, b+12 in
+// byte b) and v_perm_b32 maps each byte through a 4-entry table into the int8 planes B_re and
+// B_im, written to LDS.  Each plane fragment and 16-column activation fragment feeds one
 // v_mfma_i32_16x16x64_i8; every sum is exact in int32 (|P| <= 127 m).  The epilogue applies
 // the fp32 scales once per accumulated sum and the token's delta once per output.
 #include "common.hpp"
@@ -91,41 +91,70 @@ hipError_t launch_act_quant(const void* x, int x_bf16, int N, int two_m, int8_t*
 
 // ----------------------------------------------------------------------- GEMM ----
 
-// 16 codes (one packed word) -> int8 planes B_re and B_im in column order.
-__device__ __forceinline__ void decode_planes(uint32_t D, v4i& re, v4i& im) {
-  constexpr uint32_t lo2 = 0x03030303u;
-  constexpr uint32_t kRe = 0x00FF0001u;   // code 0 -> +1, 1 -> 0, 2 -> -1, 3 -> 0
-  constexpr uint32_t kIm = 0xFF000100u;   // code 0 -> 0, 1 -> +1, 2 -> 0, 3 -> -1
-  const uint32_t k0 = D & lo2, k1 = (D >> 2) & lo2, k2 = (D >> 4) & lo2, k3 = (D >> 6) & lo2;
-  re = v4i{(int)__builtin_amdgcn_perm(0u, kRe, k0), (int)__builtin_amdgcn_perm(0u, kRe, k1),
-           (int)__builtin_amdgcn_perm(0u, kRe, k2), (int)__builtin_amdgcn_perm(0u, kRe, k3)};
-  im = v4i{(int)__builtin_amdgcn_perm(0u, kIm, k0), (int)__builtin_amdgcn_perm(0u, kIm, k1),
-           (int)__builtin_amdgcn_perm(0u, kIm, k2), (int)__builtin_amdgcn_perm(0u, kIm, k3)};
-}
-
 enum { kOutF32 = 0, kOutBF16 = 1, kOutRaw = 2 };
 
-// Workgroup = 4 waves = 2 row blocks x 2 token blocks (16 complex rows x 8*NF tokens each).
+constexpr int kGemmWaves = 8;      // waves per workgroup, each with its own 8*NF tokens
+
+// Workgroup = 16 complex rows x (8 waves x 8*NF tokens).  Per 64-column step the workgroup
+// decodes the tile's codes once -- one half word (8 codes) per thread -- into int8 planes in a
+// double-buffered LDS tile [plane = (t, M, re/im)][row][64]; every wave then reads the 4T plane
+// fragments from LDS and multiplies them with its own activation fragments (prefetched one
+// step ahead from global memory), NF column fragments per plane fragment.
 template <int TT, int NF, int MODE>
-__global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ packed,
-                                              const float* __restrict__ scales, int n, int m,
-                                              const int8_t* __restrict__ q,
-                                              const float* __restrict__ delta, int N,
-                                              void* __restrict__ yv) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restrict__ packed,
+                                                          const float* __restrict__ scales, int n, int m,
+                                                          const int8_t* __restrict__ q,
+                                                          const float* __restrict__ delta, int N,
+                                                          void* __restrict__ yv) {
+  constexpr int kPlanes = TT * 4;                  // (t, M, re/im)
+  constexpr int KS = 2;                            // 64-column MFMA sub-steps per pipeline step
+  __shared__ __align__(16) int8_t s_a[2][kPlanes][16][64 * KS];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int r = lane & 15;          // A row / B column inside a 16x16 tile
   const int g = lane >> 4;          // 16-column group of the 64-column step
-  const int i0 = (blockIdx.x * 2 + (wave & 1)) * 16;
-  const int tok0 = (blockIdx.y * 2 + (wave >> 1)) * (8 * NF);
-  if (i0 >= n || tok0 >= N) return;   // whole wave; no workgroup barrier below
-
+  const int i0 = blockIdx.x * 16;
+  const int tok0 = (blockIdx.y * kGemmWaves + wave) * (8 * NF);
   const int dw_plane = m / 16;
-  const int ia = i0 + r;
-  const bool a_ok = ia < n;
-  const uint32_t* __restrict__ arow =
-      reinterpret_cast<const uint32_t*>(packed) + (int64_t)(a_ok ? ia : 0) * (TT * 2 * dw_plane);
   const int64_t two_m = 2 * (int64_t)m;
+  const int ksteps = (m + 64 * KS - 1) / (64 * KS);   // a partial last step is zero-filled
+
+  // decode assignment: half word h = ((row * 2T + tm) * 4KS + wq) * 2 + hh
+  constexpr int kHalves = 16 * TT * 2 * 4 * KS * 2;
+  constexpr int kPerThread = (kHalves + 64 * kGemmWaves - 1) / (64 * kGemmWaves);
+  const uint32_t* __restrict__ words = reinterpret_cast<const uint32_t*>(packed);
+  uint32_t wreg[kPerThread];
+  auto load_words = [&](int kk) {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int h = tid + u * 64 * kGemmWaves;
+      const int rr = h / (TT * 2 * 8 * KS), tm = (h / (8 * KS)) % (TT * 2), wq = (h / 2) % (4 * KS);
+      const int i = i0 + rr;
+      const int word = 4 * KS * kk + wq;
+      wreg[u] = (h < kHalves && i < n && word < dw_plane)
+          ? words[(int64_t)i * (TT * 2 * dw_plane) + tm * dw_plane + word] : 0u;
+    }
+  };
+  auto decode_to_lds = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int h = tid + u * 64 * kGemmWaves;
+      if (h >= kHalves) continue;
+      const int rr = h / (TT * 2 * 8 * KS), tm = (h / (8 * KS)) % (TT * 2), wq = (h / 2) % (4 * KS), hh = h % 2;
+      constexpr uint32_t lo2 = 0x03030303u;
+      constexpr uint32_t kRe = 0x00FF0001u;   // code 0 -> +1, 1 -> 0, 2 -> -1, 3 -> 0
+      constexpr uint32_t kIm = 0xFF000100u;   // code 0 -> 0, 1 -> +1, 2 -> 0, 3 -> -1
+      const uint32_t w = wreg[u];
+      const uint32_t ka = (w >> (4 * hh)) & lo2;        // codes 16wq + 8hh + 0..3
+      const uint32_t kb = (w >> (4 * hh + 2)) & lo2;    // codes 16wq + 8hh + 4..7
+      const int col = 16 * wq + 8 * hh;
+      *reinterpret_cast<uint2*>(&s_a[buf][tm * 2 + 0][rr][col]) =
+          make_uint2(__builtin_amdgcn_perm(0u, kRe, ka), __builtin_amdgcn_perm(0u, kRe, kb));
+      *reinterpret_cast<uint2*>(&s_a[buf][tm * 2 + 1][rr][col]) =
+          make_uint2(__builtin_amdgcn_perm(0u, kIm, ka), __builtin_amdgcn_perm(0u, kIm, kb));
+    }
+  };
 
   const int8_t* bptr[NF];
   bool b_ok[NF];
@@ -135,45 +164,53 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ packed
     b_ok[f] = tok < N;
     bptr[f] = q + (int64_t)(b_ok[f] ? tok : 0) * two_m + (r & 1) * (int64_t)m + 16 * g;
   }
-
-  v4i acc[TT][2][2][NF];
+  v4i bcur[KS][NF], bnxt[KS][NF];
+  auto load_b = [&](int kk, v4i (&b)[KS][NF]) {
 #pragma unroll
-  for (int t = 0; t < TT; ++t)
+    for (int u = 0; u < KS; ++u)
 #pragma unroll
-    for (int M = 0; M < 2; ++M)
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int f = 0; f < NF; ++f) acc[t][M][p][f] = v4i{0, 0, 0, 0};
-
-  const int ksteps = m / 64;
-  for (int kk = 0; kk < ksteps; ++kk) {
-    v4i A[TT][2][2];
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-      for (int M = 0; M < 2; ++M) {
-        const uint32_t D = a_ok ? arow[(t * 2 + M) * dw_plane + 4 * kk + g] : 0u;
-        decode_planes(D, A[t][M][0], A[t][M][1]);
+      for (int f = 0; f < NF; ++f) {
+        const int col = 64 * (KS * kk + u);
+        b[u][f] = (b_ok[f] && col < m) ? *reinterpret_cast<const v4i*>(bptr[f] + col) : v4i{0, 0, 0, 0};
       }
-    v4i Bf[NF];
+  };
+
+  v4i acc[kPlanes][NF];
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-      Bf[f] = b_ok[f] ? *reinterpret_cast<const v4i*>(bptr[f] + 64 * kk) : v4i{0, 0, 0, 0};
+  for (int p = 0; p < kPlanes; ++p)
 #pragma unroll
-    for (int t = 0; t < TT; ++t)
+    for (int f = 0; f < NF; ++f) acc[p][f] = v4i{0, 0, 0, 0};
+
+  load_words(0);
+  load_b(0, bcur);
+  decode_to_lds(0);
+  __syncthreads();
+  for (int kk = 0; kk < ksteps; ++kk) {
+    const int buf = kk & 1;
+    const bool more = kk + 1 < ksteps;
+    if (more) { load_words(kk + 1); load_b(kk + 1, bnxt); }
 #pragma unroll
-      for (int M = 0; M < 2; ++M)
+    for (int u = 0; u < KS; ++u)
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+      for (int p = 0; p < kPlanes; ++p) {
+        const v4i a = *reinterpret_cast<const v4i*>(&s_a[buf][p][r][64 * u + 16 * g]);
 #pragma unroll
-          for (int f = 0; f < NF; ++f)
-            acc[t][M][p][f] =
-                __builtin_amdgcn_mfma_i32_16x16x64_i8(A[t][M][p], Bf[f], acc[t][M][p][f], 0, 0, 0);
+        for (int f = 0; f < NF; ++f)
+          acc[p][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bcur[u][f], acc[p][f], 0, 0, 0);
+      }
+    if (more) {
+      decode_to_lds(buf ^ 1);
+#pragma unroll
+      for (int u = 0; u < KS; ++u)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) bcur[u][f] = bnxt[u][f];
+    }
+    __syncthreads();
   }
 
-  // C layout of a 16x16 tile: lane holds rows 4g..4g+3 of column r.
+  // C layout of a 16x16 tile: lane holds rows 4g..4g+3 of column r.  Plane index p = (t*2+M)*2+re/im.
   const int comp = r & 1;
+  if (tok0 >= N) return;
   if constexpr (MODE == kOutRaw) {
     int* __restrict__ P = static_cast<int*>(yv);
 #pragma unroll
@@ -181,18 +218,12 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ packed
       const int tok = tok0 + 8 * f + (r >> 1);
       if (!b_ok[f]) continue;
 #pragma unroll
-      for (int t = 0; t < TT; ++t)
+      for (int p = 0; p < kPlanes; ++p)
 #pragma unroll
-        for (int M = 0; M < 2; ++M)
-#pragma unroll
-          for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = i0 + 4 * g + e;
-              if (i < n)
-                P[((((int64_t)(t * 2 + M) * 2 + p) * 2 + comp) * N + tok) * n + i] =
-                    acc[t][M][p][f][e];
-            }
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + 4 * g + e;
+          if (i < n) P[(((int64_t)p * 2 + comp) * N + tok) * n + i] = acc[p][f][e];
+        }
     }
   } else {
     const int64_t ys = 2 * (int64_t)n;
@@ -213,8 +244,8 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ packed
         float vre = 0.f, vim = 0.f;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-          const float PUr = (float)acc[t][0][0][f][e], PUi = (float)acc[t][0][1][f][e];
-          const float PWr = (float)acc[t][1][0][f][e], PWi = (float)acc[t][1][1][f][e];
+          const float PUr = (float)acc[(t * 2 + 0) * 2 + 0][f][e], PUi = (float)acc[(t * 2 + 0) * 2 + 1][f][e];
+          const float PWr = (float)acc[(t * 2 + 1) * 2 + 0][f][e], PWi = (float)acc[(t * 2 + 1) * 2 + 1][f][e];
           if (comp == 0) {   // column a = Re x
             vre += s[t][0][0] * PUr + s[t][1][0] * PWr;
             vim += s[t][0][1] * PUi + s[t][1][1] * PWi;
@@ -248,7 +279,8 @@ static void launch_gemm_t(const uint8_t* packed, const float* scales, int n, int
                           const int8_t* q, const float* delta, int N, void* y, int mode,
                           hipStream_t s) {
   constexpr int NF = TT <= 2 ? 4 : 2;
-  const dim3 grid((n + 31) / 32, (N + 16 * NF - 1) / (16 * NF)), block(256);
+  constexpr int tok_per_wg = kGemmWaves * 8 * NF;
+  const dim3 grid((n + 15) / 16, (N + tok_per_wg - 1) / tok_per_wg), block(64 * kGemmWaves);
   if (mode == kOutF32)
     hipLaunchKernelGGL((k_gemm<TT, NF, kOutF32>), grid, block, 0, s, packed, scales, n, m, q, delta, N, y);
   else if (mode == kOutBF16)
