@@ -95,11 +95,23 @@ enum { kOutF32 = 0, kOutBF16 = 1, kOutRaw = 2 };
 
 constexpr int kGemmWaves = 8;      // waves per workgroup, each with its own 8*NF tokens
 
-// Workgroup = 16 complex rows x (8 waves x 8*NF tokens).  Per 64-column step the workgroup
+// Workgroup = 16 complex rows x (8 waves x 8*NF tokens).  Per 128-column step the workgroup
 // decodes the tile's codes once -- one half word (8 codes) per thread -- into int8 planes in a
-// double-buffered LDS tile [plane = (t, M, re/im)][row][64]; every wave then reads the 4T plane
-// fragments from LDS and multiplies them with its own activation fragments (prefetched one
-// step ahead from global memory), NF column fragments per plane fragment.
+// double-buffered LDS tile [plane = (t, M, re/im)][row][128 + pad]; every wave then reads the
+// 4T plane fragments from LDS (one read ahead of the MFMAs that use it) and multiplies them with
+// its own activation fragments, which are loaded from global memory one step ahead into a
+// ping-pong register pair, NF column fragments per plane fragment.
+//
+// No load is predicated: codes and activations are read through buffer resources sized to the
+// rows and tokens that exist, so reads past n or N return 0 (and those outputs are never stored);
+// columns past m (at most one 64-column half of the last step) get zero planes from the decoder,
+// so whatever activations sit there add nothing.
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end return 0.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFFF0);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+
 template <int TT, int NF, int MODE>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restrict__ packed,
                                                           const float* __restrict__ scales, int n, int m,
@@ -108,71 +120,72 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
                                                           void* __restrict__ yv) {
   constexpr int kPlanes = TT * 4;                  // (t, M, re/im)
   constexpr int KS = 2;                            // 64-column MFMA sub-steps per pipeline step
-  __shared__ __align__(16) int8_t s_a[2][kPlanes][16][64 * KS];
+  constexpr int kRow = 64 * KS + 16;               // LDS row pitch: 16 pad bytes spread the rows over the banks
+  __shared__ __align__(16) int8_t s_a[2][kPlanes][16][kRow];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: keeps the buffer resources scalar
   const int r = lane & 15;          // A row / B column inside a 16x16 tile
   const int g = lane >> 4;          // 16-column group of the 64-column step
   const int i0 = blockIdx.x * 16;
   const int tok0 = (blockIdx.y * kGemmWaves + wave) * (8 * NF);
   const int dw_plane = m / 16;
   const int64_t two_m = 2 * (int64_t)m;
-  const int ksteps = (m + 64 * KS - 1) / (64 * KS);   // a partial last step is zero-filled
+  const int ksteps = (m + 64 * KS - 1) / (64 * KS);
 
-  // decode assignment: half word h = ((row * 2T + tm) * 4KS + wq) * 2 + hh
+  // decode assignment: half word h = ((row * 2T + tm) * 4KS + wq) * 2 + hh.  The tile's code
+  // words are read through a buffer resource over this workgroup's rows, so rows past n read 0.
   constexpr int kHalves = 16 * TT * 2 * 4 * KS * 2;
   constexpr int kPerThread = (kHalves + 64 * kGemmWaves - 1) / (64 * kGemmWaves);
-  const uint32_t* __restrict__ words = reinterpret_cast<const uint32_t*>(packed);
+  const int64_t row_bytes = (int64_t)TT * 2 * dw_plane * 4;
+  const __amdgpu_buffer_rsrc_t rsrc_w = make_rsrc(packed + (int64_t)i0 * row_bytes, (int64_t)(n - i0) * row_bytes);
+  int voff_w[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int h = min(tid + u * 64 * kGemmWaves, kHalves - 1);
+    const int rr = h / (TT * 2 * 8 * KS), tm = (h / (8 * KS)) % (TT * 2), wq = (h / 2) % (4 * KS);
+    voff_w[u] = (int)(rr * row_bytes) + (tm * dw_plane + wq) * 4;
+  }
   uint32_t wreg[kPerThread];
   auto load_words = [&](int kk) {
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int h = tid + u * 64 * kGemmWaves;
-      const int rr = h / (TT * 2 * 8 * KS), tm = (h / (8 * KS)) % (TT * 2), wq = (h / 2) % (4 * KS);
-      const int i = i0 + rr;
-      const int word = 4 * KS * kk + wq;
-      wreg[u] = (h < kHalves && i < n && word < dw_plane)
-          ? words[(int64_t)i * (TT * 2 * dw_plane) + tm * dw_plane + word] : 0u;
-    }
+    for (int u = 0; u < kPerThread; ++u)
+      wreg[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_w, voff_w[u] + 16 * KS * kk, 0, 0);
   };
-  auto decode_to_lds = [&](int buf) {
+  auto decode_to_lds = [&](int buf, int kk) {
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
       const int h = tid + u * 64 * kGemmWaves;
-      if (h >= kHalves) continue;
+      if (kHalves % (64 * kGemmWaves) != 0 && h >= kHalves) continue;
       const int rr = h / (TT * 2 * 8 * KS), tm = (h / (8 * KS)) % (TT * 2), wq = (h / 2) % (4 * KS), hh = h % 2;
       constexpr uint32_t lo2 = 0x03030303u;
       constexpr uint32_t kRe = 0x00FF0001u;   // code 0 -> +1, 1 -> 0, 2 -> -1, 3 -> 0
       constexpr uint32_t kIm = 0xFF000100u;   // code 0 -> 0, 1 -> +1, 2 -> 0, 3 -> -1
+      const bool in_m = 4 * KS * kk + wq < dw_plane;
       const uint32_t w = wreg[u];
       const uint32_t ka = (w >> (4 * hh)) & lo2;        // codes 16wq + 8hh + 0..3
       const uint32_t kb = (w >> (4 * hh + 2)) & lo2;    // codes 16wq + 8hh + 4..7
       const int col = 16 * wq + 8 * hh;
-      *reinterpret_cast<uint2*>(&s_a[buf][tm * 2 + 0][rr][col]) =
-          make_uint2(__builtin_amdgcn_perm(0u, kRe, ka), __builtin_amdgcn_perm(0u, kRe, kb));
-      *reinterpret_cast<uint2*>(&s_a[buf][tm * 2 + 1][rr][col]) =
-          make_uint2(__builtin_amdgcn_perm(0u, kIm, ka), __builtin_amdgcn_perm(0u, kIm, kb));
+      uint2 re = make_uint2(__builtin_amdgcn_perm(0u, kRe, ka), __builtin_amdgcn_perm(0u, kRe, kb));
+      uint2 im = make_uint2(__builtin_amdgcn_perm(0u, kIm, ka), __builtin_amdgcn_perm(0u, kIm, kb));
+      if (!in_m) re = im = make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(&s_a[buf][tm * 2 + 0][rr][col]) = re;
+      *reinterpret_cast<uint2*>(&s_a[buf][tm * 2 + 1][rr][col]) = im;
     }
   };
 
-  const int8_t* bptr[NF];
-  bool b_ok[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int tok = tok0 + 8 * f + (r >> 1);
-    b_ok[f] = tok < N;
-    bptr[f] = q + (int64_t)(b_ok[f] ? tok : 0) * two_m + (r & 1) * (int64_t)m + 16 * g;
-  }
-  v4i bcur[KS][NF], bnxt[KS][NF];
+  // Activations: one buffer resource over this wave's tokens, so tokens past N read 0.  Lane
+  // (r, g) reads 16 columns 16g.. of component r&1 of token 8f + r/2.
+  const __amdgpu_buffer_rsrc_t rsrc_q =
+      make_rsrc(q + (int64_t)min(tok0, N) * two_m, (int64_t)max(N - tok0, 0) * two_m);
+  const int voff_q = (int)((r >> 1) * two_m + (r & 1) * m + 16 * g);
   auto load_b = [&](int kk, v4i (&b)[KS][NF]) {
 #pragma unroll
     for (int u = 0; u < KS; ++u)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int col = 64 * (KS * kk + u);
-        b[u][f] = (b_ok[f] && col < m) ? *reinterpret_cast<const v4i*>(bptr[f] + col) : v4i{0, 0, 0, 0};
-      }
+      for (int f = 0; f < NF; ++f)
+        b[u][f] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                      rsrc_q, voff_q + (int)(8 * f * two_m) + 64 * (KS * kk + u), 0, 0));
   };
 
   v4i acc[kPlanes][NF];
@@ -181,32 +194,49 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[p][f] = v4i{0, 0, 0, 0};
 
-  load_words(0);
-  load_b(0, bcur);
-  decode_to_lds(0);
-  __syncthreads();
-  for (int kk = 0; kk < ksteps; ++kk) {
-    const int buf = kk & 1;
-    const bool more = kk + 1 < ksteps;
-    if (more) { load_words(kk + 1); load_b(kk + 1, bnxt); }
+  // One pipeline step on LDS buffer `buf`: prefetch the next step's codes and activations,
+  // multiply this step, decode the next step into the other buffer, then one barrier.  The
+  // prefetch and decode run unconditionally (the last step reloads in-range data and decodes
+  // zero planes nobody reads), so every path into a step has the same loads in flight and the
+  // compiler's load counters wait only for this step's operands.
+  auto step = [&](int kk, int buf, v4i (&bc)[KS][NF], v4i (&bn)[KS][NF]) {
+    const int kn = min(kk + 1, ksteps - 1);
+    load_words(kn);
+    load_b(kn, bn);
+    v4i a = *reinterpret_cast<const v4i*>(&s_a[buf][0][r][16 * g]);
 #pragma unroll
-    for (int u = 0; u < KS; ++u)
+    for (int x = 0; x < KS * kPlanes; ++x) {
+      const int u = x / kPlanes, p = x % kPlanes;
+      const int xn = x + 1 < KS * kPlanes ? x + 1 : x;
+      const v4i an = *reinterpret_cast<const v4i*>(&s_a[buf][xn % kPlanes][r][64 * (xn / kPlanes) + 16 * g]);
+      // keep the next fragment's LDS read in flight under these MFMAs (the scheduler would
+      // otherwise sink it to its use and expose the LDS latency once per plane)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int p = 0; p < kPlanes; ++p) {
-        const v4i a = *reinterpret_cast<const v4i*>(&s_a[buf][p][r][64 * u + 16 * g]);
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-          acc[p][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bcur[u][f], acc[p][f], 0, 0, 0);
-      }
-    if (more) {
-      decode_to_lds(buf ^ 1);
-#pragma unroll
-      for (int u = 0; u < KS; ++u)
-#pragma unroll
-        for (int f = 0; f < NF; ++f) bcur[u][f] = bnxt[u][f];
+      for (int f = 0; f < NF; ++f)
+        acc[p][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bc[u][f], acc[p][f], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      a = an;
     }
+    decode_to_lds(buf ^ 1, kk + 1);
     __syncthreads();
+  };
+
+  v4i b0[KS][NF], b1[KS][NF];
+  load_words(0);
+  load_b(0, b0);
+  decode_to_lds(0, 0);
+  __syncthreads();
+  int kk = 0;
+  for (; kk + 1 < ksteps; kk += 2) {
+    step(kk, 0, b0, b1);
+    step(kk + 1, 1, b1, b0);
   }
+  if (kk < ksteps) step(kk, 0, b0, b1);
+
+  bool b_ok[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) b_ok[f] = tok0 + 8 * f + (r >> 1) < N;
 
   // C layout of a 16x16 tile: lane holds rows 4g..4g+3 of column r.  Plane index p = (t*2+M)*2+re/im.
   const int comp = r & 1;
