@@ -96,7 +96,7 @@ def test_prefill_quantized_attention_layer():
 
 
 @pytest.mark.parametrize("n,m,T,N", [(1, 64, 1, 1), (17, 192, 2, 7), (33, 128, 3, 40), (5, 320, 4, 33),
-                                     (48, 256, 2, 64)])
+                                     (48, 256, 2, 64), (20, 448, 1, 65), (100, 320, 3, 300)])
 def test_prefill_ragged(n, m, T, N):
     dev = device()
     codes = workloads.random_codes(T, n, m, seed=n + m + N)
