@@ -93,7 +93,8 @@ hipError_t launch_act_quant(const void* x, int x_bf16, int N, int two_m, int8_t*
 
 enum { kOutF32 = 0, kOutBF16 = 1, kOutRaw = 2 };
 
-constexpr int kGemmWaves = 8;      // waves per workgroup, each with its own 8*NF tokens
+constexpr int kGemmWaves = 8;      // waves per workgroup (two per SIMD), each with its own 8*NF tokens
+constexpr int kAhead = 3;          // plane fragments read from LDS ahead of their MFMAs
 
 // Workgroup = 16 complex rows x (8 waves x 8*NF tokens).  Per 128-column step the workgroup
 // decodes the tile's codes once -- one half word (8 codes) per thread -- into int8 planes in a
@@ -179,13 +180,12 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
   const __amdgpu_buffer_rsrc_t rsrc_q =
       make_rsrc(q + (int64_t)min(tok0, N) * two_m, (int64_t)max(N - tok0, 0) * two_m);
   const int voff_q = (int)((r >> 1) * two_m + (r & 1) * m + 16 * g);
-  auto load_b = [&](int kk, v4i (&b)[KS][NF]) {
+  // B fragments of 64-column sub-step j (= KS * step + u) into one register slot.
+  auto load_b = [&](int j, v4i (&b)[NF]) {
 #pragma unroll
-    for (int u = 0; u < KS; ++u)
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        b[u][f] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                      rsrc_q, voff_q + (int)(8 * f * two_m) + 64 * (KS * kk + u), 0, 0));
+    for (int f = 0; f < NF; ++f)
+      b[f] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                 rsrc_q, voff_q + (int)(8 * f * two_m) + 64 * j, 0, 0));
   };
 
   v4i acc[kPlanes][NF];
@@ -194,45 +194,53 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[p][f] = v4i{0, 0, 0, 0};
 
-  // One pipeline step on LDS buffer `buf`: prefetch the next step's codes and activations,
-  // multiply this step, decode the next step into the other buffer, then one barrier.  The
-  // prefetch and decode run unconditionally (the last step reloads in-range data and decodes
-  // zero planes nobody reads), so every path into a step has the same loads in flight and the
-  // compiler's load counters wait only for this step's operands.
-  auto step = [&](int kk, int buf, v4i (&bc)[KS][NF], v4i (&bn)[KS][NF]) {
+  // One pipeline step (KS = 2 sub-steps of 64 columns) on LDS buffer `buf`.  Activations use
+  // two register slots, one per sub-step, each loaded one sub-step ahead of its MFMAs; the next
+  // step's code words are loaded at the top and decoded into the other LDS buffer at the end,
+  // followed by the step's one barrier.  Loads and decode run unconditionally (the last step
+  // reloads in-range data and decodes zero planes nobody reads), so every path into a step has
+  // the same loads in flight and the compiler's load counters wait only for the operands due.
+  static_assert(KS == 2, "two activation slots, one per sub-step");
+  v4i b0[NF], b1[NF];
+  auto step = [&](int kk, int buf) {
     const int kn = min(kk + 1, ksteps - 1);
+    load_b(KS * kk + 1, b1);
     load_words(kn);
-    load_b(kn, bn);
-    v4i a = *reinterpret_cast<const v4i*>(&s_a[buf][0][r][16 * g]);
+    // Plane fragments x = (u, p) are read kAhead fragments ahead of the MFMAs that use them; the
+    // scheduling barriers keep those LDS reads in flight under the MFMAs (the scheduler would
+    // otherwise sink each read to its use and expose the LDS latency once per fragment).
+    constexpr int NX = KS * kPlanes;
+    auto lds_a = [&](int x) {
+      return *reinterpret_cast<const v4i*>(&s_a[buf][x % kPlanes][r][64 * (x / kPlanes) + 16 * g]);
+    };
+    v4i a[kAhead + 1];
 #pragma unroll
-    for (int x = 0; x < KS * kPlanes; ++x) {
+    for (int x = 0; x < kAhead; ++x) a[x] = lds_a(x);
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
       const int u = x / kPlanes, p = x % kPlanes;
-      const int xn = x + 1 < KS * kPlanes ? x + 1 : x;
-      const v4i an = *reinterpret_cast<const v4i*>(&s_a[buf][xn % kPlanes][r][64 * (xn / kPlanes) + 16 * g]);
-      // keep the next fragment's LDS read in flight under these MFMAs (the scheduler would
-      // otherwise sink it to its use and expose the LDS latency once per plane)
+      if (x == kPlanes) load_b(KS * kn, b0);   // sub-step 0 of the next step, under sub-step 1
+      if (x + kAhead < NX) a[(x + kAhead) % (kAhead + 1)] = lds_a(x + kAhead);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int f = 0; f < NF; ++f)
-        acc[p][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bc[u][f], acc[p][f], 0, 0, 0);
+        acc[p][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[x % (kAhead + 1)], u == 0 ? b0[f] : b1[f], acc[p][f], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      a = an;
     }
     decode_to_lds(buf ^ 1, kk + 1);
     __syncthreads();
   };
 
-  v4i b0[KS][NF], b1[KS][NF];
   load_words(0);
   load_b(0, b0);
   decode_to_lds(0, 0);
   __syncthreads();
   int kk = 0;
   for (; kk + 1 < ksteps; kk += 2) {
-    step(kk, 0, b0, b1);
-    step(kk + 1, 1, b1, b0);
+    step(kk, 0);
+    step(kk + 1, 1);
   }
-  if (kk < ksteps) step(kk, 0, b0, b1);
+  if (kk < ksteps) step(kk, 0);
 
   bool b_ok[NF];
 #pragma unroll
@@ -330,7 +338,7 @@ template <int TT>
 static void launch_gemm_t(const uint8_t* packed, const float* scales, int n, int m,
                           const int8_t* q, const float* delta, int N, void* y, int mode,
                           hipStream_t s) {
-  constexpr int NF = TT <= 2 ? 4 : 2;
+  constexpr int NF = TT <= 2 ? 4 : 2;   // accumulators: 4T planes x NF fragments x 4 registers
   constexpr int tok_per_wg = kGemmWaves * 8 * NF;
   const dim3 grid((n + 15) / 16, (N + tok_per_wg - 1) / tok_per_wg), block(64 * kGemmWaves);
   if (mode == kOutF32)
