@@ -49,6 +49,18 @@ def pack_bytes():
     return [tuple(int(v) for v in s.split()) for s in lines("pack_bytes.txt")]
 
 
+def pack_tile_order():
+    """-> (total bytes, [(t, M, i, j, byte offset, bit shift)]) for n = 20, m = 320, T = 2."""
+    total, rows = None, []
+    for s in lines("pack_tile_order.txt"):
+        f = s.split()
+        if f[0] == "total":
+            total = int(f[1])
+        else:
+            rows.append(tuple(int(v) for v in f))
+    return total, rows
+
+
 def storage_bits():
     return [tuple(int(v) for v in s.split()) for s in lines("storage_bits.txt")]
 

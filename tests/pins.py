@@ -243,31 +243,51 @@ def check_empty_axis(quantize, unsplit):
 
 # ----------------------------------------------------------------- pack ----
 
-def check_pack_golden(pack, unpack):
+def check_pack_golden(pack_words):
+    """Word encoding: 16 codes -> one little-endian 32-bit word, hand-worked bytes."""
     rows = golden_io.pack_bytes()
     codes = np.array([r[:16] for r in rows], dtype=np.uint8).reshape(1, 1, len(rows), 16)
     codes = np.concatenate([codes, codes], axis=1)           # U and W
-    p = pack(codes)
-    assert p.shape == (len(rows), 1, 2, 4)
+    w = np.asarray(pack_words(codes))
+    assert w.shape == (1, 2, len(rows), 1)
     for i, r in enumerate(rows):
-        assert [int(v) for v in p[i, 0, 0]] == list(r[16:]), (i, p[i, 0, 0])
-        assert [int(v) for v in p[i, 0, 1]] == list(r[16:])
-    assert np.array_equal(unpack(p), codes)
+        for M in range(2):
+            b = [(int(w[0, M, i, 0]) >> (8 * k)) & 255 for k in range(4)]
+            assert b == list(r[16:]), (i, M, b)
+
+
+def check_pack_tile_order(pack, unpack):
+    """Word order: a single nonzero code lands on the hand-worked byte and bit (n = 20,
+    m = 320, T = 2: two row tiles, the second padded; a full and a one-group chunk)."""
+    total, rows = golden_io.pack_tile_order()
+    for t, M, i, j, off, sh in rows:
+        for v in (1, 2, 3):
+            codes = np.zeros((2, 2, 20, 320), dtype=np.uint8)
+            codes[t, M, i, j] = v
+            p = np.asarray(pack(codes))
+            assert p.size == total
+            nz = np.flatnonzero(p)
+            assert list(nz) == [off], (t, M, i, j, list(nz[:4]))
+            assert int(p[off]) == v << sh, (t, M, i, j, int(p[off]))
+            assert np.array_equal(unpack(p, 20, 320, 2), codes)
 
 
 def check_pack_roundtrip(pack, unpack, packed_nbytes, seed=7):
     rng = np.random.default_rng(seed)
-    for T, n, m in ((1, 3, 64), (2, 5, 128), (3, 2, 256), (4, 1, 16)):
+    for T, n, m in ((1, 3, 64), (2, 5, 128), (3, 2, 320), (4, 17, 192), (2, 32, 1024), (1, 16, 256)):
         c = rng.integers(0, 4, size=(T, 2, n, m), dtype=np.uint8)
         p = pack(c)
         assert p.nbytes == packed_nbytes(n, m, T)
-        assert np.array_equal(unpack(p), c)
+        assert np.array_equal(unpack(p, n, m, T), c)
+        # padding rows of the last tile hold code 0: n rows of codes and nothing else is nonzero
+        ones = pack(np.ones_like(c))
+        assert int(np.unpackbits(ones).sum()) == T * 2 * n * m
 
 
 def check_storage_bits(pack):
     """Packed bytes per real parameter of R equal the pages' bit budget."""
     for T, bits in golden_io.storage_bits():
-        n, m = 8, 64
+        n, m = 16, 64
         p = pack(np.zeros((T, 2, n, m), dtype=np.uint8))
         real_params = (2 * n) * (2 * m)
         assert 8 * p.nbytes / real_params == bits

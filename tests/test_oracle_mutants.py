@@ -109,24 +109,50 @@ def test_scale_wrong_component_caught(monkeypatch):
 
 
 def test_pack_consecutive_codes_per_byte_caught():
-    def bad_pack(codes):
+    def bad_words(codes):
         T, _, n, m = codes.shape
-        out = np.zeros((n, T, 2, m // 4), dtype=np.uint8)
-        for t in range(T):
-            for M in range(2):
-                c = codes[t, M].astype(np.uint32).reshape(n, m // 4, 4)
-                out[:, t, M] = (c[..., 0] | c[..., 1] << 2 | c[..., 2] << 4 | c[..., 3] << 6).astype(np.uint8)
-        return out
-    fails(pins.check_pack_golden, bad_pack, oracle.unpack)
+        c = codes.astype(np.uint32).reshape(T, 2, n, m // 16, 4, 4)    # [word][byte][pair]: 4 in a row
+        byte = c[..., 0] | c[..., 1] << 2 | c[..., 2] << 4 | c[..., 3] << 6
+        return byte[..., 0] | byte[..., 1] << 8 | byte[..., 2] << 16 | byte[..., 3] << 24
+    fails(pins.check_pack_golden, bad_words)
 
 
 def test_pack_msb_first_caught():
-    def bad_pack(codes):
-        p = oracle.pack(codes)
-        b = p.astype(np.uint32)
+    def bad_words(codes):
+        w = oracle.pack_words(codes)
+        b = np.stack([(w >> (8 * k)) & 255 for k in range(4)], axis=-1)
         rev = ((b & 3) << 6) | ((b & 12) << 2) | ((b & 48) >> 2) | ((b & 192) >> 6)
-        return rev.astype(np.uint8)
-    fails(pins.check_pack_golden, bad_pack, oracle.unpack)
+        return rev[..., 0] | rev[..., 1] << 8 | rev[..., 2] << 16 | rev[..., 3] << 24
+    fails(pins.check_pack_golden, bad_words)
+
+
+def test_pack_row_major_order_caught():
+    """The plain row-major order [row][plane][words] is caught by the word-order fixture."""
+    def bad_pack(codes):
+        T, _, n, m = codes.shape
+        w = oracle.pack_words(codes)                                    # [T][2][n][m/16]
+        w = np.concatenate([w, np.zeros((T, 2, (-n) % 16, m // 16), dtype=w.dtype)], axis=2)
+        return np.ascontiguousarray(w.transpose(2, 0, 1, 3)).astype("<u4").view(np.uint8).reshape(-1)
+    fails(pins.check_pack_tile_order, bad_pack, oracle.unpack)
+
+
+def test_pack_groups_before_planes_caught():
+    """Swapping the plane and group levels inside a chunk is caught."""
+    def bad_pack(codes):
+        T, _, n, m = codes.shape
+        w = oracle.pack_words(codes)
+        nt = -(-n // 16)
+        w = np.concatenate([w, np.zeros((T, 2, 16 * nt - n, m // 16), dtype=w.dtype)], axis=2)
+        out = []
+        for tile in range(nt):
+            for c in range(-(-m // 256)):
+                G = min(256, m - 256 * c) // 64
+                for g in range(G):
+                    for P in range(2 * T):
+                        w0 = (256 * c + 64 * g) // 16
+                        out.append(w[P // 2, P % 2, 16 * tile:16 * tile + 16, w0:w0 + 4].reshape(-1))
+        return np.concatenate(out).astype("<u4").view(np.uint8)
+    fails(pins.check_pack_tile_order, bad_pack, oracle.unpack)
 
 
 def test_gemv_conj_on_u_caught():

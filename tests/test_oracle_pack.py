@@ -4,7 +4,11 @@ import pins
 
 
 def test_pack_golden_bytes():
-    pins.check_pack_golden(oracle.pack, oracle.unpack)
+    pins.check_pack_golden(oracle.pack_words)
+
+
+def test_pack_tile_order():
+    pins.check_pack_tile_order(oracle.pack, oracle.unpack)
 
 
 def test_pack_roundtrip_and_size():
