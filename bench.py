@@ -9,15 +9,17 @@ One step is one pass of every stage of the path over one batch of inputs:
   1. quantize + pack the layer (split, projection, axis scales, residual stages, packing);
   2. decode GEMV at batch 1 over a pool of P distinct copies of the packed layer (P * 4 MB
      >= 512 MB, more than the 256 MB Infinity Cache, so every byte streams from HBM), as
-     grouped launches (fairy2i_gemv_grouped, up to 48 layers per launch);
-  3. the same GEMV at batch 4 and batch 16 over the pool;
+     grouped launches (fairy2i_gemv_grouped, up to 48 layers per launch): x is turned into its
+     exact int8 digit form once (fairy2i_x_digits; the pool's layers share x, as q, k and v
+     do), then the int8-MFMA GEMV runs over the pool;
+  3. the bf16-MFMA GEMV over the pool at batch 1, 4 and 16;
   4. prefill: per-token int8 activation quantization of 2048 tokens and the int8-MFMA GEMM.
 Each segment is captured once into a HIP graph and replayed on torch's current stream, with
 HIP events on that stream around every replay; inputs are resident in HBM before the timed
 region starts.
 
-`value` is the headline metric: algorithmic HBM bytes of the batch-1 GEMV launches divided by
-their time (GB/s).  The JSON line also carries the roofline of that kernel, the other legs
+`value` is the headline metric: algorithmic HBM bytes of the batch-1 decode segment (digit
+form + int8 GEMV launches) divided by its time (GB/s).  The JSON line also carries the roofline of that kernel, the other legs
 (GB/s, TOPS, params/s) and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -111,7 +113,7 @@ def main():
     q0 = f2.fairy2i_quantize(R, T)
     layer_bytes = q0["packed"].numel()
     P = max(1, -(-POOL_BYTES // layer_bytes))
-    pool = q0["packed"].unsqueeze(0).repeat(P, 1, 1, 1, 1).contiguous()
+    pool = q0["packed"].unsqueeze(0).repeat(P, 1).contiguous()
     spool = q0["scales"].unsqueeze(0).repeat(P, 1, 1, 1, 1).contiguous()
     xs = {}
     for B in (1, 4, 16):
@@ -150,6 +152,15 @@ def main():
             f2.fairy2i_gemv_grouped(items[B], algo=f2.GEMV_MFMA)
         return run
 
+    xd1 = f2.XDigits(torch.empty((f2.fairy2i_x_digits_bytes(m, 1),), dtype=torch.uint8, device=dev), 1, m)
+    items_i8 = [(pool[p], spool[p], xd1, ypool[1][p]) for p in range(P)]
+
+    def seg_xdigits():
+        f2.fairy2i_x_digits(xs[1], out=xd1)
+
+    def seg_gemv_i8():
+        f2.fairy2i_gemv_grouped(items_i8, algo=f2.GEMV_MFMA_I8)
+
     def single_layers():               # one launch per layer (latency-bound small kernels)
         for p in range(P):
             f2.fairy2i_gemv(pool[p], spool[p], xs[1], y=ys[1], algo=f2.GEMV_MFMA)
@@ -160,8 +171,9 @@ def main():
     def seg_gemm():
         f2.fairy2i_gemm(q0["packed"], q0["scales"], qp, x_scale=dp, y=yp)
 
-    segments = [seg_quantize, seg_gemv(1), seg_gemv(4), seg_gemv(16), seg_act_quant, seg_gemm,
-                single_layers]
+    segments = [seg_quantize, seg_xdigits, seg_gemv_i8, seg_gemv(1), seg_gemv(4), seg_gemv(16),
+                seg_act_quant, seg_gemm, single_layers]
+    NSEG = len(segments) - 1
     for fn in segments:                     # eager warm-up (also loads every kernel)
         fn()
     torch.cuda.synchronize()
@@ -186,13 +198,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    seg = np.zeros(6)
+    seg = np.zeros(NSEG)
     t0 = time.perf_counter()
     all_events = [step() for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for e in all_events:
-        seg += np.array([e[k].elapsed_time(e[k + 1]) for k in range(6)])   # ms
+        seg += np.array([e[k].elapsed_time(e[k + 1]) for k in range(NSEG)])   # ms
     seg /= args.steps
     ms_step = float(np.sum(seg))
     # outside the timed step: the same pool as 128 separate single-layer launches
@@ -205,19 +217,25 @@ def main():
     torch.cuda.synchronize()
     single_us = e0.elapsed_time(e1) * 1e3 / (3 * P)
 
+    t_quant, t_xdig, t_i8, t_b1, t_b4, t_b16, t_aq, t_gemm = seg    # ms
     bytes_b = {B: gemv_bytes(n, m, T, B) for B in (1, 4, 16)}
-    gemv_ms = {1: seg[1], 4: seg[2], 16: seg[3]}
+    gemv_ms = {1: t_b1, 4: t_b4, 16: t_b16}
     gbs = {B: P * bytes_b[B] / (gemv_ms[B] * 1e-3) / 1e9 for B in (1, 4, 16)}
     launches = -(-P // 48)                     # grouped launches per segment
     per_launch_us = {B: gemv_ms[B] * 1e3 / launches for B in (1, 4, 16)}
+    # batch-1 decode through the digit form: the conversion reads x and writes 8m digit bytes
+    bytes_i8 = P * bytes_b[1]
+    i8_gbs = bytes_i8 / ((t_xdig + t_i8) * 1e-3) / 1e9
+    i8_launch_us = t_i8 * 1e3 / launches
+    i8_launch_gbs = bytes_i8 / launches / (i8_launch_us * 1e-6) / 1e9
     issued_ops = 16 * T * n * m * Ntok
-    gemm_tops = issued_ops / (seg[5] * 1e-3) / 1e12
+    gemm_tops = issued_ops / (t_gemm * 1e-3) / 1e12
     quant_params = 4 * n * m
     quant_read = quant_params * 4 + layer_bytes + n * T * 4 * 4
 
     out = {
         "metric": METRIC,
-        "value": round(gbs[1], 2),
+        "value": round(i8_gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -233,17 +251,22 @@ def main():
                         "decode GEMV batch 1 (value), 4, 16 over a pool of distinct layer copies; "
                         "quantize+pack; prefill act-quant + int8 GEMM over 2048 tokens",
             "rows": 2 * n, "cols": 2 * m, "T": T, "batch": 1, "pool_layers": P,
-            "x_dtype": "bf16", "y_dtype": "f32", "gemv_kernel": "bf16 MFMA, grouped launches",
+            "x_dtype": "bf16", "y_dtype": "f32",
+            "gemv_kernel": "int8 MFMA on the exact digit form of x, grouped launches",
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": round(P * bytes_b[1] / launches / (per_launch_us[1] * 1e-6) / 1e9, 2),
+            "kernel": "k_gemv_i8 (grouped, batch 1)",
+            "achieved": round(i8_launch_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(P * bytes_b[1] / launches / (per_launch_us[1] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "frac": round(i8_launch_gbs / HBM_PEAK_GBS, 4),
             "traffic": None,
         },
         "legs": {
+            "gemv_b1_i8": {"GB/s": round(i8_gbs, 2), "x_digits_us": round(t_xdig * 1e3, 3),
+                           "us_per_launch": round(i8_launch_us, 3), "launch_GB/s": round(i8_launch_gbs, 2),
+                           "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[1]},
             "gemv_b1": {"GB/s": round(gbs[1], 2), "us_per_launch": round(per_launch_us[1], 3),
                         "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[1]},
             "gemv_b4": {"GB/s": round(gbs[4], 2), "us_per_launch": round(per_launch_us[4], 3),
@@ -252,12 +275,12 @@ def main():
                          "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[16]},
             "gemv_b1_single_layer_launch": {"us_per_launch": round(single_us, 3),
                                             "GB/s": round(bytes_b[1] / (single_us * 1e-6) / 1e9, 2)},
-            "quantize": {"us": round(seg[0] * 1e3, 2),
-                         "real_params_per_s": round(quant_params / (seg[0] * 1e-3), 1),
-                         "GB/s": round(quant_read / (seg[0] * 1e-3) / 1e9, 2)},
-            "act_quant": {"us": round(seg[4] * 1e3, 2),
-                          "GB/s": round((Ntok * 2 * m * 3 + Ntok * 4) / (seg[4] * 1e-3) / 1e9, 2)},
-            "gemm": {"us": round(seg[5] * 1e3, 2), "issued_TOPS": round(gemm_tops, 2),
+            "quantize": {"us": round(t_quant * 1e3, 2),
+                         "real_params_per_s": round(quant_params / (t_quant * 1e-3), 1),
+                         "GB/s": round(quant_read / (t_quant * 1e-3) / 1e9, 2)},
+            "act_quant": {"us": round(t_aq * 1e3, 2),
+                          "GB/s": round((Ntok * 2 * m * 3 + Ntok * 4) / (t_aq * 1e-3) / 1e9, 2)},
+            "gemm": {"us": round(t_gemm * 1e3, 2), "issued_TOPS": round(gemm_tops, 2),
                      "useful_TOPS": round(gemm_tops / 2, 2),
                      "frac_of_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
                      "issued_ops": issued_ops},

@@ -25,11 +25,16 @@
  *     first half is the real part.  R's four quadrants are the blocks R11, R12, R21, R22.
  *   - Code k in {0,1,2,3} stands for i**k = (1, i, -1, -i).  Bit 0 is the axis (0 real,
  *     1 imaginary), bit 1 the sign.
- *   - packed: uint8 [n][T][2][m/4] = (row i, stage t, matrix M = 0 for U, 1 for W), m/16
- *     little-endian 32-bit words per (i, t, M).  Word w holds codes j = 16w..16w+15; code
- *     16w+p sits in bits 8*(p%4) + 2*(p/4) .. +1, so byte b holds codes b, b+4, b+8, b+12.
- *     (One shift and one mask then spread four codes into four bytes in j order.)  Four codes
- *     per byte: T*n*m/2 bytes per layer, i.e. T bits per real parameter of R.
+ *   - packed form (fairy2i_packed_bytes(n, m, T) bytes): the codes of row i, stage t, matrix
+ *     M (0 = U, 1 = W) -- plane P = 2t + M -- as little-endian 32-bit words of 16 codes.
+ *     Word w of a (row, plane) holds codes j = 16w..16w+15; code 16w+p sits in bits
+ *     8*(p%4) + 2*(p/4) .. +1, so byte b holds codes b, b+4, b+8, b+12 (one shift and one mask
+ *     spread four codes into four bytes in j order).  Words are ordered per tile of 16 rows
+ *     (the last tile padded with rows of code 0) as [chunk c of 256 columns][plane P]
+ *     [64-column group g < G_c][row r < 16][word < 4], G_c = min(4, (m - 256c) / 64), tiles one
+ *     after another: one (tile, chunk, plane) block is 16 rows x 64 columns per 256 bytes, the
+ *     A operand of the matrix-core kernels as one contiguous load.  Four codes per byte:
+ *     T*n*m/2 bytes per layer (T bits per real parameter of R) plus the padding rows.
  *   - scales: fp32 [n][T][2][2] = [row][stage][matrix][axis], axis 0 = real, 1 = imaginary.
  *   - Requirements: n >= 1, m >= 64 and m % 64 == 0, 1 <= T <= 4; pointers to packed, x, y,
  *     codes and workspaces 16-byte aligned; pointers to scales 4-byte aligned (8 for fp64).
@@ -50,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FAIRY2I_ABI_VERSION 1
+#define FAIRY2I_ABI_VERSION 2
 
 typedef enum {
   FAIRY2I_OK = 0,
@@ -67,19 +72,20 @@ typedef enum {
   FAIRY2I_F32 = 0,
   FAIRY2I_BF16 = 1,
   FAIRY2I_I8 = 2,
-  FAIRY2I_I32 = 3
+  FAIRY2I_I32 = 3,
+  FAIRY2I_X_DIGITS = 4   /* decode-GEMV x in exact int8 digit form (fairy2i_x_digits) */
 } fairy2i_dtype;
 
-/* GEMV kernels.  AUTO picks MFMA for bf16 x and VALU for fp32 x; MFMA means MFMA_BF16 (the
- * faster of the two matrix-core kernels on gfx950 at every batch size; MFMA_I8 is kept as the
- * exact-integer variant).
+/* GEMV kernels.  AUTO picks MFMA_I8 for x in digit form, MFMA_BF16 for bf16 x and VALU for
+ * fp32 x; MFMA means MFMA_BF16.
  *   VALU       fp32 add/sub/swap accumulation on the vector ALUs; fp32 or bf16 x.
  *   MFMA_BF16  codes decoded in registers to bf16 planes {+-2, 0}, multiplied with the unchanged
  *              bf16 x on v_mfma_f32_16x16x32_bf16: exact products, fp32 sums.  bf16 x.
- *   MFMA_I8    codes decoded to int8 planes {-1, 0, 1}; each bf16 column of x is scaled by one
- *              power of two and rounded to a 23-bit integer (exact unless a value is more than
- *              2^14 below the column maximum) held as three int8 digits; exact int32 sums on
- *              v_mfma_i32_16x16x64_i8.  bf16 x, B <= 2. */
+ *   MFMA_I8    codes decoded to int8 planes {-1, 0, 1}, multiplied with x in digit form (made
+ *              once per x by fairy2i_x_digits) on v_mfma_i32_16x16x64_i8: exact int32 sums,
+ *              fp32 epilogue.  x_dtype FAIRY2I_X_DIGITS, B <= 2.  The fastest decode kernel at
+ *              B <= 2 on gfx950: half the MFMA cycles and ~2/3 of the VALU work per code of
+ *              MFMA_BF16. */
 typedef enum {
   FAIRY2I_GEMV_AUTO = 0,
   FAIRY2I_GEMV_VALU = 1,
@@ -88,6 +94,10 @@ typedef enum {
   FAIRY2I_GEMV_MFMA_I8 = 4
 } fairy2i_gemv_algo;
 
+/* Bytes of the packed form of an n x m complex layer with T stages:
+ * ceil(n / 16) * 16 * T * 2 * m / 4 (0 for non-positive sizes). */
+size_t fairy2i_packed_bytes(int64_t n, int64_t m, int T);
+
 /* Quantize a real layer.  Widely-linear split (Theorem 1, "Step 1"), then for t < T:
  * projection to the nearest of {1, i, -1, -i} (first in that order on ties), per-row
  * per-stage per-matrix axis scales s = mean |Re r| (|Im r|) over the entries coded on that
@@ -95,7 +105,7 @@ typedef enum {
  * All arithmetic is fp64; the scale sums use a fixed order (256 partial sums over
  * j = l, l+256, ..., then a halving tree), so results do not depend on the launch.
  *   R        fp32 [two_n][two_m], read only.
- *   packed   out, uint8 [n][T][2][m/4].
+ *   packed   out, the packed form (fairy2i_packed_bytes(n, m, T) bytes, padding rows zeroed).
  *   scales   out, fp32 [n][T][2][2] (round-to-nearest-even of the fp64 scales).
  *   scales64 optional out (NULL skips), fp64 [n][T][2][2].
  *   codes    optional out (NULL skips), uint8 [T][2][n][m], one code per byte.
@@ -105,17 +115,35 @@ int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T,
                      hipStream_t stream);
 
 /* Pack one-byte codes uint8 [T][2][n][m] (values 0..3; higher bits are ignored) into the
- * packed layout above (ModelScope card "Model details": 2 bits per real parameter at T=2). */
+ * packed form above, padding rows zeroed (ModelScope card "Model details": 2 bits per real
+ * parameter at T=2).  packed: fairy2i_packed_bytes(n, m, T) bytes. */
 int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* packed,
                  hipStream_t stream);
 
+/* Digit form of decode-GEMV activations, the input of the MFMA_I8 kernel (exact integer
+ * arithmetic on the int8 matrix cores; same sum as the ModelScope card "Method" y = U x +
+ * W conj(x), with x held exactly as integers).  For each batch column b < B: one power of two
+ * 2^S_b with max_j |x_b,j| 2^S_b in [2^21, 2^22) (S_b = 0 for an all-zero column), X =
+ * round_half_even(x 2^S_b) -- exact for every bf16 value no more than 2^14 below the column
+ * maximum, relative error below 2^-22 of the maximum otherwise -- and X = d0 + 2^8 d1 + 2^16 d2
+ * with signed int8 digits.
+ *   x        [B][2m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16, 16-byte aligned.  1 <= B <= 2.
+ *   digits   out, fairy2i_x_digits_bytes(m, B) bytes, 16-byte aligned: int32 header
+ *            [B, m, S_0, S_1] in the first 64 bytes, then int8 [B][2][4][m] (batch column,
+ *            component Re x / Im x, digit slot; slot 3 is zero).
+ * The digit form is tied to the m and B it was made with; pass the same m and B to the GEMV. */
+size_t fairy2i_x_digits_bytes(int64_t m, int64_t B);
+int fairy2i_x_digits(const void* x, int x_dtype, int64_t m, int64_t B, void* digits, hipStream_t stream);
+
 /* Decode GEMV: y~[b] = sum_t U~(t) x[b] + W~(t) conj(x[b]) for b < B, every code an add,
- * subtract or real/imaginary swap with sign; one fp32 accumulator per (stage, matrix,
- * axis) so each scale multiplies an accumulated sum, not a weight.
+ * subtract or real/imaginary swap with sign; one accumulator per (stage, matrix, axis) so each
+ * scale multiplies an accumulated sum, not a weight.
  *   packed, scales  as produced by fairy2i_quantize.
- *   x       [B][2m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16.  1 <= B <= 16.
+ *   x       [B][2m] with x_dtype FAIRY2I_F32 or FAIRY2I_BF16, or the digit form of such an x
+ *           (x_dtype FAIRY2I_X_DIGITS, made with the same m and B).  1 <= B <= 16.
  *   y       out, [B][2n], y_dtype FAIRY2I_F32 or FAIRY2I_BF16 (round to nearest even).
- *   algo    fairy2i_gemv_algo; the MFMA kernels require x_dtype BF16, MFMA_I8 also B <= 2.
+ *   algo    fairy2i_gemv_algo; MFMA_BF16 requires x_dtype BF16, MFMA_I8 x_dtype X_DIGITS and
+ *           B <= 2; VALU takes F32 or BF16.
  * Uses no workspace. */
 int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,
@@ -134,7 +162,7 @@ typedef struct {
  * the q, k and v projections, which also share x; ModelScope card "Method": every linear layer
  * becomes a widely-linear layer).  The MFMA kernels cover all items' row tiles in one grid of
  * up to 48 items per launch, so a small layer does not pay a launch ramp and tail of its own;
- * VALU and MFMA_I8 run the items one after another.
+ * VALU runs the items one after another.  Items that share x may share its digit form.
  *   items   HOST array of `count` items (read during the call only; the pointers in it are
  *           device pointers).  Each item is checked like a fairy2i_gemv call. */
 int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, int T, int x_dtype,

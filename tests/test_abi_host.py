@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert f2.fairy2i_abi_version() == 1
+    assert f2.fairy2i_abi_version() == 2
     for s in range(8):
         assert f2.fairy2i_status_string(s) not in ("", "unknown status")
     assert f2.fairy2i_status_string(99) == "unknown status"
@@ -94,12 +94,37 @@ def test_gemv_errors(L):
     assert call(algo=7) == 4 and call(algo=-1) == 4
     assert call(algo=f2.GEMV_MFMA, xd=f2.F32) == 4
     assert call(algo=f2.GEMV_MFMA_I8, xd=f2.F32) == 4
-    assert call(algo=f2.GEMV_MFMA_I8, B=3) == 2
+    assert call(algo=f2.GEMV_MFMA_I8, xd=f2.BF16) == 4         # needs the digit form
+    assert "digit form" in last()
+    assert call(algo=f2.GEMV_MFMA_I8, xd=f2.X_DIGITS, B=3) == 2
+    assert call(algo=f2.GEMV_VALU, xd=f2.X_DIGITS) == 4
+    assert call(algo=f2.GEMV_MFMA_BF16, xd=f2.X_DIGITS) == 4
     assert call(T=0) == 3
     assert call(B=0) == 2 and call(B=17) == 2
     assert call(m=32) == 2 and call(n=0) == 2
     assert call(x=FAKE_ODD) == 5
     assert call(y=FAKE + 8) == 5
+
+
+def test_packed_bytes(L):
+    """Size of the packed form: whole 16-row tiles, T * 2 planes, m / 4 bytes per row and plane."""
+    import oracle
+    for n, m, T in ((1, 64, 1), (16, 64, 2), (17, 320, 2), (2048, 2048, 2), (5504, 4096, 3)):
+        assert L.fairy2i_packed_bytes(n, m, T) == oracle.packed_nbytes(n, m, T)
+    assert L.fairy2i_packed_bytes(0, 64, 2) == 0
+
+
+def test_x_digits_errors(L):
+    d = L.fairy2i_x_digits
+    assert L.fairy2i_x_digits_bytes(2048, 1) == 64 + 8 * 2048
+    assert L.fairy2i_x_digits_bytes(2048, 2) == 64 + 16 * 2048
+    assert d(NULL, f2.BF16, 64, 1, FAKE, S) == 1
+    assert d(FAKE, f2.BF16, 64, 1, NULL, S) == 1
+    assert d(FAKE, f2.I8, 64, 1, FAKE, S) == 4
+    assert d(FAKE, f2.BF16, 96, 1, FAKE, S) == 2
+    assert d(FAKE, f2.BF16, 64, 3, FAKE, S) == 2 and d(FAKE, f2.BF16, 64, 0, FAKE, S) == 2
+    assert d(FAKE_ODD, f2.BF16, 64, 1, FAKE, S) == 5
+    assert d(FAKE, f2.BF16, 64, 1, FAKE + 4, S) == 5
 
 
 def test_gemv_grouped_errors(L):

@@ -22,6 +22,8 @@ def run(dev, codes, scales, act, algo, y_dtype):
     packed = up(oracle.pack(codes), dev)
     s = up(scales.astype(np.float32), dev)
     x = x_to_dev(act, dev)
+    if algo == f2.GEMV_MFMA_I8:
+        x = f2.fairy2i_x_digits(x)
     y = f2.fairy2i_gemv(packed, s, x, algo=algo, y_dtype=y_dtype)
     return down(y)
 
@@ -133,36 +135,47 @@ def test_graph_replay_matches_eager():
         announce("graph replay B =", B)
         eager = f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA)
         eager_valu = f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_VALU)
+        eager_i8 = f2.fairy2i_gemv(packed, s, f2.fairy2i_x_digits(x), algo=f2.GEMV_MFMA_I8) if B <= 2 else None
         torch.cuda.synchronize()
         y = torch.empty_like(eager)
         yv = torch.empty_like(eager)
+        yi = torch.empty_like(eager)
+        xd = f2.XDigits(torch.empty((f2.fairy2i_x_digits_bytes(2048, B),), dtype=torch.uint8, device=dev), B, 2048)
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         with torch.cuda.graph(g, stream=cap):
             f2.fairy2i_gemv(packed, s, x, y=y, algo=f2.GEMV_MFMA)
             f2.fairy2i_gemv(packed, s, x, y=yv, algo=f2.GEMV_VALU)
+            if B <= 2:
+                f2.fairy2i_x_digits(x, out=xd)
+                f2.fairy2i_gemv(packed, s, xd, y=yi, algo=f2.GEMV_MFMA_I8)
         for rep in range(3):
             y.fill_(float("nan"))
             yv.fill_(float("nan"))
+            yi.fill_(float("nan"))
+            xd.buf.fill_(0x55)
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(y, eager), (B, rep)
             assert torch.equal(yv, eager_valu), (B, rep)
+            if B <= 2:
+                assert torch.equal(yi, eager_i8), (B, rep)
             f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_VALU)     # eager work between replays
             torch.cuda.synchronize()
         outs[B] = eager
 
 
-@pytest.mark.parametrize("algo", ["mfma", "valu"])
+@pytest.mark.parametrize("algo", ["mfma", "valu", "i8"])
 def test_grouped_matches_single_and_oracle(algo):
     """A grouped call over items of different n (and more items than one launch holds) gives,
     item by item, exactly the single-call result, within tolerance of the oracle."""
     dev = device()
-    m, T, B = 512, 2, 3
+    m, T, B = 512, 2, (2 if algo == "i8" else 3)
     ns = [16, 33, 1, 200, 64] * 11              # 55 items -> two launches of the grouped kernel
-    rng = np.random.default_rng(17)
     act = workloads.activations(B, 2 * m, seed=21)
     x = x_to_dev(act, dev)
+    if algo == "i8":
+        x = f2.fairy2i_x_digits(x)
     items, singles, refs = [], [], []
     for k, n in enumerate(ns):
         codes = workloads.random_codes(T, n, m, seed=1000 + k)
@@ -181,3 +194,43 @@ def test_grouped_matches_single_and_oracle(algo):
         assert torch.equal(it[3], singles[k]), k
         if k < 10:
             assert rel_l2(down(it[3]), refs[k]) <= TOL_F32, k
+
+
+@pytest.mark.parametrize("B,dtype", [(1, "bf16"), (2, "bf16"), (1, "f32"), (2, "f32")])
+def test_x_digits_represent_x(B, dtype):
+    """The digit form holds, per batch column, S with max|x| 2^S in [2^21, 2^22) and digits whose
+    value d0 + 2^8 d1 + 2^16 d2 equals round_half_even(x 2^S); for bf16 x that is x 2^S exactly
+    whenever |x| is within 2^14 of the column maximum.  Slot 3 is zero."""
+    dev = device()
+    m = 1024
+    rng = np.random.default_rng(40 + B)
+    v = rng.standard_normal((B, 2 * m)).astype(np.float32)
+    v *= np.float32(2.0) ** rng.integers(-20, 6, size=v.shape).astype(np.float32)
+    v[rng.random(v.shape) < 0.05] = 0.0
+    if B == 2:
+        v[1] = 0.0                                   # an all-zero column: S = 0, all digits 0
+    if dtype == "bf16":
+        bits = workloads.f32_to_bf16_bits(v)
+        v = workloads.bf16_bits_to_f32(bits)
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        x = torch.from_numpy(v).to(dev)
+    announce("x digits", B, dtype)
+    blob = down(f2.fairy2i_x_digits(x).buf)
+    hdr = blob[:64].view(np.int32)
+    assert hdr[0] == B and hdr[1] == m
+    dg = blob[64:].view(np.int8).reshape(B, 2, 4, m).astype(np.int64)
+    for b in range(B):
+        amax = float(np.abs(v[b]).max())
+        S = int(hdr[2 + b])
+        if amax == 0.0:
+            assert S == 0 and not dg[b].any()
+            continue
+        assert 2.0 ** 21 <= amax * 2.0 ** S < 2.0 ** 22
+        X = dg[b, :, 0] + 256 * dg[b, :, 1] + 65536 * dg[b, :, 2]
+        assert not dg[b, :, 3].any()
+        want = np.rint(v[b].reshape(2, m).astype(np.float64) * 2.0 ** S)
+        assert np.array_equal(X, want.astype(np.int64))
+        if dtype == "bf16":
+            near = np.abs(v[b].reshape(2, m)) >= amax * 2.0 ** -14
+            assert np.array_equal(X[near] * 2.0 ** -S, v[b].reshape(2, m)[near].astype(np.float64))

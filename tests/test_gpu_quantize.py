@@ -27,9 +27,9 @@ def assert_rows_match(R, T, rows, got, label):
     rows = np.asarray(rows)
     sub = np.concatenate([R[rows], R[n + rows]], axis=0)
     codes, s32, s64, _ = oracle.quantize(sub, T)
-    packed = oracle.pack(codes)
+    m = R.shape[1] // 2
     assert np.array_equal(got["codes"][:, :, rows], codes), label + ": codes"
-    assert np.array_equal(got["packed"][rows], packed), label + ": packed"
+    assert np.array_equal(oracle.unpack(got["packed"], n, m, T)[:, :, rows], codes), label + ": packed"
     assert np.array_equal(got["scales64"][rows].view(np.uint64), s64.view(np.uint64)), label + ": scales64"
     assert np.array_equal(got["scales"][rows].view(np.uint32), s32.view(np.uint32)), label + ": scales"
 
@@ -66,7 +66,7 @@ def test_mlp_sampled_rows(layer, T):
     rows = np.unique(np.concatenate([[0, 1, n - 1], rng.choice(n, 93, replace=False)]))
     assert_rows_match(R, T, rows, got, layer.name)
     # codes and packed agree everywhere (the packed bytes are the codes, four to a byte)
-    assert np.array_equal(oracle.unpack(got["packed"]), got["codes"])
+    assert np.array_equal(oracle.unpack(got["packed"], n, layer.m, T), got["codes"])
 
 
 def constructed_edge_matrix(n, m, seed):

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libfairy2i.so")
 FAIRY2I_OK = 0
 STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_STAGES", 4: "ERR_DTYPE",
                 5: "ERR_ALIGN", 6: "ERR_WORKSPACE", 7: "ERR_HIP"}
-F32, BF16, I8, I32 = 0, 1, 2, 3
+F32, BF16, I8, I32, X_DIGITS = 0, 1, 2, 3, 4
 GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_MFMA_BF16, GEMV_MFMA_I8 = 0, 1, 2, 3, 4
 
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.int32: I32}
@@ -33,6 +33,9 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "fairy2i_quantize": (_INT, [_P, _I64, _I64, _INT, _P, _P, _P, _P, _P]),
     "fairy2i_pack": (_INT, [_P, _I64, _I64, _INT, _P, _P]),
+    "fairy2i_packed_bytes": (_SZ, [_I64, _I64, _INT]),
+    "fairy2i_x_digits_bytes": (_SZ, [_I64, _I64]),
+    "fairy2i_x_digits": (_INT, [_P, _INT, _I64, _I64, _P, _P]),
     "fairy2i_gemv": (_INT, [_P, _P, _I64, _I64, _INT, _P, _INT, _I64, _P, _INT, _INT, _P]),
     "fairy2i_act_quant": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P]),
     "fairy2i_gemm_workspace_bytes": (_SZ, [_I64, _I64, _INT, _I64, _INT]),
@@ -103,13 +106,17 @@ def fairy2i_last_error() -> str:
     return lib().fairy2i_last_error().decode(errors="replace")
 
 
+def fairy2i_packed_bytes(n: int, m: int, T: int) -> int:
+    return int(lib().fairy2i_packed_bytes(n, m, T))
+
+
 def fairy2i_quantize(R: torch.Tensor, T: int, *, want_scales64: bool = False,
                      want_codes: bool = False, packed=None, scales=None, stream=None):
-    """R fp32 [2n][2m] on the GPU -> dict(packed, scales[, scales64][, codes])."""
+    """R fp32 [2n][2m] on the GPU -> dict(packed (flat uint8), scales[, scales64][, codes])."""
     two_n, two_m = R.shape
     n, m = two_n // 2, two_m // 2
     dev = R.device
-    packed = packed if packed is not None else torch.empty((n, T, 2, m // 4), dtype=torch.uint8, device=dev)
+    packed = packed if packed is not None else torch.empty((fairy2i_packed_bytes(n, m, T),), dtype=torch.uint8, device=dev)
     scales = scales if scales is not None else torch.empty((n, T, 2, 2), dtype=torch.float32, device=dev)
     s64 = torch.empty((n, T, 2, 2), dtype=torch.float64, device=dev) if want_scales64 else None
     codes = torch.empty((T, 2, n, m), dtype=torch.uint8, device=dev) if want_codes else None
@@ -124,22 +131,61 @@ def fairy2i_quantize(R: torch.Tensor, T: int, *, want_scales64: bool = False,
 
 
 def fairy2i_pack(codes: torch.Tensor, packed=None, stream=None) -> torch.Tensor:
-    """codes uint8 [T][2][n][m] -> packed uint8 [n][T][2][m/4]."""
+    """codes uint8 [T][2][n][m] -> the packed form (flat uint8, fairy2i_packed_bytes)."""
     T, _, n, m = codes.shape
-    packed = packed if packed is not None else torch.empty((n, T, 2, m // 4), dtype=torch.uint8, device=codes.device)
+    packed = packed if packed is not None else torch.empty((fairy2i_packed_bytes(n, m, T),), dtype=torch.uint8, device=codes.device)
     _check(lib().fairy2i_pack(_ptr(codes), n, m, T, _ptr(packed), _stream(stream)))
     return packed
 
 
-def fairy2i_gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, *,
+class XDigits:
+    """Digit form of decode-GEMV activations (fairy2i_x_digits): the uint8 buffer and the B and m
+    it was made with."""
+
+    def __init__(self, buf: torch.Tensor, B: int, m: int):
+        self.buf, self.B, self.m = buf, B, m
+
+    @property
+    def device(self):
+        return self.buf.device
+
+
+def _x_cols(x) -> int:
+    """Complex columns m of a GEMV/GEMM activation argument."""
+    return x.m if isinstance(x, XDigits) else x.shape[1] // 2
+
+
+def _x_args(x):
+    """(pointer, x_dtype, B) of a GEMV activation argument: a [B][2m] tensor or an XDigits."""
+    if isinstance(x, XDigits):
+        return _ptr(x.buf), X_DIGITS, x.B
+    return _ptr(x), _DTYPE[x.dtype], x.shape[0]
+
+
+def fairy2i_x_digits_bytes(m: int, B: int) -> int:
+    return int(lib().fairy2i_x_digits_bytes(m, B))
+
+
+def fairy2i_x_digits(x: torch.Tensor, out: XDigits | None = None, stream=None) -> XDigits:
+    """x [B][2m] (bf16 / fp32, B <= 2) -> its exact int8 digit form for the int8 MFMA GEMV."""
+    B, two_m = x.shape
+    m = two_m // 2
+    if out is None:
+        out = XDigits(torch.empty((fairy2i_x_digits_bytes(m, B),), dtype=torch.uint8, device=x.device), B, m)
+    _check(lib().fairy2i_x_digits(_ptr(x), _DTYPE[x.dtype], m, B, _ptr(out.buf), _stream(stream)))
+    return out
+
+
+def fairy2i_gemv(packed: torch.Tensor, scales: torch.Tensor, x, *,
                  y_dtype=torch.float32, algo: int = GEMV_AUTO, y=None, stream=None) -> torch.Tensor:
-    """packed [n][T][2][m/4], scales [n][T][2][2], x [B][2m] -> y [B][2n]."""
-    n, T, _, q = packed.shape
-    m = 4 * q
-    B = x.shape[0]
+    """packed form, scales [n][T][2][2], x [B][2m] (or its XDigits) -> y [B][2n].  n and T come
+    from the scales, m from x."""
+    n, T = scales.shape[0], scales.shape[1]
+    m = _x_cols(x)
+    xp, xdt, B = _x_args(x)
     if y is None:
         y = torch.empty((B, 2 * n), dtype=y_dtype, device=x.device)
-    _check(lib().fairy2i_gemv(_ptr(packed), _ptr(scales), n, m, T, _ptr(x), _DTYPE[x.dtype], B,
+    _check(lib().fairy2i_gemv(_ptr(packed), _ptr(scales), n, m, T, xp, xdt, B,
                               _ptr(y), _DTYPE[y.dtype], algo, _stream(stream)))
     return y
 
@@ -150,10 +196,11 @@ def fairy2i_gemv_grouped(items, *, algo: int = GEMV_AUTO, stream=None):
     items = list(items)
     arr = (GemvItem * len(items))()
     for k, (packed, scales, x, y) in enumerate(items):
-        arr[k] = GemvItem(packed.data_ptr(), scales.data_ptr(), x.data_ptr(), y.data_ptr(), packed.shape[0])
-    packed0, _, x0, y0 = items[0]
-    _, T, _, q = packed0.shape
-    _check(lib().fairy2i_gemv_grouped(arr, len(items), 4 * q, T, _DTYPE[x0.dtype], x0.shape[0],
+        arr[k] = GemvItem(packed.data_ptr(), scales.data_ptr(), _x_args(x)[0], y.data_ptr(), scales.shape[0])
+    _, scales0, x0, y0 = items[0]
+    T = scales0.shape[1]
+    _, xdt, B = _x_args(x0)
+    _check(lib().fairy2i_gemv_grouped(arr, len(items), _x_cols(x0), T, xdt, B,
                                       _DTYPE[y0.dtype], algo, _stream(stream)))
     return [it[3] for it in items]
 
@@ -176,8 +223,8 @@ def fairy2i_gemm(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, *,
     """Prefill over N tokens.  x [N][2m] bf16/fp32 (x_scale receives delta if given) or int8
     (x_scale = delta input).  y_dtype float32/bfloat16 -> y [N][2n]; int32 -> raw
     accumulators [T][2][2][2][N][n]."""
-    n, T, _, q4 = packed.shape
-    m = 4 * q4
+    n, T = scales.shape[0], scales.shape[1]
+    m = x.shape[1] // 2
     N = x.shape[0]
     if y is None:
         shape = (T, 2, 2, 2, N, n) if y_dtype == torch.int32 else (N, 2 * n)

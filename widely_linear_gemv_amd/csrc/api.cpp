@@ -99,28 +99,66 @@ int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* pac
   return hip_status(f2i::launch_pack(codes, (int)n, (int)m, T, packed, stream), "pack launch");
 }
 
+// Checks the dtype / algorithm / batch combination of a GEMV call and resolves AUTO and MFMA to
+// the kernel that runs.  Returns minus the status (with the message recorded) on a bad combination.
+static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B) {
+  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16 && x_dtype != FAIRY2I_X_DIGITS)
+    return -fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32, BF16 or X_DIGITS", x_dtype);
+  if (y_dtype != FAIRY2I_F32 && y_dtype != FAIRY2I_BF16)
+    return -fail(FAIRY2I_ERR_DTYPE, "y_dtype %d: need F32 or BF16", y_dtype);
+  if (algo < FAIRY2I_GEMV_AUTO || algo > FAIRY2I_GEMV_MFMA_I8)
+    return -fail(FAIRY2I_ERR_DTYPE, "unknown GEMV algorithm %d", algo);
+  if (B < 1 || B > 16) return -fail(FAIRY2I_ERR_SHAPE, "B = %lld: need 1 <= B <= 16", (long long)B);
+  int kernel = algo;
+  if (kernel == FAIRY2I_GEMV_AUTO)
+    kernel = x_dtype == FAIRY2I_X_DIGITS ? FAIRY2I_GEMV_MFMA_I8
+           : x_dtype == FAIRY2I_BF16     ? FAIRY2I_GEMV_MFMA_BF16 : FAIRY2I_GEMV_VALU;
+  if (kernel == FAIRY2I_GEMV_MFMA) kernel = FAIRY2I_GEMV_MFMA_BF16;
+  if (kernel == FAIRY2I_GEMV_MFMA_I8) {
+    if (x_dtype != FAIRY2I_X_DIGITS)
+      return -fail(FAIRY2I_ERR_DTYPE, "the int8 MFMA GEMV takes x in digit form (fairy2i_x_digits)");
+    if (B > 2) return -fail(FAIRY2I_ERR_SHAPE, "B = %lld: the int8 MFMA GEMV takes B <= 2", (long long)B);
+  } else if (x_dtype == FAIRY2I_X_DIGITS) {
+    return -fail(FAIRY2I_ERR_DTYPE, "x in digit form needs the int8 MFMA GEMV");
+  } else if (kernel == FAIRY2I_GEMV_MFMA_BF16 && x_dtype != FAIRY2I_BF16) {
+    return -fail(FAIRY2I_ERR_DTYPE, "the bf16 MFMA GEMV takes bf16 x only");
+  }
+  return kernel;
+}
+
+size_t fairy2i_packed_bytes(int64_t n, int64_t m, int T) {
+  if (n < 1 || m < 1 || T < 1) return 0;
+  return (size_t)((n + 15) / 16) * 16 * (size_t)T * 2 * (size_t)(m / 4);
+}
+
+size_t fairy2i_x_digits_bytes(int64_t m, int64_t B) {
+  if (m < 1 || B < 1) return 0;
+  return f2i::x_digits_bytes(m, B);
+}
+
+int fairy2i_x_digits(const void* x, int x_dtype, int64_t m, int64_t B, void* digits, hipStream_t stream) {
+  if (!x || !digits) return fail(FAIRY2I_ERR_NULL, "x and digits are required");
+  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32 or BF16", x_dtype);
+  if (m < 64 || m > kMaxCols || m % 64 != 0)
+    return fail(FAIRY2I_ERR_SHAPE, "m = %lld: need m >= 64 and m %% 64 == 0", (long long)m);
+  if (B < 1 || B > 2) return fail(FAIRY2I_ERR_SHAPE, "B = %lld: the digit form takes 1 <= B <= 2", (long long)B);
+  if (!aligned(x, 16) || !aligned(digits, 16))
+    return fail(FAIRY2I_ERR_ALIGN, "x and digits need 16-byte alignment");
+  return hip_status(f2i::launch_x_digits(x, x_dtype == FAIRY2I_BF16, (int)m, (int)B, digits, stream),
+                    "x digits launch");
+}
+
 int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,
                  hipStream_t stream) {
   if (!packed || !scales || !x || !y) return fail(FAIRY2I_ERR_NULL, "packed, scales, x and y are required");
-  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16)
-    return fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32 or BF16", x_dtype);
-  if (y_dtype != FAIRY2I_F32 && y_dtype != FAIRY2I_BF16)
-    return fail(FAIRY2I_ERR_DTYPE, "y_dtype %d: need F32 or BF16", y_dtype);
-  if (algo < FAIRY2I_GEMV_AUTO || algo > FAIRY2I_GEMV_MFMA_I8)
-    return fail(FAIRY2I_ERR_DTYPE, "unknown GEMV algorithm %d", algo);
-  if (algo >= FAIRY2I_GEMV_MFMA && x_dtype != FAIRY2I_BF16)
-    return fail(FAIRY2I_ERR_DTYPE, "the MFMA GEMV kernels take bf16 x only");
+  const int kernel = gemv_kernel(x_dtype, y_dtype, algo, B);
+  if (kernel < 0) return -kernel;
   if (int s = check_stages(T)) return s;
   if (int s = check_nm(n, m)) return s;
-  if (B < 1 || B > 16) return fail(FAIRY2I_ERR_SHAPE, "B = %lld: need 1 <= B <= 16", (long long)B);
-  if (algo == FAIRY2I_GEMV_MFMA_I8 && B > 2)
-    return fail(FAIRY2I_ERR_SHAPE, "B = %lld: the int8 MFMA GEMV takes B <= 2", (long long)B);
   if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(scales, 4))
     return fail(FAIRY2I_ERR_ALIGN, "packed, x and y need 16-byte alignment, scales 4");
-  int kernel = algo;
-  if (kernel == FAIRY2I_GEMV_AUTO) kernel = x_dtype == FAIRY2I_BF16 ? FAIRY2I_GEMV_MFMA : FAIRY2I_GEMV_VALU;
-  if (kernel == FAIRY2I_GEMV_MFMA) kernel = FAIRY2I_GEMV_MFMA_BF16;
   if (kernel == FAIRY2I_GEMV_MFMA_I8)
     return hip_status(f2i::launch_gemv_i8(packed, scales, (int)n, (int)m, T, x, (int)B, y,
                                           y_dtype == FAIRY2I_BF16, stream),
@@ -142,27 +180,16 @@ int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, i
   for (int k = 0; k < count; ++k)
     if (!items[k].packed || !items[k].scales || !items[k].x || !items[k].y)
       return fail(FAIRY2I_ERR_NULL, "item %d: packed, scales, x and y are required", k);
-  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16)
-    return fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32 or BF16", x_dtype);
-  if (y_dtype != FAIRY2I_F32 && y_dtype != FAIRY2I_BF16)
-    return fail(FAIRY2I_ERR_DTYPE, "y_dtype %d: need F32 or BF16", y_dtype);
-  if (algo < FAIRY2I_GEMV_AUTO || algo > FAIRY2I_GEMV_MFMA_I8)
-    return fail(FAIRY2I_ERR_DTYPE, "unknown GEMV algorithm %d", algo);
-  if (algo >= FAIRY2I_GEMV_MFMA && x_dtype != FAIRY2I_BF16)
-    return fail(FAIRY2I_ERR_DTYPE, "the MFMA GEMV kernels take bf16 x only");
+  const int kernel = gemv_kernel(x_dtype, y_dtype, algo, B);
+  if (kernel < 0) return -kernel;
   if (int s = check_stages(T)) return s;
   for (int k = 0; k < count; ++k)
     if (int s = check_nm(items[k].n, m)) return s;
-  if (B < 1 || B > 16) return fail(FAIRY2I_ERR_SHAPE, "B = %lld: need 1 <= B <= 16", (long long)B);
-  if (algo == FAIRY2I_GEMV_MFMA_I8 && B > 2)
-    return fail(FAIRY2I_ERR_SHAPE, "B = %lld: the int8 MFMA GEMV takes B <= 2", (long long)B);
   for (int k = 0; k < count; ++k)
     if (!aligned(items[k].packed, 16) || !aligned(items[k].x, 16) || !aligned(items[k].y, 16) ||
         !aligned(items[k].scales, 4))
       return fail(FAIRY2I_ERR_ALIGN, "item %d: packed, x and y need 16-byte alignment, scales 4", k);
-  const bool grouped = algo == FAIRY2I_GEMV_MFMA_BF16 || algo == FAIRY2I_GEMV_MFMA ||
-                       (algo == FAIRY2I_GEMV_AUTO && x_dtype == FAIRY2I_BF16);
-  if (!grouped) {
+  if (kernel == FAIRY2I_GEMV_VALU) {
     for (int k = 0; k < count; ++k) {
       const fairy2i_gemv_item& it = items[k];
       int s = fairy2i_gemv(it.packed, it.scales, it.n, m, T, it.x, x_dtype, B, it.y, y_dtype, algo, stream);
@@ -181,8 +208,10 @@ int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, i
       tiles += (int)((it.n + 15) / 16);
     }
     grp.tile_start[grp.count] = tiles;
-    hipError_t e = f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, y_dtype == FAIRY2I_BF16, stream);
-    if (e != hipSuccess) return hip_status(e, "gemv (grouped bf16 mfma) launch");
+    hipError_t e = kernel == FAIRY2I_GEMV_MFMA_I8
+                       ? f2i::launch_gemv_i8_group(grp, (int)m, T, (int)B, y_dtype == FAIRY2I_BF16, stream)
+                       : f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, y_dtype == FAIRY2I_BF16, stream);
+    if (e != hipSuccess) return hip_status(e, "gemv (grouped mfma) launch");
   }
   return ok();
 }

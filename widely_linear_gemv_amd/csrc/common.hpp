@@ -43,6 +43,18 @@ struct GemvItem {
   void* y;
   int n;
 };
+// Packed form: 16-code words ordered per 16-row tile as [chunk of 256 columns][plane P = 2t+M]
+// [64-column group < G_c][row][word < 4], tiles one after another, the last tile padded with
+// rows of code 0.  Word index of word wq (columns 16wq .. 16wq+15) of plane P of row i:
+__host__ __device__ __forceinline__ int64_t tiled_word(int i, int P, int wq, int m, int T) {
+  const int c = wq >> 4, g = (wq >> 2) & 3, w = wq & 3;
+  const int groups = min(4, (m - 256 * c) >> 6);        // 64-column groups in chunk c
+  return (int64_t)(i >> 4) * 16 * (2 * T) * (m >> 4)    // 16 rows x 2T planes x m/16 words
+       + (int64_t)c * (2 * T) * 256                      // full chunks before c
+       + P * groups * 64 + g * 64 + (i & 15) * 4 + w;
+}
+__host__ __device__ __forceinline__ int padded_rows(int n) { return (n + 15) & ~15; }
+
 constexpr int kMaxGroup = 48;   // items per launch; the table travels in the kernel arguments
 struct GemvGroup {
   int count;
@@ -58,7 +70,10 @@ hipError_t launch_gemv_valu(const uint8_t* packed, const float* scales, int n, i
 hipError_t launch_gemv_mfma(const uint8_t* packed, const float* scales, int n, int m, int T,
                             const void* x, int B, void* y, int y_bf16, void* unused, hipStream_t s);
 hipError_t launch_gemv_i8(const uint8_t* packed, const float* scales, int n, int m, int T,
-                          const void* x, int B, void* y, int y_bf16, hipStream_t s);
+                          const void* digits, int B, void* y, int y_bf16, hipStream_t s);
+hipError_t launch_gemv_i8_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
+size_t x_digits_bytes(int64_t m, int64_t B);
+hipError_t launch_x_digits(const void* x, int x_bf16, int m, int B, void* blob, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int x_bf16, int N, int two_m, int8_t* q, float* delta,
                             hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* scales, int n, int m, int T,

@@ -5,25 +5,30 @@
 // (B_re, B_im in {-1, 0, 1}; products reduce to additions, subtractions, skips); 36Kr article,
 // parallel stages.
 //
-// Weight planes are int8 {-1, 0, +1}; x enters as an exact integer: every bf16 value of a batch
-// column is scaled by one power of two 2^S (chosen so that max|x| * 2^S < 2^22) and rounded to
-// an integer X, which is split into three signed int8 digits X = l0 + 2^8 l1 + 2^16 l2.  All
-// products and sums are then exact int32 arithmetic (v_mfma_i32_16x16x64_i8); the only rounding
-// is X itself (relative 2^-23 of the column maximum; none for bf16 values within 2^14 of it)
-// and the fp32 epilogue.  Why not bf16 MFMA here: on gfx950 MFMA and VALU time add, and this
-// form costs half the MFMA cycles and ~0.94 instead of ~1.5 VALU operations per code.
+// Weight planes are int8 {-1, 0, +1}; x enters as an exact integer.  A separate pass turns x
+// into its digit form once: each batch column b is scaled by one power of two 2^S_b (chosen so
+// that max|x_b| 2^S_b lies in [2^21, 2^22)) and rounded to an integer X, split into three signed
+// int8 digits X = d0 + 2^8 d1 + 2^16 d2.  All products and sums of the GEMV are then exact
+// int32 arithmetic (v_mfma_i32_16x16x64_i8); the only roundings are X itself (none for a bf16
+// value no more than 2^14 below its column maximum) and the fp32 epilogue.  Against the bf16
+// matrix-core form this halves the MFMA cycles per code (64 columns per instruction instead of
+// 32) and needs ~0.94 instead of ~1.5 VALU operations per code for the planes; on gfx950 the
+// two add up on a SIMD, so their sum sets the speed once the codes stream at full bandwidth.
 //
+//  * Digit form (one buffer per x): int32 header [B, m, S_0, S_1] in the first 64 bytes, then
+//    int8 [B][2][4][m] -- batch column, component (a = Re x, b = Im x), digit slot (3 = zero).
 //  * Codes -> planes: the packed word of 16 codes holds code 4d+b in bits 8b+2d..8b+2d+1, so
 //    (w >> 2d) & 0x03030303 puts codes 4d..4d+3 in bytes 0..3 (column order), and v_perm_b32
 //    maps each byte through the 4-entry tables {+1, 0, -1, 0} (B_re) and {0, +1, 0, -1} (B_im).
-//  * K assignment: a workgroup owns 16 complex rows; its waves take 256-column chunks in turn.
-//    In a chunk lane group g owns columns 64g..64g+63 (one 16-byte load of 4 packed words per
-//    plane) and at MFMA step s = 0..3 contributes columns 64g+16s..64g+16s+15.
-//  * x digits live in LDS, converted once per workgroup: column c = 8b + 4comp + l of the MFMA
-//    (batch b, component a = Re x / b = Im x, digit l, slot 3 empty), row stride m + 16 bytes.
-//  * Epilogue: each lane scales its int32 sums by 2^(8l-S) and the fp32 axis scales, then the
-//    digits and components of a batch column are summed across lanes (xor 1, 2, 4) and the waves
-//    through LDS in a fixed order.
+//  * B operand: MFMA column c = 8b + 4comp + l holds digit l of component comp of batch entry
+//    b; lane (c, g) loads the 16 digits of its k-group straight from the digit form.
+//  * K assignment and grouping as in the bf16 kernel: one wave owns a 16-row tile of one item
+//    of a grouped call and streams its 256-column chunks, one 1 KB load per plane, prefetching
+//    the next chunk's codes and digits while the current one is decoded and multiplied.  In a
+//    chunk lane group g owns columns 64g..64g+63 and at MFMA step s contributes columns
+//    64g+16s..+15.
+//  * Epilogue: each lane scales its int32 sums by 2^(8l - S_b) and the fp32 axis scales, and
+//    the digits and components of a batch entry are summed across lanes (xor 1, 2, 4).
 #include "common.hpp"
 
 namespace f2i {
@@ -31,8 +36,13 @@ namespace f2i {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kI8Chunk = 256;
-constexpr int kI8MaxWaves = 8;
-constexpr int kI8Stride = 16;       // LDS row padding (bytes) against bank conflicts
+constexpr int kDigitHeader = 64;     // bytes before the digits in the digit form
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t i8_rsrc(const void* base, int64_t bytes) {
+  const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFF00);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+constexpr uint32_t kI8NoLoad = 0x80000000u;   // buffer offset past every range: the load returns 0
 
 __device__ __forceinline__ void decode_i8(uint32_t w, v4i& re, v4i& im) {
   constexpr uint32_t lo2 = 0x03030303u;
@@ -45,151 +55,200 @@ __device__ __forceinline__ void decode_i8(uint32_t w, v4i& re, v4i& im) {
            (int)__builtin_amdgcn_perm(0u, kIm, k2), (int)__builtin_amdgcn_perm(0u, kIm, k3)};
 }
 
-// Power-of-two exponent S with amax * 2^S < 2^22 (0 for an all-zero column).
+// Power-of-two exponent S with amax * 2^S in [2^21, 2^22) (0 for an all-zero column).
 __device__ __forceinline__ int digit_exponent(float amax) {
   if (!(amax > 0.f)) return 0;
   const int e = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;   // floor(log2 amax), normal
   return 21 - (e < -126 ? -126 : e);
 }
 
+// ------------------------------------------------------------------ digit form of x ----
+
+template <typename XT> struct Load8x;
+template <> struct Load8x<float> {
+  __device__ static void run(const float* p, float* v) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+template <> struct Load8x<uint16_t> {
+  __device__ static void run(const uint16_t* p, float* v) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  }
+};
+
+// One workgroup per batch column: max |x| (order-free, exact), S, then the digits of all 2m
+// values and the zero slot.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_x_digits(const XT* __restrict__ x, int m, int B,
+                                                  uint8_t* __restrict__ blob) {
+  __shared__ float s_max[256 / kWave];
+  const int b = blockIdx.x;
+  const XT* __restrict__ xb = x + (int64_t)b * 2 * m;
+  float amax = 0.f;
+  for (int j = threadIdx.x * 8; j < 2 * m; j += 256 * 8) {
+    float v[8];
+    Load8x<XT>::run(xb + j, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & (kWave - 1)) == 0) s_max[threadIdx.x / kWave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const int S = digit_exponent(amax);
+  int* hdr = reinterpret_cast<int*>(blob);
+  if (threadIdx.x == 0) {
+    if (b == 0) { hdr[0] = B; hdr[1] = m; }
+    hdr[2 + b] = S;
+  }
+  int8_t* __restrict__ dg = reinterpret_cast<int8_t*>(blob + kDigitHeader) + (int64_t)b * 8 * m;
+  for (int j2 = threadIdx.x * 8; j2 < 2 * m; j2 += 256 * 8) {
+    const int comp = j2 / m, j = j2 % m;         // m % 64 == 0: 8 values never straddle comps
+    float v[8];
+    Load8x<XT>::run(xb + j2, v);
+    uint32_t d[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int X = (int)rintf(ldexpf(v[e], S));     // |X| <= 2^22, scaling exact
+      const int l0 = ((X + 128) & 255) - 128;
+      const int X1 = (X - l0) >> 8;
+      const int l1 = ((X1 + 128) & 255) - 128;
+      const int l2 = (X1 - l1) >> 8;
+      const int sh = 8 * (e & 3);
+      d[0][e >> 2] |= (uint32_t)(l0 & 255) << sh;
+      d[1][e >> 2] |= (uint32_t)(l1 & 255) << sh;
+      d[2][e >> 2] |= (uint32_t)(l2 & 255) << sh;
+    }
+    int8_t* base = dg + (int64_t)comp * 4 * m + j;
+#pragma unroll
+    for (int l = 0; l < 3; ++l) *reinterpret_cast<uint2*>(base + (int64_t)l * m) = make_uint2(d[l][0], d[l][1]);
+    *reinterpret_cast<uint2*>(base + (int64_t)3 * m) = make_uint2(0u, 0u);
+  }
+}
+
+size_t x_digits_bytes(int64_t m, int64_t B) { return (size_t)kDigitHeader + (size_t)B * 8 * (size_t)m; }
+
+hipError_t launch_x_digits(const void* x, int x_bf16, int m, int B, void* blob, hipStream_t s) {
+  if (x_bf16)
+    hipLaunchKernelGGL(k_x_digits<uint16_t>, dim3(B), dim3(256), 0, s, static_cast<const uint16_t*>(x), m, B,
+                       static_cast<uint8_t*>(blob));
+  else
+    hipLaunchKernelGGL(k_x_digits<float>, dim3(B), dim3(256), 0, s, static_cast<const float*>(x), m, B,
+                       static_cast<uint8_t*>(blob));
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------- GEMV ----
+
+__device__ __forceinline__ int find_item_i8(const GemvGroup& g, int tile) {
+  int lo = 0, hi = g.count - 1;
+  while (lo < hi) {                       // last item with tile_start <= tile
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 template <int TT, typename YT>
-__global__ __launch_bounds__(64 * kI8MaxWaves) void k_gemv_i8(
-    const uint8_t* __restrict__ packed, const float* __restrict__ scales, int n, int m,
-    const uint16_t* __restrict__ x, int B, YT* __restrict__ y) {
-  extern __shared__ __align__(16) int8_t s_x[];          // [16 columns][m + 16]
-  __shared__ float s_sc[16][TT][4];
-  __shared__ float s_y[kI8MaxWaves][2][2][16];             // [wave][batch][re/im][row]
-  __shared__ float s_max[kI8MaxWaves][2];
-  const int nw = blockDim.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+__global__ __launch_bounds__(kWave) void k_gemv_i8(const GemvGroup grp, int m, int B) {
+  const int item = find_item_i8(grp, blockIdx.x);
+  const GemvItem it = grp.items[item];
+  const int n = it.n;
+  const uint8_t* __restrict__ packed = static_cast<const uint8_t*>(it.packed);
+  const float* __restrict__ scales = it.scales;
+  const uint8_t* __restrict__ blob = static_cast<const uint8_t*>(it.x);
+  YT* __restrict__ y = static_cast<YT*>(it.y);
+
+  const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
-  const int i0 = blockIdx.x * 16;
-  const int ia = i0 + r;
-  const bool a_ok = ia < n;
-  const int dw_plane = m / 16;
-  const int ld = m + kI8Stride;
-  const uint32_t* __restrict__ arow =
-      reinterpret_cast<const uint32_t*>(packed) + (int64_t)(a_ok ? ia : 0) * (TT * 2 * dw_plane);
-  const int nchunk = (m + kI8Chunk - 1) / kI8Chunk;
+  const int tile = blockIdx.x - grp.tile_start[item];
+  const int i0 = tile * 16;
+  const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
+  // The tile's codes and the digit form through buffer resources: batch entries past B read 0,
+  // and so does every load of a lane group past column m (offset kI8NoLoad).
+  const __amdgpu_buffer_rsrc_t rsrc_a = i8_rsrc(packed + (int64_t)tile * tile_bytes, tile_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc_x = i8_rsrc(blob + kDigitHeader, (int64_t)B * 8 * m);
+  const uint32_t voff_x = (uint32_t)(r * m);          // column r = 8b + 4comp + l -> slot r
 
-  // 1. issue the code loads of the first chunk before anything else
-  uint4 wd[TT][2];
-  auto load_codes = [&](int c) {
-    const int jg = c * kI8Chunk + 64 * g;
-    const bool k_ok = a_ok && jg < m;
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-      for (int M = 0; M < 2; ++M)
-        wd[t][M] = k_ok ? *reinterpret_cast<const uint4*>(arow + (t * 2 + M) * dw_plane + jg / 16)
-                        : make_uint4(0u, 0u, 0u, 0u);
-  };
-  if (wave < nchunk) load_codes(wave);
-
-  // 2. scales of the tile -> LDS
-  for (int idx = threadIdx.x; idx < 16 * TT * 4; idx += blockDim.x) {
-    const int row = idx / (TT * 4), rest = idx % (TT * 4);
-    const int i = i0 + row;
-    s_sc[row][rest / 4][rest % 4] = i < n ? scales[(int64_t)i * TT * 4 + rest] : 0.f;
-  }
-
-  // 3. x -> exact int8 digits in LDS.  Pass one: column maxima.
-  const int per_b = 2 * m;                        // values per batch column
-  float amax[2] = {0.f, 0.f};
-  for (int b = 0; b < B; ++b)
-    for (int j = threadIdx.x * 8; j < per_b; j += blockDim.x * 8) {
-      const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)b * per_b + j);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) amax[b] = fmaxf(amax[b], fmaxf(fabsf(bf16_lo(w4[h])), fabsf(bf16_hi(w4[h]))));
-    }
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) amax[b] = fmaxf(amax[b], __shfl_xor(amax[b], off));
-    if (lane == 0) s_max[wave][b] = amax[b];
-  }
-  __syncthreads();
-  int S[2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    float mx = 0.f;
-    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, s_max[w][b]);
-    S[b] = digit_exponent(mx);
-  }
-  // Pass two: digits.  Column c = 8b + 4comp + l; slots l = 3 and batches >= B are zero.
-  for (int idx = threadIdx.x * 8; idx < 2 * per_b; idx += blockDim.x * 8) {
-    const int b = idx / per_b, j2 = idx % per_b;       // j2 in [0, 2m): comp = j2 / m
-    const int comp = j2 / m, j = j2 % m;
-    uint32_t dg[3][2] = {{0, 0}, {0, 0}, {0, 0}};
-    if (b < B) {
-      const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)b * per_b + j2);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xv = (e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1]);
-        const int X = (int)rintf(ldexpf(xv, S[b]));    // |X| < 2^22, exact scaling
-        const int l0 = ((X + 128) & 255) - 128;
-        const int X1 = (X - l0) >> 8;
-        const int l1 = ((X1 + 128) & 255) - 128;
-        const int l2 = (X1 - l1) >> 8;
-        const int sh = 8 * (e & 3);
-        dg[0][e >> 2] |= (uint32_t)(l0 & 255) << sh;
-        dg[1][e >> 2] |= (uint32_t)(l1 & 255) << sh;
-        dg[2][e >> 2] |= (uint32_t)(l2 & 255) << sh;
-      }
-    }
-#pragma unroll
-    for (int l = 0; l < 3; ++l)
-      *reinterpret_cast<uint2*>(s_x + (int64_t)(8 * b + 4 * comp + l) * ld + j) = make_uint2(dg[l][0], dg[l][1]);
-  }
-  // zero the empty columns (l = 3 of every (b, comp)) once; they are never written above
-  for (int idx = threadIdx.x * 8; idx < 4 * m; idx += blockDim.x * 8) {
-    const int q = idx / m, j = idx % m;                // q = 2b + comp
-    *reinterpret_cast<uint2*>(s_x + (int64_t)(4 * q + 3) * ld + j) = make_uint2(0u, 0u);
-  }
-  __syncthreads();
-
-  // 4. main loop
   v4i acc[TT][2][2];
 #pragma unroll
   for (int t = 0; t < TT; ++t)
 #pragma unroll
     for (int M = 0; M < 2; ++M) { acc[t][M][0] = v4i{0, 0, 0, 0}; acc[t][M][1] = v4i{0, 0, 0, 0}; }
-  const int8_t* xcol = s_x + (int64_t)r * ld;          // B column r of this lane
-  for (int c = wave; c < nchunk; c += nw) {
-    const int jg = c * kI8Chunk + 64 * g;
-    const bool k_ok = jg < m;
+
+  const int nchunk = (m + kI8Chunk - 1) / kI8Chunk;
+  // Operands of one chunk: every plane's 16-row x 256-column block (1 KB when the chunk is full:
+  // lane l = 16g + r takes row r, columns 64g..64g+63) and the digits of every MFMA step.
+  struct Chunk { uint4 w[TT][2]; v4i x[4]; };
+  auto load_chunk = [&](int c, Chunk& ch) {
+    const int groups = min(4, (m - kI8Chunk * c) >> 6);
+    const bool k_ok = g < groups;
+    const uint32_t cbase = (uint32_t)c * (TT * 2) * 1024;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const v4i bv = k_ok ? *reinterpret_cast<const v4i*>(xcol + jg + 16 * s) : v4i{0, 0, 0, 0};
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int M = 0; M < 2; ++M)
+        ch.w[t][M] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kI8NoLoad, 0, 0));
+    const int jg = c * kI8Chunk + 64 * g;            // first column of this lane group
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      ch.x[s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc_x, k_ok ? voff_x + (uint32_t)(jg + 16 * s) : kI8NoLoad, 0, 0));
+  };
+  auto compute_chunk = [&](const Chunk& ch) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int t = 0; t < TT; ++t)
 #pragma unroll
         for (int M = 0; M < 2; ++M) {
-          const uint4 q = wd[t][M];
+          const uint4 q = ch.w[t][M];
           const uint32_t w = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
           v4i are, aim;
           decode_i8(w, are, aim);
-          acc[t][M][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(are, bv, acc[t][M][0], 0, 0, 0);
-          acc[t][M][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aim, bv, acc[t][M][1], 0, 0, 0);
+          acc[t][M][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(are, ch.x[s], acc[t][M][0], 0, 0, 0);
+          acc[t][M][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aim, ch.x[s], acc[t][M][1], 0, 0, 0);
         }
+  };
+  // The chunks stream through two operand sets; the scheduling barriers keep each prefetch
+  // ahead of the compute it overlaps (the scheduler would otherwise sink the loads to their
+  // use), and the prefetch is unconditional (the last one reloads the last chunk) so every path
+  // has the same loads in flight.
+  {
+    Chunk c0, c1;
+    load_chunk(0, c0);
+    int c = 0;
+    for (; c + 1 < nchunk; c += 2) {
+      load_chunk(c + 1, c1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk(c0);
+      load_chunk(min(c + 2, nchunk - 1), c0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk(c1);
     }
-    if (c + nw < nchunk) load_codes(c + nw);
+    if (c < nchunk) compute_chunk(c0);
   }
 
-  // 5. epilogue.  Lane holds rows 4g..4g+3 of column r = 8b + 4comp + l.
+  // Epilogue.  Lane holds rows 4g..4g+3 of column r = 8b + 4comp + l.
   const int bl = r >> 3, comp = (r >> 2) & 1, l = r & 3;
-  const float wdig = ldexpf(1.0f, 8 * l - (bl < 2 ? S[bl] : 0));
+  const int* hdr = reinterpret_cast<const int*>(blob);
+  const int S = bl < B ? hdr[2 + bl] : 0;
+  const float wdig = ldexpf(1.0f, 8 * l - S);
+  const int64_t ys = 2 * (int64_t)n;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int row = 4 * g + e;
+    const int i = i0 + 4 * g + e;
+    const float* sc = scales + (int64_t)min(i, n - 1) * TT * 4;
     float vre = 0.f, vim = 0.f;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      const float sUr = s_sc[row][t][0], sUi = s_sc[row][t][1];
-      const float sWr = s_sc[row][t][2], sWi = s_sc[row][t][3];
+      const float sUr = sc[4 * t], sUi = sc[4 * t + 1], sWr = sc[4 * t + 2], sWi = sc[4 * t + 3];
       const float CUr = (float)acc[t][0][0][e], CUi = (float)acc[t][0][1][e];
       const float CWr = (float)acc[t][1][0][e], CWi = (float)acc[t][1][1][e];
       if (comp == 0) {    // a = Re x:  Re += sUr*P(U,re) + sWr*P(W,re) ; Im += sUi*P(U,im) + sWi*P(W,im)
@@ -207,60 +266,45 @@ __global__ __launch_bounds__(64 * kI8MaxWaves) void k_gemv_i8(
       vre += __shfl_xor(vre, off);
       vim += __shfl_xor(vim, off);
     }
-    if ((r & 7) == 0) {
-      s_y[wave][bl][0][row] = vre;
-      s_y[wave][bl][1][row] = vim;
-    }
-  }
-  __syncthreads();
-  const int64_t ys = 2 * (int64_t)n;
-  for (int idx = threadIdx.x; idx < 2 * 2 * 16; idx += blockDim.x) {
-    const int row = idx & 15, part = (idx >> 4) & 1, b = idx >> 5;
-    const int i = i0 + row;
-    if (b < B && i < n) {
-      float v = s_y[0][b][part][row];
-      for (int w = 1; w < nw; ++w) v += s_y[w][b][part][row];
-      store_out(y, (int64_t)b * ys + (part ? n + i : i), v);
+    if ((r & 7) == 0 && bl < B && i < n) {
+      store_out(y, (int64_t)bl * ys + i, vre);
+      store_out(y, (int64_t)bl * ys + n + i, vim);
     }
   }
 }
 
-size_t gemv_i8_lds_bytes(int m) { return (size_t)16 * (m + kI8Stride); }
+template <int TT, typename YT>
+static void launch_i8_t(const GemvGroup& grp, int m, int B, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv_i8<TT, YT>), dim3(grp.tile_start[grp.count]), dim3(kWave), 0, s, grp, m, B);
+}
 
-hipError_t launch_gemv_i8(const uint8_t* packed, const float* scales, int n, int m, int T,
-                          const void* x, int B, void* y, int y_bf16, hipStream_t s) {
-  const int nchunk = (m + kI8Chunk - 1) / kI8Chunk;
-  const int nw = nchunk < kI8MaxWaves ? nchunk : kI8MaxWaves;
-  const dim3 grid((n + 15) / 16), block(64 * nw);
-  const size_t lds = gemv_i8_lds_bytes(m);
-  const uint16_t* xx = static_cast<const uint16_t*>(x);
-#define F2I_GEMV_I8(TT, YT)                                                                       \
-  do {                                                                                            \
-    auto kern = k_gemv_i8<TT, YT>;                                                                \
-    if (lds > 65536) {                                                                            \
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                     \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);   \
-      if (e != hipSuccess) return e;                                                              \
-    }                                                                                             \
-    hipLaunchKernelGGL(kern, grid, block, lds, s, packed, scales, n, m, xx, B, static_cast<YT*>(y)); \
-  } while (0)
+hipError_t launch_gemv_i8_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s) {
   if (y_bf16) {
     switch (T) {
-      case 1: F2I_GEMV_I8(1, uint16_t); break;
-      case 2: F2I_GEMV_I8(2, uint16_t); break;
-      case 3: F2I_GEMV_I8(3, uint16_t); break;
-      default: F2I_GEMV_I8(4, uint16_t); break;
+      case 1: launch_i8_t<1, uint16_t>(grp, m, B, s); break;
+      case 2: launch_i8_t<2, uint16_t>(grp, m, B, s); break;
+      case 3: launch_i8_t<3, uint16_t>(grp, m, B, s); break;
+      default: launch_i8_t<4, uint16_t>(grp, m, B, s); break;
     }
   } else {
     switch (T) {
-      case 1: F2I_GEMV_I8(1, float); break;
-      case 2: F2I_GEMV_I8(2, float); break;
-      case 3: F2I_GEMV_I8(3, float); break;
-      default: F2I_GEMV_I8(4, float); break;
+      case 1: launch_i8_t<1, float>(grp, m, B, s); break;
+      case 2: launch_i8_t<2, float>(grp, m, B, s); break;
+      case 3: launch_i8_t<3, float>(grp, m, B, s); break;
+      default: launch_i8_t<4, float>(grp, m, B, s); break;
     }
   }
-#undef F2I_GEMV_I8
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_i8(const uint8_t* packed, const float* scales, int n, int m, int T,
+                          const void* digits, int B, void* y, int y_bf16, hipStream_t s) {
+  GemvGroup grp;
+  grp.count = 1;
+  grp.tile_start[0] = 0;
+  grp.tile_start[1] = (n + 15) / 16;
+  grp.items[0] = GemvItem{packed, scales, digits, y, n};
+  return launch_gemv_i8_group(grp, m, T, B, y_bf16, s);
 }
 
 }  // namespace f2i

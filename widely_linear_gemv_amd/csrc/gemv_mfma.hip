@@ -19,11 +19,12 @@
 //        re = im ^ 0x40004000            gives the real-axis plane
 //    -- 1.5 VALU operations per code for both planes.  Element order inside a lane is
 //    (0, 2, 1, 3, 4, 6, 5, 7) of each 8-code group; the B operand is permuted to match.
-//  * K assignment: a workgroup handles 16 rows; its waves (up to 8) take 256-column chunks in
-//    turn.  In a chunk, lane group g owns columns 64g..64g+63 (one 16-byte load of 4 words per
-//    plane) and at MFMA step s = 0..7 contributes columns 64g+8s .. 64g+8s+7.  All loads of a
-//    chunk (codes of every plane, x of every step) are issued before the first MFMA, and the
-//    rows' scales are staged in LDS at kernel start: a small layer is one memory round trip.
+//  * K assignment: one wave owns a 16-row tile and streams its 256-column chunks, the next
+//    chunk's loads in flight while the current one is multiplied.  The packed form stores a
+//    tile's (chunk, plane) block as 16 rows x 64-column groups of 16 bytes in [group][row]
+//    order, so each plane of a chunk is one 1 KB load with lane l = 16g + r taking row r,
+//    columns 64g..64g+63; at MFMA step s = 0..7 lane group g contributes columns
+//    64g+8s .. 64g+8s+7.
 //  * Grouped launches: one grid covers the row tiles of several GEMVs of the same m (for
 //    example the q, k and v projections that share x); each workgroup finds its GEMV by binary
 //    search over the first-tile table passed in the kernel arguments.
@@ -31,9 +32,8 @@
 //    columns per MFMA, two column groups for B > 8.  Each lane loads 8 consecutive bf16 of x and
 //    swaps elements 1,2 and 5,6 with v_perm_b32.
 //  * One 16x16 fp32 accumulator per (stage, matrix, plane, column group).  The epilogue applies
-//    the fp32 scales (and the factor 1/2 of the +-2 encoding) once per accumulated sum, adds the
-//    a and b columns of a batch entry across two lanes, and sums the waves through LDS in a
-//    fixed order.
+//    the fp32 scales (and the factor 1/2 of the +-2 encoding) once per accumulated sum and adds
+//    the a and b columns of a batch entry across two lanes.
 #include "common.hpp"
 
 namespace f2i {
@@ -42,9 +42,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kChunk = 256;        // columns per wave work unit
-constexpr int kMaxWaves = 8;       // upper bound of waves per 16-row tile (LDS sizing)
-constexpr int kWavesPerTile = 4;   // waves per tile; each streams its chunks with prefetch
+constexpr int kChunk = 256;        // columns per chunk of the packed form
 
 // Eight codes (h = which half of the word) of one packed word -> A operands of both planes.
 template <int H>
@@ -65,6 +63,13 @@ __device__ __forceinline__ v4u permute_b(uint4 w) {
              __builtin_amdgcn_perm(w.w, w.z, 0x05040100u), __builtin_amdgcn_perm(w.w, w.z, 0x07060302u)};
 }
 
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, int64_t bytes) {
+  const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFF00);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+constexpr uint32_t kNoLoad = 0x80000000u;   // buffer offset past every range: the load returns 0
+
 // Workgroup tile -> GEMV item: first tile of every item (tile_start[count] = total tiles).
 __device__ __forceinline__ int find_item(const GemvGroup& g, int tile) {
   int lo = 0, hi = g.count - 1;
@@ -76,9 +81,7 @@ __device__ __forceinline__ int find_item(const GemvGroup& g, int tile) {
 }
 
 template <int TT, int CG, typename YT>
-__global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_mfma(const GemvGroup grp, int m, int B) {
-  __shared__ float s_sc[16][TT][4];              // halved scales of the tile's rows
-  __shared__ float s_y[kMaxWaves][16][2][16];    // [wave][batch][re/im][row]
+__global__ __launch_bounds__(kWave) void k_gemv_mfma(const GemvGroup grp, int m, int B) {
   const int item = find_item(grp, blockIdx.x);
   const GemvItem it = grp.items[item];
   const int n = it.n;
@@ -87,34 +90,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_mfma(const GemvGroup gr
   const uint16_t* __restrict__ x = static_cast<const uint16_t*>(it.x);
   YT* __restrict__ y = static_cast<YT*>(it.y);
 
-  const int nw = blockDim.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
-  const int i0 = (blockIdx.x - grp.tile_start[item]) * 16;
-  const int ia = i0 + r;
-  const bool a_ok = ia < n;
-  const int dw_plane = m / 16;
-  const uint32_t* __restrict__ arow =
-      reinterpret_cast<const uint32_t*>(packed) + (int64_t)(a_ok ? ia : 0) * (TT * 2 * dw_plane);
-
-  // Scales of the 16 rows go to LDS now, so the epilogue needs no global round trip.
-  for (int idx = threadIdx.x; idx < 16 * TT * 4; idx += blockDim.x) {
-    const int row = idx / (TT * 4), rest = idx % (TT * 4);
-    const int i = i0 + row;
-    s_sc[row][rest / 4][rest % 4] = i < n ? 0.5f * scales[(int64_t)i * TT * 4 + rest] : 0.f;
-  }
+  const int tile = blockIdx.x - grp.tile_start[item];
+  const int i0 = tile * 16;
+  const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
+  // The tile's codes and x through buffer resources: batch entries past B read 0, and so does
+  // every load of a lane group past column m (offset kNoLoad).
+  const __amdgpu_buffer_rsrc_t rsrc_a = gemv_rsrc(packed + (int64_t)tile * tile_bytes, tile_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc_x = gemv_rsrc(x, (int64_t)B * 2 * m * 2);
 
   // B column of this lane: batch b = 8*cg + (r >> 1), component r & 1
   const int comp = r & 1;
-  const uint16_t* xb[CG];
-  bool b_ok[CG];
+  uint32_t voff_x[CG];
 #pragma unroll
-  for (int cg = 0; cg < CG; ++cg) {
-    const int b = cg * 8 + (r >> 1);
-    b_ok[cg] = b < B;
-    xb[cg] = x + (int64_t)(b_ok[cg] ? b : 0) * 2 * m + comp * m;
-  }
+  for (int cg = 0; cg < CG; ++cg) voff_x[cg] = (uint32_t)(((cg * 8 + (r >> 1)) * 2 * m + comp * m) * 2);
 
   v4f acc[TT][2][2][CG];
 #pragma unroll
@@ -127,40 +117,39 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_mfma(const GemvGroup gr
         for (int cg = 0; cg < CG; ++cg) acc[t][M][p][cg] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int nchunk = (m + kChunk - 1) / kChunk;
-  constexpr bool kPrefetch = CG == 1;              // two column groups need the registers
-  uint4 wd[TT][2], xr[8][CG];                      // operands of the chunk being computed
-  auto load_chunk = [&](int c, uint4 (&w)[TT][2], uint4 (&xx)[8][CG]) {
-    const int jg = c * kChunk + 64 * g;            // first column of this lane group
-    const bool k_ok = c < nchunk && jg < m;        // m % 64 == 0: a group is all in or all out
+  // Operands of one chunk: every plane's 16-row x 256-column block (1 KB when the chunk is
+  // full: lane l = 16g + r takes bytes 16l.., i.e. row r, columns 64g..64g+63) and x of every
+  // MFMA step.
+  struct Chunk { uint4 w[TT][2]; uint4 x[8][CG]; };
+  auto load_chunk = [&](int c, Chunk& ch) {
+    const int groups = min(4, (m - kChunk * c) >> 6);
+    const bool k_ok = g < groups;
+    const uint32_t cbase = (uint32_t)c * (TT * 2) * 1024;
 #pragma unroll
     for (int t = 0; t < TT; ++t)
 #pragma unroll
       for (int M = 0; M < 2; ++M)
-        w[t][M] = (a_ok && k_ok)
-            ? *reinterpret_cast<const uint4*>(arow + (t * 2 + M) * dw_plane + jg / 16)
-            : make_uint4(0u, 0u, 0u, 0u);
+        ch.w[t][M] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, 0));
+    const int jg = c * kChunk + 64 * g;            // first column of this lane group
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg)
-        xx[s][cg] = (b_ok[cg] && k_ok) ? *reinterpret_cast<const uint4*>(xb[cg] + jg + 8 * s)
-                                       : make_uint4(0u, 0u, 0u, 0u);
+        ch.x[s][cg] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            rsrc_x, k_ok ? voff_x[cg] + (uint32_t)((jg + 8 * s) * 2) : kNoLoad, 0, 0));
   };
-  load_chunk(wave, wd, xr);
-  for (int c = wave; c < nchunk; c += nw) {
-    // prefetch the next chunk of this wave while the current one is decoded and multiplied
-    uint4 wn[TT][2], xn[8][CG];
-    if (kPrefetch && c + nw < nchunk) load_chunk(c + nw, wn, xn);
+  auto compute_chunk = [&](const Chunk& ch) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       v4u bv[CG];
 #pragma unroll
-      for (int cg = 0; cg < CG; ++cg) bv[cg] = permute_b(xr[s][cg]);
+      for (int cg = 0; cg < CG; ++cg) bv[cg] = permute_b(ch.x[s][cg]);
 #pragma unroll
       for (int t = 0; t < TT; ++t)
 #pragma unroll
         for (int M = 0; M < 2; ++M) {
-          const uint4 q = wd[t][M];
+          const uint4 q = ch.w[t][M];
           const uint32_t w = (s >> 1) == 0 ? q.x : (s >> 1) == 1 ? q.y : (s >> 1) == 2 ? q.z : q.w;
           v4u are, aim;
           if (s & 1) decode_bf16<1>(w, are, aim); else decode_bf16<0>(w, are, aim);
@@ -173,32 +162,41 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_mfma(const GemvGroup gr
           }
         }
     }
-    if (!kPrefetch) {
-      if (c + nw < nchunk) load_chunk(c + nw, wd, xr);
-    } else if (c + nw < nchunk) {
-#pragma unroll
-      for (int t = 0; t < TT; ++t)
-#pragma unroll
-        for (int M = 0; M < 2; ++M) wd[t][M] = wn[t][M];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int cg = 0; cg < CG; ++cg) xr[s][cg] = xn[s][cg];
+  };
+  // The chunks stream through two operand sets: the next chunk's loads are issued before the
+  // current one is decoded and multiplied.  The scheduling barriers keep each prefetch ahead of
+  // the compute it overlaps (the scheduler would otherwise sink the loads to their use), and
+  // the prefetch is unconditional (the last one reloads the last chunk) so every path has the
+  // same loads in flight.
+  {
+    Chunk c0, c1;
+    load_chunk(0, c0);
+    int c = 0;
+    for (; c + 1 < nchunk; c += 2) {
+      load_chunk(c + 1, c1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk(c0);
+      load_chunk(min(c + 2, nchunk - 1), c0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk(c1);
     }
+    if (c < nchunk) compute_chunk(c0);
   }
-  __syncthreads();                                 // s_sc is ready
 
-  // Epilogue.  C tile: lane holds rows 4g..4g+3 of column r = 2*bl + comp.
+  // Epilogue.  C tile: lane holds rows 4g..4g+3 of column r = 2*bl + comp.  Scales are halved
+  // (the planes carry +-2).
+  const int64_t ys = 2 * (int64_t)n;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int row = 4 * g + e;
+    const int i = i0 + 4 * g + e;
+    const float* sc = scales + (int64_t)min(i, n - 1) * TT * 4;
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
       float vre = 0.f, vim = 0.f;
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-        const float sUr = s_sc[row][t][0], sUi = s_sc[row][t][1];
-        const float sWr = s_sc[row][t][2], sWi = s_sc[row][t][3];
+        const float sUr = 0.5f * sc[4 * t], sUi = 0.5f * sc[4 * t + 1];
+        const float sWr = 0.5f * sc[4 * t + 2], sWi = 0.5f * sc[4 * t + 3];
         const float CUr = acc[t][0][0][cg][e], CUi = acc[t][0][1][cg][e];
         const float CWr = acc[t][1][0][cg][e], CWi = acc[t][1][1][cg][e];
         if (comp == 0) {    // a = Re x:  Re += sUr*P(U,re) + sWr*P(W,re) ; Im += sUi*P(U,im) + sWi*P(W,im)
@@ -211,30 +209,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_mfma(const GemvGroup gr
       }
       vre += __shfl_xor(vre, 1);
       vim += __shfl_xor(vim, 1);
-      if (comp == 0) {
-        s_y[wave][cg * 8 + (r >> 1)][0][row] = vre;
-        s_y[wave][cg * 8 + (r >> 1)][1][row] = vim;
+      const int b = cg * 8 + (r >> 1);
+      if (comp == 0 && b < B && i < n) {
+        store_out(y, (int64_t)b * ys + i, vre);
+        store_out(y, (int64_t)b * ys + n + i, vim);
       }
-    }
-  }
-  __syncthreads();
-  const int64_t ys = 2 * (int64_t)n;
-  for (int idx = threadIdx.x; idx < 16 * 2 * 16; idx += blockDim.x) {
-    const int row = idx & 15, part = (idx >> 4) & 1, b = idx >> 5;
-    const int i = i0 + row;
-    if (b < B && i < n) {
-      float v = s_y[0][b][part][row];
-      for (int w = 1; w < nw; ++w) v += s_y[w][b][part][row];
-      store_out(y, (int64_t)b * ys + (part ? n + i : i), v);
     }
   }
 }
 
 template <int TT, typename YT>
 static void launch_t(const GemvGroup& grp, int m, int B, hipStream_t s) {
-  const int nchunk = (m + kChunk - 1) / kChunk;
-  const int nw = nchunk < kWavesPerTile ? nchunk : kWavesPerTile;
-  const dim3 grid(grp.tile_start[grp.count]), block(64 * nw);
+  const dim3 grid(grp.tile_start[grp.count]), block(kWave);
   if (B <= 8)
     hipLaunchKernelGGL((k_gemv_mfma<TT, 1, YT>), grid, block, 0, s, grp, m, B);
   else

@@ -8,8 +8,8 @@
 // independent and summed).
 //
 // One wave per complex row.  Lane l reads packed words l, l+64, ... of each (stage, matrix)
-// plane -- 16 codes each (code p of a word in bits 8*(p%4) + 2*(p/4)), coalesced -- and the
-// 16 matching x values.  For each code it negates
+// plane -- 16 codes each (code p of a word in bits 8*(p%4) + 2*(p/4)), found through the
+// tiled word order of the packed form -- and the 16 matching x values.  For each code it negates
 // the (a, b) pair when the sign bit is set and adds it to the real-axis or imaginary-axis
 // accumulator; the scales of that plane multiply the accumulated sums once per lane, and the
 // wave reduces the per-lane outputs with cross-lane adds at the end.  All sums are fp32.
@@ -51,8 +51,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const uint8_t* __restrict__ p
   const int i = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (i >= n) return;                       // the whole wave leaves together
   const int dw_plane = m / 16;
-  const uint32_t* __restrict__ prow =
-      reinterpret_cast<const uint32_t*>(packed + (int64_t)i * T * (m / 2));
+  const uint32_t* __restrict__ words = reinterpret_cast<const uint32_t*>(packed);
   const int64_t xs = 2 * (int64_t)m;        // x row stride
   const int64_t ys = 2 * (int64_t)n;
 
@@ -66,9 +65,8 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const uint8_t* __restrict__ p
         float ra[NB], rb[NB], ia[NB], ib[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) { ra[b] = rb[b] = ia[b] = ib[b] = 0.f; }
-        const uint32_t* __restrict__ pl = prow + (t * 2 + M) * dw_plane;
         for (int q = lane; q < dw_plane; q += kWave) {
-          const uint32_t w = pl[q];
+          const uint32_t w = words[tiled_word(i, t * 2 + M, q, m, T)];
           const int j0 = q * 16;
 #pragma unroll
           for (int b = 0; b < NB; ++b) {

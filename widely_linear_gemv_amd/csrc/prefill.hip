@@ -135,23 +135,30 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
   const int ksteps = (m + 64 * KS - 1) / (64 * KS);
 
   // decode assignment: half word h = ((row * 2T + tm) * 4KS + wq) * 2 + hh.  The tile's code
-  // words are read through a buffer resource over this workgroup's rows, so rows past n read 0.
+  // words are read through a buffer resource over this workgroup's tile of the packed form (the
+  // last tile's padding rows hold code 0; their outputs are never stored).  Step kk covers
+  // words 8kk .. 8kk+7 of each row and plane: chunk kk/2, 64-column groups 2(kk%2) and 2(kk%2)+1.
+  static_assert(KS == 2, "a step is half a 256-column chunk of the packed form");
   constexpr int kHalves = 16 * TT * 2 * 4 * KS * 2;
   constexpr int kPerThread = (kHalves + 64 * kGemmWaves - 1) / (64 * kGemmWaves);
-  const int64_t row_bytes = (int64_t)TT * 2 * dw_plane * 4;
-  const __amdgpu_buffer_rsrc_t rsrc_w = make_rsrc(packed + (int64_t)i0 * row_bytes, (int64_t)(n - i0) * row_bytes);
-  int voff_w[kPerThread];
+  const int64_t tile_bytes = (int64_t)16 * TT * 2 * dw_plane * 4;
+  const __amdgpu_buffer_rsrc_t rsrc_w = make_rsrc(packed + (int64_t)blockIdx.x * tile_bytes, tile_bytes);
+  int woff[kPerThread], wtm[kPerThread];
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
     const int h = min(tid + u * 64 * kGemmWaves, kHalves - 1);
     const int rr = h / (TT * 2 * 8 * KS), tm = (h / (8 * KS)) % (TT * 2), wq = (h / 2) % (4 * KS);
-    voff_w[u] = (int)(rr * row_bytes) + (tm * dw_plane + wq) * 4;
+    woff[u] = (wq >> 2) * 64 + rr * 4 + (wq & 3);      // group within the step, row, word
+    wtm[u] = tm;
   }
   uint32_t wreg[kPerThread];
   auto load_words = [&](int kk) {
+    const int c = kk >> 1;
+    const int groups = min(4, (m - 256 * c) >> 6);
+    const int base = c * (TT * 2) * 256 + (kk & 1) * 128;
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u)
-      wreg[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_w, voff_w[u] + 16 * KS * kk, 0, 0);
+      wreg[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_w, 4 * (base + wtm[u] * groups * 64 + woff[u]), 0, 0);
   };
   auto decode_to_lds = [&](int buf, int kk) {
 #pragma unroll

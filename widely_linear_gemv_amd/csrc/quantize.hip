@@ -12,7 +12,8 @@
 // The scale sums of a stage are the 256 per-thread partial sums (each in j order) reduced by
 // a halving tree, so the fp64 scales -- and therefore every later stage's codes -- do not
 // depend on the launch.  Codes of the row are kept in LDS (one byte each) and written out
-// packed sixteen to a 32-bit word at the end.  Instead of keeping fp64 residuals for every j, each
+// packed sixteen to a 32-bit word at the end, in the tiled word order of the packed form;
+// workgroups past the last row write the zero words of the last tile's padding rows.  Instead of keeping fp64 residuals for every j, each
 // stage recomputes r from the fp32 inputs and subtracts the earlier stages' terms in stage order,
 // which reproduces the same fp64 values bit for bit.
 #include "common.hpp"
@@ -57,6 +58,12 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
   __shared__ double s_part[4][kQThreads];                   // [U re, U im, W re, W im][thread]
   __shared__ int s_cnt[2][kQThreads / kWave];               // real-axis counts per wave
   __shared__ double s_scale[4][2][2];                       // fp64 scales [t][M][axis]
+  if ((int)blockIdx.x >= n) {                                // padding row of the last tile
+    uint32_t* __restrict__ pw = reinterpret_cast<uint32_t*>(packed);
+    for (int q = threadIdx.x; q < 2 * T * (m / 16); q += kQThreads)
+      pw[tiled_word(blockIdx.x, q / (m / 16), q % (m / 16), m, T)] = 0u;
+    return;
+  }
 
   const int i = blockIdx.x;
   const int l = threadIdx.x;
@@ -147,43 +154,46 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     __syncthreads();
   }
 
-  // packed row i: [t][M][m/4] bytes, the LDS code bytes sixteen to a word.
-  const int dw_row = T * m / 8;
-  uint32_t* __restrict__ prow = reinterpret_cast<uint32_t*>(packed + (int64_t)i * T * (m / 2));
+  // packed row i: the LDS code bytes ([t][M][m]) sixteen to a word, in the tiled word order.
+  const int dw_plane = m / 16;
+  uint32_t* __restrict__ pw = reinterpret_cast<uint32_t*>(packed);
   const uint4* sc4 = reinterpret_cast<const uint4*>(s_codes);
-  for (int q = l; q < dw_row; q += kQThreads) prow[q] = pack16(sc4[q]);
+  for (int q = l; q < 2 * T * dw_plane; q += kQThreads)
+    pw[tiled_word(i, q / dw_plane, q % dw_plane, m, T)] = pack16(sc4[q]);
 
   if (codes_out) {   // [T][2][n][m]
-    const int dw_plane = m / 4;
+    const int dw_codes = m / 4;
     for (int p = 0; p < 2 * T; ++p) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(codes_out + ((int64_t)p * n + i) * m);
       const uint32_t* src = reinterpret_cast<const uint32_t*>(s_codes + (int64_t)p * m);
-      for (int q = l; q < dw_plane; q += kQThreads) dst[q] = src[q];
+      for (int q = l; q < dw_codes; q += kQThreads) dst[q] = src[q];
     }
   }
 }
 
-// codes uint8 [T][2][n][m] -> packed [n][T][2][m/4]; one thread per packed dword (16 codes).
+// codes uint8 [T][2][n][m] -> the packed form; one thread per packed word (16 codes), rows
+// padded to whole 16-row tiles with code 0.
 __global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ codes, int n, int m,
                                               int T, uint8_t* __restrict__ packed) {
   const int dw_plane = m / 16;
   const int dw_row = 2 * T * dw_plane;
-  const int64_t total = (int64_t)n * dw_row;
+  const int64_t total = (int64_t)padded_rows(n) * dw_row;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int i = (int)(idx / dw_row);
   const int q = (int)(idx % dw_row);
   const int p = q / dw_plane;        // t * 2 + M
   const int qq = q % dw_plane;
-  const uint4 w = *reinterpret_cast<const uint4*>(codes + ((int64_t)p * n + i) * m + 16 * qq);
-  reinterpret_cast<uint32_t*>(packed)[idx] = pack16(w);
+  uint32_t word = 0u;
+  if (i < n) word = pack16(*reinterpret_cast<const uint4*>(codes + ((int64_t)p * n + i) * m + 16 * qq));
+  reinterpret_cast<uint32_t*>(packed)[tiled_word(i, p, qq, m, T)] = word;
 }
 
 hipError_t launch_quantize(const float* R, int n, int m, int T, uint8_t* packed, float* scales,
                            double* scales64, uint8_t* codes, hipStream_t s) {
   const size_t lds = (size_t)2 * T * m;
   const int nch = (m + kQThreads - 1) / kQThreads;
-  const dim3 grid(n), block(kQThreads);
+  const dim3 grid(padded_rows(n)), block(kQThreads);
   if (nch <= 1)
     hipLaunchKernelGGL(k_quantize<1>, grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
   else if (nch <= 8)
@@ -196,7 +206,7 @@ hipError_t launch_quantize(const float* R, int n, int m, int T, uint8_t* packed,
 }
 
 hipError_t launch_pack(const uint8_t* codes, int n, int m, int T, uint8_t* packed, hipStream_t s) {
-  const int64_t total = (int64_t)n * 2 * T * (m / 16);
+  const int64_t total = (int64_t)padded_rows(n) * 2 * T * (m / 16);
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(256), 0, s, codes, n, m, T, packed);
   return hipGetLastError();
