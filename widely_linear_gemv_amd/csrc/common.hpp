@@ -55,6 +55,15 @@ __host__ __device__ __forceinline__ int64_t tiled_word(int i, int P, int wq, int
 }
 __host__ __device__ __forceinline__ int padded_rows(int n) { return (n + 15) & ~15; }
 
+// Waves per 16-row tile of the matrix-core GEMVs: one wave streams a whole tile when there are
+// enough tiles to fill the chip (about 1536 waves); a small launch splits each tile's chunks over
+// 2 or 4 waves instead.
+inline int gemv_waves_per_tile(int tiles, int m) {
+  const int nchunk = (m + 255) / 256;
+  if (tiles >= 1536 || nchunk < 2) return 1;
+  return nchunk >= 4 ? 4 : 2;
+}
+
 constexpr int kMaxGroup = 48;   // items per launch; the table travels in the kernel arguments
 struct GemvGroup {
   int count;

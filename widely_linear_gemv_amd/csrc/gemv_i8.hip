@@ -154,8 +154,8 @@ __device__ __forceinline__ int find_item_i8(const GemvGroup& g, int tile) {
   return lo;
 }
 
-template <int TT, typename YT>
-__global__ __launch_bounds__(kWave) void k_gemv_i8(const GemvGroup grp, int m, int B) {
+template <int TT, int NW, typename YT>
+__global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int m, int B) {
   const int item = find_item_i8(grp, blockIdx.x);
   const GemvItem it = grp.items[item];
   const int n = it.n;
@@ -164,7 +164,8 @@ __global__ __launch_bounds__(kWave) void k_gemv_i8(const GemvGroup grp, int m, i
   const uint8_t* __restrict__ blob = static_cast<const uint8_t*>(it.x);
   YT* __restrict__ y = static_cast<YT*>(it.y);
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int r = lane & 15, g = lane >> 4;
   const int tile = blockIdx.x - grp.tile_start[item];
   const int i0 = tile * 16;
@@ -222,20 +223,22 @@ __global__ __launch_bounds__(kWave) void k_gemv_i8(const GemvGroup grp, int m, i
   // has the same loads in flight.
   {
     Chunk c0, c1;
-    load_chunk(0, c0);
-    int c = 0;
-    for (; c + 1 < nchunk; c += 2) {
-      load_chunk(c + 1, c1);
+    int c = wave;                                  // wave w takes chunks w, w + NW, ...
+    load_chunk(c, c0);
+    for (; c + NW < nchunk; c += 2 * NW) {
+      load_chunk(c + NW, c1);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c0);
-      load_chunk(min(c + 2, nchunk - 1), c0);
+      load_chunk(min(c + 2 * NW, nchunk - 1), c0);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c1);
     }
     if (c < nchunk) compute_chunk(c0);
   }
 
-  // Epilogue.  Lane holds rows 4g..4g+3 of column r = 8b + 4comp + l.
+  // Epilogue.  Lane holds rows 4g..4g+3 of column r = 8b + 4comp + l.  With several waves per
+  // tile their sums meet in LDS and are added in wave order.
+  __shared__ float s_y[NW > 1 ? NW : 1][2][2][16];      // [wave][batch][re/im][row]
   const int bl = r >> 3, comp = (r >> 2) & 1, l = r & 3;
   const int* hdr = reinterpret_cast<const int*>(blob);
   const int S = bl < B ? hdr[2 + bl] : 0;
@@ -266,16 +269,36 @@ __global__ __launch_bounds__(kWave) void k_gemv_i8(const GemvGroup grp, int m, i
       vre += __shfl_xor(vre, off);
       vim += __shfl_xor(vim, off);
     }
-    if ((r & 7) == 0 && bl < B && i < n) {
+    if (NW > 1) {
+      if ((r & 7) == 0) { s_y[wave][bl][0][4 * g + e] = vre; s_y[wave][bl][1][4 * g + e] = vim; }
+    } else if ((r & 7) == 0 && bl < B && i < n) {
       store_out(y, (int64_t)bl * ys + i, vre);
       store_out(y, (int64_t)bl * ys + n + i, vim);
+    }
+  }
+  if constexpr (NW > 1) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 2 * 2 * 16; idx += kWave * NW) {
+      const int row = idx & 15, part = (idx >> 4) & 1, b = idx >> 5;
+      const int i = i0 + row;
+      if (b < B && i < n) {
+        float v = s_y[0][b][part][row];
+        for (int w = 1; w < NW; ++w) v += s_y[w][b][part][row];
+        store_out(y, (int64_t)b * ys + (part ? n + i : i), v);
+      }
     }
   }
 }
 
 template <int TT, typename YT>
 static void launch_i8_t(const GemvGroup& grp, int m, int B, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv_i8<TT, YT>), dim3(grp.tile_start[grp.count]), dim3(kWave), 0, s, grp, m, B);
+  const int tiles = grp.tile_start[grp.count];
+  const dim3 grid(tiles);
+  switch (gemv_waves_per_tile(tiles, m)) {
+    case 4: hipLaunchKernelGGL((k_gemv_i8<TT, 4, YT>), grid, dim3(4 * kWave), 0, s, grp, m, B); break;
+    case 2: hipLaunchKernelGGL((k_gemv_i8<TT, 2, YT>), grid, dim3(2 * kWave), 0, s, grp, m, B); break;
+    default: hipLaunchKernelGGL((k_gemv_i8<TT, 1, YT>), grid, dim3(kWave), 0, s, grp, m, B); break;
+  }
 }
 
 hipError_t launch_gemv_i8_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s) {

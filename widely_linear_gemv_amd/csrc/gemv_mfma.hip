@@ -80,8 +80,8 @@ __device__ __forceinline__ int find_item(const GemvGroup& g, int tile) {
   return lo;
 }
 
-template <int TT, int CG, typename YT>
-__global__ __launch_bounds__(kWave) void k_gemv_mfma(const GemvGroup grp, int m, int B) {
+template <int TT, int CG, int NW, typename YT>
+__global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, int m, int B) {
   const int item = find_item(grp, blockIdx.x);
   const GemvItem it = grp.items[item];
   const int n = it.n;
@@ -90,7 +90,8 @@ __global__ __launch_bounds__(kWave) void k_gemv_mfma(const GemvGroup grp, int m,
   const uint16_t* __restrict__ x = static_cast<const uint16_t*>(it.x);
   YT* __restrict__ y = static_cast<YT*>(it.y);
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int r = lane & 15, g = lane >> 4;
   const int tile = blockIdx.x - grp.tile_start[item];
   const int i0 = tile * 16;
@@ -170,13 +171,13 @@ __global__ __launch_bounds__(kWave) void k_gemv_mfma(const GemvGroup grp, int m,
   // same loads in flight.
   {
     Chunk c0, c1;
-    load_chunk(0, c0);
-    int c = 0;
-    for (; c + 1 < nchunk; c += 2) {
-      load_chunk(c + 1, c1);
+    int c = wave;                                  // wave w takes chunks w, w + NW, ...
+    load_chunk(c, c0);
+    for (; c + NW < nchunk; c += 2 * NW) {
+      load_chunk(c + NW, c1);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c0);
-      load_chunk(min(c + 2, nchunk - 1), c0);
+      load_chunk(min(c + 2 * NW, nchunk - 1), c0);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c1);
     }
@@ -184,7 +185,9 @@ __global__ __launch_bounds__(kWave) void k_gemv_mfma(const GemvGroup grp, int m,
   }
 
   // Epilogue.  C tile: lane holds rows 4g..4g+3 of column r = 2*bl + comp.  Scales are halved
-  // (the planes carry +-2).
+  // (the planes carry +-2).  With several waves per tile their sums meet in LDS and are added
+  // in wave order.
+  __shared__ float s_y[NW > 1 ? NW : 1][16][2][16];     // [wave][batch][re/im][row]
   const int64_t ys = 2 * (int64_t)n;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -210,21 +213,43 @@ __global__ __launch_bounds__(kWave) void k_gemv_mfma(const GemvGroup grp, int m,
       vre += __shfl_xor(vre, 1);
       vim += __shfl_xor(vim, 1);
       const int b = cg * 8 + (r >> 1);
-      if (comp == 0 && b < B && i < n) {
+      if (NW > 1) {
+        if (comp == 0) { s_y[wave][b][0][4 * g + e] = vre; s_y[wave][b][1][4 * g + e] = vim; }
+      } else if (comp == 0 && b < B && i < n) {
         store_out(y, (int64_t)b * ys + i, vre);
         store_out(y, (int64_t)b * ys + n + i, vim);
       }
     }
   }
+  if constexpr (NW > 1) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 8 * CG * 2 * 16; idx += kWave * NW) {
+      const int row = idx & 15, part = (idx >> 4) & 1, b = idx >> 5;
+      const int i = i0 + row;
+      if (b < B && i < n) {
+        float v = s_y[0][b][part][row];
+        for (int w = 1; w < NW; ++w) v += s_y[w][b][part][row];
+        store_out(y, (int64_t)b * ys + (part ? n + i : i), v);
+      }
+    }
+  }
+}
+
+template <int TT, int CG, typename YT>
+static void launch_cg(const GemvGroup& grp, int m, int B, hipStream_t s) {
+  const int tiles = grp.tile_start[grp.count];
+  const dim3 grid(tiles);
+  switch (gemv_waves_per_tile(tiles, m)) {
+    case 4: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 4, YT>), grid, dim3(4 * kWave), 0, s, grp, m, B); break;
+    case 2: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 2, YT>), grid, dim3(2 * kWave), 0, s, grp, m, B); break;
+    default: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 1, YT>), grid, dim3(kWave), 0, s, grp, m, B); break;
+  }
 }
 
 template <int TT, typename YT>
 static void launch_t(const GemvGroup& grp, int m, int B, hipStream_t s) {
-  const dim3 grid(grp.tile_start[grp.count]), block(kWave);
-  if (B <= 8)
-    hipLaunchKernelGGL((k_gemv_mfma<TT, 1, YT>), grid, block, 0, s, grp, m, B);
-  else
-    hipLaunchKernelGGL((k_gemv_mfma<TT, 2, YT>), grid, block, 0, s, grp, m, B);
+  if (B <= 8) launch_cg<TT, 1, YT>(grp, m, B, s);
+  else launch_cg<TT, 2, YT>(grp, m, B, s);
 }
 
 hipError_t launch_gemv_mfma_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s) {
