@@ -80,41 +80,56 @@ template <> struct Load8x<uint16_t> {
   }
 };
 
-// One workgroup per batch column: max |x| (order-free, exact), S, then the digits of all 2m
-// values and the zero slot.
+// One workgroup of 1024 threads per batch column: max |x| (order-free, exact), S, then the
+// digits of all 2m values and the zero slot.  For 2m <= 8192 every thread keeps its 8 values in
+// registers between the two passes; longer columns are read twice.
+constexpr int kDigitThreads = 1024;
+
 template <typename XT>
-__global__ __launch_bounds__(256) void k_x_digits(const XT* __restrict__ x, int m, int B,
-                                                  uint8_t* __restrict__ blob) {
-  __shared__ float s_max[256 / kWave];
+__global__ __launch_bounds__(kDigitThreads) void k_x_digits(const XT* __restrict__ x, int m, int B,
+                                                            uint8_t* __restrict__ blob) {
+  __shared__ float s_max[kDigitThreads / kWave];
   const int b = blockIdx.x;
   const XT* __restrict__ xb = x + (int64_t)b * 2 * m;
+  const int stride = kDigitThreads * 8;
+  const bool one_pass = 2 * m <= stride;
+  float keep[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float amax = 0.f;
-  for (int j = threadIdx.x * 8; j < 2 * m; j += 256 * 8) {
+  for (int j = threadIdx.x * 8; j < 2 * m; j += stride) {
     float v[8];
     Load8x<XT>::run(xb + j, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    for (int e = 0; e < 8; ++e) { amax = fmaxf(amax, fabsf(v[e])); keep[e] = v[e]; }
   }
 #pragma unroll
   for (int off = kWave / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((threadIdx.x & (kWave - 1)) == 0) s_max[threadIdx.x / kWave] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  amax = 0.f;
+#pragma unroll
+  for (int w = 0; w < kDigitThreads / kWave; ++w) amax = fmaxf(amax, s_max[w]);
   const int S = digit_exponent(amax);
+  // 2^S as two exact power-of-two factors (S can exceed the fp32 exponent range for tiny columns)
+  const float f1 = ldexpf(1.0f, S / 2), f2 = ldexpf(1.0f, S - S / 2);
   int* hdr = reinterpret_cast<int*>(blob);
   if (threadIdx.x == 0) {
     if (b == 0) { hdr[0] = B; hdr[1] = m; }
     hdr[2 + b] = S;
   }
   int8_t* __restrict__ dg = reinterpret_cast<int8_t*>(blob + kDigitHeader) + (int64_t)b * 8 * m;
-  for (int j2 = threadIdx.x * 8; j2 < 2 * m; j2 += 256 * 8) {
+  for (int j2 = threadIdx.x * 8; j2 < 2 * m; j2 += stride) {
     const int comp = j2 / m, j = j2 % m;         // m % 64 == 0: 8 values never straddle comps
     float v[8];
-    Load8x<XT>::run(xb + j2, v);
+    if (one_pass) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = keep[e];
+    } else {
+      Load8x<XT>::run(xb + j2, v);
+    }
     uint32_t d[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int X = (int)rintf(ldexpf(v[e], S));     // |X| <= 2^22, scaling exact
+      const int X = (int)rintf((v[e] * f1) * f2);     // |X| <= 2^22, scaling exact
       const int l0 = ((X + 128) & 255) - 128;
       const int X1 = (X - l0) >> 8;
       const int l1 = ((X1 + 128) & 255) - 128;
@@ -135,10 +150,10 @@ size_t x_digits_bytes(int64_t m, int64_t B) { return (size_t)kDigitHeader + (siz
 
 hipError_t launch_x_digits(const void* x, int x_bf16, int m, int B, void* blob, hipStream_t s) {
   if (x_bf16)
-    hipLaunchKernelGGL(k_x_digits<uint16_t>, dim3(B), dim3(256), 0, s, static_cast<const uint16_t*>(x), m, B,
+    hipLaunchKernelGGL(k_x_digits<uint16_t>, dim3(B), dim3(kDigitThreads), 0, s, static_cast<const uint16_t*>(x), m, B,
                        static_cast<uint8_t*>(blob));
   else
-    hipLaunchKernelGGL(k_x_digits<float>, dim3(B), dim3(256), 0, s, static_cast<const float*>(x), m, B,
+    hipLaunchKernelGGL(k_x_digits<float>, dim3(B), dim3(kDigitThreads), 0, s, static_cast<const float*>(x), m, B,
                        static_cast<uint8_t*>(blob));
   return hipGetLastError();
 }

@@ -154,12 +154,18 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     __syncthreads();
   }
 
-  // packed row i: the LDS code bytes ([t][M][m]) sixteen to a word, in the tiled word order.
+  // packed row i: the LDS code bytes ([t][M][m]) sixteen to a word, in the tiled word order;
+  // each thread stores one 64-column group of a plane (4 words, 16 contiguous bytes).
   const int dw_plane = m / 16;
+  const int gp_plane = m / 64;
   uint32_t* __restrict__ pw = reinterpret_cast<uint32_t*>(packed);
   const uint4* sc4 = reinterpret_cast<const uint4*>(s_codes);
-  for (int q = l; q < 2 * T * dw_plane; q += kQThreads)
-    pw[tiled_word(i, q / dw_plane, q % dw_plane, m, T)] = pack16(sc4[q]);
+  for (int q = l; q < 2 * T * gp_plane; q += kQThreads) {
+    const int P = q / gp_plane, w0 = 4 * (q % gp_plane);
+    const uint4* src = sc4 + P * dw_plane + w0;
+    *reinterpret_cast<uint4*>(pw + tiled_word(i, P, w0, m, T)) =
+        make_uint4(pack16(src[0]), pack16(src[1]), pack16(src[2]), pack16(src[3]));
+  }
 
   if (codes_out) {   // [T][2][n][m]
     const int dw_codes = m / 4;
