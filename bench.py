@@ -50,6 +50,26 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_PROFILE = "profiles/gemv_i8_grouped_attention4096_T2_hbm_traffic.md"
+
+
+def measured_traffic_per_layer():
+    """HBM bytes per layer of the grouped int8 GEMV, from the committed FETCH_SIZE / WRITE_SIZE
+    summary (copy-calibrated), or None when the kernel source changed since it was taken."""
+    import hashlib
+    import re
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        text = open(os.path.join(here, TRAFFIC_PROFILE)).read()
+        total = int(re.search(r"traffic_bytes_per_launch: (\d+)", text).group(1))
+        layers = int(re.search(r"layers_per_launch: (\d+)", text).group(1))
+        src, digest = re.search(r"kernel_source: (\S+) sha256 ([0-9a-f]+)", text).groups()
+        now = hashlib.sha256(open(os.path.join(here, src), "rb").read()).hexdigest()
+    except (OSError, AttributeError, ValueError):
+        return None
+    return total / layers if now == digest else None
+
+
 def gemv_bytes(n, m, T, B, x_bytes=2, y_bytes=4):
     """Algorithmic bytes of one GEMV: codes + fp32 scales + x + y."""
     return T * n * m // 2 + n * T * 2 * 2 * 4 + B * 2 * m * x_bytes + B * 2 * n * y_bytes
@@ -229,6 +249,7 @@ def main():
     i8_gbs = bytes_i8 / (t_dec * 1e-3) / 1e9
     i8_launch_us = t_i8 * 1e3 / launches
     i8_launch_gbs = bytes_i8 / launches / (i8_launch_us * 1e-6) / 1e9
+    traffic_layer = measured_traffic_per_layer()
     issued_ops = 16 * T * n * m * Ntok
     gemm_tops = issued_ops / (t_gemm * 1e-3) / 1e12
     quant_params = 4 * n * m
@@ -262,7 +283,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(i8_launch_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": (None if traffic_layer is None
+                        else int(round(traffic_layer * P / launches))),
         },
         "legs": {
             "gemv_b1_i8": {"GB/s": round(i8_gbs, 2), "segment_us": round(t_dec * 1e3, 3),
