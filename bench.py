@@ -1,6 +1,6 @@
 """Benchmark of the Fairy2i widely-linear hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile-steps]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-stack]
 
 Workload: the LLaMA-2 7B attention projection (R 4096 x 4096 -> U, W 2048 x 2048 complex),
 T = 2 residual stages, bf16 activations, all inputs synthetic and seeded (workloads.py).
@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer stack legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 256 MiB device copy (counter calibration for profiles)")
@@ -105,6 +106,70 @@ def cpu_baseline(R, T, x1, budget_s):
                   f"({per*1e3:.1f} ms each); quantizer on {len(rows)} of {n} complex rows "
                   f"took {tq:.3f} s ({len(rows)*m*4/tq/1e6:.2f} M real params/s)",
     }
+
+
+def stack_legs(f2, torch, dev, T, reps):
+    """The LLaMA-2 7B linear stack (32 layers x 7 projections, 6.48e9 real weights): quantize all
+    224 matrices, then one decode step (grouped launches per shared input) at batch 1 (int8 digit
+    form) and batch 8 (bf16), each captured in a HIP graph.  Weights are drawn on the GPU (torch's
+    generator seeded 5000 + 7 L + p, N(0, 0.02^2)): 25.9 GB of fp32 R is too much for the host
+    generator.  Runs outside the timed step."""
+    from widely_linear_gemv_amd.stack import DecodeStep, GROUPS, PROJECTIONS
+    R, out = [], []
+    for L in range(32):
+        for p, (_, rows, cols, _) in enumerate(PROJECTIONS):
+            g = torch.Generator(device=dev)
+            g.manual_seed(5000 + 7 * L + p)
+            R.append(torch.randn((rows, cols), generator=g, device=dev) * 0.02)
+            n, m = rows // 2, cols // 2
+            out.append({"packed": torch.empty((f2.fairy2i_packed_bytes(n, m, T),), dtype=torch.uint8, device=dev),
+                        "scales": torch.empty((n, T, 2, 2), dtype=torch.float32, device=dev)})
+
+    def quantize_all():
+        for r, o in zip(R, out):
+            f2.fairy2i_quantize(r, T, packed=o["packed"], scales=o["scales"])
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps          # ms
+
+    t_q = timed(quantize_all)
+    layers = [[(out[7 * L + p]["packed"], out[7 * L + p]["scales"]) for p in range(7)] for L in range(32)]
+    r_bytes = sum(r.numel() * 4 for r in R)
+    legs = {"stack_quantize": {"matrices": 224, "ms": round(t_q, 3), "R_GB/s": round(r_bytes / (t_q * 1e-3) / 1e9, 1),
+                               "real_params_per_s": round(sum(r.numel() for r in R) / (t_q * 1e-3), 1)}}
+    del R
+    for B in (1, 8):
+        xs = []
+        for L in range(32):
+            lx = []
+            for gi in range(GROUPS):
+                cols = next(c for (_, _, c, grp) in PROJECTIONS if grp == gi)
+                g = torch.Generator(device=dev)
+                g.manual_seed(6000 + 7 * L + gi)
+                lx.append(torch.randn((B, cols), generator=g, device=dev).to(torch.bfloat16))
+            xs.append(lx)
+        step = DecodeStep(layers, xs)
+        t = timed(step.run)
+        nbytes = sum(gemv_bytes(rows // 2, cols // 2, T, B) for L in range(32) for (_, rows, cols, _) in PROJECTIONS)
+        legs[f"stack_decode_b{B}"] = {"gemvs": 224, "launches": 256, "us": round(t * 1e3, 1),
+                                      "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes,
+                                      "kernel": "int8 digit form" if B <= 2 else "bf16"}
+    return legs
 
 
 def main():
@@ -310,6 +375,8 @@ def main():
             "wall_s": round(wall, 3),
         },
     }
+    if not args.no_stack:
+        out["legs"].update(stack_legs(f2, torch, dev, T, reps=5))
     if not args.no_cpu_baseline:
         x1 = workloads.activations(1, 2 * m, workloads.ATTN_X_SEEDS[1]).values
         out["cpu_baseline"] = cpu_baseline(R_np, T, x1, args.cpu_seconds)

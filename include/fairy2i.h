@@ -135,6 +135,18 @@ int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* pac
 size_t fairy2i_x_digits_bytes(int64_t m, int64_t B);
 int fairy2i_x_digits(const void* x, int x_dtype, int64_t m, int64_t B, void* digits, hipStream_t stream);
 
+/* Dequantize a packed layer to its real form (the fake-quantized layer of QAT and a third route
+ * to the layer's map): U^ = sum_t (s_re(t) b_re(t) + i s_im(t) b_im(t)) and likewise W^
+ * (zhichai.net note, "Step 2" dequantization and "Step 3" stage sum), then the real blocks of
+ * y = U^ x + W^ conj(x) (Note "Step 1"; ModelScope card "Method"):
+ *     R11 = Re U^ + Re W^   R12 = Im W^ - Im U^   R21 = Im U^ + Im W^   R22 = Re U^ - Re W^.
+ * The stage sums run over t in order in fp32.
+ *   packed, scales  as produced by fairy2i_quantize.
+ *   R       out, [2n][2m] row-major, R_dtype FAIRY2I_F32 or FAIRY2I_BF16 (round to nearest even),
+ *           16-byte aligned. */
+int fairy2i_dequantize(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
+                       void* R, int R_dtype, hipStream_t stream);
+
 /* Decode GEMV: y~[b] = sum_t U~(t) x[b] + W~(t) conj(x[b]) for b < B, every code an add,
  * subtract or real/imaginary swap with sign; one accumulator per (stage, matrix, axis) so each
  * scale multiplies an accumulated sum, not a weight.

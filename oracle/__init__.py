@@ -27,13 +27,13 @@ Model quality (perplexity, zero-shot accuracy) needs trained weights and
 datasets and is parity unpinned; nothing here computes it.
 """
 from .widely_linear import split, unsplit
-from .phase_quant import project, ordered_row_sum, quantize, dequantize, REDUCE_LANES
+from .phase_quant import project, ordered_row_sum, quantize, dequantize, dequantize_real, REDUCE_LANES
 from .packing import pack, pack_words, unpack, packed_nbytes
 from .gemv import gemv_ref, gemv_ref_real, code_planes
 from .prefill import act_quant_ref, gemm_int_ref, gemm_int_ref_loops, gemm_epilogue_ref
 
 __all__ = [
-    "split", "unsplit", "project", "ordered_row_sum", "quantize", "dequantize", "REDUCE_LANES",
+    "split", "unsplit", "project", "ordered_row_sum", "quantize", "dequantize", "dequantize_real", "REDUCE_LANES",
     "pack", "pack_words", "unpack", "packed_nbytes", "gemv_ref", "gemv_ref_real", "code_planes",
     "act_quant_ref", "gemm_int_ref", "gemm_int_ref_loops", "gemm_epilogue_ref",
 ]

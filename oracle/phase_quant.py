@@ -137,3 +137,12 @@ def dequantize(codes: np.ndarray, scales: np.ndarray) -> tuple[np.ndarray, np.nd
             acc = acc + (s[:, t, M, 0][:, None] * b_re + 1j * s[:, t, M, 1][:, None] * b_im)
         out.append(acc)
     return out[0], out[1]
+
+
+def dequantize_real(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The real form R^ [2n][2m] (fp64) of a quantized layer: the stage sums of "Step 2"
+    dequantization ("Step 3": the layer is the sum of its stage terms), mapped back to the real
+    blocks by the inverse of the "Step 1" split."""
+    from .widely_linear import unsplit
+    U, W = dequantize(codes, scales)
+    return unsplit(U, W)

@@ -416,3 +416,22 @@ def check_gemm_epilogue(gemm_int_ref, gemm_epilogue_ref, gemv_ref, seed=12, T=3,
     y1 = gemm_epilogue_ref(gemm_int_ref(codes, q), scales, delta)
     y2 = gemv_ref(codes, scales, q.astype(np.float64) * delta.astype(np.float64)[:, None])
     assert rel_l2(y1, y2) <= 1e-12
+
+
+def check_dequantize_real(dequantize_real, gemv_ref, seed=12, T=3, n=5, m=32, B=2):
+    """The real form applied to x~ is the multiplication-free GEMV (a different route: per-code
+    adds and swaps), and a single code with unit scales lands on the hand-derived blocks."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 4, size=(T, 2, n, m), dtype=np.uint8)
+    scales = rng.random((n, T, 2, 2)).astype(np.float32)
+    x = rng.standard_normal((B, 2 * m))
+    R = dequantize_real(codes, scales)
+    assert R.shape == (2 * n, 2 * m)
+    assert rel_l2(x @ R.T, gemv_ref(codes, scales, x)) <= 1e-12
+    # U has code 1 (= i, scale s_im = 3) at (0, 0), W code 2 (= -1, scale s_re = 5), T = 1:
+    # U^ = 3i, W^ = -5 -> R11 = 0 + (-5), R12 = 0 - 3, R21 = 3 + 0, R22 = 0 - (-5)
+    c = np.zeros((1, 2, 1, 1), dtype=np.uint8)
+    c[0, 0, 0, 0], c[0, 1, 0, 0] = 1, 2
+    s = np.zeros((1, 1, 2, 2))
+    s[0, 0, 0, 1], s[0, 0, 1, 0] = 3.0, 5.0
+    assert np.array_equal(dequantize_real(c, s), np.array([[-5.0, -3.0], [3.0, 5.0]]))

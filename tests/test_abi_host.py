@@ -114,6 +114,16 @@ def test_packed_bytes(L):
     assert L.fairy2i_packed_bytes(0, 64, 2) == 0
 
 
+def test_dequantize_errors(L):
+    d = L.fairy2i_dequantize
+    assert d(NULL, FAKE, 8, 64, 2, FAKE, f2.F32, S) == 1
+    assert d(FAKE, FAKE, 8, 64, 2, NULL, f2.F32, S) == 1
+    assert d(FAKE, FAKE, 8, 64, 2, FAKE, f2.I8, S) == 4
+    assert d(FAKE, FAKE, 8, 64, 0, FAKE, f2.F32, S) == 3
+    assert d(FAKE, FAKE, 8, 96, 2, FAKE, f2.F32, S) == 2
+    assert d(FAKE, FAKE, 8, 64, 2, FAKE + 8, f2.BF16, S) == 5
+
+
 def test_x_digits_errors(L):
     d = L.fairy2i_x_digits
     assert L.fairy2i_x_digits_bytes(2048, 1) == 64 + 8 * 2048

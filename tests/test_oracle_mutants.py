@@ -197,3 +197,14 @@ def test_gemm_transposed_plane_caught():
         P = oracle.gemm_int_ref(codes, q)
         return P[:, :, ::-1]                   # B_re and B_im swapped
     fails(pins.check_gemm_routes, bad, oracle.gemm_int_ref_loops)
+
+
+def test_dequantize_real_swapped_blocks_caught():
+    """R12 and R21 exchanged (the transpose-like slip) fails the route and hand checks."""
+    def bad(codes, scales):
+        R = oracle.dequantize_real(codes, scales)
+        n, m = R.shape[0] // 2, R.shape[1] // 2
+        out = R.copy()
+        out[:n, m:], out[n:, :m] = R[n:, :m], R[:n, m:]
+        return out
+    fails(pins.check_dequantize_real, bad, oracle.gemv_ref)

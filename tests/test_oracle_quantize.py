@@ -54,3 +54,7 @@ def test_scales32_are_rne_of_scales64():
     _, s32, s64, _ = oracle.quantize(R, 3)
     assert s32.dtype == np.float32
     assert np.array_equal(s32, s64.astype(np.float32))
+
+
+def test_dequantize_real_routes():
+    pins.check_dequantize_real(oracle.dequantize_real, oracle.gemv_ref)

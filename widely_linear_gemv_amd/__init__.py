@@ -34,6 +34,7 @@ SIGNATURES = {
     "fairy2i_quantize": (_INT, [_P, _I64, _I64, _INT, _P, _P, _P, _P, _P]),
     "fairy2i_pack": (_INT, [_P, _I64, _I64, _INT, _P, _P]),
     "fairy2i_packed_bytes": (_SZ, [_I64, _I64, _INT]),
+    "fairy2i_dequantize": (_INT, [_P, _P, _I64, _I64, _INT, _P, _INT, _P]),
     "fairy2i_x_digits_bytes": (_SZ, [_I64, _I64]),
     "fairy2i_x_digits": (_INT, [_P, _INT, _I64, _I64, _P, _P]),
     "fairy2i_gemv": (_INT, [_P, _P, _I64, _I64, _INT, _P, _INT, _I64, _P, _INT, _INT, _P]),
@@ -136,6 +137,17 @@ def fairy2i_pack(codes: torch.Tensor, packed=None, stream=None) -> torch.Tensor:
     packed = packed if packed is not None else torch.empty((fairy2i_packed_bytes(n, m, T),), dtype=torch.uint8, device=codes.device)
     _check(lib().fairy2i_pack(_ptr(codes), n, m, T, _ptr(packed), _stream(stream)))
     return packed
+
+
+def fairy2i_dequantize(packed: torch.Tensor, scales: torch.Tensor, m: int, *, R_dtype=torch.float32,
+                       R=None, stream=None) -> torch.Tensor:
+    """packed form + scales [n][T][2][2] -> the real layer R^ [2n][2m] (fp32 or bf16)."""
+    n, T = scales.shape[0], scales.shape[1]
+    if R is None:
+        R = torch.empty((2 * n, 2 * m), dtype=R_dtype, device=packed.device)
+    _check(lib().fairy2i_dequantize(_ptr(packed), _ptr(scales), n, m, T, _ptr(R), _DTYPE[R.dtype],
+                                    _stream(stream)))
+    return R
 
 
 class XDigits:

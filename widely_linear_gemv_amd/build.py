@@ -38,6 +38,7 @@ SOURCES = {
     "gemv_mfma.hip": [],
     "gemv_i8.hip": [],
     "prefill.hip": ["-ffp-contract=off"],
+    "dequant.hip": ["-ffp-contract=off"],
     "api.cpp": ["-x", "hip"],
 }
 

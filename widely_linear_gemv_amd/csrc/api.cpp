@@ -216,6 +216,19 @@ int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, i
   return ok();
 }
 
+int fairy2i_dequantize(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
+                       void* R, int R_dtype, hipStream_t stream) {
+  if (!packed || !scales || !R) return fail(FAIRY2I_ERR_NULL, "packed, scales and R are required");
+  if (R_dtype != FAIRY2I_F32 && R_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "R_dtype %d: need F32 or BF16", R_dtype);
+  if (int s = check_stages(T)) return s;
+  if (int s = check_nm(n, m)) return s;
+  if (!aligned(packed, 16) || !aligned(R, 16) || !aligned(scales, 4))
+    return fail(FAIRY2I_ERR_ALIGN, "packed and R need 16-byte alignment, scales 4");
+  return hip_status(f2i::launch_dequant(packed, scales, (int)n, (int)m, T, R, R_dtype == FAIRY2I_BF16, stream),
+                    "dequantize launch");
+}
+
 int fairy2i_act_quant(const void* x, int x_dtype, int64_t N, int64_t two_m, int8_t* q,
                       float* delta, hipStream_t stream) {
   if (!x || !q || !delta) return fail(FAIRY2I_ERR_NULL, "x, q and delta are required");

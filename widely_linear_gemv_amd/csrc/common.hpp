@@ -83,6 +83,8 @@ hipError_t launch_gemv_i8(const uint8_t* packed, const float* scales, int n, int
 hipError_t launch_gemv_i8_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
 size_t x_digits_bytes(int64_t m, int64_t B);
 hipError_t launch_x_digits(const void* x, int x_bf16, int m, int B, void* blob, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* packed, const float* scales, int n, int m, int T, void* R,
+                          int r_bf16, hipStream_t s);
 hipError_t launch_act_quant(const void* x, int x_bf16, int N, int two_m, int8_t* q, float* delta,
                             hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* scales, int n, int m, int T,

@@ -1,0 +1,60 @@
+"""One decode step over a stack of widely-linear layers, as grouped launches.
+
+Sources: ModelScope card "Fairy2i-W2", "Method" (every linear layer of the model becomes a
+widely-linear layer y = U x + W conj(x)); 36Kr article, parallel stages (the stage terms, and
+the projections that read the same input, are independent).
+
+Per transformer layer the seven projections form four groups by their input: q, k and v share x;
+o reads its own; gate and up share x; down reads its own.  A group is one digit-form pass of its
+x (batch <= 2, int8 matrix cores) and one grouped GEMV launch, so a 32-layer stack is 128
+launches of each kind -- captured once in a HIP graph and replayed.  This module only sequences
+calls of the C ABI (through the binding); all arithmetic runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (GEMV_AUTO, GEMV_MFMA_I8, XDigits, fairy2i_gemv_grouped, fairy2i_x_digits,
+               fairy2i_x_digits_bytes)
+
+# LLaMA-2 7B projections of one layer: name, real rows (2n), real columns (2m), input group
+PROJECTIONS = (("q", 4096, 4096, 0), ("k", 4096, 4096, 0), ("v", 4096, 4096, 0), ("o", 4096, 4096, 1),
+               ("gate", 11008, 4096, 2), ("up", 11008, 4096, 2), ("down", 4096, 11008, 3))
+GROUPS = 4
+
+
+class DecodeStep:
+    """layers[L][p] = (packed, scales) for projection p of layer L (shapes as PROJECTIONS);
+    xs[L][g] = bf16 input [B][2m] of group g of layer L.  Outputs: self.ys[L][p] fp32 [B][2n]."""
+
+    def __init__(self, layers, xs, *, algo: int | None = None):
+        self.layers, self.xs = layers, xs
+        B = xs[0][0].shape[0]
+        self.B = B
+        self.algo = algo if algo is not None else (GEMV_MFMA_I8 if B <= 2 else GEMV_AUTO)
+        dev = xs[0][0].device
+        self.ys = [[torch.empty((B, rows), dtype=torch.float32, device=dev)
+                    for (_, rows, _, _) in PROJECTIONS] for _ in layers]
+        self.digits = None
+        if self.algo == GEMV_MFMA_I8:
+            self.digits = [[XDigits(torch.empty((fairy2i_x_digits_bytes(x.shape[1] // 2, B),),
+                                                dtype=torch.uint8, device=dev), B, x.shape[1] // 2)
+                            for x in layer_xs] for layer_xs in xs]
+
+    def run(self, stream=None):
+        for L, projs in enumerate(self.layers):
+            for g in range(GROUPS):
+                x = self.xs[L][g]
+                if self.digits is not None:
+                    x = fairy2i_x_digits(x, out=self.digits[L][g], stream=stream)
+                items = [(projs[p][0], projs[p][1], x, self.ys[L][p])
+                         for p, (_, _, _, grp) in enumerate(PROJECTIONS) if grp == g]
+                fairy2i_gemv_grouped(items, algo=self.algo, stream=stream)
+        return self.ys
+
+    def capture(self):
+        """Capture one step into a HIP graph (on a side stream); returns the graph."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            self.run()
+        return g
