@@ -114,6 +114,13 @@ int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T,
                      uint8_t* packed, float* scales, double* scales64, uint8_t* codes,
                      hipStream_t stream);
 
+/* fairy2i_quantize for a bf16 layer (checkpoints are commonly stored in bf16): R is bf16
+ * [two_n][two_m] (raw bits, 2-byte aligned), widened exactly to fp64; everything else as
+ * fairy2i_quantize, so a bf16 layer quantizes exactly like its fp32 widening. */
+int fairy2i_quantize_bf16(const uint16_t* R, int64_t two_n, int64_t two_m, int T,
+                          uint8_t* packed, float* scales, double* scales64, uint8_t* codes,
+                          hipStream_t stream);
+
 /* Pack one-byte codes uint8 [T][2][n][m] (values 0..3; higher bits are ignored) into the
  * packed form above, padding rows zeroed (ModelScope card "Model details": 2 bits per real
  * parameter at T=2).  packed: fairy2i_packed_bytes(n, m, T) bytes. */

@@ -69,6 +69,14 @@ def test_quantize_errors(L):
     assert q(FAKE, 256, 256, 2, FAKE, FAKE, FAKE + 4, NULL, S) == 5     # scales64 needs 8
 
 
+def test_quantize_bf16_errors(L):
+    q = L.fairy2i_quantize_bf16
+    assert q(NULL, 256, 256, 2, FAKE, FAKE, NULL, NULL, S) == 1
+    assert q(FAKE, 256, 256, 5, FAKE, FAKE, NULL, NULL, S) == 3
+    assert q(FAKE, 255, 256, 2, FAKE, FAKE, NULL, NULL, S) == 2
+    assert q(FAKE + 1, 256, 256, 2, FAKE, FAKE, NULL, NULL, S) == 5
+
+
 def test_pack_errors(L):
     p = L.fairy2i_pack
     assert p(NULL, 4, 64, 2, FAKE, S) == 1

@@ -123,3 +123,21 @@ def test_pack_matches_oracle(T, n, m):
     announce("pack", T, n, m)
     got = down(f2.fairy2i_pack(up(noisy, dev)))
     assert np.array_equal(got, oracle.pack(codes))     # bits above the code are ignored
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_bf16_weights(T):
+    """A bf16 layer quantizes exactly like its fp32 widening (bit-exact codes and scales)."""
+    dev = device()
+    R = workloads.ATTN.weight()[:512, :1024]
+    bits = workloads.f32_to_bf16_bits(R)
+    Rw = workloads.bf16_bits_to_f32(bits)
+    announce("quantize bf16 weights T =", T)
+    out = f2.fairy2i_quantize(torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16), T,
+                              want_scales64=True, want_codes=True)
+    got = {k: down(v) for k, v in out.items()}
+    codes, s32, s64, _ = oracle.quantize(Rw, T)
+    assert np.array_equal(got["codes"], codes)
+    assert np.array_equal(got["packed"], oracle.pack(codes))
+    assert np.array_equal(got["scales64"].view(np.uint64), s64.view(np.uint64))
+    assert np.array_equal(got["scales"].view(np.uint32), s32.view(np.uint32))

@@ -71,8 +71,8 @@ const char* fairy2i_status_string(int status) {
   }
 }
 
-int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T, uint8_t* packed,
-                     float* scales, double* scales64, uint8_t* codes, hipStream_t stream) {
+static int quantize_any(const void* R, int r_bf16, int64_t two_n, int64_t two_m, int T, uint8_t* packed,
+                        float* scales, double* scales64, uint8_t* codes, hipStream_t stream) {
   if (!R || !packed || !scales) return fail(FAIRY2I_ERR_NULL, "R, packed and scales are required");
   if (int s = check_stages(T)) return s;
   if (two_n < 2 || two_n % 2 || two_m < 2 || two_m % 2)
@@ -82,11 +82,21 @@ int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T, uint8_
   if (int s = check_nm(n, m)) return s;
   if (2 * T * m > 65536)
     return fail(FAIRY2I_ERR_SHAPE, "2*T*m = %lld exceeds 65536", (long long)(2 * T * m));
-  if (!aligned(R, 4) || !aligned(packed, 16) || !aligned(scales, 4) ||
+  if (!aligned(R, r_bf16 ? 2 : 4) || !aligned(packed, 16) || !aligned(scales, 4) ||
       (scales64 && !aligned(scales64, 8)) || (codes && !aligned(codes, 16)))
-    return fail(FAIRY2I_ERR_ALIGN, "R/scales need 4, scales64 8, packed/codes 16-byte alignment");
-  return hip_status(f2i::launch_quantize(R, (int)n, (int)m, T, packed, scales, scales64, codes, stream),
+    return fail(FAIRY2I_ERR_ALIGN, "R needs 4 (fp32) or 2 (bf16), scales 4, scales64 8, packed/codes 16-byte alignment");
+  return hip_status(f2i::launch_quantize(R, r_bf16, (int)n, (int)m, T, packed, scales, scales64, codes, stream),
                     "quantize launch");
+}
+
+int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T, uint8_t* packed,
+                     float* scales, double* scales64, uint8_t* codes, hipStream_t stream) {
+  return quantize_any(R, 0, two_n, two_m, T, packed, scales, scales64, codes, stream);
+}
+
+int fairy2i_quantize_bf16(const uint16_t* R, int64_t two_n, int64_t two_m, int T, uint8_t* packed,
+                          float* scales, double* scales64, uint8_t* codes, hipStream_t stream) {
+  return quantize_any(R, 1, two_n, two_m, T, packed, scales, scales64, codes, stream);
 }
 
 int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* packed,

@@ -57,11 +57,11 @@ __host__ __device__ __forceinline__ int padded_rows(int n) { return (n + 15) & ~
 
 // Waves per 16-row tile of the matrix-core GEMVs: one wave streams a whole tile when there are
 // enough tiles to fill the chip (about 1536 waves); a small launch splits each tile's chunks over
-// 2 or 4 waves instead.
+// up to 8 waves instead (at least one chunk each).
 inline int gemv_waves_per_tile(int tiles, int m) {
   const int nchunk = (m + 255) / 256;
   if (tiles >= 1536 || nchunk < 2) return 1;
-  return nchunk >= 4 ? 4 : 2;
+  return nchunk >= 8 ? 8 : nchunk >= 4 ? 4 : 2;
 }
 
 constexpr int kMaxGroup = 48;   // items per launch; the table travels in the kernel arguments
@@ -71,7 +71,7 @@ struct GemvGroup {
   GemvItem items[kMaxGroup];
 };
 hipError_t launch_gemv_mfma_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
-hipError_t launch_quantize(const float* R, int n, int m, int T, uint8_t* packed, float* scales,
+hipError_t launch_quantize(const void* R, int r_bf16, int n, int m, int T, uint8_t* packed, float* scales,
                            double* scales64, uint8_t* codes, hipStream_t s);
 hipError_t launch_pack(const uint8_t* codes, int n, int m, int T, uint8_t* packed, hipStream_t s);
 hipError_t launch_gemv_valu(const uint8_t* packed, const float* scales, int n, int m, int T,

@@ -240,6 +240,7 @@ static void launch_cg(const GemvGroup& grp, int m, int B, hipStream_t s) {
   const int tiles = grp.tile_start[grp.count];
   const dim3 grid(tiles);
   switch (gemv_waves_per_tile(tiles, m)) {
+    case 8: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 8, YT>), grid, dim3(8 * kWave), 0, s, grp, m, B); break;
     case 4: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 4, YT>), grid, dim3(4 * kWave), 0, s, grp, m, B); break;
     case 2: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 2, YT>), grid, dim3(2 * kWave), 0, s, grp, m, B); break;
     default: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 1, YT>), grid, dim3(kWave), 0, s, grp, m, B); break;

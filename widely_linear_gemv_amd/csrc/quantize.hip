@@ -48,11 +48,15 @@ __device__ __forceinline__ uint32_t pack16(uint4 w) {
   return (w.x & lo2) | ((w.y & lo2) << 2) | ((w.z & lo2) << 4) | ((w.w & lo2) << 6);
 }
 
-// MAXC > 0: the row's fp32 inputs stay in registers (m <= 256 * MAXC).  MAXC == 0: they are
-// re-read from memory each stage (any m).
-template <int MAXC>
+// One real weight as fp32: fp32 as is, bf16 widened exactly.
+__device__ __forceinline__ float r_value(float v) { return v; }
+__device__ __forceinline__ float r_value(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// MAXC > 0: the row's inputs stay in registers (m <= 256 * MAXC).  MAXC == 0: they are re-read
+// from memory each stage (any m).  RT: fp32 or bf16 (raw bits) weights.
+template <int MAXC, typename RT>
 __global__ __launch_bounds__(kQThreads) void k_quantize(
-    const float* __restrict__ R, int n, int m, int T, uint8_t* __restrict__ packed,
+    const RT* __restrict__ R, int n, int m, int T, uint8_t* __restrict__ packed,
     float* __restrict__ scales, double* __restrict__ scales64, uint8_t* __restrict__ codes_out) {
   extern __shared__ __align__(16) uint8_t s_codes[];        // [T][2][m], one code per byte
   __shared__ double s_part[4][kQThreads];                   // [U re, U im, W re, W im][thread]
@@ -68,8 +72,8 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
   const int i = blockIdx.x;
   const int l = threadIdx.x;
   const int64_t ld = 2 * (int64_t)m;
-  const float* __restrict__ r0 = R + (int64_t)i * ld;          // row i of R
-  const float* __restrict__ r1 = R + (int64_t)(n + i) * ld;    // row n+i of R
+  const RT* __restrict__ r0 = R + (int64_t)i * ld;             // row i of R
+  const RT* __restrict__ r1 = R + (int64_t)(n + i) * ld;       // row n+i of R
   const int nch = (m + kQThreads - 1) / kQThreads;
 
   constexpr int NR = MAXC > 0 ? MAXC : 1;
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const int j = l + c * kQThreads;
-      if (j < m) { qa[c] = r0[j]; qb[c] = r0[m + j]; qc[c] = r1[j]; qd[c] = r1[m + j]; }
+      if (j < m) { qa[c] = r_value(r0[j]); qb[c] = r_value(r0[m + j]); qc[c] = r_value(r1[j]); qd[c] = r_value(r1[m + j]); }
       else { qa[c] = qb[c] = qc[c] = qd[c] = 0.f; }
     }
   }
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     } else {
       for (int c = 0; c < nch; ++c) {
         const int j = l + c * kQThreads;
-        if (j < m) body(j, r0[j], r0[m + j], r1[j], r1[m + j]);
+        if (j < m) body(j, r_value(r0[j]), r_value(r0[m + j]), r_value(r1[j]), r_value(r1[m + j]));
       }
     }
 
@@ -195,19 +199,28 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ codes,
   reinterpret_cast<uint32_t*>(packed)[tiled_word(i, p, qq, m, T)] = word;
 }
 
-hipError_t launch_quantize(const float* R, int n, int m, int T, uint8_t* packed, float* scales,
-                           double* scales64, uint8_t* codes, hipStream_t s) {
+template <typename RT>
+static void launch_quantize_t(const RT* R, int n, int m, int T, uint8_t* packed, float* scales,
+                              double* scales64, uint8_t* codes, hipStream_t s) {
   const size_t lds = (size_t)2 * T * m;
   const int nch = (m + kQThreads - 1) / kQThreads;
   const dim3 grid(padded_rows(n)), block(kQThreads);
   if (nch <= 1)
-    hipLaunchKernelGGL(k_quantize<1>, grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+    hipLaunchKernelGGL((k_quantize<1, RT>), grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
   else if (nch <= 8)
-    hipLaunchKernelGGL(k_quantize<8>, grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+    hipLaunchKernelGGL((k_quantize<8, RT>), grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
   else if (nch <= 24)
-    hipLaunchKernelGGL(k_quantize<24>, grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+    hipLaunchKernelGGL((k_quantize<24, RT>), grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
   else
-    hipLaunchKernelGGL(k_quantize<0>, grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+    hipLaunchKernelGGL((k_quantize<0, RT>), grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+}
+
+hipError_t launch_quantize(const void* R, int r_bf16, int n, int m, int T, uint8_t* packed, float* scales,
+                           double* scales64, uint8_t* codes, hipStream_t s) {
+  if (r_bf16)
+    launch_quantize_t(static_cast<const uint16_t*>(R), n, m, T, packed, scales, scales64, codes, s);
+  else
+    launch_quantize_t(static_cast<const float*>(R), n, m, T, packed, scales, scales64, codes, s);
   return hipGetLastError();
 }
 
