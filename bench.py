@@ -13,7 +13,8 @@ One step is one pass of every stage of the path over one batch of inputs:
      exact int8 digit form once (fairy2i_x_digits; the pool's layers share x, as q, k and v
      do), then the int8-MFMA GEMV runs over the pool;
   3. the bf16-MFMA GEMV over the pool at batch 1, 4 and 16;
-  4. prefill: per-token int8 activation quantization of 2048 tokens and the int8-MFMA GEMM.
+  4. prefill: per-token int8 activation quantization of 2048 tokens and the int8-MFMA GEMM;
+  5. the real form of the quantized layer (dequantize, the fake-quant forward).
 Each segment is captured once into a HIP graph and replayed on torch's current stream, with
 HIP events on that stream around every replay; inputs are resident in HBM before the timed
 region starts.
@@ -251,6 +252,11 @@ def main():
         for p in range(P):
             f2.fairy2i_gemv(pool[p], spool[p], xd1, y=ys[1], algo=f2.GEMV_MFMA_I8)
 
+    Rhat = torch.empty((2 * n, 2 * m), dtype=torch.float32, device=dev)
+
+    def seg_dequant():                 # the real form of the layer (fake-quant forward)
+        f2.fairy2i_dequantize(q0["packed"], q0["scales"], m, R=Rhat)
+
     def seg_act_quant():
         f2.fairy2i_act_quant(xp, q=qp, delta=dp)
 
@@ -258,7 +264,7 @@ def main():
         f2.fairy2i_gemm(q0["packed"], q0["scales"], qp, x_scale=dp, y=yp)
 
     segments = [seg_quantize, seg_decode_i8, seg_gemv_i8, seg_gemv(1), seg_gemv(4), seg_gemv(16),
-                seg_act_quant, seg_gemm, single_layers]
+                seg_act_quant, seg_gemm, seg_dequant, single_layers]
     NSEG = len(segments) - 1
     for fn in segments:                     # eager warm-up (also loads every kernel)
         fn()
@@ -303,7 +309,7 @@ def main():
     torch.cuda.synchronize()
     single_us = e0.elapsed_time(e1) * 1e3 / (3 * P)
 
-    t_quant, t_dec, t_i8, t_b1, t_b4, t_b16, t_aq, t_gemm = seg    # ms
+    t_quant, t_dec, t_i8, t_b1, t_b4, t_b16, t_aq, t_gemm, t_deq = seg    # ms
     bytes_b = {B: gemv_bytes(n, m, T, B) for B in (1, 4, 16)}
     gemv_ms = {1: t_b1, 4: t_b4, 16: t_b16}
     gbs = {B: P * bytes_b[B] / (gemv_ms[B] * 1e-3) / 1e9 for B in (1, 4, 16)}
@@ -372,6 +378,8 @@ def main():
                      "useful_TOPS": round(gemm_tops / 2, 2),
                      "frac_of_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
                      "issued_ops": issued_ops},
+            "dequantize": {"us": round(t_deq * 1e3, 2),
+                           "GB/s": round((layer_bytes + n * T * 16 + 4 * n * m * 4) / (t_deq * 1e-3) / 1e9, 2)},
             "wall_s": round(wall, 3),
         },
     }

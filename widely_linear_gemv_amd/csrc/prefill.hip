@@ -107,6 +107,105 @@ constexpr int kAhead = 3;          // plane fragments read from LDS ahead of the
 // rows and tokens that exist, so reads past n or N return 0 (and those outputs are never stored);
 // columns past m (at most one 64-column half of the last step) get zero planes from the decoder,
 // so whatever activations sit there add nothing.
+// Epilogue of a 16-row x 8*NF-token wave tile: acc[p][f] with plane p = (t*2+M)*2 + re/im and
+// column fragment f (tokens tok0 + 8f + r/2, component r & 1).
+template <int TT, int NF, int MODE>
+__device__ __forceinline__ void gemm_epilogue(const v4i (&acc)[TT * 4][NF], const float* __restrict__ scales,
+                                              int n, int N, const float* __restrict__ delta,
+                                              void* __restrict__ yv, int i0, int tok0, int r, int g) {
+  constexpr int kPlanes = TT * 4;
+  bool b_ok[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) b_ok[f] = tok0 + 8 * f + (r >> 1) < N;
+
+  // C layout of a 16x16 tile: lane holds rows 4g..4g+3 of column r.  Plane index p = (t*2+M)*2+re/im.
+  // Each lane stores its four consecutive rows with one 16-byte (8-byte for bf16) store when n is
+  // a multiple of 4, which keeps every store row-aligned; otherwise it stores them one by one.
+  const int comp = r & 1;
+  if (tok0 >= N) return;
+  const int ib = i0 + 4 * g;                 // first of this lane's four rows
+  const bool vec = (n % 4) == 0;
+  if constexpr (MODE == kOutRaw) {
+    int* __restrict__ P = static_cast<int*>(yv);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int tok = tok0 + 8 * f + (r >> 1);
+      if (!b_ok[f] || ib >= n) continue;
+#pragma unroll
+      for (int p = 0; p < kPlanes; ++p) {
+        int* dst = P + (((int64_t)p * 2 + comp) * N + tok) * n + ib;
+        if (vec) {
+          *reinterpret_cast<v4i*>(dst) = acc[p][f];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ib + e < n) dst[e] = acc[p][f][e];
+        }
+      }
+    }
+  } else {
+    const int64_t ys = 2 * (int64_t)n;
+    float s[4][TT][2][2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int M = 0; M < 2; ++M)
+#pragma unroll
+          for (int ax = 0; ax < 2; ++ax)
+            s[e][t][M][ax] = ib + e < n ? scales[(((int64_t)(ib + e) * TT + t) * 2 + M) * 2 + ax] : 0.f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int tok = tok0 + 8 * f + (r >> 1);
+      const float d = delta[b_ok[f] ? tok : 0];
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float vre = 0.f, vim = 0.f;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const float PUr = (float)acc[(t * 2 + 0) * 2 + 0][f][e], PUi = (float)acc[(t * 2 + 0) * 2 + 1][f][e];
+          const float PWr = (float)acc[(t * 2 + 1) * 2 + 0][f][e], PWi = (float)acc[(t * 2 + 1) * 2 + 1][f][e];
+          if (comp == 0) {   // column a = Re x
+            vre += s[e][t][0][0] * PUr + s[e][t][1][0] * PWr;
+            vim += s[e][t][0][1] * PUi + s[e][t][1][1] * PWi;
+          } else {           // column b = Im x
+            vre += s[e][t][1][1] * PWi - s[e][t][0][1] * PUi;
+            vim += s[e][t][0][0] * PUr - s[e][t][1][0] * PWr;
+          }
+        }
+        vre += __shfl_xor(vre, 1);   // lanes r and r^1 hold columns a and b of one token
+        vim += __shfl_xor(vim, 1);
+        o[e] = d * (comp == 0 ? vre : vim);   // lane a stores Re y, lane b stores Im y
+      }
+      if (!b_ok[f] || ib >= n) continue;
+      const int64_t off = (int64_t)tok * ys + (comp == 0 ? 0 : n) + ib;
+      if (MODE == kOutF32) {
+        float* __restrict__ y = static_cast<float*>(yv) + off;
+        if (vec) {
+          *reinterpret_cast<float4*>(y) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ib + e < n) y[e] = o[e];
+        }
+      } else {
+        uint16_t* __restrict__ y = static_cast<uint16_t*>(yv) + off;
+        if (vec) {
+          *reinterpret_cast<uint2*>(y) =
+              make_uint2((uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16),
+                         (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ib + e < n) y[e] = f32_to_bf16_rne(o[e]);
+        }
+      }
+    }
+  }
+}
+
 // Raw buffer resource over [base, base + bytes): loads at offsets past the end return 0.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFFF0);
@@ -249,96 +348,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
   }
   if (kk < ksteps) step(kk, 0);
 
-  bool b_ok[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) b_ok[f] = tok0 + 8 * f + (r >> 1) < N;
-
-  // C layout of a 16x16 tile: lane holds rows 4g..4g+3 of column r.  Plane index p = (t*2+M)*2+re/im.
-  // Each lane stores its four consecutive rows with one 16-byte (8-byte for bf16) store when n is
-  // a multiple of 4, which keeps every store row-aligned; otherwise it stores them one by one.
-  const int comp = r & 1;
-  if (tok0 >= N) return;
-  const int ib = i0 + 4 * g;                 // first of this lane's four rows
-  const bool vec = (n % 4) == 0;
-  if constexpr (MODE == kOutRaw) {
-    int* __restrict__ P = static_cast<int*>(yv);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int tok = tok0 + 8 * f + (r >> 1);
-      if (!b_ok[f] || ib >= n) continue;
-#pragma unroll
-      for (int p = 0; p < kPlanes; ++p) {
-        int* dst = P + (((int64_t)p * 2 + comp) * N + tok) * n + ib;
-        if (vec) {
-          *reinterpret_cast<v4i*>(dst) = acc[p][f];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (ib + e < n) dst[e] = acc[p][f][e];
-        }
-      }
-    }
-  } else {
-    const int64_t ys = 2 * (int64_t)n;
-    float s[4][TT][2][2];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int t = 0; t < TT; ++t)
-#pragma unroll
-        for (int M = 0; M < 2; ++M)
-#pragma unroll
-          for (int ax = 0; ax < 2; ++ax)
-            s[e][t][M][ax] = ib + e < n ? scales[(((int64_t)(ib + e) * TT + t) * 2 + M) * 2 + ax] : 0.f;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int tok = tok0 + 8 * f + (r >> 1);
-      const float d = delta[b_ok[f] ? tok : 0];
-      float o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float vre = 0.f, vim = 0.f;
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-          const float PUr = (float)acc[(t * 2 + 0) * 2 + 0][f][e], PUi = (float)acc[(t * 2 + 0) * 2 + 1][f][e];
-          const float PWr = (float)acc[(t * 2 + 1) * 2 + 0][f][e], PWi = (float)acc[(t * 2 + 1) * 2 + 1][f][e];
-          if (comp == 0) {   // column a = Re x
-            vre += s[e][t][0][0] * PUr + s[e][t][1][0] * PWr;
-            vim += s[e][t][0][1] * PUi + s[e][t][1][1] * PWi;
-          } else {           // column b = Im x
-            vre += s[e][t][1][1] * PWi - s[e][t][0][1] * PUi;
-            vim += s[e][t][0][0] * PUr - s[e][t][1][0] * PWr;
-          }
-        }
-        vre += __shfl_xor(vre, 1);   // lanes r and r^1 hold columns a and b of one token
-        vim += __shfl_xor(vim, 1);
-        o[e] = d * (comp == 0 ? vre : vim);   // lane a stores Re y, lane b stores Im y
-      }
-      if (!b_ok[f] || ib >= n) continue;
-      const int64_t off = (int64_t)tok * ys + (comp == 0 ? 0 : n) + ib;
-      if (MODE == kOutF32) {
-        float* __restrict__ y = static_cast<float*>(yv) + off;
-        if (vec) {
-          *reinterpret_cast<float4*>(y) = make_float4(o[0], o[1], o[2], o[3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (ib + e < n) y[e] = o[e];
-        }
-      } else {
-        uint16_t* __restrict__ y = static_cast<uint16_t*>(yv) + off;
-        if (vec) {
-          *reinterpret_cast<uint2*>(y) =
-              make_uint2((uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16),
-                         (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (ib + e < n) y[e] = f32_to_bf16_rne(o[e]);
-        }
-      }
-    }
-  }
+  gemm_epilogue<TT, NF, MODE>(acc, scales, n, N, delta, yv, i0, tok0, r, g);
 }
 
 template <int TT>
