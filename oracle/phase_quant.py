@@ -24,6 +24,9 @@ Readings taken where the pages are silent or open:
     `ordered_row_sum`, so that a GPU implementation can reproduce the fp64
     scales bit for bit.
   * U and W are quantized independently, each with its own residual chain.
+  * Alternative granularity (per_tensor=True): one (s_re, s_im) pair per stage and matrix
+    for the whole matrix, the mean over all its entries on that axis.  The sum is the
+    per-row ordered sums added one row after another in row order.
 """
 from __future__ import annotations
 
@@ -71,7 +74,14 @@ def ordered_row_sum(v: np.ndarray) -> np.ndarray:
     return p[:, 0]
 
 
-def _stage(r_re: np.ndarray, r_im: np.ndarray):
+def _tensor_mean(row_sums: np.ndarray, row_counts: np.ndarray) -> float:
+    """Per-tensor mean: row sums added in row order (one after another), over the total count."""
+    total = float(np.add.accumulate(np.asarray(row_sums, dtype=np.float64))[-1])
+    count = int(np.sum(row_counts))
+    return total / count if count > 0 else 0.0
+
+
+def _stage(r_re: np.ndarray, r_im: np.ndarray, per_tensor: bool = False):
     """One quantization stage on residual r (rows x m): codes, fp64 scales, new residual."""
     k = project(r_re, r_im)
     on_re = (k == 0) | (k == 2)
@@ -80,8 +90,12 @@ def _stage(r_re: np.ndarray, r_im: np.ndarray):
     n_im = on_im.sum(axis=1)
     s_sum_re = ordered_row_sum(np.where(on_re, np.abs(r_re), 0.0))
     s_sum_im = ordered_row_sum(np.where(on_im, np.abs(r_im), 0.0))
-    s_re = np.where(n_re > 0, s_sum_re / np.maximum(n_re, 1), 0.0)
-    s_im = np.where(n_im > 0, s_sum_im / np.maximum(n_im, 1), 0.0)
+    if per_tensor:
+        s_re = np.full(r_re.shape[0], _tensor_mean(s_sum_re, n_re))
+        s_im = np.full(r_re.shape[0], _tensor_mean(s_sum_im, n_im))
+    else:
+        s_re = np.where(n_re > 0, s_sum_re / np.maximum(n_re, 1), 0.0)
+        s_im = np.where(n_im > 0, s_sum_im / np.maximum(n_im, 1), 0.0)
     # r <- r - w_hat with w_hat = s_re*b_re + i*s_im*b_im ("Step 3")
     sr = s_re[:, None]
     si = s_im[:, None]
@@ -90,8 +104,9 @@ def _stage(r_re: np.ndarray, r_im: np.ndarray):
     return k, s_re, s_im, new_re, new_im
 
 
-def quantize(R: np.ndarray, T: int):
-    """Quantize a real weight R [2n][2m] with T residual stages.
+def quantize(R: np.ndarray, T: int, per_tensor: bool = False):
+    """Quantize a real weight R [2n][2m] with T residual stages (per_tensor: one scale pair per
+    stage and matrix, repeated on every row of the scale arrays).
 
     Returns (codes, scales32, scales64, residual_norms):
       codes          uint8 [T][2][n][m]   (matrix index 0 = U, 1 = W)
@@ -111,7 +126,7 @@ def quantize(R: np.ndarray, T: int):
         r_im = np.imag(Z).copy()
         norms[M, 0] = np.sqrt(np.sum(r_re * r_re) + np.sum(r_im * r_im))
         for t in range(T):
-            k, s_re, s_im, r_re, r_im = _stage(r_re, r_im)
+            k, s_re, s_im, r_re, r_im = _stage(r_re, r_im, per_tensor)
             codes[t, M] = k
             scales64[:, t, M, 0] = s_re
             scales64[:, t, M, 1] = s_im

@@ -435,3 +435,42 @@ def check_dequantize_real(dequantize_real, gemv_ref, seed=12, T=3, n=5, m=32, B=
     s = np.zeros((1, 1, 2, 2))
     s[0, 0, 0, 1], s[0, 0, 1, 0] = 3.0, 5.0
     assert np.array_equal(dequantize_real(c, s), np.array([[-5.0, -3.0], [3.0, 5.0]]))
+
+
+def check_per_tensor_scales(quantize, split, seed=21, T=2):
+    """Per-tensor scales: (i) a one-row matrix gives the per-row result; (ii) every row carries
+    the same pair; (iii) for the final codes each pair minimises the whole matrix's squared
+    error on its axis (the least-squares scale is the mean |component| over the coded entries);
+    (iv) a hand-worked 2 x 1 case."""
+    rng = np.random.default_rng(seed)
+    R1 = (rng.standard_normal((2, 128)) * 0.02).astype(np.float32)
+    a = quantize(R1, T, per_tensor=True)
+    b = quantize(R1, T)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+    R = (rng.standard_normal((16, 64)) * 0.02).astype(np.float32)
+    codes, s32, s64, _ = quantize(R, T, per_tensor=True)
+    assert np.all(s64 == s64[:1])
+    U, W = split(R)
+    for M, Z in enumerate((U, W)):
+        r = Z.copy()
+        for t in range(T):
+            k = codes[t, M].astype(np.int64)
+            on_re = (k == 0) | (k == 2)
+            s_re, s_im = s64[0, t, M]
+            # d/ds sum over re-axis entries of (|Re r| - s)^2 = 0  <=>  s = mean |Re r|
+            if on_re.any():
+                assert abs(np.mean(np.abs(r.real[on_re])) - s_re) <= 1e-15 * max(1.0, abs(s_re)) + 1e-18
+            if (~on_re).any():
+                assert abs(np.mean(np.abs(r.imag[~on_re])) - s_im) <= 1e-15 * max(1.0, abs(s_im)) + 1e-18
+            b_re = np.where(k == 0, 1.0, np.where(k == 2, -1.0, 0.0))
+            b_im = np.where(k == 1, 1.0, np.where(k == 3, -1.0, 0.0))
+            r = r - (s_re * b_re + 1j * s_im * b_im)
+    # hand-worked: a 4 x 2 R whose split is U = [2, 4]^T (one column, both entries on the real
+    # axis) and W = 0.  Per row the scales are 2 and 4; per tensor both rows get (2 + 4) / 2 = 3.
+    Rh = np.zeros((4, 2), dtype=np.float32)
+    Rh[0, 0] = Rh[2, 1] = 2.0          # row 0: ReU = 2 (R11 = 2, R22 = 2)
+    Rh[1, 0] = Rh[3, 1] = 4.0          # row 1: ReU = 4
+    codes, _, s64, _ = quantize(Rh, 1, per_tensor=True)
+    assert np.all(codes[0, 0] == 0) and s64[0, 0, 0, 0] == 3.0 and s64[1, 0, 0, 0] == 3.0
+    codes, _, s64, _ = quantize(Rh, 1)
+    assert s64[0, 0, 0, 0] == 2.0 and s64[1, 0, 0, 0] == 4.0

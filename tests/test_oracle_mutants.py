@@ -63,7 +63,7 @@ def test_sequential_sum_order_caught():
 def test_scale_mean_over_all_entries_caught(monkeypatch):
     real_stage = pq._stage
 
-    def bad_stage(r_re, r_im):
+    def bad_stage(r_re, r_im, per_tensor=False):
         k, s_re, s_im, _, _ = real_stage(r_re, r_im)
         m = r_re.shape[1]
         on_re = (k == 0) | (k == 2)
@@ -81,7 +81,7 @@ def test_scale_mean_over_all_entries_caught(monkeypatch):
 def test_residual_sign_error_caught(monkeypatch):
     real_stage = pq._stage
 
-    def bad_stage(r_re, r_im):
+    def bad_stage(r_re, r_im, per_tensor=False):
         k, s_re, s_im, _, _ = real_stage(r_re, r_im)
         new_re = np.where(k == 0, r_re + s_re[:, None], np.where(k == 2, r_re - s_re[:, None], r_re))
         new_im = np.where(k == 1, r_im - s_im[:, None], np.where(k == 3, r_im + s_im[:, None], r_im))
@@ -95,7 +95,7 @@ def test_residual_sign_error_caught(monkeypatch):
 def test_scale_wrong_component_caught(monkeypatch):
     real_stage = pq._stage
 
-    def bad_stage(r_re, r_im):
+    def bad_stage(r_re, r_im, per_tensor=False):
         k, s_re, s_im, _, _ = real_stage(r_re, r_im)
         on_re = (k == 0) | (k == 2)
         n_re = np.maximum(on_re.sum(axis=1), 1)
@@ -208,3 +208,14 @@ def test_dequantize_real_swapped_blocks_caught():
         out[:n, m:], out[n:, :m] = R[n:, :m], R[:n, m:]
         return out
     fails(pins.check_dequantize_real, bad, oracle.gemv_ref)
+
+
+def test_per_tensor_mean_of_row_means_caught():
+    """Averaging the per-row means (instead of the tensor-wide mean) fails the pins."""
+    def bad(R, T, per_tensor=False):
+        codes, s32, s64, norms = oracle.quantize(R, T)
+        if per_tensor:
+            s64 = np.broadcast_to(s64.mean(axis=0, keepdims=True), s64.shape).copy()
+            s32 = s64.astype(np.float32)
+        return codes, s32, s64, norms
+    fails(pins.check_per_tensor_scales, bad, oracle.split)

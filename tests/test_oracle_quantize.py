@@ -58,3 +58,7 @@ def test_scales32_are_rne_of_scales64():
 
 def test_dequantize_real_routes():
     pins.check_dequantize_real(oracle.dequantize_real, oracle.gemv_ref)
+
+
+def test_per_tensor_scales():
+    pins.check_per_tensor_scales(oracle.quantize, oracle.split)
