@@ -25,8 +25,9 @@ Readings taken where the pages are silent or open:
     scales bit for bit.
   * U and W are quantized independently, each with its own residual chain.
   * Alternative granularity (per_tensor=True): one (s_re, s_im) pair per stage and matrix
-    for the whole matrix, the mean over all its entries on that axis.  The sum is the
-    per-row ordered sums added one row after another in row order.
+    for the whole matrix, the mean over all its entries on that axis.  The sum combines the
+    per-row ordered sums in the same fixed order, with rows in place of columns
+    (`ordered_row_sum` over the vector of row sums).
 """
 from __future__ import annotations
 
@@ -75,8 +76,8 @@ def ordered_row_sum(v: np.ndarray) -> np.ndarray:
 
 
 def _tensor_mean(row_sums: np.ndarray, row_counts: np.ndarray) -> float:
-    """Per-tensor mean: row sums added in row order (one after another), over the total count."""
-    total = float(np.add.accumulate(np.asarray(row_sums, dtype=np.float64))[-1])
+    """Per-tensor mean: the row sums combined in the pinned order, over the total count."""
+    total = float(ordered_row_sum(np.asarray(row_sums, dtype=np.float64)[None, :])[0])
     count = int(np.sum(row_counts))
     return total / count if count > 0 else 0.0
 
