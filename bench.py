@@ -14,7 +14,8 @@ One step is one pass of every stage of the path over one batch of inputs:
      do), then the int8-MFMA GEMV runs over the pool;
   3. the bf16-MFMA GEMV over the pool at batch 1, 4 and 16;
   4. prefill: per-token int8 activation quantization of 2048 tokens and the int8-MFMA GEMM;
-  5. the real form of the quantized layer (dequantize, the fake-quant forward).
+  5. the real form of the quantized layer (dequantize, the fake-quant forward);
+  6. quantize + pack with per-tensor axis scales (the other scale granularity).
 Each segment is captured once into a HIP graph and replayed on torch's current stream, with
 HIP events on that stream around every replay; inputs are resident in HBM before the timed
 region starts.
@@ -257,6 +258,11 @@ def main():
     def seg_dequant():                 # the real form of the layer (fake-quant forward)
         f2.fairy2i_dequantize(q0["packed"], q0["scales"], m, R=Rhat)
 
+    ws_t = torch.empty((f2.fairy2i_quantize_tensor_workspace_bytes(n, m, T),), dtype=torch.uint8, device=dev)
+
+    def seg_quantize_tensor():         # the per-tensor-scale quantizer (2T + 1 launches)
+        f2.fairy2i_quantize_tensor(R, T, workspace=ws_t, packed=qout["packed"], scales=qout["scales"])
+
     def seg_act_quant():
         f2.fairy2i_act_quant(xp, q=qp, delta=dp)
 
@@ -264,7 +270,7 @@ def main():
         f2.fairy2i_gemm(q0["packed"], q0["scales"], qp, x_scale=dp, y=yp)
 
     segments = [seg_quantize, seg_decode_i8, seg_gemv_i8, seg_gemv(1), seg_gemv(4), seg_gemv(16),
-                seg_act_quant, seg_gemm, seg_dequant, single_layers]
+                seg_act_quant, seg_gemm, seg_dequant, seg_quantize_tensor, single_layers]
     NSEG = len(segments) - 1
     for fn in segments:                     # eager warm-up (also loads every kernel)
         fn()
@@ -309,7 +315,7 @@ def main():
     torch.cuda.synchronize()
     single_us = e0.elapsed_time(e1) * 1e3 / (3 * P)
 
-    t_quant, t_dec, t_i8, t_b1, t_b4, t_b16, t_aq, t_gemm, t_deq = seg    # ms
+    t_quant, t_dec, t_i8, t_b1, t_b4, t_b16, t_aq, t_gemm, t_deq, t_qt = seg    # ms
     bytes_b = {B: gemv_bytes(n, m, T, B) for B in (1, 4, 16)}
     gemv_ms = {1: t_b1, 4: t_b4, 16: t_b16}
     gbs = {B: P * bytes_b[B] / (gemv_ms[B] * 1e-3) / 1e9 for B in (1, 4, 16)}
@@ -372,6 +378,8 @@ def main():
             "quantize": {"us": round(t_quant * 1e3, 2),
                          "real_params_per_s": round(quant_params / (t_quant * 1e-3), 1),
                          "GB/s": round(quant_read / (t_quant * 1e-3) / 1e9, 2)},
+            "quantize_per_tensor": {"us": round(t_qt * 1e3, 2),
+                                    "real_params_per_s": round(quant_params / (t_qt * 1e-3), 1)},
             "act_quant": {"us": round(t_aq * 1e3, 2),
                           "GB/s": round((Ntok * 2 * m * 3 + Ntok * 4) / (t_aq * 1e-3) / 1e9, 2)},
             "gemm": {"us": round(t_gemm * 1e3, 2), "issued_TOPS": round(gemm_tops, 2),

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FAIRY2I_ABI_VERSION 2
+#define FAIRY2I_ABI_VERSION 3
 
 typedef enum {
   FAIRY2I_OK = 0,
@@ -120,6 +120,31 @@ int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T,
 int fairy2i_quantize_bf16(const uint16_t* R, int64_t two_n, int64_t two_m, int T,
                           uint8_t* packed, float* scales, double* scales64, uint8_t* codes,
                           hipStream_t stream);
+
+/* Device workspace bytes of fairy2i_quantize_tensor for n complex rows: 40 n rounded up to a
+ * multiple of 16, plus 128 (0 when n is out of range; m and T do not enter). */
+size_t fairy2i_quantize_tensor_workspace_bytes(int64_t n, int64_t m, int T);
+
+/* fairy2i_quantize with per-tensor axis scales, the other reading of the axis-wise scales of
+ * "Step 2" (zhichai.net note; ModelScope card "Method"), whose granularity the pages leave open:
+ * one (s_re, s_im) pair per stage and matrix, s_re the mean of |Re r| over every entry of the
+ * matrix coded on the real axis (s_im likewise; 0 if none), residual as in fairy2i_quantize.
+ * The row sums are those of fairy2i_quantize; the tensor sum combines them in the same fixed
+ * order with rows in place of columns (256 partial sums over rows l, l+256, ..., halving tree),
+ * so the result does not depend on the launch.  Counts are exact.
+ *   R, R_dtype  [two_n][two_m], FAIRY2I_F32 (4-byte aligned) or FAIRY2I_BF16 (raw bits,
+ *               2-byte aligned, widened exactly).
+ *   workspace   device memory of at least fairy2i_quantize_tensor_workspace_bytes(n, m, T)
+ *               bytes, 16-byte aligned, owned by the caller; its contents are ignored on entry
+ *               and undefined on return.  Calls that share one workspace must not overlap.
+ *   packed, scales, scales64, codes  as fairy2i_quantize; every row of scales (scales64) holds
+ *               the same pairs, so every consumer of fairy2i_quantize's output takes them as is.
+ * Runs as 2T + 1 launches on stream.  Extra requirement: m <= 32768.  Error codes as
+ * fairy2i_quantize, plus FAIRY2I_ERR_WORKSPACE for a short workspace and FAIRY2I_ERR_DTYPE
+ * for another R_dtype. */
+int fairy2i_quantize_tensor(const void* R, int R_dtype, int64_t two_n, int64_t two_m, int T,
+                            void* workspace, size_t workspace_bytes, uint8_t* packed, float* scales,
+                            double* scales64, uint8_t* codes, hipStream_t stream);
 
 /* Pack one-byte codes uint8 [T][2][n][m] (values 0..3; higher bits are ignored) into the
  * packed form above, padding rows zeroed (ModelScope card "Model details": 2 bits per real

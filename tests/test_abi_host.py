@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert f2.fairy2i_abi_version() == 2
+    assert f2.fairy2i_abi_version() == 3
     for s in range(8):
         assert f2.fairy2i_status_string(s) not in ("", "unknown status")
     assert f2.fairy2i_status_string(99) == "unknown status"
@@ -75,6 +75,31 @@ def test_quantize_bf16_errors(L):
     assert q(FAKE, 256, 256, 5, FAKE, FAKE, NULL, NULL, S) == 3
     assert q(FAKE, 255, 256, 2, FAKE, FAKE, NULL, NULL, S) == 2
     assert q(FAKE + 1, 256, 256, 2, FAKE, FAKE, NULL, NULL, S) == 5
+
+
+def test_quantize_tensor_workspace_bytes(L):
+    w = L.fairy2i_quantize_tensor_workspace_bytes
+    assert w(1, 64, 2) == 48 + 128
+    assert w(2048, 2048, 2) == 40 * 2048 + 128
+    assert w(5, 64, 1) == 208 + 128          # 200 rounded up to 16
+    assert w(0, 64, 2) == 0 and w(-3, 64, 2) == 0
+
+
+def test_quantize_tensor_errors(L):
+    q = L.fairy2i_quantize_tensor
+    ws = 1 << 20
+
+    def call(R=FAKE, dt=f2.F32, two_n=256, two_m=256, T=2, w=FAKE, wb=ws, packed=FAKE, sc=FAKE):
+        return q(R, dt, two_n, two_m, T, w, wb, packed, sc, NULL, NULL, S)
+
+    assert call(R=NULL) == 1 and call(w=NULL) == 1 and call(sc=NULL) == 1
+    assert call(dt=f2.I8) == 4
+    assert call(T=0) == 3
+    assert call(two_n=255) == 2 and call(two_m=200) == 2
+    assert call(two_m=2 * 32832) == 2                      # m > 32768
+    assert call(wb=L.fairy2i_quantize_tensor_workspace_bytes(128, 128, 2) - 1) == 6
+    assert call(R=FAKE + 2) == 5 and call(w=FAKE + 8) == 5
+    assert call(R=FAKE + 2, dt=f2.BF16, w=FAKE + 8) == 5   # bf16 R may sit at 2 bytes; workspace not
 
 
 def test_pack_errors(L):

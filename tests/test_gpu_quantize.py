@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import announce, device, down, up
+from gpu_util import TOL_F32, announce, device, down, rel_l2, up, x_to_dev
 
 import widely_linear_gemv_amd as f2
 
@@ -141,3 +141,71 @@ def test_bf16_weights(T):
     assert np.array_equal(got["packed"], oracle.pack(codes))
     assert np.array_equal(got["scales64"].view(np.uint64), s64.view(np.uint64))
     assert np.array_equal(got["scales"].view(np.uint32), s32.view(np.uint32))
+
+
+def gpu_quantize_tensor(R, T, dev, *, dirty=True, bf16_bits=None):
+    n, m = R.shape[0] // 2, R.shape[1] // 2
+    ws = torch.full((f2.fairy2i_quantize_tensor_workspace_bytes(n, m, T),), 0xA5, dtype=torch.uint8, device=dev)
+    packed = torch.full((f2.fairy2i_packed_bytes(n, m, T),), 0xFF if dirty else 0, dtype=torch.uint8, device=dev)
+    Rg = up(R, dev) if bf16_bits is None else torch.from_numpy(bf16_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = f2.fairy2i_quantize_tensor(Rg, T, want_scales64=True, want_codes=True, workspace=ws, packed=packed)
+    return {k: down(v) for k, v in out.items()}
+
+
+def assert_tensor_match(R, T, got, label):
+    codes, s32, s64, _ = oracle.quantize(R, T, per_tensor=True)
+    assert np.array_equal(got["codes"], codes), label + ": codes"
+    assert np.array_equal(got["packed"], oracle.pack(codes)), label + ": packed (padding rows zero)"
+    assert np.array_equal(got["scales64"].view(np.uint64), s64.view(np.uint64)), label + ": scales64"
+    assert np.array_equal(got["scales"].view(np.uint32), s32.view(np.uint32)), label + ": scales"
+
+
+@pytest.mark.parametrize("n,m,T", [(4, 64, 2), (7, 320, 3), (33, 512, 1), (5, 2048, 4),
+                                   (9, 5504, 2), (3, 6208, 2), (300, 256, 2), (1, 64, 1)])
+def test_tensor_scales_edge_cases(n, m, T):
+    """Per-tensor scales: ties, zeros, empty axes, ragged m and n (padding rows written as zero
+    over a dirty buffer), the register-resident and re-reading kernel variants, T = 1..4, more
+    than 256 rows (several row sums per lane of the combining step)."""
+    dev = device()
+    R = constructed_edge_matrix(n, m, seed=n * 1000 + m + T + 7)
+    announce("quantize per-tensor edge", n, m, T)
+    assert_tensor_match(R, T, gpu_quantize_tensor(R, T, dev), f"tensor n={n} m={m} T={T}")
+
+
+def test_tensor_scales_attention():
+    """The 4096 x 4096 attention layer with per-tensor scales, compared in full."""
+    dev = device()
+    R = workloads.ATTN.weight()
+    announce("quantize per-tensor 4096x4096 T=2")
+    assert_tensor_match(R, 2, gpu_quantize_tensor(R, 2, dev), "attention")
+
+
+def test_tensor_scales_bf16_and_reuse():
+    """bf16 weights quantize like their fp32 widening; a second call on the same (now used)
+    workspace and a smaller matrix gives the fresh result."""
+    dev = device()
+    R = workloads.weight(2 * 600, 2 * 1024, seed=66)
+    bits = workloads.f32_to_bf16_bits(R)
+    announce("quantize per-tensor bf16 1200x2048 T=2")
+    assert_tensor_match(workloads.bf16_bits_to_f32(bits), 2, gpu_quantize_tensor(R, 2, dev, bf16_bits=bits), "bf16")
+    n, m, T = 600, 1024, 2
+    ws = torch.empty((f2.fairy2i_quantize_tensor_workspace_bytes(n, m, T),), dtype=torch.uint8, device=dev)
+    for rows in (600, 77):
+        Rs = np.concatenate([R[:rows, :2 * 256], R[n:n + rows, :2 * 256]], axis=0)
+        out = f2.fairy2i_quantize_tensor(up(Rs, dev), T, want_scales64=True, want_codes=True, workspace=ws)
+        assert_tensor_match(Rs, T, {k: down(v) for k, v in out.items()}, f"reuse rows={rows}")
+
+
+def test_tensor_scales_feed_gemv():
+    """The per-tensor output is an ordinary packed layer: the int8 decode GEMV on it matches the
+    oracle GEMV with the same scales (relative L2 <= 1e-5)."""
+    dev = device()
+    n, m, T = 96, 512, 2
+    R = workloads.weight(2 * n, 2 * m, seed=67)
+    out = f2.fairy2i_quantize_tensor(up(R, dev), T)
+    act = workloads.activations(1, 2 * m, seed=68)
+    announce("per-tensor layer into the int8 GEMV")
+    xd = f2.fairy2i_x_digits(x_to_dev(act, dev))
+    y = down(f2.fairy2i_gemv(out["packed"], out["scales"], xd, algo=f2.GEMV_MFMA_I8))
+    codes, s32, _, _ = oracle.quantize(R, T, per_tensor=True)
+    assert rel_l2(y, oracle.gemv_ref(codes, s32, act.values)) <= TOL_F32

@@ -33,6 +33,8 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "fairy2i_quantize": (_INT, [_P, _I64, _I64, _INT, _P, _P, _P, _P, _P]),
     "fairy2i_quantize_bf16": (_INT, [_P, _I64, _I64, _INT, _P, _P, _P, _P, _P]),
+    "fairy2i_quantize_tensor_workspace_bytes": (_SZ, [_I64, _I64, _INT]),
+    "fairy2i_quantize_tensor": (_INT, [_P, _INT, _I64, _I64, _INT, _P, _SZ, _P, _P, _P, _P, _P]),
     "fairy2i_pack": (_INT, [_P, _I64, _I64, _INT, _P, _P]),
     "fairy2i_packed_bytes": (_SZ, [_I64, _I64, _INT]),
     "fairy2i_dequantize": (_INT, [_P, _P, _I64, _I64, _INT, _P, _INT, _P]),
@@ -112,6 +114,10 @@ def fairy2i_packed_bytes(n: int, m: int, T: int) -> int:
     return int(lib().fairy2i_packed_bytes(n, m, T))
 
 
+def fairy2i_quantize_tensor_workspace_bytes(n: int, m: int, T: int) -> int:
+    return int(lib().fairy2i_quantize_tensor_workspace_bytes(n, m, T))
+
+
 def fairy2i_quantize(R: torch.Tensor, T: int, *, want_scales64: bool = False,
                      want_codes: bool = False, packed=None, scales=None, stream=None):
     """R fp32 or bf16 [2n][2m] on the GPU -> dict(packed (flat uint8), scales[, scales64][, codes])."""
@@ -124,6 +130,30 @@ def fairy2i_quantize(R: torch.Tensor, T: int, *, want_scales64: bool = False,
     codes = torch.empty((T, 2, n, m), dtype=torch.uint8, device=dev) if want_codes else None
     fn = lib().fairy2i_quantize_bf16 if R.dtype == torch.bfloat16 else lib().fairy2i_quantize
     _check(fn(_ptr(R), two_n, two_m, T, _ptr(packed), _ptr(scales), _ptr(s64), _ptr(codes), _stream(stream)))
+    out = {"packed": packed, "scales": scales}
+    if s64 is not None:
+        out["scales64"] = s64
+    if codes is not None:
+        out["codes"] = codes
+    return out
+
+
+def fairy2i_quantize_tensor(R: torch.Tensor, T: int, *, want_scales64: bool = False,
+                            want_codes: bool = False, workspace=None, packed=None, scales=None,
+                            stream=None):
+    """fairy2i_quantize with per-tensor axis scales (every row of scales holds the same pairs)."""
+    two_n, two_m = R.shape
+    n, m = two_n // 2, two_m // 2
+    dev = R.device
+    if workspace is None:
+        workspace = torch.empty((fairy2i_quantize_tensor_workspace_bytes(n, m, T),), dtype=torch.uint8, device=dev)
+    packed = packed if packed is not None else torch.empty((fairy2i_packed_bytes(n, m, T),), dtype=torch.uint8, device=dev)
+    scales = scales if scales is not None else torch.empty((n, T, 2, 2), dtype=torch.float32, device=dev)
+    s64 = torch.empty((n, T, 2, 2), dtype=torch.float64, device=dev) if want_scales64 else None
+    codes = torch.empty((T, 2, n, m), dtype=torch.uint8, device=dev) if want_codes else None
+    _check(lib().fairy2i_quantize_tensor(_ptr(R), _DTYPE[R.dtype], two_n, two_m, T, _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _ptr(packed),
+                                         _ptr(scales), _ptr(s64), _ptr(codes), _stream(stream)))
     out = {"packed": packed, "scales": scales}
     if s64 is not None:
         out["scales64"] = s64

@@ -99,6 +99,39 @@ int fairy2i_quantize_bf16(const uint16_t* R, int64_t two_n, int64_t two_m, int T
   return quantize_any(R, 1, two_n, two_m, T, packed, scales, scales64, codes, stream);
 }
 
+size_t fairy2i_quantize_tensor_workspace_bytes(int64_t n, int64_t m, int T) {
+  (void)m;
+  (void)T;
+  if (n < 1 || n > kMaxRows) return 0;
+  return f2i::quantize_tensor_workspace_bytes(n);
+}
+
+int fairy2i_quantize_tensor(const void* R, int R_dtype, int64_t two_n, int64_t two_m, int T,
+                            void* workspace, size_t workspace_bytes, uint8_t* packed, float* scales,
+                            double* scales64, uint8_t* codes, hipStream_t stream) {
+  if (!R || !packed || !scales || !workspace)
+    return fail(FAIRY2I_ERR_NULL, "R, workspace, packed and scales are required");
+  if (R_dtype != FAIRY2I_F32 && R_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "R_dtype %d: need F32 or BF16", R_dtype);
+  if (int s = check_stages(T)) return s;
+  if (two_n < 2 || two_n % 2 || two_m < 2 || two_m % 2)
+    return fail(FAIRY2I_ERR_SHAPE, "R is %lld x %lld; both sizes must be even",
+                (long long)two_n, (long long)two_m);
+  const int64_t n = two_n / 2, m = two_m / 2;
+  if (int s = check_nm(n, m)) return s;
+  if (2 * m > 65536) return fail(FAIRY2I_ERR_SHAPE, "m = %lld exceeds 32768", (long long)m);
+  const size_t need = f2i::quantize_tensor_workspace_bytes(n);
+  if (workspace_bytes < need)
+    return fail(FAIRY2I_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  const int bf16 = R_dtype == FAIRY2I_BF16;
+  if (!aligned(R, bf16 ? 2 : 4) || !aligned(workspace, 16) || !aligned(packed, 16) || !aligned(scales, 4) ||
+      (scales64 && !aligned(scales64, 8)) || (codes && !aligned(codes, 16)))
+    return fail(FAIRY2I_ERR_ALIGN, "R needs 4 (fp32) or 2 (bf16), scales 4, scales64 8, workspace/packed/codes 16-byte alignment");
+  return hip_status(f2i::launch_quantize_tensor(R, bf16, (int)n, (int)m, T, workspace, packed, scales,
+                                                scales64, codes, stream),
+                    "per-tensor quantize launch");
+}
+
 int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* packed,
                  hipStream_t stream) {
   if (!codes || !packed) return fail(FAIRY2I_ERR_NULL, "codes and packed are required");

@@ -73,6 +73,9 @@ struct GemvGroup {
 hipError_t launch_gemv_mfma_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
 hipError_t launch_quantize(const void* R, int r_bf16, int n, int m, int T, uint8_t* packed, float* scales,
                            double* scales64, uint8_t* codes, hipStream_t s);
+size_t quantize_tensor_workspace_bytes(int64_t n);
+hipError_t launch_quantize_tensor(const void* R, int r_bf16, int n, int m, int T, void* ws, uint8_t* packed,
+                                  float* scales, double* scales64, uint8_t* codes, hipStream_t s);
 hipError_t launch_pack(const uint8_t* codes, int n, int m, int T, uint8_t* packed, hipStream_t s);
 hipError_t launch_gemv_valu(const uint8_t* packed, const float* scales, int n, int m, int T,
                             const void* x, int x_bf16, int B, void* y, int y_bf16, hipStream_t s);

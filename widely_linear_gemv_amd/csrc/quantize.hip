@@ -48,6 +48,19 @@ __device__ __forceinline__ uint32_t pack16(uint4 w) {
   return (w.x & lo2) | ((w.y & lo2) << 2) | ((w.z & lo2) << 4) | ((w.w & lo2) << 6);
 }
 
+// The four sums s_part[q][0..255] combined in the fixed order: halving steps 128 and 64 through
+// LDS, then 32..1 across the first wave; lane 0 ends with the results.  Call with l < kWave.
+__device__ __forceinline__ void tree_sum4(const double (*s_part)[kQThreads], int l, double v[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    v[q] = (s_part[q][l] + s_part[q][l + 128]) + (s_part[q][l + 64] + s_part[q][l + 192]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = v[q] + __shfl_xor(v[q], off);
+  }
+}
+
 // One real weight as fp32: fp32 as is, bf16 widened exactly.
 __device__ __forceinline__ float r_value(float v) { return v; }
 __device__ __forceinline__ float r_value(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
@@ -131,14 +144,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     __syncthreads();
     if (l < kWave) {
       double v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)   // halving steps 128 and 64 of the tree
-        v[q] = (s_part[q][l] + s_part[q][l + 128]) + (s_part[q][l + 64] + s_part[q][l + 192]);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {   // steps 32..1; lane 0 ends with the sum
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = v[q] + __shfl_xor(v[q], off);
-      }
+      tree_sum4(s_part, l, v);
       if (l == 0) {
 #pragma unroll
         for (int M = 0; M < 2; ++M) {
@@ -179,6 +185,212 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
       for (int q = l; q < dw_codes; q += kQThreads) dst[q] = src[q];
     }
   }
+}
+
+// ---- per-tensor scales ----
+// A stage's scale pair needs the sums of every row, so each stage is two launches: a row kernel
+// that runs the stage on one complex row per workgroup (the same column mapping, fixed-order row
+// sums and code packing as k_quantize) and writes the row's four axis sums and two real-axis
+// counts to a workspace, then one workgroup that combines the row sums in the same fixed order
+// (rows in place of columns) into the tensor scales.  The row kernel of stage t writes planes
+// 2t and 2t+1 of the packed form; later stages read those codes back from it.  A last launch
+// repeats the tensor scales on every row of the scales arrays.
+//
+// Workspace: sums fp64 [4][n] (U re, U im, W re, W im), counts int32 [2][n] (U, W real axis),
+// then at a 16-byte boundary the tensor scales fp64 [4 stages][2][2].
+size_t quantize_tensor_workspace_bytes(int64_t n) {
+  return ((size_t)(40 * n) + 15) / 16 * 16 + 128;
+}
+
+template <int MAXC, typename RT>
+__global__ __launch_bounds__(kQThreads) void k_quantize_tensor_stage(
+    const RT* __restrict__ R, int n, int m, int T, int t, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ codes_out, double* __restrict__ sums, int* __restrict__ counts,
+    const double* __restrict__ tscale) {
+  extern __shared__ __align__(16) uint8_t s_codes[];        // [2][m]: stage t's codes of U, W
+  __shared__ double s_part[4][kQThreads];
+  __shared__ int s_cnt[2][kQThreads / kWave];
+  __shared__ double s_scale[16];                            // earlier stages: [tp][M][axis]
+  uint32_t* __restrict__ pw = reinterpret_cast<uint32_t*>(packed);
+  if ((int)blockIdx.x >= n) {                                // padding row of the last tile
+    for (int q = threadIdx.x; q < 2 * (m / 16); q += kQThreads)
+      pw[tiled_word(blockIdx.x, 2 * t + q / (m / 16), q % (m / 16), m, T)] = 0u;
+    return;
+  }
+  const int i = blockIdx.x;
+  const int l = threadIdx.x;
+  if (l < 4 * t) s_scale[l] = tscale[l];
+  __syncthreads();
+  const int64_t ld = 2 * (int64_t)m;
+  const RT* __restrict__ r0 = R + (int64_t)i * ld;
+  const RT* __restrict__ r1 = R + (int64_t)(n + i) * ld;
+  const int nch = (m + kQThreads - 1) / kQThreads;
+
+  constexpr int NR = MAXC > 0 ? MAXC : 1;
+  float qa[NR], qb[NR], qc[NR], qd[NR];
+  if constexpr (MAXC > 0) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int j = l + c * kQThreads;
+      if (j < m) { qa[c] = r_value(r0[j]); qb[c] = r_value(r0[m + j]); qc[c] = r_value(r1[j]); qd[c] = r_value(r1[m + j]); }
+      else { qa[c] = qb[c] = qc[c] = qd[c] = 0.f; }
+    }
+  }
+
+  double sre[2] = {0.0, 0.0}, sim[2] = {0.0, 0.0};
+  int nre[2] = {0, 0};
+  auto body = [&](int j, float A, float B, float C, float D) {
+    const int sh = 8 * (j & 3) + 2 * ((j >> 2) & 3);          // bit position of code j in its word
+#pragma unroll
+    for (int M = 0; M < 2; ++M) {
+      double re, im;
+      split_entry(M, A, B, C, D, re, im);
+      for (int tp = 0; tp < t; ++tp) {                        // earlier stages, in order
+        const int kp = (pw[tiled_word(i, 2 * tp + M, j >> 4, m, T)] >> sh) & 3;
+        if (kp == 0) re = re - s_scale[(tp * 2 + M) * 2];
+        else if (kp == 2) re = re + s_scale[(tp * 2 + M) * 2];
+        else if (kp == 1) im = im - s_scale[(tp * 2 + M) * 2 + 1];
+        else im = im + s_scale[(tp * 2 + M) * 2 + 1];
+      }
+      const int k = project4(re, im);
+      s_codes[M * m + j] = (uint8_t)k;
+      if ((k & 1) == 0) { sre[M] += fabs(re); nre[M] += 1; }
+      else { sim[M] += fabs(im); }
+    }
+  };
+  if constexpr (MAXC > 0) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int j = l + c * kQThreads;
+      if (j < m) body(j, qa[c], qb[c], qc[c], qd[c]);
+    }
+  } else {
+    for (int c = 0; c < nch; ++c) {
+      const int j = l + c * kQThreads;
+      if (j < m) body(j, r_value(r0[j]), r_value(r0[m + j]), r_value(r1[j]), r_value(r1[m + j]));
+    }
+  }
+
+  s_part[0][l] = sre[0];
+  s_part[1][l] = sim[0];
+  s_part[2][l] = sre[1];
+  s_part[3][l] = sim[1];
+  const int cu = wave_sum(nre[0]);
+  const int cw = wave_sum(nre[1]);
+  if ((l & (kWave - 1)) == 0) { s_cnt[0][l / kWave] = cu; s_cnt[1][l / kWave] = cw; }
+  __syncthreads();
+  if (l < kWave) {
+    double v[4];
+    tree_sum4(s_part, l, v);
+    if (l == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sums[(int64_t)q * n + i] = v[q];
+      counts[i] = s_cnt[0][0] + s_cnt[0][1] + s_cnt[0][2] + s_cnt[0][3];
+      counts[n + i] = s_cnt[1][0] + s_cnt[1][1] + s_cnt[1][2] + s_cnt[1][3];
+    }
+  }
+
+  // planes 2t, 2t+1 of row i, one 64-column group (16 bytes) per thread and step
+  const int dw_plane = m / 16;
+  const int gp_plane = m / 64;
+  const uint4* sc4 = reinterpret_cast<const uint4*>(s_codes);
+  for (int q = l; q < 2 * gp_plane; q += kQThreads) {
+    const int M = q / gp_plane, w0 = 4 * (q % gp_plane);
+    const uint4* src = sc4 + M * dw_plane + w0;
+    *reinterpret_cast<uint4*>(pw + tiled_word(i, 2 * t + M, w0, m, T)) =
+        make_uint4(pack16(src[0]), pack16(src[1]), pack16(src[2]), pack16(src[3]));
+  }
+  if (codes_out) {   // [T][2][n][m]
+    for (int M = 0; M < 2; ++M) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(codes_out + ((int64_t)(2 * t + M) * n + i) * m);
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(s_codes + (int64_t)M * m);
+      for (int q = l; q < m / 4; q += kQThreads) dst[q] = src[q];
+    }
+  }
+}
+
+// Stage t's tensor scales: lane l adds the row sums of rows l, l+256, ... in row order starting
+// from +0, then the halving tree; the counts are summed exactly in 64 bits.
+__global__ __launch_bounds__(kQThreads) void k_quantize_tensor_reduce(
+    int n, int m, int t, const double* __restrict__ sums, const int* __restrict__ counts,
+    double* __restrict__ tscale) {
+  __shared__ double s_part[4][kQThreads];
+  __shared__ long long s_cnt[2][kQThreads / kWave];
+  const int l = threadIdx.x;
+  double p[4] = {0.0, 0.0, 0.0, 0.0};
+  long long c[2] = {0, 0};
+  for (int r = l; r < n; r += kQThreads) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = p[q] + sums[(int64_t)q * n + r];
+    c[0] += counts[r];
+    c[1] += counts[n + r];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s_part[q][l] = p[q];
+  const long long cu = wave_sum(c[0]);
+  const long long cw = wave_sum(c[1]);
+  if ((l & (kWave - 1)) == 0) { s_cnt[0][l / kWave] = cu; s_cnt[1][l / kWave] = cw; }
+  __syncthreads();
+  if (l < kWave) {
+    double v[4];
+    tree_sum4(s_part, l, v);
+    if (l == 0) {
+      const long long total = (long long)n * m;
+#pragma unroll
+      for (int M = 0; M < 2; ++M) {
+        const long long n_re = s_cnt[M][0] + s_cnt[M][1] + s_cnt[M][2] + s_cnt[M][3];
+        const long long n_im = total - n_re;
+        tscale[(t * 2 + M) * 2] = n_re > 0 ? v[2 * M] / (double)n_re : 0.0;
+        tscale[(t * 2 + M) * 2 + 1] = n_im > 0 ? v[2 * M + 1] / (double)n_im : 0.0;
+      }
+    }
+  }
+}
+
+// The tensor scales [T][2][2] repeated on every row of scales (fp32, nearest even) and scales64.
+__global__ __launch_bounds__(256) void k_quantize_tensor_scales(
+    int n, int T, const double* __restrict__ tscale, float* __restrict__ scales,
+    double* __restrict__ scales64) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)n * T * 4) return;
+  const double v = tscale[idx % (4 * T)];
+  scales[idx] = (float)v;
+  if (scales64) scales64[idx] = v;
+}
+
+template <typename RT>
+static void launch_quantize_tensor_t(const RT* R, int n, int m, int T, uint8_t* ws, uint8_t* packed,
+                                     float* scales, double* scales64, uint8_t* codes, hipStream_t s) {
+  double* sums = reinterpret_cast<double*>(ws);
+  int* counts = reinterpret_cast<int*>(ws + (size_t)32 * n);
+  double* tscale = reinterpret_cast<double*>(ws + ((size_t)(40 * (int64_t)n) + 15) / 16 * 16);
+  const size_t lds = (size_t)2 * m;
+  const int nch = (m + kQThreads - 1) / kQThreads;
+  const dim3 grid(padded_rows(n)), block(kQThreads);
+  for (int t = 0; t < T; ++t) {
+    if (nch <= 1)
+      hipLaunchKernelGGL((k_quantize_tensor_stage<1, RT>), grid, block, lds, s, R, n, m, T, t, packed, codes, sums, counts, tscale);
+    else if (nch <= 8)
+      hipLaunchKernelGGL((k_quantize_tensor_stage<8, RT>), grid, block, lds, s, R, n, m, T, t, packed, codes, sums, counts, tscale);
+    else if (nch <= 24)
+      hipLaunchKernelGGL((k_quantize_tensor_stage<24, RT>), grid, block, lds, s, R, n, m, T, t, packed, codes, sums, counts, tscale);
+    else
+      hipLaunchKernelGGL((k_quantize_tensor_stage<0, RT>), grid, block, lds, s, R, n, m, T, t, packed, codes, sums, counts, tscale);
+    hipLaunchKernelGGL(k_quantize_tensor_reduce, dim3(1), block, 0, s, n, m, t, sums, counts, tscale);
+  }
+  const int64_t total = (int64_t)n * T * 4;
+  hipLaunchKernelGGL(k_quantize_tensor_scales, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     n, T, tscale, scales, scales64);
+}
+
+hipError_t launch_quantize_tensor(const void* R, int r_bf16, int n, int m, int T, void* ws, uint8_t* packed,
+                                  float* scales, double* scales64, uint8_t* codes, hipStream_t s) {
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  if (r_bf16)
+    launch_quantize_tensor_t(static_cast<const uint16_t*>(R), n, m, T, w, packed, scales, scales64, codes, s);
+  else
+    launch_quantize_tensor_t(static_cast<const float*>(R), n, m, T, w, packed, scales, scales64, codes, s);
+  return hipGetLastError();
 }
 
 // codes uint8 [T][2][n][m] -> the packed form; one thread per packed word (16 codes), rows
