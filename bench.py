@@ -10,8 +10,9 @@ One step is one pass of every stage of the path over one batch of inputs:
   2. decode GEMV at batch 1 over a pool of P distinct copies of the packed layer (P * 4 MB
      >= 512 MB, more than the 256 MB Infinity Cache, so every byte streams from HBM), as
      grouped launches (fairy2i_gemv_grouped, up to 48 layers per launch): x is turned into its
-     exact int8 digit form once (fairy2i_x_digits; the pool's layers share x, as q, k and v
-     do), then the int8-MFMA GEMV runs over the pool;
+     exact fp6 digit form once (fairy2i_x_digits_f6; the pool's layers share x, as q, k and v
+     do), then the fp4-MFMA GEMV runs over the pool; the same with the int8 digit form and the
+     int8-MFMA GEMV;
   3. the bf16-MFMA GEMV over the pool at batch 1, 4 and 16;
   4. prefill: per-token int8 activation quantization of 2048 tokens and the int8-MFMA GEMM;
   5. the real form of the quantized layer (dequantize, the fake-quant forward);
@@ -20,8 +21,8 @@ Each segment is captured once into a HIP graph and replayed on torch's current s
 HIP events on that stream around every replay; inputs are resident in HBM before the timed
 region starts.
 
-`value` is the headline metric: algorithmic HBM bytes of the batch-1 decode segment (digit
-form + int8 GEMV launches) divided by its time (GB/s).  The JSON line also carries the roofline of that kernel, the other legs
+`value` is the headline metric: algorithmic HBM bytes of the batch-1 decode segment (fp6 digit
+form + fp4 GEMV launches) divided by its time (GB/s).  The JSON line also carries the roofline of that kernel, the other legs
 (GB/s, TOPS, params/s) and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -53,7 +54,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_PROFILE = "profiles/gemv_i8_grouped_attention4096_T2_hbm_traffic.md"
+TRAFFIC_PROFILE = "profiles/gemv_f4_grouped_attention4096_T2_hbm_traffic.md"
 
 
 def measured_traffic_per_layer():
@@ -112,8 +113,8 @@ def cpu_baseline(R, T, x1, budget_s):
 
 def stack_legs(f2, torch, dev, T, reps):
     """The LLaMA-2 7B linear stack (32 layers x 7 projections, 6.48e9 real weights): quantize all
-    224 matrices, then one decode step (grouped launches per shared input) at batch 1 (int8 digit
-    form) and batch 8 (bf16), each captured in a HIP graph.  Weights are drawn on the GPU (torch's
+    224 matrices, then one decode step (grouped launches per shared input) at batch 1 (fp6 digit
+    form, fp4 matrix cores) and batch 8 (bf16), each captured in a HIP graph.  Weights are drawn on the GPU (torch's
     generator seeded 5000 + 7 L + p, N(0, 0.02^2)): 25.9 GB of fp32 R is too much for the host
     generator.  Runs outside the timed step."""
     from widely_linear_gemv_amd.stack import DecodeStep, GROUPS, PROJECTIONS
@@ -170,7 +171,7 @@ def stack_legs(f2, torch, dev, T, reps):
         nbytes = sum(gemv_bytes(rows // 2, cols // 2, T, B) for L in range(32) for (_, rows, cols, _) in PROJECTIONS)
         legs[f"stack_decode_b{B}"] = {"gemvs": 224, "launches": 256, "us": round(t * 1e3, 1),
                                       "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes,
-                                      "kernel": "int8 digit form" if B <= 2 else "bf16"}
+                                      "kernel": "fp4 x fp6 digit form" if B <= 2 else "bf16"}
     return legs
 
 
@@ -249,9 +250,20 @@ def main():
     def seg_gemv_i8():                 # the GEMV launches alone (per-launch kernel time)
         f2.fairy2i_gemv_grouped(items_i8, algo=f2.GEMV_MFMA_I8)
 
+    xf1 = f2.XDigits(torch.empty((f2.fairy2i_x_digits_f6_bytes(m, 1),), dtype=torch.uint8, device=dev), 1, m,
+                     f2.X_DIGITS_F6)
+    items_f4 = [(pool[p], spool[p], xf1, ypool[1][p]) for p in range(P)]
+
+    def seg_decode_f4():               # the batch-1 decode path on the fp4 matrix cores
+        f2.fairy2i_x_digits_f6(xs[1], out=xf1)
+        f2.fairy2i_gemv_grouped(items_f4, algo=f2.GEMV_MFMA_F4)
+
+    def seg_gemv_f4():
+        f2.fairy2i_gemv_grouped(items_f4, algo=f2.GEMV_MFMA_F4)
+
     def single_layers():               # one launch per layer (latency-bound small kernels)
         for p in range(P):
-            f2.fairy2i_gemv(pool[p], spool[p], xd1, y=ys[1], algo=f2.GEMV_MFMA_I8)
+            f2.fairy2i_gemv(pool[p], spool[p], xf1, y=ys[1], algo=f2.GEMV_MFMA_F4)
 
     Rhat = torch.empty((2 * n, 2 * m), dtype=torch.float32, device=dev)
 
@@ -269,8 +281,9 @@ def main():
     def seg_gemm():
         f2.fairy2i_gemm(q0["packed"], q0["scales"], qp, x_scale=dp, y=yp)
 
-    segments = [seg_quantize, seg_decode_i8, seg_gemv_i8, seg_gemv(1), seg_gemv(4), seg_gemv(16),
-                seg_act_quant, seg_gemm, seg_dequant, seg_quantize_tensor, single_layers]
+    segments = [seg_quantize, seg_decode_f4, seg_gemv_f4, seg_decode_i8, seg_gemv_i8, seg_gemv(1),
+                seg_gemv(4), seg_gemv(16), seg_act_quant, seg_gemm, seg_dequant, seg_quantize_tensor,
+                single_layers]
     NSEG = len(segments) - 1
     for fn in segments:                     # eager warm-up (also loads every kernel)
         fn()
@@ -315,17 +328,21 @@ def main():
     torch.cuda.synchronize()
     single_us = e0.elapsed_time(e1) * 1e3 / (3 * P)
 
-    t_quant, t_dec, t_i8, t_b1, t_b4, t_b16, t_aq, t_gemm, t_deq, t_qt = seg    # ms
+    t_quant, t_decf4, t_f4, t_dec, t_i8, t_b1, t_b4, t_b16, t_aq, t_gemm, t_deq, t_qt = seg    # ms
     bytes_b = {B: gemv_bytes(n, m, T, B) for B in (1, 4, 16)}
     gemv_ms = {1: t_b1, 4: t_b4, 16: t_b16}
     gbs = {B: P * bytes_b[B] / (gemv_ms[B] * 1e-3) / 1e9 for B in (1, 4, 16)}
     launches = -(-P // 48)                     # grouped launches per segment
     per_launch_us = {B: gemv_ms[B] * 1e3 / launches for B in (1, 4, 16)}
-    # batch-1 decode through the digit form: the conversion reads x and writes 8m digit bytes
-    bytes_i8 = P * bytes_b[1]
-    i8_gbs = bytes_i8 / (t_dec * 1e-3) / 1e9
+    # batch-1 decode through a digit form of x (made once per x, shared by the pool's layers as
+    # q, k and v share theirs), then the grouped GEMV launches
+    bytes_pool = P * bytes_b[1]
+    f4_gbs = bytes_pool / (t_decf4 * 1e-3) / 1e9
+    f4_launch_us = t_f4 * 1e3 / launches
+    f4_launch_gbs = bytes_pool / launches / (f4_launch_us * 1e-6) / 1e9
+    i8_gbs = bytes_pool / (t_dec * 1e-3) / 1e9
     i8_launch_us = t_i8 * 1e3 / launches
-    i8_launch_gbs = bytes_i8 / launches / (i8_launch_us * 1e-6) / 1e9
+    i8_launch_gbs = bytes_pool / launches / (i8_launch_us * 1e-6) / 1e9
     traffic_layer = measured_traffic_per_layer()
     issued_ops = 16 * T * n * m * Ntok
     gemm_tops = issued_ops / (t_gemm * 1e-3) / 1e12
@@ -334,7 +351,7 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": round(i8_gbs, 2),
+        "value": round(f4_gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -351,21 +368,25 @@ def main():
                         "quantize+pack; prefill act-quant + int8 GEMM over 2048 tokens",
             "rows": 2 * n, "cols": 2 * m, "T": T, "batch": 1, "pool_layers": P,
             "x_dtype": "bf16", "y_dtype": "f32",
-            "gemv_kernel": "int8 MFMA on the exact digit form of x, grouped launches",
+            "gemv_kernel": "fp4 x fp6 MFMA (sum/difference sign planes) on the exact fp6 digit form "
+                           "of x, grouped launches",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gemv_i8 (grouped, batch 1)",
-            "achieved": round(i8_launch_gbs, 2),
+            "kernel": "k_gemv_f4 (grouped, batch 1)",
+            "achieved": round(f4_launch_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(i8_launch_gbs / HBM_PEAK_GBS, 4),
+            "frac": round(f4_launch_gbs / HBM_PEAK_GBS, 4),
             "traffic": (None if traffic_layer is None
                         else int(round(traffic_layer * P / launches))),
         },
         "legs": {
             "gemv_b1_i8": {"GB/s": round(i8_gbs, 2), "segment_us": round(t_dec * 1e3, 3),
                            "us_per_launch": round(i8_launch_us, 3), "launch_GB/s": round(i8_launch_gbs, 2),
+                           "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[1]},
+            "gemv_b1_f4": {"GB/s": round(f4_gbs, 2), "segment_us": round(t_decf4 * 1e3, 3),
+                           "us_per_launch": round(f4_launch_us, 3), "launch_GB/s": round(f4_launch_gbs, 2),
                            "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[1]},
             "gemv_b1": {"GB/s": round(gbs[1], 2), "us_per_launch": round(per_launch_us[1], 3),
                         "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[1]},

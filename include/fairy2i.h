@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FAIRY2I_ABI_VERSION 3
+#define FAIRY2I_ABI_VERSION 4
 
 typedef enum {
   FAIRY2I_OK = 0,
@@ -73,25 +73,32 @@ typedef enum {
   FAIRY2I_BF16 = 1,
   FAIRY2I_I8 = 2,
   FAIRY2I_I32 = 3,
-  FAIRY2I_X_DIGITS = 4   /* decode-GEMV x in exact int8 digit form (fairy2i_x_digits) */
+  FAIRY2I_X_DIGITS = 4,     /* decode-GEMV x in exact int8 digit form (fairy2i_x_digits) */
+  FAIRY2I_X_DIGITS_F6 = 5   /* decode-GEMV x in exact fp6 digit form (fairy2i_x_digits_f6) */
 } fairy2i_dtype;
 
-/* GEMV kernels.  AUTO picks MFMA_I8 for x in digit form, MFMA_BF16 for bf16 x and VALU for
- * fp32 x; MFMA means MFMA_BF16.
+/* GEMV kernels.  AUTO picks MFMA_F4 for x in fp6 digit form, MFMA_I8 for x in int8 digit form,
+ * MFMA_BF16 for bf16 x and VALU for fp32 x; MFMA means MFMA_BF16.
  *   VALU       fp32 add/sub/swap accumulation on the vector ALUs; fp32 or bf16 x.
  *   MFMA_BF16  codes decoded in registers to bf16 planes {+-2, 0}, multiplied with the unchanged
  *              bf16 x on v_mfma_f32_16x16x32_bf16: exact products, fp32 sums.  bf16 x.
  *   MFMA_I8    codes decoded to int8 planes {-1, 0, 1}, multiplied with x in digit form (made
  *              once per x by fairy2i_x_digits) on v_mfma_i32_16x16x64_i8: exact int32 sums,
- *              fp32 epilogue.  x_dtype FAIRY2I_X_DIGITS, B <= 2.  The fastest decode kernel at
- *              B <= 2 on gfx950: half the MFMA cycles and ~2/3 of the VALU work per code of
- *              MFMA_BF16. */
+ *              fp32 epilogue.  x_dtype FAIRY2I_X_DIGITS, B <= 2.  Half the MFMA cycles and
+ *              ~2/3 of the VALU work per code of MFMA_BF16.
+ *   MFMA_F4    codes read as fp4 planes of u = B_re + B_im and v = B_re - B_im (both +-1 for
+ *              every codeword, eight bit operations per 16 codes), multiplied with x in fp6
+ *              digit form (fairy2i_x_digits_f6) on v_mfma_scale_f32_16x16x128_f8f6f4: exact
+ *              integer sums in fp32, B_re and B_im sums as (u +- v) / 2, fp32 epilogue.
+ *              x_dtype FAIRY2I_X_DIGITS_F6, B <= 2.  The fastest decode kernel on gfx950: half
+ *              the MFMA cycles and about half the VALU work per code of MFMA_I8. */
 typedef enum {
   FAIRY2I_GEMV_AUTO = 0,
   FAIRY2I_GEMV_VALU = 1,
   FAIRY2I_GEMV_MFMA = 2,
   FAIRY2I_GEMV_MFMA_BF16 = 3,
-  FAIRY2I_GEMV_MFMA_I8 = 4
+  FAIRY2I_GEMV_MFMA_I8 = 4,
+  FAIRY2I_GEMV_MFMA_F4 = 5
 } fairy2i_gemv_algo;
 
 /* Bytes of the packed form of an n x m complex layer with T stages:
@@ -167,6 +174,20 @@ int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* pac
 size_t fairy2i_x_digits_bytes(int64_t m, int64_t B);
 int fairy2i_x_digits(const void* x, int x_dtype, int64_t m, int64_t B, void* digits, hipStream_t stream);
 
+/* fp6 digit form of decode-GEMV activations, the input of the MFMA_F4 kernel.  The same X_b =
+ * round_half_even(x_b 2^S_b) as fairy2i_x_digits (same S_b, same exactness), written with eight
+ * balanced base-8 digits X = sum_l 8^l d_l, d_l in [-4, 3], each stored as fp6 e2m3 (exact).
+ *   x        [B][2m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16, 16-byte aligned.  1 <= B <= 2.
+ *   digits   out, fairy2i_x_digits_f6_bytes(m, B) = 64 + ceil(m / 256) * 4096 * B bytes,
+ *            16-byte aligned: int32 header [B, m, S_0, S_1] in the first 64 bytes, then
+ *            32-byte records ordered [256-column chunk][half][b][lane], each holding the 32 fp6
+ *            digits (6 bits each, little-endian) that one lane of the MFMA_F4 kernel multiplies
+ *            with its fp4 codes, in the column order those codes take in the packed words;
+ *            every byte is written.
+ * The form is tied to the m and B it was made with; pass the same m and B to the GEMV. */
+size_t fairy2i_x_digits_f6_bytes(int64_t m, int64_t B);
+int fairy2i_x_digits_f6(const void* x, int x_dtype, int64_t m, int64_t B, void* digits, hipStream_t stream);
+
 /* Dequantize a packed layer to its real form (the fake-quantized layer of QAT and a third route
  * to the layer's map): U^ = sum_t (s_re(t) b_re(t) + i s_im(t) b_im(t)) and likewise W^
  * (zhichai.net note, "Step 2" dequantization and "Step 3" stage sum), then the real blocks of
@@ -183,11 +204,13 @@ int fairy2i_dequantize(const uint8_t* packed, const float* scales, int64_t n, in
  * subtract or real/imaginary swap with sign; one accumulator per (stage, matrix, axis) so each
  * scale multiplies an accumulated sum, not a weight.
  *   packed, scales  as produced by fairy2i_quantize.
- *   x       [B][2m] with x_dtype FAIRY2I_F32 or FAIRY2I_BF16, or the digit form of such an x
- *           (x_dtype FAIRY2I_X_DIGITS, made with the same m and B).  1 <= B <= 16.
+ *   x       [B][2m] with x_dtype FAIRY2I_F32 or FAIRY2I_BF16, or a digit form of such an x
+ *           (x_dtype FAIRY2I_X_DIGITS or FAIRY2I_X_DIGITS_F6, made with the same m and B).
+ *           1 <= B <= 16.
  *   y       out, [B][2n], y_dtype FAIRY2I_F32 or FAIRY2I_BF16 (round to nearest even).
  *   algo    fairy2i_gemv_algo; MFMA_BF16 requires x_dtype BF16, MFMA_I8 x_dtype X_DIGITS and
- *           B <= 2; VALU takes F32 or BF16.
+ *           B <= 2, MFMA_F4 x_dtype X_DIGITS_F6, B <= 2 and m <= 2^19 (its fp32 sums stay
+ *           exact integers); VALU takes F32 or BF16.
  * Uses no workspace. */
 int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert f2.fairy2i_abi_version() == 3
+    assert f2.fairy2i_abi_version() == 4
     for s in range(8):
         assert f2.fairy2i_status_string(s) not in ("", "unknown status")
     assert f2.fairy2i_status_string(99) == "unknown status"
@@ -132,11 +132,29 @@ def test_gemv_errors(L):
     assert call(algo=f2.GEMV_MFMA_I8, xd=f2.X_DIGITS, B=3) == 2
     assert call(algo=f2.GEMV_VALU, xd=f2.X_DIGITS) == 4
     assert call(algo=f2.GEMV_MFMA_BF16, xd=f2.X_DIGITS) == 4
+    assert call(algo=f2.GEMV_MFMA_F4, xd=f2.X_DIGITS) == 4          # needs the fp6 form
+    assert call(algo=f2.GEMV_MFMA_F4, xd=f2.BF16) == 4
+    assert call(algo=f2.GEMV_MFMA_I8, xd=f2.X_DIGITS_F6) == 4
+    assert call(algo=f2.GEMV_VALU, xd=f2.X_DIGITS_F6) == 4
+    assert call(algo=f2.GEMV_MFMA_F4, xd=f2.X_DIGITS_F6, B=3) == 2
+    assert call(algo=f2.GEMV_MFMA_F4, xd=f2.X_DIGITS_F6, m=(1 << 19) + 64) == 2   # fp32 sums exact
+    assert call(algo=f2.GEMV_AUTO, xd=f2.X_DIGITS_F6, m=(1 << 19) + 64) == 2      # AUTO -> F4
     assert call(T=0) == 3
     assert call(B=0) == 2 and call(B=17) == 2
     assert call(m=32) == 2 and call(n=0) == 2
     assert call(x=FAKE_ODD) == 5
     assert call(y=FAKE + 8) == 5
+
+
+def test_x_digits_f6_bytes_and_errors(L):
+    b = L.fairy2i_x_digits_f6_bytes
+    assert b(64, 1) == 64 + 4096 and b(2048, 1) == 64 + 8 * 4096 and b(320, 2) == 64 + 2 * 2 * 4096
+    assert b(0, 1) == 0 and b(64, 0) == 0
+    d = L.fairy2i_x_digits_f6
+    assert d(NULL, f2.BF16, 64, 1, FAKE, S) == 1 and d(FAKE, f2.BF16, 64, 1, NULL, S) == 1
+    assert d(FAKE, f2.I8, 64, 1, FAKE, S) == 4
+    assert d(FAKE, f2.BF16, 96, 1, FAKE, S) == 2 and d(FAKE, f2.BF16, 64, 3, FAKE, S) == 2
+    assert d(FAKE + 8, f2.BF16, 64, 1, FAKE, S) == 5 and d(FAKE, f2.F32, 64, 1, FAKE + 8, S) == 5
 
 
 def test_packed_bytes(L):

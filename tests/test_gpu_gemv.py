@@ -15,7 +15,9 @@ import widely_linear_gemv_amd as f2
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = {"valu": f2.GEMV_VALU, "mfma": f2.GEMV_MFMA, "bf16": f2.GEMV_MFMA_BF16, "i8": f2.GEMV_MFMA_I8}
+ALGOS = {"valu": f2.GEMV_VALU, "mfma": f2.GEMV_MFMA, "bf16": f2.GEMV_MFMA_BF16, "i8": f2.GEMV_MFMA_I8,
+         "f4": f2.GEMV_MFMA_F4}
+DIGITS = {"i8": f2.fairy2i_x_digits, "f4": f2.fairy2i_x_digits_f6}     # kernels that take a digit form
 
 
 def run(dev, codes, scales, act, algo, y_dtype):
@@ -24,6 +26,8 @@ def run(dev, codes, scales, act, algo, y_dtype):
     x = x_to_dev(act, dev)
     if algo == f2.GEMV_MFMA_I8:
         x = f2.fairy2i_x_digits(x)
+    elif algo == f2.GEMV_MFMA_F4:
+        x = f2.fairy2i_x_digits_f6(x)
     y = f2.fairy2i_gemv(packed, s, x, algo=algo, y_dtype=y_dtype)
     return down(y)
 
@@ -56,7 +60,7 @@ def test_tiny_fp32_x():
 
 
 @pytest.mark.parametrize("B,algo", [(1, "valu"), (4, "valu"), (16, "valu"), (1, "bf16"), (4, "bf16"),
-                                    (16, "bf16"), (1, "i8"), (1, "mfma"), (4, "mfma"), (16, "mfma")])
+                                    (16, "bf16"), (1, "i8"), (1, "f4"), (1, "mfma"), (4, "mfma"), (16, "mfma")])
 def test_attention(B, algo):
     dev = device()
     codes, s32 = attention_layer()
@@ -74,16 +78,16 @@ def test_mlp_shapes(shape, T, B):
     codes = workloads.random_codes(T, n, m, seed=layer.seed + T)
     scales = workloads.random_scales(n, T, seed=layer.seed + 10 * T)
     act = workloads.activations(B, 2 * m, workloads.MLP_X_SEEDS[shape] + B)
-    for algo in ("mfma", "valu", "bf16") + (("i8",) if B <= 2 else ()):
+    for algo in ("mfma", "valu", "bf16") + (("i8", "f4") if B <= 2 else ()):
         check(dev, codes, scales, act, algo, f"{shape} T={T} B={B}")
 
 
 @pytest.mark.parametrize("n,m,T,B", [(1, 64, 1, 1), (17, 192, 2, 3), (33, 128, 4, 5), (5, 320, 3, 16),
                                      (16, 64, 2, 2), (100, 1024, 2, 7), (19, 5504, 3, 2), (40, 6208, 2, 1)])
-@pytest.mark.parametrize("algo", ["valu", "bf16", "i8"])
+@pytest.mark.parametrize("algo", ["valu", "bf16", "i8", "f4"])
 def test_ragged_and_small(n, m, T, B, algo):
-    if algo == "i8" and B > 2:
-        pytest.skip("the int8 kernel takes B <= 2")
+    if algo in DIGITS and B > 2:
+        pytest.skip("the digit-form kernels take B <= 2")
     """Ragged row tiles, m not a multiple of 128 (half-empty last MFMA step), every T, odd B."""
     dev = device()
     codes = workloads.random_codes(T, n, m, seed=n + m + T + B)
@@ -92,7 +96,7 @@ def test_ragged_and_small(n, m, T, B, algo):
     check(dev, codes, scales, act, algo, f"n={n} m={m} T={T} B={B}")
 
 
-@pytest.mark.parametrize("algo,B", [("valu", 4), ("bf16", 4), ("i8", 2)])
+@pytest.mark.parametrize("algo,B", [("valu", 4), ("bf16", 4), ("i8", 2), ("f4", 2), ("f4", 1)])
 def test_zero_and_wide_range_x(algo, B):
     """x with exact zeros and magnitudes spread over 2^-6 .. 2^8 inside each 32-column block."""
     dev = device()
@@ -136,11 +140,15 @@ def test_graph_replay_matches_eager():
         eager = f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA)
         eager_valu = f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_VALU)
         eager_i8 = f2.fairy2i_gemv(packed, s, f2.fairy2i_x_digits(x), algo=f2.GEMV_MFMA_I8) if B <= 2 else None
+        eager_f4 = f2.fairy2i_gemv(packed, s, f2.fairy2i_x_digits_f6(x), algo=f2.GEMV_MFMA_F4) if B <= 2 else None
         torch.cuda.synchronize()
         y = torch.empty_like(eager)
         yv = torch.empty_like(eager)
         yi = torch.empty_like(eager)
+        yf = torch.empty_like(eager)
         xd = f2.XDigits(torch.empty((f2.fairy2i_x_digits_bytes(2048, B),), dtype=torch.uint8, device=dev), B, 2048)
+        xf = f2.XDigits(torch.empty((f2.fairy2i_x_digits_f6_bytes(2048, B),), dtype=torch.uint8, device=dev), B,
+                        2048, f2.X_DIGITS_F6)
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         with torch.cuda.graph(g, stream=cap):
@@ -149,33 +157,38 @@ def test_graph_replay_matches_eager():
             if B <= 2:
                 f2.fairy2i_x_digits(x, out=xd)
                 f2.fairy2i_gemv(packed, s, xd, y=yi, algo=f2.GEMV_MFMA_I8)
+                f2.fairy2i_x_digits_f6(x, out=xf)
+                f2.fairy2i_gemv(packed, s, xf, y=yf, algo=f2.GEMV_MFMA_F4)
         for rep in range(3):
             y.fill_(float("nan"))
             yv.fill_(float("nan"))
             yi.fill_(float("nan"))
+            yf.fill_(float("nan"))
             xd.buf.fill_(0x55)
+            xf.buf.fill_(0x55)
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(y, eager), (B, rep)
             assert torch.equal(yv, eager_valu), (B, rep)
             if B <= 2:
                 assert torch.equal(yi, eager_i8), (B, rep)
+                assert torch.equal(yf, eager_f4), (B, rep)
             f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_VALU)     # eager work between replays
             torch.cuda.synchronize()
         outs[B] = eager
 
 
-@pytest.mark.parametrize("algo", ["mfma", "valu", "i8"])
+@pytest.mark.parametrize("algo", ["mfma", "valu", "i8", "f4"])
 def test_grouped_matches_single_and_oracle(algo):
     """A grouped call over items of different n (and more items than one launch holds) gives,
     item by item, exactly the single-call result, within tolerance of the oracle."""
     dev = device()
-    m, T, B = 512, 2, (2 if algo == "i8" else 3)
+    m, T, B = 512, 2, (2 if algo in DIGITS else 3)
     ns = [16, 33, 1, 200, 64] * 11              # 55 items -> two launches of the grouped kernel
     act = workloads.activations(B, 2 * m, seed=21)
     x = x_to_dev(act, dev)
-    if algo == "i8":
-        x = f2.fairy2i_x_digits(x)
+    if algo in DIGITS:
+        x = DIGITS[algo](x)
     items, singles, refs = [], [], []
     for k, n in enumerate(ns):
         codes = workloads.random_codes(T, n, m, seed=1000 + k)
@@ -234,3 +247,81 @@ def test_x_digits_represent_x(B, dtype):
         if dtype == "bf16":
             near = np.abs(v[b].reshape(2, m)) >= amax * 2.0 ** -14
             assert np.array_equal(X[near] * 2.0 ** -S, v[b].reshape(2, m)[near].astype(np.float64))
+
+
+def f6_value(bits):
+    """fp6 e2m3 (sign, 2 exponent bits, 3 mantissa bits; bias 1) -> float."""
+    sgn = -1.0 if bits & 0x20 else 1.0
+    e, mant = (bits >> 3) & 3, bits & 7
+    return sgn * (mant / 8.0 if e == 0 else (1.0 + mant / 8.0) * 2.0 ** (e - 1))
+
+
+def f6_record_columns(g, s):
+    """Columns (within a 256-column chunk) of the 32 digits of a record of lane group g, half s: the
+    order in which the fp4 planes of the packed words list their codes.  Element q comes from word
+    2s + q // 16 of the lane's 64 columns; within the word from nibble j = q % 8, its lower code
+    (bits 0-1) for (q // 8) % 2 == 0, else its upper code; code p of a word sits at bits
+    8 (p % 4) + 2 (p // 4)."""
+    cols = []
+    for q in range(32):
+        word, upper, j = 2 * s + q // 16, (q // 8) % 2, q % 8
+        bit = 4 * j + 2 * upper
+        p = 4 * ((bit % 8) // 2) + bit // 8
+        cols.append(64 * g + 16 * word + p)
+    return cols
+
+
+@pytest.mark.parametrize("B,dtype,m", [(1, "bf16", 1088), (2, "f32", 1024), (1, "f32", 64)])
+def test_x_digits_f6_represent_x(B, dtype, m):
+    """The fp6 digit form holds the same S as the int8 form, and in every record 32 fp6 digits in
+    [-4, 3] whose value sum_l 8^l d_l over the eight digit records of a column equals
+    round_half_even(x 2^S); bytes 24..31 of each record and the records of absent 64-column groups
+    are zero."""
+    dev = device()
+    rng = np.random.default_rng(50 + B + m)
+    v = rng.standard_normal((B, 2 * m)).astype(np.float32)
+    v *= np.float32(2.0) ** rng.integers(-20, 6, size=v.shape).astype(np.float32)
+    v[rng.random(v.shape) < 0.05] = 0.0
+    if B == 2:
+        v[1] = 0.0
+    if dtype == "bf16":
+        bits = workloads.f32_to_bf16_bits(v)
+        v = workloads.bf16_bits_to_f32(bits)
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        x = torch.from_numpy(v).to(dev)
+    announce("x digits f6", B, dtype, m)
+    xf = f2.fairy2i_x_digits_f6(x)
+    blob = down(xf.buf)
+    assert blob.size == f2.fairy2i_x_digits_f6_bytes(m, B)
+    hdr = blob[:64].view(np.int32)
+    assert hdr[0] == B and hdr[1] == m
+    S_i8 = down(f2.fairy2i_x_digits(x).buf)[:64].view(np.int32)[2:2 + B]
+    nchunk = -(-m // 256)
+    rec = blob[64:].reshape(nchunk, 2, B, 64, 32)
+    assert not rec[..., 24:].any()
+    for b in range(B):
+        S = int(hdr[2 + b])
+        assert S == S_i8[b]
+        want = np.rint(v[b].reshape(2, m).astype(np.float64) * 2.0 ** S).astype(np.int64)
+        X = np.zeros((2, m), dtype=np.int64)
+        seen = np.zeros((2, m), dtype=bool)
+        for c in range(nchunk):
+            for s in range(2):
+                for g in range(4):
+                    present = 256 * c + 64 * g < m
+                    cols = f6_record_columns(g, s)
+                    for comp in range(2):
+                        for l in range(8):
+                            r = rec[c, s, b, 16 * g + 8 * comp + l]
+                            word = int.from_bytes(r[:24].tobytes(), "little")
+                            for q in range(32):
+                                d = f6_value((word >> (6 * q)) & 0x3F)
+                                if not present:
+                                    assert d == 0.0
+                                    continue
+                                assert d == int(d) and -4 <= d <= 3
+                                X[comp, 256 * c + cols[q]] += int(d) * 8 ** l
+                                seen[comp, 256 * c + cols[q]] = True
+        assert seen.all()
+        assert np.array_equal(X, want)

@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libfairy2i.so")
 FAIRY2I_OK = 0
 STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_STAGES", 4: "ERR_DTYPE",
                 5: "ERR_ALIGN", 6: "ERR_WORKSPACE", 7: "ERR_HIP"}
-F32, BF16, I8, I32, X_DIGITS = 0, 1, 2, 3, 4
-GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_MFMA_BF16, GEMV_MFMA_I8 = 0, 1, 2, 3, 4
+F32, BF16, I8, I32, X_DIGITS, X_DIGITS_F6 = 0, 1, 2, 3, 4, 5
+GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_MFMA_BF16, GEMV_MFMA_I8, GEMV_MFMA_F4 = 0, 1, 2, 3, 4, 5
 
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.int32: I32}
 
@@ -40,6 +40,8 @@ SIGNATURES = {
     "fairy2i_dequantize": (_INT, [_P, _P, _I64, _I64, _INT, _P, _INT, _P]),
     "fairy2i_x_digits_bytes": (_SZ, [_I64, _I64]),
     "fairy2i_x_digits": (_INT, [_P, _INT, _I64, _I64, _P, _P]),
+    "fairy2i_x_digits_f6_bytes": (_SZ, [_I64, _I64]),
+    "fairy2i_x_digits_f6": (_INT, [_P, _INT, _I64, _I64, _P, _P]),
     "fairy2i_gemv": (_INT, [_P, _P, _I64, _I64, _INT, _P, _INT, _I64, _P, _INT, _INT, _P]),
     "fairy2i_act_quant": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P]),
     "fairy2i_gemm_workspace_bytes": (_SZ, [_I64, _I64, _INT, _I64, _INT]),
@@ -182,11 +184,12 @@ def fairy2i_dequantize(packed: torch.Tensor, scales: torch.Tensor, m: int, *, R_
 
 
 class XDigits:
-    """Digit form of decode-GEMV activations (fairy2i_x_digits): the uint8 buffer and the B and m
-    it was made with."""
+    """A digit form of decode-GEMV activations: the uint8 buffer, the B and m it was made with,
+    and its dtype code (X_DIGITS: int8 digits of fairy2i_x_digits; X_DIGITS_F6: fp6 digits of
+    fairy2i_x_digits_f6)."""
 
-    def __init__(self, buf: torch.Tensor, B: int, m: int):
-        self.buf, self.B, self.m = buf, B, m
+    def __init__(self, buf: torch.Tensor, B: int, m: int, dtype: int = X_DIGITS):
+        self.buf, self.B, self.m, self.dtype = buf, B, m, dtype
 
     @property
     def device(self):
@@ -201,7 +204,7 @@ def _x_cols(x) -> int:
 def _x_args(x):
     """(pointer, x_dtype, B) of a GEMV activation argument: a [B][2m] tensor or an XDigits."""
     if isinstance(x, XDigits):
-        return _ptr(x.buf), X_DIGITS, x.B
+        return _ptr(x.buf), x.dtype, x.B
     return _ptr(x), _DTYPE[x.dtype], x.shape[0]
 
 
@@ -216,6 +219,21 @@ def fairy2i_x_digits(x: torch.Tensor, out: XDigits | None = None, stream=None) -
     if out is None:
         out = XDigits(torch.empty((fairy2i_x_digits_bytes(m, B),), dtype=torch.uint8, device=x.device), B, m)
     _check(lib().fairy2i_x_digits(_ptr(x), _DTYPE[x.dtype], m, B, _ptr(out.buf), _stream(stream)))
+    return out
+
+
+def fairy2i_x_digits_f6_bytes(m: int, B: int) -> int:
+    return int(lib().fairy2i_x_digits_f6_bytes(m, B))
+
+
+def fairy2i_x_digits_f6(x: torch.Tensor, out: XDigits | None = None, stream=None) -> XDigits:
+    """x [B][2m] (bf16 / fp32, B <= 2) -> its exact fp6 digit form for the fp4 MFMA GEMV."""
+    B, two_m = x.shape
+    m = two_m // 2
+    if out is None:
+        out = XDigits(torch.empty((fairy2i_x_digits_f6_bytes(m, B),), dtype=torch.uint8, device=x.device),
+                      B, m, X_DIGITS_F6)
+    _check(lib().fairy2i_x_digits_f6(_ptr(x), _DTYPE[x.dtype], m, B, _ptr(out.buf), _stream(stream)))
     return out
 
 

@@ -37,6 +37,7 @@ SOURCES = {
     "gemv_valu.hip": [],
     "gemv_mfma.hip": [],
     "gemv_i8.hip": [],
+    "gemv_f4.hip": [],
     "prefill.hip": ["-ffp-contract=off"],
     "dequant.hip": ["-ffp-contract=off"],
     "api.cpp": ["-x", "hip"],

@@ -40,6 +40,16 @@ int check_stages(int T) {
   return FAIRY2I_OK;
 }
 
+// The fp4 GEMV's fp32 sums stay exact integers up to 24 m < 2^24.
+constexpr int64_t kMaxColsF4 = int64_t(1) << 19;
+
+int check_f4_cols(int kernel, int64_t m) {
+  if (kernel == FAIRY2I_GEMV_MFMA_F4 && m > kMaxColsF4)
+    return fail(FAIRY2I_ERR_SHAPE, "m = %lld: the fp4 MFMA GEMV takes m <= %lld", (long long)m,
+                (long long)kMaxColsF4);
+  return FAIRY2I_OK;
+}
+
 int check_nm(int64_t n, int64_t m) {
   if (n < 1 || n > kMaxRows) return fail(FAIRY2I_ERR_SHAPE, "n = %lld out of range", (long long)n);
   if (m < 64 || m > kMaxCols || m % 64 != 0)
@@ -145,24 +155,32 @@ int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* pac
 // Checks the dtype / algorithm / batch combination of a GEMV call and resolves AUTO and MFMA to
 // the kernel that runs.  Returns minus the status (with the message recorded) on a bad combination.
 static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B) {
-  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16 && x_dtype != FAIRY2I_X_DIGITS)
-    return -fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32, BF16 or X_DIGITS", x_dtype);
+  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16 && x_dtype != FAIRY2I_X_DIGITS &&
+      x_dtype != FAIRY2I_X_DIGITS_F6)
+    return -fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32, BF16, X_DIGITS or X_DIGITS_F6", x_dtype);
   if (y_dtype != FAIRY2I_F32 && y_dtype != FAIRY2I_BF16)
     return -fail(FAIRY2I_ERR_DTYPE, "y_dtype %d: need F32 or BF16", y_dtype);
-  if (algo < FAIRY2I_GEMV_AUTO || algo > FAIRY2I_GEMV_MFMA_I8)
+  if (algo < FAIRY2I_GEMV_AUTO || algo > FAIRY2I_GEMV_MFMA_F4)
     return -fail(FAIRY2I_ERR_DTYPE, "unknown GEMV algorithm %d", algo);
   if (B < 1 || B > 16) return -fail(FAIRY2I_ERR_SHAPE, "B = %lld: need 1 <= B <= 16", (long long)B);
   int kernel = algo;
   if (kernel == FAIRY2I_GEMV_AUTO)
-    kernel = x_dtype == FAIRY2I_X_DIGITS ? FAIRY2I_GEMV_MFMA_I8
-           : x_dtype == FAIRY2I_BF16     ? FAIRY2I_GEMV_MFMA_BF16 : FAIRY2I_GEMV_VALU;
+    kernel = x_dtype == FAIRY2I_X_DIGITS    ? FAIRY2I_GEMV_MFMA_I8
+           : x_dtype == FAIRY2I_X_DIGITS_F6 ? FAIRY2I_GEMV_MFMA_F4
+           : x_dtype == FAIRY2I_BF16        ? FAIRY2I_GEMV_MFMA_BF16 : FAIRY2I_GEMV_VALU;
   if (kernel == FAIRY2I_GEMV_MFMA) kernel = FAIRY2I_GEMV_MFMA_BF16;
   if (kernel == FAIRY2I_GEMV_MFMA_I8) {
     if (x_dtype != FAIRY2I_X_DIGITS)
       return -fail(FAIRY2I_ERR_DTYPE, "the int8 MFMA GEMV takes x in digit form (fairy2i_x_digits)");
     if (B > 2) return -fail(FAIRY2I_ERR_SHAPE, "B = %lld: the int8 MFMA GEMV takes B <= 2", (long long)B);
+  } else if (kernel == FAIRY2I_GEMV_MFMA_F4) {
+    if (x_dtype != FAIRY2I_X_DIGITS_F6)
+      return -fail(FAIRY2I_ERR_DTYPE, "the fp4 MFMA GEMV takes x in fp6 digit form (fairy2i_x_digits_f6)");
+    if (B > 2) return -fail(FAIRY2I_ERR_SHAPE, "B = %lld: the fp4 MFMA GEMV takes B <= 2", (long long)B);
   } else if (x_dtype == FAIRY2I_X_DIGITS) {
     return -fail(FAIRY2I_ERR_DTYPE, "x in digit form needs the int8 MFMA GEMV");
+  } else if (x_dtype == FAIRY2I_X_DIGITS_F6) {
+    return -fail(FAIRY2I_ERR_DTYPE, "x in fp6 digit form needs the fp4 MFMA GEMV");
   } else if (kernel == FAIRY2I_GEMV_MFMA_BF16 && x_dtype != FAIRY2I_BF16) {
     return -fail(FAIRY2I_ERR_DTYPE, "the bf16 MFMA GEMV takes bf16 x only");
   }
@@ -192,6 +210,24 @@ int fairy2i_x_digits(const void* x, int x_dtype, int64_t m, int64_t B, void* dig
                     "x digits launch");
 }
 
+size_t fairy2i_x_digits_f6_bytes(int64_t m, int64_t B) {
+  if (m < 1 || B < 1) return 0;
+  return f2i::x_digits_f6_bytes(m, B);
+}
+
+int fairy2i_x_digits_f6(const void* x, int x_dtype, int64_t m, int64_t B, void* digits, hipStream_t stream) {
+  if (!x || !digits) return fail(FAIRY2I_ERR_NULL, "x and digits are required");
+  if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32 or BF16", x_dtype);
+  if (m < 64 || m > kMaxCols || m % 64 != 0)
+    return fail(FAIRY2I_ERR_SHAPE, "m = %lld: need m >= 64 and m %% 64 == 0", (long long)m);
+  if (B < 1 || B > 2) return fail(FAIRY2I_ERR_SHAPE, "B = %lld: the fp6 digit form takes 1 <= B <= 2", (long long)B);
+  if (!aligned(x, 16) || !aligned(digits, 16))
+    return fail(FAIRY2I_ERR_ALIGN, "x and digits need 16-byte alignment");
+  return hip_status(f2i::launch_x_digits_f6(x, x_dtype == FAIRY2I_BF16, (int)m, (int)B, digits, stream),
+                    "x fp6 digits launch");
+}
+
 int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,
                  hipStream_t stream) {
@@ -200,8 +236,13 @@ int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t 
   if (kernel < 0) return -kernel;
   if (int s = check_stages(T)) return s;
   if (int s = check_nm(n, m)) return s;
+  if (int s = check_f4_cols(kernel, m)) return s;
   if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(scales, 4))
     return fail(FAIRY2I_ERR_ALIGN, "packed, x and y need 16-byte alignment, scales 4");
+  if (kernel == FAIRY2I_GEMV_MFMA_F4)
+    return hip_status(f2i::launch_gemv_f4(packed, scales, (int)n, (int)m, T, x, (int)B, y,
+                                          y_dtype == FAIRY2I_BF16, stream),
+                      "gemv (fp4 mfma) launch");
   if (kernel == FAIRY2I_GEMV_MFMA_I8)
     return hip_status(f2i::launch_gemv_i8(packed, scales, (int)n, (int)m, T, x, (int)B, y,
                                           y_dtype == FAIRY2I_BF16, stream),
@@ -228,6 +269,7 @@ int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, i
   if (int s = check_stages(T)) return s;
   for (int k = 0; k < count; ++k)
     if (int s = check_nm(items[k].n, m)) return s;
+  if (int s = check_f4_cols(kernel, m)) return s;
   for (int k = 0; k < count; ++k)
     if (!aligned(items[k].packed, 16) || !aligned(items[k].x, 16) || !aligned(items[k].y, 16) ||
         !aligned(items[k].scales, 4))
@@ -251,9 +293,10 @@ int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, i
       tiles += (int)((it.n + 15) / 16);
     }
     grp.tile_start[grp.count] = tiles;
-    hipError_t e = kernel == FAIRY2I_GEMV_MFMA_I8
-                       ? f2i::launch_gemv_i8_group(grp, (int)m, T, (int)B, y_dtype == FAIRY2I_BF16, stream)
-                       : f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, y_dtype == FAIRY2I_BF16, stream);
+    const int ybf = y_dtype == FAIRY2I_BF16;
+    hipError_t e = kernel == FAIRY2I_GEMV_MFMA_F4 ? f2i::launch_gemv_f4_group(grp, (int)m, T, (int)B, ybf, stream)
+                 : kernel == FAIRY2I_GEMV_MFMA_I8 ? f2i::launch_gemv_i8_group(grp, (int)m, T, (int)B, ybf, stream)
+                 : f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, ybf, stream);
     if (e != hipSuccess) return hip_status(e, "gemv (grouped mfma) launch");
   }
   return ok();

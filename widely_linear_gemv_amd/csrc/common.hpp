@@ -84,6 +84,11 @@ hipError_t launch_gemv_mfma(const uint8_t* packed, const float* scales, int n, i
 hipError_t launch_gemv_i8(const uint8_t* packed, const float* scales, int n, int m, int T,
                           const void* digits, int B, void* y, int y_bf16, hipStream_t s);
 hipError_t launch_gemv_i8_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
+hipError_t launch_gemv_f4(const uint8_t* packed, const float* scales, int n, int m, int T,
+                          const void* digits, int B, void* y, int y_bf16, hipStream_t s);
+hipError_t launch_gemv_f4_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
+size_t x_digits_f6_bytes(int64_t m, int64_t B);
+hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blob, hipStream_t s);
 size_t x_digits_bytes(int64_t m, int64_t B);
 hipError_t launch_x_digits(const void* x, int x_bf16, int m, int B, void* blob, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* packed, const float* scales, int n, int m, int T, void* R,

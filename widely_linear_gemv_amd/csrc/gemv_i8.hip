@@ -30,19 +30,13 @@
 //  * Epilogue: each lane scales its int32 sums by 2^(8l - S_b) and the fp32 axis scales, and
 //    the digits and components of a batch entry are summed across lanes (xor 1, 2, 4).
 #include "common.hpp"
+#include "digits.hpp"
 
 namespace f2i {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kI8Chunk = 256;
-constexpr int kDigitHeader = 64;     // bytes before the digits in the digit form
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t i8_rsrc(const void* base, int64_t bytes) {
-  const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFF00);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
-}
-constexpr uint32_t kI8NoLoad = 0x80000000u;   // buffer offset past every range: the load returns 0
 
 __device__ __forceinline__ void decode_i8(uint32_t w, v4i& re, v4i& im) {
   constexpr uint32_t lo2 = 0x03030303u;
@@ -55,30 +49,7 @@ __device__ __forceinline__ void decode_i8(uint32_t w, v4i& re, v4i& im) {
            (int)__builtin_amdgcn_perm(0u, kIm, k2), (int)__builtin_amdgcn_perm(0u, kIm, k3)};
 }
 
-// Power-of-two exponent S with amax * 2^S in [2^21, 2^22) (0 for an all-zero column).
-__device__ __forceinline__ int digit_exponent(float amax) {
-  if (!(amax > 0.f)) return 0;
-  const int e = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;   // floor(log2 amax), normal
-  return 21 - (e < -126 ? -126 : e);
-}
-
 // ------------------------------------------------------------------ digit form of x ----
-
-template <typename XT> struct Load8x;
-template <> struct Load8x<float> {
-  __device__ static void run(const float* p, float* v) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
-template <> struct Load8x<uint16_t> {
-  __device__ static void run(const uint16_t* p, float* v) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-  }
-};
 
 // One workgroup of 1024 threads per batch column: max |x| (order-free, exact), S, then the
 // digits of all 2m values and the zero slot.  For 2m <= 8192 every thread keeps its 8 values in
@@ -94,20 +65,7 @@ __global__ __launch_bounds__(kDigitThreads) void k_x_digits(const XT* __restrict
   const int stride = kDigitThreads * 8;
   const bool one_pass = 2 * m <= stride;
   float keep[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float amax = 0.f;
-  for (int j = threadIdx.x * 8; j < 2 * m; j += stride) {
-    float v[8];
-    Load8x<XT>::run(xb + j, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { amax = fmaxf(amax, fabsf(v[e])); keep[e] = v[e]; }
-  }
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  if ((threadIdx.x & (kWave - 1)) == 0) s_max[threadIdx.x / kWave] = amax;
-  __syncthreads();
-  amax = 0.f;
-#pragma unroll
-  for (int w = 0; w < kDigitThreads / kWave; ++w) amax = fmaxf(amax, s_max[w]);
+  const float amax = column_amax<XT, kDigitThreads>(xb, 2 * m, keep, s_max);
   const int S = digit_exponent(amax);
   // 2^S as two exact power-of-two factors (S can exceed the fp32 exponent range for tiny columns)
   const float f1 = ldexpf(1.0f, S / 2), f2 = ldexpf(1.0f, S - S / 2);
@@ -186,9 +144,9 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
   const int i0 = tile * 16;
   const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
   // The tile's codes and the digit form through buffer resources: batch entries past B read 0,
-  // and so does every load of a lane group past column m (offset kI8NoLoad).
-  const __amdgpu_buffer_rsrc_t rsrc_a = i8_rsrc(packed + (int64_t)tile * tile_bytes, tile_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc_x = i8_rsrc(blob + kDigitHeader, (int64_t)B * 8 * m);
+  // and so does every load of a lane group past column m (offset kNoLoad).
+  const __amdgpu_buffer_rsrc_t rsrc_a = range_rsrc(packed + (int64_t)tile * tile_bytes, tile_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc_x = range_rsrc(blob + kDigitHeader, (int64_t)B * 8 * m);
   const uint32_t voff_x = (uint32_t)(r * m);          // column r = 8b + 4comp + l -> slot r
 
   v4i acc[TT][2][2];
@@ -210,12 +168,12 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
 #pragma unroll
       for (int M = 0; M < 2; ++M)
         ch.w[t][M] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kI8NoLoad, 0, 0));
+            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, 0));
     const int jg = c * kI8Chunk + 64 * g;            // first column of this lane group
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       ch.x[s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-          rsrc_x, k_ok ? voff_x + (uint32_t)(jg + 16 * s) : kI8NoLoad, 0, 0));
+          rsrc_x, k_ok ? voff_x + (uint32_t)(jg + 16 * s) : kNoLoad, 0, 0));
   };
   auto compute_chunk = [&](const Chunk& ch) {
 #pragma unroll

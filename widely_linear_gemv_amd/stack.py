@@ -6,16 +6,21 @@ the projections that read the same input, are independent).
 
 Per transformer layer the seven projections form four groups by their input: q, k and v share x;
 o reads its own; gate and up share x; down reads its own.  A group is one digit-form pass of its
-x (batch <= 2, int8 matrix cores) and one grouped GEMV launch, so a 32-layer stack is 128
-launches of each kind -- captured once in a HIP graph and replayed.  This module only sequences
+x (batch <= 2: fp6 digits for the fp4 matrix cores, or int8 digits) and one grouped GEMV launch,
+so a 32-layer stack is 128 launches of each kind -- captured once in a HIP graph and replayed.  This module only sequences
 calls of the C ABI (through the binding); all arithmetic runs in the library's kernels.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (GEMV_AUTO, GEMV_MFMA_I8, XDigits, fairy2i_gemv_grouped, fairy2i_x_digits,
-               fairy2i_x_digits_bytes)
+from . import (GEMV_AUTO, GEMV_MFMA_F4, GEMV_MFMA_I8, X_DIGITS, X_DIGITS_F6, XDigits,
+               fairy2i_gemv_grouped, fairy2i_x_digits, fairy2i_x_digits_bytes, fairy2i_x_digits_f6,
+               fairy2i_x_digits_f6_bytes)
+
+# the digit form each digit-form kernel takes: (size in bytes, converter, dtype code)
+_DIGIT_FORMS = {GEMV_MFMA_F4: (fairy2i_x_digits_f6_bytes, fairy2i_x_digits_f6, X_DIGITS_F6),
+                GEMV_MFMA_I8: (fairy2i_x_digits_bytes, fairy2i_x_digits, X_DIGITS)}
 
 # LLaMA-2 7B projections of one layer: name, real rows (2n), real columns (2m), input group
 PROJECTIONS = (("q", 4096, 4096, 0), ("k", 4096, 4096, 0), ("v", 4096, 4096, 0), ("o", 4096, 4096, 1),
@@ -31,14 +36,15 @@ class DecodeStep:
         self.layers, self.xs = layers, xs
         B = xs[0][0].shape[0]
         self.B = B
-        self.algo = algo if algo is not None else (GEMV_MFMA_I8 if B <= 2 else GEMV_AUTO)
+        self.algo = algo if algo is not None else (GEMV_MFMA_F4 if B <= 2 else GEMV_AUTO)
         dev = xs[0][0].device
         self.ys = [[torch.empty((B, rows), dtype=torch.float32, device=dev)
                     for (_, rows, _, _) in PROJECTIONS] for _ in layers]
         self.digits = None
-        if self.algo == GEMV_MFMA_I8:
-            self.digits = [[XDigits(torch.empty((fairy2i_x_digits_bytes(x.shape[1] // 2, B),),
-                                                dtype=torch.uint8, device=dev), B, x.shape[1] // 2)
+        if self.algo in _DIGIT_FORMS:
+            nbytes, self._convert, code = _DIGIT_FORMS[self.algo]
+            self.digits = [[XDigits(torch.empty((nbytes(x.shape[1] // 2, B),), dtype=torch.uint8, device=dev),
+                                    B, x.shape[1] // 2, code)
                             for x in layer_xs] for layer_xs in xs]
 
     def run(self, stream=None):
@@ -46,7 +52,7 @@ class DecodeStep:
             for g in range(GROUPS):
                 x = self.xs[L][g]
                 if self.digits is not None:
-                    x = fairy2i_x_digits(x, out=self.digits[L][g], stream=stream)
+                    x = self._convert(x, out=self.digits[L][g], stream=stream)
                 items = [(projs[p][0], projs[p][1], x, self.ys[L][p])
                          for p, (_, _, _, grp) in enumerate(PROJECTIONS) if grp == g]
                 fairy2i_gemv_grouped(items, algo=self.algo, stream=stream)
