@@ -92,9 +92,10 @@ __device__ __forceinline__ uint32_t fp6_int(int d) {
 
 // One workgroup of 256 threads per (256-column chunk, batch entry): all of them read the whole
 // column (2m values, from L2 after the first workgroup) for max |x| and S -- the same value in
-// every workgroup, as the maximum is order-free -- then thread i < 64 computes work item i of its
-// chunk: 8 columns (a quarter of a record's elements) of one component in one (half s, lane group
-// g), all eight digits.
+// every workgroup, as the maximum is order-free.  Then four neighbouring threads share one work
+// item, 8 columns (a quarter of a record's elements) of one component in one (half s, lane group
+// g): each takes two of the columns and all eight of their digits, and the four 12-bit pieces
+// of each digit's 48 bits are merged across the four lanes; each lane stores two digits' pieces.
 constexpr int kF6Threads = 256;
 
 template <typename XT>
@@ -110,6 +111,15 @@ __global__ __launch_bounds__(kF6Threads) void k_x_digits_f6(const XT* __restrict
   __shared__ float s_max[kF6Threads / kWave];
   const int c = blockIdx.x, b = blockIdx.y;
   const XT* __restrict__ xb = x + (int64_t)b * 2 * m;
+  const int item = threadIdx.x >> 2, part = threadIdx.x & 3;    // part: columns 2 part, 2 part + 1
+  const int quarter = item & 3, comp = (item >> 2) & 1, g = (item >> 3) & 3, s = (item >> 5) & 1;
+  const bool present = kF4Chunk * c + 64 * g < m;
+  float xv[2] = {0.f, 0.f};                  // this thread's two values, loaded before the max pass
+  if (present) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+      xv[jj] = x_value(xb + (int64_t)comp * m + kF4Chunk * c + f4_column(g, s, 8 * quarter + 2 * part + jj));
+  }
   float keep[8];
   const float amax = column_amax<XT, kF6Threads>(xb, 2 * m, keep, s_max);
   const int S = digit_exponent(amax);
@@ -119,31 +129,40 @@ __global__ __launch_bounds__(kF6Threads) void k_x_digits_f6(const XT* __restrict
     if (b == 0) { hdr[0] = B; hdr[1] = m; }
     hdr[2 + b] = S;
   }
-  const int item = threadIdx.x;
-  if (item >= 64) return;
-  const int quarter = item & 3, comp = (item >> 2) & 1, g = (item >> 3) & 3, s = (item >> 5) & 1;
-  uint64_t bits[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (kF4Chunk * c + 64 * g < m) {
+  uint32_t bits[8] = {0, 0, 0, 0, 0, 0, 0, 0};                   // 12 bits per digit
+  if (present) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = kF4Chunk * c + f4_column(g, s, 8 * quarter + j);
-      int X = (int)rintf((x_value(xb + (int64_t)comp * m + col) * f1) * f2);   // |X| <= 2^22
+    for (int jj = 0; jj < 2; ++jj) {
+      int X = (int)rintf((xv[jj] * f1) * f2);                     // |X| <= 2^22
 #pragma unroll
       for (int l = 0; l < 8; ++l) {
         const int d = ((X + 4) & 7) - 4;
         X = (X - d) >> 3;
-        bits[l] |= (uint64_t)fp6_int(d) << (6 * j);
+        bits[l] |= fp6_int(d) << (6 * jj);
       }
     }
   }
+  // digit l's 48 bits: piece of lane part at bits 12 part; lanes 4 item .. 4 item + 3 merge them
+  uint64_t full[8];
 #pragma unroll
   for (int l = 0; l < 8; ++l) {
+    uint64_t v = (uint64_t)bits[l] << (12 * part);
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo |= __shfl_xor(lo, 1);
+    hi |= __shfl_xor(hi, 1);
+    lo |= __shfl_xor(lo, 2);
+    hi |= __shfl_xor(hi, 2);
+    full[l] = ((uint64_t)hi << 32) | lo;
+  }
+#pragma unroll
+  for (int l = 0; l < 8; ++l) {
+    if ((l >> 1) != part) continue;                              // this lane stores digits 2 part, 2 part + 1
     const int lane = 16 * g + 8 * comp + l;
     uint8_t* rec = blob + kDigitHeader + ((((int64_t)c * 2 + s) * B + b) * 64 + lane) * kF6Record;
     uint16_t* r16 = reinterpret_cast<uint16_t*>(rec + 6 * quarter);
-    r16[0] = (uint16_t)bits[l];
-    r16[1] = (uint16_t)(bits[l] >> 16);
-    r16[2] = (uint16_t)(bits[l] >> 32);
+    r16[0] = (uint16_t)full[l];
+    r16[1] = (uint16_t)(full[l] >> 16);
+    r16[2] = (uint16_t)(full[l] >> 32);
     if (quarter == 3) *reinterpret_cast<uint2*>(rec + 24) = make_uint2(0u, 0u);
   }
 }
