@@ -118,8 +118,8 @@ def cpu_baseline(R, T, x1, budget_s):
 
 def stack_legs(f2, torch, dev, T, reps):
     """The LLaMA-2 7B linear stack (32 layers x 7 projections, 6.48e9 real weights): quantize all
-    224 matrices, then one decode step (grouped launches per shared input) at batch 1 (fp6 digit
-    form, fp4 matrix cores) and batch 8 (bf16), each captured in a HIP graph.  Weights are drawn on the GPU (torch's
+    224 matrices, then one decode step (grouped launches per shared input, the stack's default
+    kernel) at batch 1 and batch 8, each captured in a HIP graph.  Weights are drawn on the GPU (torch's
     generator seeded 5000 + 7 L + p, N(0, 0.02^2)): 25.9 GB of fp32 R is too much for the host
     generator.  Runs outside the timed step."""
     from widely_linear_gemv_amd.stack import DecodeStep, GROUPS, PROJECTIONS
@@ -176,7 +176,7 @@ def stack_legs(f2, torch, dev, T, reps):
         nbytes = sum(gemv_bytes(rows // 2, cols // 2, T, B) for L in range(32) for (_, rows, cols, _) in PROJECTIONS)
         legs[f"stack_decode_b{B}"] = {"gemvs": 224, "launches": 256, "us": round(t * 1e3, 1),
                                       "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes,
-                                      "kernel": "fp4 x fp6 digit form" if B <= 2 else "bf16"}
+                                      "kernel": "bf16 matrix cores (default for these latency-bound launches)"}
     return legs
 
 

@@ -53,10 +53,11 @@ def check(host, acts, ys, label):
             assert rel_l2(got, want) <= TOL_F32, (label, L, PROJECTIONS[p][0])
 
 
-@pytest.mark.parametrize("B,algo", [(1, None), (2, f2.GEMV_MFMA_I8), (2, None), (8, None)],
-                         ids=["b1-default", "b2-i8", "b2-default", "b8-default"])
+@pytest.mark.parametrize("B,algo", [(1, None), (1, f2.GEMV_MFMA_F4), (2, f2.GEMV_MFMA_F4),
+                                    (2, f2.GEMV_MFMA_I8), (8, None)],
+                         ids=["b1-default", "b1-f4", "b2-f4", "b2-i8", "b8-default"])
 def test_two_layer_stack(B, algo):
-    """Default kernels: the fp4 GEMV on the fp6 digit form at B <= 2, bf16 matrix cores above."""
+    """Default kernel (bf16 matrix cores on the bf16 x) and the digit-form kernels."""
     dev = device()
     host, dev_layers, xs, acts = build(dev, 2, B)
     step = DecodeStep(dev_layers, xs, algo=algo)

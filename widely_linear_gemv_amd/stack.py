@@ -5,9 +5,12 @@ widely-linear layer y = U x + W conj(x)); 36Kr article, parallel stages (the sta
 the projections that read the same input, are independent).
 
 Per transformer layer the seven projections form four groups by their input: q, k and v share x;
-o reads its own; gate and up share x; down reads its own.  A group is one digit-form pass of its
-x (batch <= 2: fp6 digits for the fp4 matrix cores, or int8 digits) and one grouped GEMV launch,
-so a 32-layer stack is 128 launches of each kind -- captured once in a HIP graph and replayed.  This module only sequences
+o reads its own; gate and up share x; down reads its own.  A group is one grouped GEMV launch, so
+a 32-layer stack is 128 launches, captured once in a HIP graph and replayed.  By default the
+launches take the bf16 x as it is (bf16 matrix cores): these launches are small (4-23 MB) and
+latency-bound, and a digit-form pass per group (needed by the fp4 and int8 kernels, which are
+faster per launch) costs more than it saves.  With algo=GEMV_MFMA_F4 or GEMV_MFMA_I8 each group
+first makes the digit form of its x.  This module only sequences
 calls of the C ABI (through the binding); all arithmetic runs in the library's kernels.
 """
 from __future__ import annotations
@@ -36,7 +39,7 @@ class DecodeStep:
         self.layers, self.xs = layers, xs
         B = xs[0][0].shape[0]
         self.B = B
-        self.algo = algo if algo is not None else (GEMV_MFMA_F4 if B <= 2 else GEMV_AUTO)
+        self.algo = algo if algo is not None else GEMV_AUTO
         dev = xs[0][0].device
         self.ys = [[torch.empty((B, rows), dtype=torch.float32, device=dev)
                     for (_, rows, _, _) in PROJECTIONS] for _ in layers]
