@@ -96,8 +96,11 @@ def test_prefill_quantized_attention_layer():
 
 
 @pytest.mark.parametrize("n,m,T,N", [(1, 64, 1, 1), (17, 192, 2, 7), (33, 128, 3, 40), (5, 320, 4, 33),
-                                     (48, 256, 2, 64), (20, 448, 1, 65), (100, 320, 3, 300)])
+                                     (48, 256, 2, 64), (20, 448, 1, 65), (100, 320, 3, 300),
+                                     (300, 256, 2, 70)])
 def test_prefill_ragged(n, m, T, N):
+    """Ragged rows (workgroups of 8 tiles with absent tiles), columns (a partial 256-column
+    chunk), tokens (a partial token block), every T, and edge activations."""
     dev = device()
     codes = workloads.random_codes(T, n, m, seed=n + m + N)
     scales = workloads.random_scales(n, T, seed=T + N)

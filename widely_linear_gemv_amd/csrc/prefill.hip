@@ -8,13 +8,14 @@
 // cores, and its rounding is fixed exactly (see the header).
 //
 // GEMM: output rows are (complex row i, stage t, matrix M, plane), output columns are
-// (token, component a = Re x or b = Im x).  A workgroup owns 16 complex rows and 8 waves of 8*NF
-// tokens.  Per 64-column step the workgroup decodes the tile's code words once: a shift and a
-// mask spread four codes into four bytes (the packed layout puts codes b, b+4, b+8, b+12 in
-// byte b) and v_perm_b32 maps each byte through a 4-entry table into the int8 planes B_re and
-// B_im, written to LDS.  Each plane fragment and 16-column activation fragment feeds one
-// v_mfma_i32_16x16x64_i8; every sum is exact in int32 (|P| <= 127 m).  The epilogue applies
-// the fp32 scales once per accumulated sum and the token's delta once per output.
+// (token, component a = Re x or b = Im x).  A workgroup owns 8 tiles of 16 complex rows (one per
+// wave) and 8*NF tokens.  The activations of each 256-column chunk are staged once per workgroup
+// in LDS and shared by its 8 waves; each wave decodes its own tile's code words in registers: a
+// shift and a mask spread four codes into four bytes (the packed layout puts codes b, b+4, b+8,
+// b+12 in byte b) and v_perm_b32 maps each byte through a 4-entry table into the int8 planes B_re
+// and B_im.  Each plane fragment and 16-column activation fragment feeds one
+// v_mfma_i32_16x16x64_i8; every sum is exact in int32 (|P| <= 127 m).  The epilogue applies the
+// fp32 scales once per accumulated sum and the token's delta once per output.
 #include "common.hpp"
 
 namespace f2i {
@@ -93,20 +94,9 @@ hipError_t launch_act_quant(const void* x, int x_bf16, int N, int two_m, int8_t*
 
 enum { kOutF32 = 0, kOutBF16 = 1, kOutRaw = 2 };
 
-constexpr int kGemmWaves = 8;      // waves per workgroup (two per SIMD), each with its own 8*NF tokens
-constexpr int kAhead = 3;          // plane fragments read from LDS ahead of their MFMAs
+constexpr int kGemmWaves = 8;      // waves per workgroup, one 16-row tile each
+constexpr int kActPitch = 256 + 16; // LDS row pitch (bytes) of one (token, component) activation row
 
-// Workgroup = 16 complex rows x (8 waves x 8*NF tokens).  Per 128-column step the workgroup
-// decodes the tile's codes once -- one half word (8 codes) per thread -- into int8 planes in a
-// double-buffered LDS tile [plane = (t, M, re/im)][row][128 + pad]; every wave then reads the
-// 4T plane fragments from LDS (one read ahead of the MFMAs that use it) and multiplies them with
-// its own activation fragments, which are loaded from global memory one step ahead into a
-// ping-pong register pair, NF column fragments per plane fragment.
-//
-// No load is predicated: codes and activations are read through buffer resources sized to the
-// rows and tokens that exist, so reads past n or N return 0 (and those outputs are never stored);
-// columns past m (at most one 64-column half of the last step) get zero planes from the decoder,
-// so whatever activations sit there add nothing.
 // Epilogue of a 16-row x 8*NF-token wave tile: acc[p][f] with plane p = (t*2+M)*2 + re/im and
 // column fragment f (tokens tok0 + 8f + r/2, component r & 1).
 template <int TT, int NF, int MODE>
@@ -212,6 +202,19 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t byt
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
 }
 
+// Workgroup = 8 tiles of 16 complex rows (wave w takes tile 8 blockIdx.x + w) x 8*NF tokens.  Per
+// 256-column chunk (the chunk of the packed form) the workgroup stages the tokens' activations,
+// [token][component][256 columns] int8 with a padded row pitch, in one of two LDS buffers; every
+// wave then runs the chunk's four 64-column MFMA steps on it: lane (r, g) decodes word s of its
+// row r, 64-column group g for each of the 2T planes (columns 64g + 16s .. +15, the k order of
+// the decode GEMVs) and multiplies both ternary planes with the NF activation fragments it reads
+// from LDS at the same columns.  The next chunk's code words and activations are loaded at the
+// top of a chunk and the activations written to the other LDS buffer at its end, followed by the
+// chunk's one barrier.
+//
+// No load is predicated: codes and activations are read through buffer resources sized to the
+// tiles and tokens that exist, so reads past n or N return 0 (those outputs are never stored);
+// activation columns past m and code groups past m read as 0 (offset past every range).
 template <int TT, int NF, int MODE>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restrict__ packed,
                                                           const float* __restrict__ scales, int n, int m,
@@ -219,80 +222,27 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
                                                           const float* __restrict__ delta, int N,
                                                           void* __restrict__ yv) {
   constexpr int kPlanes = TT * 4;                  // (t, M, re/im)
-  constexpr int KS = 2;                            // 64-column MFMA sub-steps per pipeline step
-  constexpr int kRow = 64 * KS + 16;               // LDS row pitch: 16 pad bytes spread the rows over the banks
-  __shared__ __align__(16) int8_t s_a[2][kPlanes][16][kRow];
+  constexpr int kRows = 8 * NF * 2;                // (token, component) activation rows
+  constexpr int kSeg = kRows * 16 / (64 * kGemmWaves);   // 16-byte staging segments per thread
+  static_assert(kSeg * 64 * kGemmWaves == kRows * 16, "whole segments per thread");
+  constexpr uint32_t kNoLoad = 0x80000000u;        // buffer offset past every range: reads 0
+  __shared__ __align__(16) int8_t s_b[2][kRows * kActPitch];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: keeps the buffer resources scalar
   const int r = lane & 15;          // A row / B column inside a 16x16 tile
-  const int g = lane >> 4;          // 16-column group of the 64-column step
-  const int i0 = blockIdx.x * 16;
-  const int tok0 = (blockIdx.y * kGemmWaves + wave) * (8 * NF);
-  const int dw_plane = m / 16;
+  const int g = lane >> 4;          // 64-column group of the chunk
+  const int tiles = (n + 15) / 16;
+  const int tile = blockIdx.x * kGemmWaves + wave;
+  const int i0 = tile * 16;
+  const int tok0 = blockIdx.y * (8 * NF);
   const int64_t two_m = 2 * (int64_t)m;
-  const int ksteps = (m + 64 * KS - 1) / (64 * KS);
-
-  // decode assignment: half word h = ((row * 2T + tm) * 4KS + wq) * 2 + hh.  The tile's code
-  // words are read through a buffer resource over this workgroup's tile of the packed form (the
-  // last tile's padding rows hold code 0; their outputs are never stored).  Step kk covers
-  // words 8kk .. 8kk+7 of each row and plane: chunk kk/2, 64-column groups 2(kk%2) and 2(kk%2)+1.
-  static_assert(KS == 2, "a step is half a 256-column chunk of the packed form");
-  constexpr int kHalves = 16 * TT * 2 * 4 * KS * 2;
-  constexpr int kPerThread = (kHalves + 64 * kGemmWaves - 1) / (64 * kGemmWaves);
-  const int64_t tile_bytes = (int64_t)16 * TT * 2 * dw_plane * 4;
-  const __amdgpu_buffer_rsrc_t rsrc_w = make_rsrc(packed + (int64_t)blockIdx.x * tile_bytes, tile_bytes);
-  int woff[kPerThread], wtm[kPerThread];
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
-    const int h = min(tid + u * 64 * kGemmWaves, kHalves - 1);
-    const int rr = h / (TT * 2 * 8 * KS), tm = (h / (8 * KS)) % (TT * 2), wq = (h / 2) % (4 * KS);
-    woff[u] = (wq >> 2) * 64 + rr * 4 + (wq & 3);      // group within the step, row, word
-    wtm[u] = tm;
-  }
-  uint32_t wreg[kPerThread];
-  auto load_words = [&](int kk) {
-    const int c = kk >> 1;
-    const int groups = min(4, (m - 256 * c) >> 6);
-    const int base = c * (TT * 2) * 256 + (kk & 1) * 128;
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u)
-      wreg[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_w, 4 * (base + wtm[u] * groups * 64 + woff[u]), 0, 0);
-  };
-  auto decode_to_lds = [&](int buf, int kk) {
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int h = tid + u * 64 * kGemmWaves;
-      if (kHalves % (64 * kGemmWaves) != 0 && h >= kHalves) continue;
-      const int rr = h / (TT * 2 * 8 * KS), tm = (h / (8 * KS)) % (TT * 2), wq = (h / 2) % (4 * KS), hh = h % 2;
-      constexpr uint32_t lo2 = 0x03030303u;
-      constexpr uint32_t kRe = 0x00FF0001u;   // code 0 -> +1, 1 -> 0, 2 -> -1, 3 -> 0
-      constexpr uint32_t kIm = 0xFF000100u;   // code 0 -> 0, 1 -> +1, 2 -> 0, 3 -> -1
-      const bool in_m = 4 * KS * kk + wq < dw_plane;
-      const uint32_t w = wreg[u];
-      const uint32_t ka = (w >> (4 * hh)) & lo2;        // codes 16wq + 8hh + 0..3
-      const uint32_t kb = (w >> (4 * hh + 2)) & lo2;    // codes 16wq + 8hh + 4..7
-      const int col = 16 * wq + 8 * hh;
-      uint2 re = make_uint2(__builtin_amdgcn_perm(0u, kRe, ka), __builtin_amdgcn_perm(0u, kRe, kb));
-      uint2 im = make_uint2(__builtin_amdgcn_perm(0u, kIm, ka), __builtin_amdgcn_perm(0u, kIm, kb));
-      if (!in_m) re = im = make_uint2(0u, 0u);
-      *reinterpret_cast<uint2*>(&s_a[buf][tm * 2 + 0][rr][col]) = re;
-      *reinterpret_cast<uint2*>(&s_a[buf][tm * 2 + 1][rr][col]) = im;
-    }
-  };
-
-  // Activations: one buffer resource over this wave's tokens, so tokens past N read 0.  Lane
-  // (r, g) reads 16 columns 16g.. of component r&1 of token 8f + r/2.
+  const int nchunk = (m + 255) / 256;
+  const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
+  const __amdgpu_buffer_rsrc_t rsrc_w =
+      make_rsrc(packed + (int64_t)min(tile, tiles - 1) * tile_bytes, tile < tiles ? tile_bytes : 0);
   const __amdgpu_buffer_rsrc_t rsrc_q =
       make_rsrc(q + (int64_t)min(tok0, N) * two_m, (int64_t)max(N - tok0, 0) * two_m);
-  const int voff_q = (int)((r >> 1) * two_m + (r & 1) * m + 16 * g);
-  // B fragments of 64-column sub-step j (= KS * step + u) into one register slot.
-  auto load_b = [&](int j, v4i (&b)[NF]) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-      b[f] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                 rsrc_q, voff_q + (int)(8 * f * two_m) + 64 * j, 0, 0));
-  };
 
   v4i acc[kPlanes][NF];
 #pragma unroll
@@ -300,55 +250,78 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[p][f] = v4i{0, 0, 0, 0};
 
-  // One pipeline step (KS = 2 sub-steps of 64 columns) on LDS buffer `buf`.  Activations use
-  // two register slots, one per sub-step, each loaded one sub-step ahead of its MFMAs; the next
-  // step's code words are loaded at the top and decoded into the other LDS buffer at the end,
-  // followed by the step's one barrier.  Loads and decode run unconditionally (the last step
-  // reloads in-range data and decodes zero planes nobody reads), so every path into a step has
-  // the same loads in flight and the compiler's load counters wait only for the operands due.
-  static_assert(KS == 2, "two activation slots, one per sub-step");
-  v4i b0[NF], b1[NF];
-  auto step = [&](int kk, int buf) {
-    const int kn = min(kk + 1, ksteps - 1);
-    load_b(KS * kk + 1, b1);
-    load_words(kn);
-    // Plane fragments x = (u, p) are read kAhead fragments ahead of the MFMAs that use them; the
-    // scheduling barriers keep those LDS reads in flight under the MFMAs (the scheduler would
-    // otherwise sink each read to its use and expose the LDS latency once per fragment).
-    constexpr int NX = KS * kPlanes;
-    auto lds_a = [&](int x) {
-      return *reinterpret_cast<const v4i*>(&s_a[buf][x % kPlanes][r][64 * (x / kPlanes) + 16 * g]);
-    };
-    v4i a[kAhead + 1];
+  // the wave's 16-row x 256-column block of each plane (t, M): 16 bytes per lane
+  auto load_words = [&](int c, uint4 (&w)[TT * 2]) {
+    const int groups = min(4, (m - 256 * c) >> 6);
+    const bool ok = g < groups;
 #pragma unroll
-    for (int x = 0; x < kAhead; ++x) a[x] = lds_a(x);
+    for (int tm = 0; tm < TT * 2; ++tm)
+      w[tm] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc_w, ok ? (uint32_t)(c * (TT * 2) * 1024 + tm * groups * 256 + lane * 16) : kNoLoad, 0, 0));
+  };
+  // staging segment e = tid + 512 k: activation row e / 16 (token (e/16)/2, component (e/16)&1),
+  // columns 16 (e % 16) .. +15 of the chunk
+  auto load_act = [&](int c, v4i (&st)[kSeg]) {
 #pragma unroll
-    for (int x = 0; x < NX; ++x) {
-      const int u = x / kPlanes, p = x % kPlanes;
-      if (x == kPlanes) load_b(KS * kn, b0);   // sub-step 0 of the next step, under sub-step 1
-      if (x + kAhead < NX) a[(x + kAhead) % (kAhead + 1)] = lds_a(x + kAhead);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        acc[p][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[x % (kAhead + 1)], u == 0 ? b0[f] : b1[f], acc[p][f], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int k = 0; k < kSeg; ++k) {
+      const int e = tid + 64 * kGemmWaves * k, row = e >> 4, sg = e & 15;
+      const bool ok = 256 * c + 16 * sg < m;
+      st[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc_q, ok ? (uint32_t)((row >> 1) * two_m + (row & 1) * m + 256 * c + 16 * sg) : kNoLoad, 0, 0));
     }
-    decode_to_lds(buf ^ 1, kk + 1);
-    __syncthreads();
+  };
+  auto store_act = [&](int buf, const v4i (&st)[kSeg]) {
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k) {
+      const int e = tid + 64 * kGemmWaves * k, row = e >> 4, sg = e & 15;
+      *reinterpret_cast<v4i*>(&s_b[buf][row * kActPitch + 16 * sg]) = st[k];
+    }
+  };
+  auto mfma_step = [&](int buf, const uint4 (&w)[TT * 2], int s) {
+    v4i b[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)      // column r: token 8f + r/2, component r & 1
+      b[f] = *reinterpret_cast<const v4i*>(&s_b[buf][((8 * f + (r >> 1)) * 2 + (r & 1)) * kActPitch + 64 * g + 16 * s]);
+    constexpr uint32_t lo2 = 0x03030303u;
+    constexpr uint32_t kRe = 0x00FF0001u;   // code 0 -> +1, 1 -> 0, 2 -> -1, 3 -> 0
+    constexpr uint32_t kIm = 0xFF000100u;   // code 0 -> 0, 1 -> +1, 2 -> 0, 3 -> -1
+#pragma unroll
+    for (int tm = 0; tm < TT * 2; ++tm) {
+      const uint32_t x = s == 0 ? w[tm].x : s == 1 ? w[tm].y : s == 2 ? w[tm].z : w[tm].w;
+      const uint32_t k0 = x & lo2, k1 = (x >> 2) & lo2, k2 = (x >> 4) & lo2, k3 = (x >> 6) & lo2;
+      const v4i re = v4i{(int)__builtin_amdgcn_perm(0u, kRe, k0), (int)__builtin_amdgcn_perm(0u, kRe, k1),
+                         (int)__builtin_amdgcn_perm(0u, kRe, k2), (int)__builtin_amdgcn_perm(0u, kRe, k3)};
+      const v4i im = v4i{(int)__builtin_amdgcn_perm(0u, kIm, k0), (int)__builtin_amdgcn_perm(0u, kIm, k1),
+                         (int)__builtin_amdgcn_perm(0u, kIm, k2), (int)__builtin_amdgcn_perm(0u, kIm, k3)};
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        acc[tm * 2 + 0][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(re, b[f], acc[tm * 2 + 0][f], 0, 0, 0);
+        acc[tm * 2 + 1][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(im, b[f], acc[tm * 2 + 1][f], 0, 0, 0);
+      }
+    }
   };
 
-  load_words(0);
-  load_b(0, b0);
-  decode_to_lds(0, 0);
+  uint4 w0[TT * 2], w1[TT * 2];
+  v4i st[kSeg];
+  load_words(0, w0);
+  load_act(0, st);
+  store_act(0, st);
   __syncthreads();
-  int kk = 0;
-  for (; kk + 1 < ksteps; kk += 2) {
-    step(kk, 0);
-    step(kk + 1, 1);
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    const int cn = min(c + 1, nchunk - 1);   // the last chunk reloads itself: same loads on every path
+    load_words(cn, w1);
+    load_act(cn, st);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) mfma_step(buf, w0, s);
+    store_act(buf ^ 1, st);                  // its last readers passed the previous barrier
+    __syncthreads();
+#pragma unroll
+    for (int tm = 0; tm < TT * 2; ++tm) w0[tm] = w1[tm];
   }
-  if (kk < ksteps) step(kk, 0);
 
-  gemm_epilogue<TT, NF, MODE>(acc, scales, n, N, delta, yv, i0, tok0, r, g);
+  if (tile < tiles) gemm_epilogue<TT, NF, MODE>(acc, scales, n, N, delta, yv, i0, tok0, r, g);
 }
 
 template <int TT>
@@ -356,8 +329,10 @@ static void launch_gemm_t(const uint8_t* packed, const float* scales, int n, int
                           const int8_t* q, const float* delta, int N, void* y, int mode,
                           hipStream_t s) {
   constexpr int NF = TT <= 2 ? 4 : 2;   // accumulators: 4T planes x NF fragments x 4 registers
-  constexpr int tok_per_wg = kGemmWaves * 8 * NF;
-  const dim3 grid((n + 15) / 16, (N + tok_per_wg - 1) / tok_per_wg), block(64 * kGemmWaves);
+  constexpr int tok_per_wg = 8 * NF;
+  const int tiles = (n + 15) / 16;
+  const dim3 grid((tiles + kGemmWaves - 1) / kGemmWaves, (N + tok_per_wg - 1) / tok_per_wg),
+      block(64 * kGemmWaves);
   if (mode == kOutF32)
     hipLaunchKernelGGL((k_gemm<TT, NF, kOutF32>), grid, block, 0, s, packed, scales, n, m, q, delta, N, y);
   else if (mode == kOutBF16)
