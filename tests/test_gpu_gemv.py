@@ -325,3 +325,31 @@ def test_x_digits_f6_represent_x(B, dtype, m):
                                 seen[comp, 256 * c + cols[q]] = True
         assert seen.all()
         assert np.array_equal(X, want)
+
+
+@pytest.mark.parametrize("B,m,T", [(3, 320, 2), (4, 2048, 2), (9, 320, 1), (16, 320, 3), (16, 2048, 2)])
+def test_grouped_large_batch_shared_x(B, m, T):
+    """Grouped launches of at least 1536 row tiles at B >= 3 run the shared-x bf16 kernel (x
+    staged per chunk in LDS for 8 tiles of one item).  Items of 2048 rows plus ragged ones (37,
+    1, 200 rows: workgroups with absent tiles), a partial last chunk (m = 320), odd B and both
+    column groups; every item (or a sample at m = 2048) against the oracle."""
+    dev = device()
+    ns = [2048] * 12 + [37, 1, 200]
+    act = workloads.activations(B, 2 * m, seed=70 + B + m)
+    x = x_to_dev(act, dev)
+    items, host = [], []
+    for k, n in enumerate(ns):
+        codes = workloads.random_codes(T, n, m, seed=3000 + 17 * k + B)
+        scales = workloads.random_scales(n, T, seed=4000 + k)
+        y = torch.full((B, 2 * n), float("nan"), dtype=torch.float32, device=dev)
+        items.append((up(oracle.pack(codes), dev), up(scales, dev), x, y))
+        host.append((codes, scales))
+    assert sum((n + 15) // 16 for n in ns) >= 1536
+    announce("grouped large batch", B, m, T)
+    f2.fairy2i_gemv_grouped(items, algo=f2.GEMV_MFMA_BF16)
+    torch.cuda.synchronize()
+    check_items = range(len(ns)) if m <= 320 else (0, 11, 12, 13, 14)
+    for k in check_items:
+        codes, scales = host[k]
+        want = oracle.gemv_ref(codes, scales, act.values)
+        assert rel_l2(down(items[k][3]), want) <= TOL_F32, (k, ns[k])

@@ -34,6 +34,11 @@
 //  * One 16x16 fp32 accumulator per (stage, matrix, plane, column group).  The epilogue applies
 //    the fp32 scales (and the factor 1/2 of the +-2 encoding) once per accumulated sum and adds
 //    the a and b columns of a batch entry across two lanes.
+//  * Large launches at batch 3-16 (k_gemv_mfma_sx): a workgroup takes 8 consecutive tiles of one
+//    item, one per wave, and stages each chunk's x -- the same for all 8 -- once in LDS, already
+//    permuted into the B-operand order; the waves read their B operands from there.  Loading x
+//    per wave costs as many bytes as the codes at B = 4 and four times as many at B = 16, and
+//    holding two chunks of it in registers leaves one wave per SIMD; shared, it costs neither.
 #include "common.hpp"
 
 namespace f2i {
@@ -78,6 +83,30 @@ __device__ __forceinline__ int find_item(const GemvGroup& g, int tile) {
     if (g.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Widely-linear combination of one output row (lane element e) for column group cg: the Re y and
+// Im y contributions of this lane's column (component comp of one batch entry), before the a and b
+// columns of the entry are added across lanes.  Scales are halved (the planes carry +-2).
+template <int TT, int CG>
+__device__ __forceinline__ void combine_row(const v4f (&acc)[TT][2][2][CG], const float* sc, int e, int cg,
+                                            int comp, float& vre, float& vim) {
+  vre = 0.f;
+  vim = 0.f;
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const float sUr = 0.5f * sc[4 * t], sUi = 0.5f * sc[4 * t + 1];
+    const float sWr = 0.5f * sc[4 * t + 2], sWi = 0.5f * sc[4 * t + 3];
+    const float CUr = acc[t][0][0][cg][e], CUi = acc[t][0][1][cg][e];
+    const float CWr = acc[t][1][0][cg][e], CWi = acc[t][1][1][cg][e];
+    if (comp == 0) {    // a = Re x:  Re += sUr*P(U,re) + sWr*P(W,re) ; Im += sUi*P(U,im) + sWi*P(W,im)
+      vre += sUr * CUr + sWr * CWr;
+      vim += sUi * CUi + sWi * CWi;
+    } else {            // b = Im x:  Re += sWi*P(W,im) - sUi*P(U,im) ; Im += sUr*P(U,re) - sWr*P(W,re)
+      vre += sWi * CWi - sUi * CUi;
+      vim += sUr * CUr - sWr * CWr;
+    }
+  }
 }
 
 template <int TT, int CG, int NW, typename YT>
@@ -195,21 +224,8 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
     const float* sc = scales + (int64_t)min(i, n - 1) * TT * 4;
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
-      float vre = 0.f, vim = 0.f;
-#pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        const float sUr = 0.5f * sc[4 * t], sUi = 0.5f * sc[4 * t + 1];
-        const float sWr = 0.5f * sc[4 * t + 2], sWi = 0.5f * sc[4 * t + 3];
-        const float CUr = acc[t][0][0][cg][e], CUi = acc[t][0][1][cg][e];
-        const float CWr = acc[t][1][0][cg][e], CWi = acc[t][1][1][cg][e];
-        if (comp == 0) {    // a = Re x:  Re += sUr*P(U,re) + sWr*P(W,re) ; Im += sUi*P(U,im) + sWi*P(W,im)
-          vre += sUr * CUr + sWr * CWr;
-          vim += sUi * CUi + sWi * CWi;
-        } else {            // b = Im x:  Re += sWi*P(W,im) - sUi*P(U,im) ; Im += sUr*P(U,re) - sWr*P(W,re)
-          vre += sWi * CWi - sUi * CUi;
-          vim += sUr * CUr - sWr * CWr;
-        }
-      }
+      float vre, vim;
+      combine_row<TT, CG>(acc, sc, e, cg, comp, vre, vim);
       vre += __shfl_xor(vre, 1);
       vim += __shfl_xor(vim, 1);
       const int b = cg * 8 + (r >> 1);
@@ -235,11 +251,162 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
   }
 }
 
+constexpr int kSxWaves = 8;             // tiles (waves) per workgroup of the shared-x kernel
+constexpr int kSxPitch = 2 * kChunk + 16;  // LDS bytes per (batch, component) row of a chunk's x
+
+// Shared-x form for large launches.  grp.tile_start counts workgroups of kSxWaves tiles here, so
+// a workgroup never spans two items (their x differ); tiles past an item's last read no codes and
+// store nothing.  Per chunk the workgroup stages x[b][comp][256 columns] (bf16, permuted per 8
+// columns) in one of two LDS buffers, one 16-byte unit per thread and column group, and waits
+// once; codes are loaded one chunk ahead as in k_gemv_mfma.
+template <int TT, int CG, typename YT>
+__global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGroup grp, int m, int B) {
+  constexpr int kXRows = 16 * CG;                 // (batch, component) rows of the B operand
+  constexpr int kSeg = kXRows * (2 * kChunk / 16) / (kWave * kSxWaves);   // 16-byte units per thread
+  static_assert(kSeg * kWave * kSxWaves == kXRows * (2 * kChunk / 16), "whole units per thread");
+  __shared__ __align__(16) uint8_t s_x[2][kXRows * kSxPitch];
+  const int item = find_item(grp, blockIdx.x);
+  const GemvItem it = grp.items[item];
+  const int n = it.n;
+  const uint8_t* __restrict__ packed = static_cast<const uint8_t*>(it.packed);
+  const float* __restrict__ scales = it.scales;
+  const uint16_t* __restrict__ x = static_cast<const uint16_t*>(it.x);
+  YT* __restrict__ y = static_cast<YT*>(it.y);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
+  const int r = lane & 15, g = lane >> 4;
+  const int comp = r & 1;
+  const int tiles = (n + 15) / 16;
+  const int tile = kSxWaves * (blockIdx.x - grp.tile_start[item]) + wave;
+  const int i0 = tile * 16;
+  const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      gemv_rsrc(packed + (int64_t)min(tile, tiles - 1) * tile_bytes, tile < tiles ? tile_bytes : 0);
+  const __amdgpu_buffer_rsrc_t rsrc_x = gemv_rsrc(x, (int64_t)B * 2 * m * 2);
+
+  v4f acc[TT][2][2][CG];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int M = 0; M < 2; ++M)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg) acc[t][M][p][cg] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunk = (m + kChunk - 1) / kChunk;
+  // staging unit e = tid + 512 k: row e / 32 (batch row / 2, component row & 1), columns 8 (e % 32)
+  auto load_x = [&](int c, uint4 (&st)[kSeg]) {
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k) {
+      const int e = tid + kWave * kSxWaves * k, row = e >> 5, u = e & 31;
+      const bool ok = kChunk * c + 8 * u < m;
+      st[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc_x, ok ? (uint32_t)((row * m + kChunk * c + 8 * u) * 2) : kNoLoad, 0, 0));
+    }
+  };
+  auto store_x = [&](int buf, const uint4 (&st)[kSeg]) {
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k) {
+      const int e = tid + kWave * kSxWaves * k, row = e >> 5, u = e & 31;
+      *reinterpret_cast<v4u*>(&s_x[buf][row * kSxPitch + 16 * u]) = permute_b(st[k]);
+    }
+  };
+  auto load_w = [&](int c, uint4 (&w)[TT][2]) {
+    const int groups = min(4, (m - kChunk * c) >> 6);
+    const bool k_ok = g < groups;
+    const uint32_t cbase = (uint32_t)c * (TT * 2) * 1024;
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int M = 0; M < 2; ++M)
+        w[t][M] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, 0));
+  };
+  auto compute_chunk = [&](int buf, const uint4 (&wc)[TT][2]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      v4u bv[CG];
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg)   // column r: batch 8 cg + r/2, component r & 1; columns 64g + 8s ..
+        bv[cg] = *reinterpret_cast<const v4u*>(&s_x[buf][((cg * 8 + (r >> 1)) * 2 + comp) * kSxPitch + (64 * g + 8 * s) * 2]);
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int M = 0; M < 2; ++M) {
+          const uint4 q = wc[t][M];
+          const uint32_t w = (s >> 1) == 0 ? q.x : (s >> 1) == 1 ? q.y : (s >> 1) == 2 ? q.z : q.w;
+          v4u are, aim;
+          if (s & 1) decode_bf16<1>(w, are, aim); else decode_bf16<0>(w, are, aim);
+#pragma unroll
+          for (int cg = 0; cg < CG; ++cg) {
+            acc[t][M][0][cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, are), __builtin_bit_cast(v8bf, bv[cg]), acc[t][M][0][cg], 0, 0, 0);
+            acc[t][M][1][cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, aim), __builtin_bit_cast(v8bf, bv[cg]), acc[t][M][1][cg], 0, 0, 0);
+          }
+        }
+    }
+  };
+
+  uint4 w0[TT][2], w1[TT][2];
+  uint4 st[kSeg];
+  load_w(0, w0);
+  load_x(0, st);
+  store_x(0, st);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int cn = min(c + 1, nchunk - 1);   // the last chunk reloads itself: same loads on every path
+    load_w(cn, w1);
+    load_x(cn, st);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_chunk(c & 1, w0);
+    store_x((c & 1) ^ 1, st);                // its last readers passed the previous barrier
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TT; ++t) { w0[t][0] = w1[t][0]; w0[t][1] = w1[t][1]; }
+  }
+  if (tile >= tiles) return;
+
+  const int64_t ys = 2 * (int64_t)n;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = i0 + 4 * g + e;
+    const float* sc = scales + (int64_t)min(i, n - 1) * TT * 4;
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      float vre, vim;
+      combine_row<TT, CG>(acc, sc, e, cg, comp, vre, vim);
+      vre += __shfl_xor(vre, 1);
+      vim += __shfl_xor(vim, 1);
+      const int b = cg * 8 + (r >> 1);
+      if (comp == 0 && b < B && i < n) {
+        store_out(y, (int64_t)b * ys + i, vre);
+        store_out(y, (int64_t)b * ys + n + i, vim);
+      }
+    }
+  }
+}
+
 template <int TT, int CG, typename YT>
 static void launch_cg(const GemvGroup& grp, int m, int B, hipStream_t s) {
   const int tiles = grp.tile_start[grp.count];
+  const int nw = gemv_waves_per_tile(tiles, m);
+  if (nw == 1 && B >= 3) {                 // large launch, batch 3-16: shared x
+    GemvGroup sx = grp;
+    int blocks = 0;
+    for (int k = 0; k < sx.count; ++k) {
+      sx.tile_start[k] = blocks;
+      blocks += ((sx.items[k].n + 15) / 16 + kSxWaves - 1) / kSxWaves;
+    }
+    sx.tile_start[sx.count] = blocks;
+    hipLaunchKernelGGL((k_gemv_mfma_sx<TT, CG, YT>), dim3(blocks), dim3(kSxWaves * kWave), 0, s, sx, m, B);
+    return;
+  }
   const dim3 grid(tiles);
-  switch (gemv_waves_per_tile(tiles, m)) {
+  switch (nw) {
     case 8: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 8, YT>), grid, dim3(8 * kWave), 0, s, grp, m, B); break;
     case 4: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 4, YT>), grid, dim3(4 * kWave), 0, s, grp, m, B); break;
     case 2: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 2, YT>), grid, dim3(2 * kWave), 0, s, grp, m, B); break;
