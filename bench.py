@@ -7,8 +7,9 @@ T = 2 residual stages, bf16 activations, all inputs synthetic and seeded (worklo
 
 One step is one pass of every stage of the path over one batch of inputs:
   1. quantize + pack the layer (split, projection, axis scales, residual stages, packing);
-  2. decode GEMV at batch 1 over a pool of P distinct copies of the packed layer (P * 4 MB
-     >= 512 MB, more than the 256 MB Infinity Cache, so every byte streams from HBM), as
+  2. decode GEMV at batch 1 over a pool of P = 256 distinct copies of the packed layer (1 GiB,
+     four times the 256 MB Infinity Cache, so every pass streams from HBM and no segment gains
+     from the pool reads of the one before it, as a decode step over a 1.6 GB stack would not), as
      grouped launches (fairy2i_gemv_grouped, up to 48 layers per launch): x is turned into its
      exact fp6 digit form once (fairy2i_x_digits_f6; the pool's layers share x, as q, k and v
      do), then the fp4-MFMA GEMV runs over the pool; the same with the int8 digit form and the
@@ -41,7 +42,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
 METRIC = "packed 2-bit widely-linear GEMV HBM GB/s (% peak) + prefill GEMM int8 TOPS"
-POOL_BYTES = 512 * 2 ** 20
+POOL_BYTES = 2 ** 30     # 4x the 256 MB Infinity Cache: every pass streams from HBM
 
 
 def parse():

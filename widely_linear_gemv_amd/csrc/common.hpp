@@ -70,6 +70,24 @@ struct GemvGroup {
   int tile_start[kMaxGroup + 1];   // first 16-row tile of each item; [count] = total tiles
   GemvItem items[kMaxGroup];
 };
+// Buffer resource over [base, base + bytes): loads at offsets past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
+  const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFF00);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+constexpr uint32_t kNoLoad = 0x80000000u;   // buffer offset past every range: the load returns 0
+
+// Workgroup -> item of a grouped launch: the last item whose first workgroup (tile_start, in the
+// launch's own unit of tiles or tile groups) is at or before `block`.
+__device__ __forceinline__ int find_item(const GemvGroup& g, int block) {
+  int lo = 0, hi = g.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.tile_start[mid] <= block) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 hipError_t launch_gemv_mfma_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
 hipError_t launch_quantize(const void* R, int r_bf16, int n, int m, int T, uint8_t* packed, float* scales,
                            double* scales64, uint8_t* codes, hipStream_t s);

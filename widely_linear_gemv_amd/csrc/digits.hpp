@@ -7,13 +7,6 @@ namespace f2i {
 
 constexpr int kDigitHeader = 64;     // bytes before the digits: int32 [B, m, S_0 .. S_{B-1}]
 
-// Buffer resource over [base, base + bytes): loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
-  const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFF00);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
-}
-constexpr uint32_t kNoLoad = 0x80000000u;   // buffer offset past every range: the load returns 0
-
 // Power-of-two exponent S with amax * 2^S in [2^21, 2^22) (0 for an all-zero column).
 __device__ __forceinline__ int digit_exponent(float amax) {
   if (!(amax > 0.f)) return 0;

@@ -184,18 +184,9 @@ hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blo
 
 // ------------------------------------------------------------------------- GEMV ----
 
-__device__ __forceinline__ int find_item_f4(const GemvGroup& g, int tile) {
-  int lo = 0, hi = g.count - 1;
-  while (lo < hi) {                       // last item with tile_start <= tile
-    const int mid = (lo + hi + 1) >> 1;
-    if (g.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 template <int TT, int NW, int BT, typename YT>
 __global__ __launch_bounds__(kWave * NW) void k_gemv_f4(const GemvGroup grp, int m, int B) {
-  const int item = find_item_f4(grp, blockIdx.x);
+  const int item = find_item(grp, blockIdx.x);
   const GemvItem it = grp.items[item];
   const int n = it.n;
   const uint8_t* __restrict__ packed = static_cast<const uint8_t*>(it.packed);

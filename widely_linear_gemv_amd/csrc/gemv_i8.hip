@@ -118,18 +118,9 @@ hipError_t launch_x_digits(const void* x, int x_bf16, int m, int B, void* blob, 
 
 // ------------------------------------------------------------------------- GEMV ----
 
-__device__ __forceinline__ int find_item_i8(const GemvGroup& g, int tile) {
-  int lo = 0, hi = g.count - 1;
-  while (lo < hi) {                       // last item with tile_start <= tile
-    const int mid = (lo + hi + 1) >> 1;
-    if (g.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 template <int TT, int NW, typename YT>
 __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int m, int B) {
-  const int item = find_item_i8(grp, blockIdx.x);
+  const int item = find_item(grp, blockIdx.x);
   const GemvItem it = grp.items[item];
   const int n = it.n;
   const uint8_t* __restrict__ packed = static_cast<const uint8_t*>(it.packed);

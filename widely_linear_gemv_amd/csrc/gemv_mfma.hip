@@ -68,26 +68,6 @@ __device__ __forceinline__ v4u permute_b(uint4 w) {
              __builtin_amdgcn_perm(w.w, w.z, 0x05040100u), __builtin_amdgcn_perm(w.w, w.z, 0x07060302u)};
 }
 
-// Raw buffer resource over [base, base + bytes): loads at offsets past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, int64_t bytes) {
-  const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFF00);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
-}
-constexpr uint32_t kNoLoad = 0x80000000u;   // buffer offset past every range: the load returns 0
-
-// Workgroup tile -> GEMV item: first tile of every item (tile_start[count] = total tiles).
-__device__ __forceinline__ int find_item(const GemvGroup& g, int tile) {
-  int lo = 0, hi = g.count - 1;
-  while (lo < hi) {                       // last item with tile_start <= tile
-    const int mid = (lo + hi + 1) >> 1;
-    if (g.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Widely-linear combination of one output row (lane element e) for column group cg: the Re y and
-// Im y contributions of this lane's column (component comp of one batch entry), before the a and b
-// columns of the entry are added across lanes.  Scales are halved (the planes carry +-2).
 template <int TT, int CG>
 __device__ __forceinline__ void combine_row(const v4f (&acc)[TT][2][2][CG], const float* sc, int e, int cg,
                                             int comp, float& vre, float& vim) {
@@ -127,8 +107,8 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
   const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
   // The tile's codes and x through buffer resources: batch entries past B read 0, and so does
   // every load of a lane group past column m (offset kNoLoad).
-  const __amdgpu_buffer_rsrc_t rsrc_a = gemv_rsrc(packed + (int64_t)tile * tile_bytes, tile_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc_x = gemv_rsrc(x, (int64_t)B * 2 * m * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_a = range_rsrc(packed + (int64_t)tile * tile_bytes, tile_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc_x = range_rsrc(x, (int64_t)B * 2 * m * 2);
 
   // B column of this lane: batch b = 8*cg + (r >> 1), component r & 1
   const int comp = r & 1;
@@ -283,8 +263,8 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
   const int i0 = tile * 16;
   const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
   const __amdgpu_buffer_rsrc_t rsrc_a =
-      gemv_rsrc(packed + (int64_t)min(tile, tiles - 1) * tile_bytes, tile < tiles ? tile_bytes : 0);
-  const __amdgpu_buffer_rsrc_t rsrc_x = gemv_rsrc(x, (int64_t)B * 2 * m * 2);
+      range_rsrc(packed + (int64_t)min(tile, tiles - 1) * tile_bytes, tile < tiles ? tile_bytes : 0);
+  const __amdgpu_buffer_rsrc_t rsrc_x = range_rsrc(x, (int64_t)B * 2 * m * 2);
 
   v4f acc[TT][2][2][CG];
 #pragma unroll

@@ -196,12 +196,6 @@ __device__ __forceinline__ void gemm_epilogue(const v4i (&acc)[TT * 4][NF], cons
   }
 }
 
-// Raw buffer resource over [base, base + bytes): loads at offsets past the end return 0.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFFF0);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
-}
-
 // Workgroup = 8 tiles of 16 complex rows (wave w takes tile 8 blockIdx.x + w) x 8*NF tokens.  Per
 // 256-column chunk (the chunk of the packed form) the workgroup stages the tokens' activations,
 // [token][component][256 columns] int8 with a padded row pitch, in one of two LDS buffers; every
@@ -225,7 +219,6 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
   constexpr int kRows = 8 * NF * 2;                // (token, component) activation rows
   constexpr int kSeg = kRows * 16 / (64 * kGemmWaves);   // 16-byte staging segments per thread
   static_assert(kSeg * 64 * kGemmWaves == kRows * 16, "whole segments per thread");
-  constexpr uint32_t kNoLoad = 0x80000000u;        // buffer offset past every range: reads 0
   __shared__ __align__(16) int8_t s_b[2][kRows * kActPitch];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -240,9 +233,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
   const int nchunk = (m + 255) / 256;
   const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
   const __amdgpu_buffer_rsrc_t rsrc_w =
-      make_rsrc(packed + (int64_t)min(tile, tiles - 1) * tile_bytes, tile < tiles ? tile_bytes : 0);
+      range_rsrc(packed + (int64_t)min(tile, tiles - 1) * tile_bytes, tile < tiles ? tile_bytes : 0);
   const __amdgpu_buffer_rsrc_t rsrc_q =
-      make_rsrc(q + (int64_t)min(tok0, N) * two_m, (int64_t)max(N - tok0, 0) * two_m);
+      range_rsrc(q + (int64_t)min(tok0, N) * two_m, (int64_t)max(N - tok0, 0) * two_m);
 
   v4i acc[kPlanes][NF];
 #pragma unroll
