@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
 #pragma unroll
       for (int M = 0; M < 2; ++M)
         ch.w[t][M] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, 0));
+            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, kStreamLoad));
     const int jg = c * kI8Chunk + 64 * g;            // first column of this lane group
 #pragma unroll
     for (int s = 0; s < 4; ++s)

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
 #pragma unroll
       for (int M = 0; M < 2; ++M)
         ch.w[t][M] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, 0));
+            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, kStreamLoad));
     const int jg = c * kChunk + 64 * g;            // first column of this lane group
 #pragma unroll
     for (int s = 0; s < 8; ++s)
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
 #pragma unroll
       for (int M = 0; M < 2; ++M)
         w[t][M] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, 0));
+            rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, kStreamLoad));
   };
   auto compute_chunk = [&](int buf, const uint4 (&wc)[TT][2]) {
 #pragma unroll
