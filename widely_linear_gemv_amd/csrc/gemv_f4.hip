@@ -262,21 +262,22 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_f4(const GemvGroup grp, int
   // Operand sets stream through registers: chunk c + (D - 1) NW is loaded before chunk c is
   // multiplied, with D = 3 sets for one batch entry and T <= 2 and D = 2 otherwise (where operands
   // and accumulators take more registers).  The scheduling barriers keep each prefetch ahead of
-  // the compute it overlaps (the scheduler would otherwise sink the loads to their use), and every
-  // prefetch is issued (clamped to the last chunk) so every path has the same loads in flight.
+  // the compute it overlaps (the scheduler would otherwise sink the loads to their use).  Every
+  // prefetch is issued, so every path has the same loads in flight; one past the last chunk has a
+  // negative group count and so loads at the out-of-range offset, which reads nothing.
   if constexpr (BT == 1 && TT <= 2) {
     Chunk c0, c1, c2;
     int c = wave;                                  // wave w takes chunks w, w + NW, ...
     load_chunk(c, c0);
-    load_chunk(min(c + NW, nchunk - 1), c1);
+    load_chunk(c + NW, c1);
     for (; c + 2 * NW < nchunk; c += 3 * NW) {
       load_chunk(c + 2 * NW, c2);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c0);
-      load_chunk(min(c + 3 * NW, nchunk - 1), c0);
+      load_chunk(c + 3 * NW, c0);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c1);
-      load_chunk(min(c + 4 * NW, nchunk - 1), c1);
+      load_chunk(c + 4 * NW, c1);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c2);
     }
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_f4(const GemvGroup grp, int
       load_chunk(c + NW, c1);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c0);
-      load_chunk(min(c + 2 * NW, nchunk - 1), c0);
+      load_chunk(c + 2 * NW, c0);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c1);
     }

@@ -183,8 +183,8 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
   };
   // The chunks stream through two operand sets; the scheduling barriers keep each prefetch
   // ahead of the compute it overlaps (the scheduler would otherwise sink the loads to their
-  // use), and the prefetch is unconditional (the last one reloads the last chunk) so every path
-  // has the same loads in flight.
+  // use).  The prefetch is unconditional, so every path has the same loads in flight; one past
+  // the last chunk has a negative group count and loads at the out-of-range offset (reads nothing).
   {
     Chunk c0, c1;
     int c = wave;                                  // wave w takes chunks w, w + NW, ...
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
       load_chunk(c + NW, c1);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c0);
-      load_chunk(min(c + 2 * NW, nchunk - 1), c0);
+      load_chunk(c + 2 * NW, c0);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c1);
     }

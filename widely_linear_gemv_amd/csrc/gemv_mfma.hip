@@ -175,9 +175,9 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
   };
   // The chunks stream through two operand sets: the next chunk's loads are issued before the
   // current one is decoded and multiplied.  The scheduling barriers keep each prefetch ahead of
-  // the compute it overlaps (the scheduler would otherwise sink the loads to their use), and
-  // the prefetch is unconditional (the last one reloads the last chunk) so every path has the
-  // same loads in flight.
+  // the compute it overlaps (the scheduler would otherwise sink the loads to their use).  The
+  // prefetch is unconditional, so every path has the same loads in flight; one past the last
+  // chunk has a negative group count and loads at the out-of-range offset (reads nothing).
   {
     Chunk c0, c1;
     int c = wave;                                  // wave w takes chunks w, w + NW, ...
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
       load_chunk(c + NW, c1);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c0);
-      load_chunk(min(c + 2 * NW, nchunk - 1), c0);
+      load_chunk(c + 2 * NW, c0);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c1);
     }
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
   store_x(0, st);
   __syncthreads();
   for (int c = 0; c < nchunk; ++c) {
-    const int cn = min(c + 1, nchunk - 1);   // the last chunk reloads itself: same loads on every path
+    const int cn = c + 1;   // past the last chunk every load takes the out-of-range offset
     load_w(cn, w1);
     load_x(cn, st);
     __builtin_amdgcn_sched_barrier(0);

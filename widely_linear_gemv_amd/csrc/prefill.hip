@@ -302,7 +302,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
   __syncthreads();
   for (int c = 0; c < nchunk; ++c) {
     const int buf = c & 1;
-    const int cn = min(c + 1, nchunk - 1);   // the last chunk reloads itself: same loads on every path
+    const int cn = c + 1;   // past the last chunk every load takes the out-of-range offset
     load_words(cn, w1);
     load_act(cn, st);
     __builtin_amdgcn_sched_barrier(0);
