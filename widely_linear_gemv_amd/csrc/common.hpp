@@ -81,6 +81,27 @@ constexpr uint32_t kNoLoad = 0x80000000u;   // buffer offset past every range: t
 // vector cache.  Measured +4-6 % on the fp4 GEMV; results are unaffected.
 constexpr int kStreamLoad = 18;
 
+// Scales of one 16-row tile, [row][t][M][axis] fp32 (16 x 4T floats; rows past n read as 0).
+// A GEMV issues the load ahead of its operand stream (lane l takes floats lT .. lT + T - 1) and
+// parks the values in LDS once they arrive, so its epilogue waits on no memory round trip.
+template <int TT>
+struct TileScales {
+  float v[TT];
+  __device__ __forceinline__ void load(const float* scales, int i0, int n, int lane) {
+    const __amdgpu_buffer_rsrc_t rs =
+        range_rsrc(scales + (int64_t)i0 * TT * 4, (int64_t)(min(n, i0 + 16) - i0) * TT * 16);
+#pragma unroll
+    for (int q = 0; q < TT; ++q)
+      v[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)((lane * TT + q) * 4), 0, 0));
+  }
+  // lds: this wave's 16 x 4T floats
+  __device__ __forceinline__ void park(float* lds, int lane) const {
+#pragma unroll
+    for (int q = 0; q < TT; ++q) lds[lane * TT + q] = v[q];
+    __builtin_amdgcn_wave_barrier();
+  }
+};
+
 // Workgroup -> item of a grouped launch: the last item whose first workgroup (tile_start, in the
 // launch's own unit of tiles or tile groups) is at or before `block`.
 __device__ __forceinline__ int find_item(const GemvGroup& g, int block) {

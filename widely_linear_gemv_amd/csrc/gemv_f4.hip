@@ -185,7 +185,7 @@ hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blo
 // ------------------------------------------------------------------------- GEMV ----
 
 template <int TT, int NW, int BT, typename YT>
-__global__ __launch_bounds__(kWave * NW) void k_gemv_f4(const GemvGroup grp, int m, int B) {
+__global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_gemv_f4(const GemvGroup grp, int m, int B) {
   const int item = find_item(grp, blockIdx.x);
   const GemvItem it = grp.items[item];
   const int n = it.n;
@@ -265,11 +265,15 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_f4(const GemvGroup grp, int
   // the compute it overlaps (the scheduler would otherwise sink the loads to their use).  Every
   // prefetch is issued, so every path has the same loads in flight; one past the last chunk has a
   // negative group count and so loads at the out-of-range offset, which reads nothing.
+  __shared__ float s_sc[NW][16 * TT * 4];
+  TileScales<TT> tsc;
+  tsc.load(scales, i0, n, lane);               // ahead of the first chunk's loads
   if constexpr (BT == 1 && TT <= 2) {
     Chunk c0, c1, c2;
     int c = wave;                                  // wave w takes chunks w, w + NW, ...
     load_chunk(c, c0);
     load_chunk(c + NW, c1);
+    tsc.park(s_sc[wave], lane);
     for (; c + 2 * NW < nchunk; c += 3 * NW) {
       load_chunk(c + 2 * NW, c2);
       __builtin_amdgcn_sched_barrier(0);
@@ -287,6 +291,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_f4(const GemvGroup grp, int
     Chunk c0, c1;
     int c = wave;
     load_chunk(c, c0);
+    tsc.park(s_sc[wave], lane);
     for (; c + NW < nchunk; c += 2 * NW) {
       load_chunk(c + NW, c1);
       __builtin_amdgcn_sched_barrier(0);
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_f4(const GemvGroup grp, int
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = i0 + 4 * g + e;
-      const float* sc = scales + (int64_t)min(i, n - 1) * TT * 4;
+      const float* sc = &s_sc[wave][(4 * g + e) * TT * 4];
       float vre = 0.f, vim = 0.f;
 #pragma unroll
       for (int t = 0; t < TT; ++t) {

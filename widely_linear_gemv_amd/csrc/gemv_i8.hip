@@ -185,10 +185,14 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
   // ahead of the compute it overlaps (the scheduler would otherwise sink the loads to their
   // use).  The prefetch is unconditional, so every path has the same loads in flight; one past
   // the last chunk has a negative group count and loads at the out-of-range offset (reads nothing).
+  __shared__ float s_sc[NW][16 * TT * 4];
+  TileScales<TT> tsc;
+  tsc.load(scales, i0, n, lane);               // ahead of the first chunk's loads
   {
     Chunk c0, c1;
     int c = wave;                                  // wave w takes chunks w, w + NW, ...
     load_chunk(c, c0);
+    tsc.park(s_sc[wave], lane);
     for (; c + NW < nchunk; c += 2 * NW) {
       load_chunk(c + NW, c1);
       __builtin_amdgcn_sched_barrier(0);
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = i0 + 4 * g + e;
-    const float* sc = scales + (int64_t)min(i, n - 1) * TT * 4;
+    const float* sc = &s_sc[wave][(4 * g + e) * TT * 4];
     float vre = 0.f, vim = 0.f;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {

@@ -178,10 +178,14 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
   // the compute it overlaps (the scheduler would otherwise sink the loads to their use).  The
   // prefetch is unconditional, so every path has the same loads in flight; one past the last
   // chunk has a negative group count and loads at the out-of-range offset (reads nothing).
+  __shared__ float s_sc[NW][16 * TT * 4];
+  TileScales<TT> tsc;
+  tsc.load(scales, i0, n, lane);               // ahead of the first chunk's loads
   {
     Chunk c0, c1;
     int c = wave;                                  // wave w takes chunks w, w + NW, ...
     load_chunk(c, c0);
+    tsc.park(s_sc[wave], lane);
     for (; c + NW < nchunk; c += 2 * NW) {
       load_chunk(c + NW, c1);
       __builtin_amdgcn_sched_barrier(0);
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = i0 + 4 * g + e;
-    const float* sc = scales + (int64_t)min(i, n - 1) * TT * 4;
+    const float* sc = &s_sc[wave][(4 * g + e) * TT * 4];
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
       float vre, vim;
@@ -331,11 +335,15 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
     }
   };
 
+  __shared__ float s_sc[kSxWaves][16 * TT * 4];
+  TileScales<TT> tsc;
+  tsc.load(scales, i0, n, lane);               // ahead of the first chunk's loads
   uint4 w0[TT][2], w1[TT][2];
   uint4 st[kSeg];
   load_w(0, w0);
   load_x(0, st);
   store_x(0, st);
+  tsc.park(s_sc[wave], lane);
   __syncthreads();
   for (int c = 0; c < nchunk; ++c) {
     const int cn = c + 1;   // past the last chunk every load takes the out-of-range offset
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = i0 + 4 * g + e;
-    const float* sc = scales + (int64_t)min(i, n - 1) * TT * 4;
+    const float* sc = &s_sc[wave][(4 * g + e) * TT * 4];
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
       float vre, vim;
