@@ -33,6 +33,33 @@ __device__ __forceinline__ int project4(double re, double im) {
   return k;
 }
 
+// One earlier stage's term off the residual: the signed scale on the code's axis.  The terms are
+// selected rather than branched on; re - 0.0 leaves re unchanged bit for bit and re - (-s) is
+// re + s, so this is exactly r minus the stage's dequantized codeword.
+__device__ __forceinline__ void residual_step(double& re, double& im, int kp, double sr, double si) {
+  re = re - (kp == 0 ? sr : kp == 2 ? -sr : 0.0);
+  im = im - (kp == 1 ? si : kp == 3 ? -si : 0.0);
+}
+
+// Code of one residual entry and its share of the stage's axis sums and real-axis count (adding
+// +0.0 to a non-negative partial sum changes nothing, so the unselected axis adds zero).
+__device__ __forceinline__ int project_accumulate(double re, double im, double& sre, double& sim, int& nre) {
+  const int k = project4(re, im);
+  const bool real_axis = (k & 1) == 0;
+  sre += real_axis ? fabs(re) : 0.0;
+  sim += real_axis ? 0.0 : fabs(im);
+  nre += real_axis ? 1 : 0;
+  return k;
+}
+
+// A workgroup-uniform fp64 value (an LDS broadcast) moved into scalar registers.
+__device__ __forceinline__ double uniform_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Theorem 1 closed form for one block entry (A, B, C, D) = (R11, R12, R21, R22)[i][j].
 __device__ __forceinline__ void split_entry(int M, float A, float B, float C, float D,
                                             double& re, double& im) {
@@ -101,24 +128,31 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
   }
 
   for (int t = 0; t < T; ++t) {
+    if constexpr (MAXC > 0) {
+      // Keep only the fp32 inputs live across stages: without this the fp64 split of every
+      // column is hoisted out of the stage loop (four times the registers, lower occupancy).
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) asm volatile("" : "+v"(qa[c]), "+v"(qb[c]), "+v"(qc[c]), "+v"(qd[c]));
+    }
     double sre[2] = {0.0, 0.0}, sim[2] = {0.0, 0.0};
     int nre[2] = {0, 0};
+    double ps[3][2][2];                                   // scales of the earlier stages
+#pragma unroll
+    for (int tp = 0; tp < 3; ++tp)
+#pragma unroll
+      for (int M = 0; M < 2; ++M) {
+        ps[tp][M][0] = tp < t ? uniform_f64(s_scale[tp][M][0]) : 0.0;
+        ps[tp][M][1] = tp < t ? uniform_f64(s_scale[tp][M][1]) : 0.0;
+      }
     auto body = [&](int j, float A, float B, float C, float D) {
 #pragma unroll
       for (int M = 0; M < 2; ++M) {
         double re, im;
         split_entry(M, A, B, C, D, re, im);
-        for (int tp = 0; tp < t; ++tp) {                  // earlier stages, in order
-          const int kp = s_codes[(tp * 2 + M) * m + j];
-          if (kp == 0) re = re - s_scale[tp][M][0];
-          else if (kp == 2) re = re + s_scale[tp][M][0];
-          else if (kp == 1) im = im - s_scale[tp][M][1];
-          else im = im + s_scale[tp][M][1];
-        }
-        const int k = project4(re, im);
-        s_codes[(t * 2 + M) * m + j] = (uint8_t)k;
-        if ((k & 1) == 0) { sre[M] += fabs(re); nre[M] += 1; }
-        else { sim[M] += fabs(im); }
+#pragma unroll
+        for (int tp = 0; tp < 3; ++tp)                    // earlier stages, in order
+          if (tp < t) residual_step(re, im, s_codes[(tp * 2 + M) * m + j], ps[tp][M][0], ps[tp][M][1]);
+        s_codes[(t * 2 + M) * m + j] = (uint8_t)project_accumulate(re, im, sre[M], sim[M], nre[M]);
       }
     };
     if constexpr (MAXC > 0) {
@@ -239,23 +273,26 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_tensor_stage(
 
   double sre[2] = {0.0, 0.0}, sim[2] = {0.0, 0.0};
   int nre[2] = {0, 0};
+  double ps[3][2][2];                                         // scales of the earlier stages
+#pragma unroll
+  for (int tp = 0; tp < 3; ++tp)
+#pragma unroll
+    for (int M = 0; M < 2; ++M) {
+      ps[tp][M][0] = tp < t ? uniform_f64(s_scale[(tp * 2 + M) * 2]) : 0.0;
+      ps[tp][M][1] = tp < t ? uniform_f64(s_scale[(tp * 2 + M) * 2 + 1]) : 0.0;
+    }
   auto body = [&](int j, float A, float B, float C, float D) {
     const int sh = 8 * (j & 3) + 2 * ((j >> 2) & 3);          // bit position of code j in its word
 #pragma unroll
     for (int M = 0; M < 2; ++M) {
       double re, im;
       split_entry(M, A, B, C, D, re, im);
-      for (int tp = 0; tp < t; ++tp) {                        // earlier stages, in order
-        const int kp = (pw[tiled_word(i, 2 * tp + M, j >> 4, m, T)] >> sh) & 3;
-        if (kp == 0) re = re - s_scale[(tp * 2 + M) * 2];
-        else if (kp == 2) re = re + s_scale[(tp * 2 + M) * 2];
-        else if (kp == 1) im = im - s_scale[(tp * 2 + M) * 2 + 1];
-        else im = im + s_scale[(tp * 2 + M) * 2 + 1];
-      }
-      const int k = project4(re, im);
-      s_codes[M * m + j] = (uint8_t)k;
-      if ((k & 1) == 0) { sre[M] += fabs(re); nre[M] += 1; }
-      else { sim[M] += fabs(im); }
+#pragma unroll
+      for (int tp = 0; tp < 3; ++tp)                          // earlier stages, in order
+        if (tp < t)
+          residual_step(re, im, (pw[tiled_word(i, 2 * tp + M, j >> 4, m, T)] >> sh) & 3,
+                        ps[tp][M][0], ps[tp][M][1]);
+      s_codes[M * m + j] = (uint8_t)project_accumulate(re, im, sre[M], sim[M], nre[M]);
     }
   };
   if constexpr (MAXC > 0) {
