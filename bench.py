@@ -9,11 +9,11 @@ One step is one pass of every stage of the path over one batch of inputs:
   1. quantize + pack the layer (split, projection, axis scales, residual stages, packing);
   2. decode GEMV at batch 1 over a pool of P = 256 distinct copies of the packed layer (1 GiB,
      four times the 256 MB Infinity Cache, so every pass streams from HBM and no segment gains
-     from the pool reads of the one before it, as a decode step over a 1.6 GB stack would not), as
-     grouped launches (fairy2i_gemv_grouped, up to 48 layers per launch): x is turned into its
-     exact fp6 digit form once (fairy2i_x_digits_f6; the pool's layers share x, as q, k and v
-     do), then the fp4-MFMA GEMV runs over the pool; the same with the int8 digit form and the
-     int8-MFMA GEMV;
+     from the pool reads of the one before it, as a decode step over a 1.6 GB stack would not),
+     stored back to back and run as one strided-batch launch (fairy2i_gemv_strided): x is turned
+     into its exact fp6 digit form once (fairy2i_x_digits_f6; the pool's layers share x, as q, k
+     and v do), then the fp4-MFMA GEMV runs over the pool; the same with the int8 digit form and
+     the int8-MFMA GEMV;
   3. the bf16-MFMA GEMV over the pool at batch 1, 4 and 16;
   4. prefill: per-token int8 activation quantization of 2048 tokens and the int8-MFMA GEMM;
   5. the real form of the quantized layer (dequantize, the fake-quant forward);
@@ -23,10 +23,11 @@ HIP events on that stream around every replay; inputs are resident in HBM before
 region starts.
 
 `value` is the headline metric: algorithmic HBM bytes of the batch-1 decode segment (fp6 digit
-form + fp4 GEMV launches) divided by its time (GB/s).  The JSON line also carries the roofline
+form + fp4 GEMV launch) divided by its time (GB/s).  The JSON line also carries the roofline
 of that GEMV kernel -- its launches timed, after the steps, in one graph of 8 back-to-back passes
 over the pool, so that graph-launch latency between segments does not count as kernel time --
-the other legs (GB/s, TOPS, params/s) and the CPU oracle timed on a bounded sample of the same
+the other legs (GB/s, TOPS, params/s; the same pool through the grouped call, 48 layers per
+launch; one launch per layer) and the CPU oracle timed on a bounded sample of the same
 workload.
 """
 from __future__ import annotations
@@ -63,11 +64,11 @@ def parse():
 ROOF_PASSES = 8           # passes over the pool per roofline graph
 ROOF_WARM = 10            # untimed replays first (~15 ms of the same launches)
 ROOF_REPLAYS = 3
-TRAFFIC_PROFILE = "profiles/gemv_f4_grouped_attention4096_T2_hbm_traffic.md"
+TRAFFIC_PROFILE = "profiles/gemv_f4_strided_attention4096_T2_hbm_traffic.md"
 
 
 def measured_traffic_per_layer():
-    """HBM bytes per layer of the grouped int8 GEMV, from the committed FETCH_SIZE / WRITE_SIZE
+    """HBM bytes per layer of the batch-1 fp4 GEMV launch, from the committed FETCH_SIZE / WRITE_SIZE
     summary (copy-calibrated), or None when the kernel source changed since it was taken."""
     import hashlib
     import re
@@ -178,7 +179,7 @@ def stack_legs(f2, torch, dev, T, reps):
         step = DecodeStep(layers, xs)
         t = timed(step.run)
         nbytes = sum(gemv_bytes(rows // 2, cols // 2, T, B) for L in range(32) for (_, rows, cols, _) in PROJECTIONS)
-        legs[f"stack_decode_b{B}"] = {"gemvs": 224, "launches": 256, "us": round(t * 1e3, 1),
+        legs[f"stack_decode_b{B}"] = {"gemvs": 224, "launches": 128, "us": round(t * 1e3, 1),
                                       "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes,
                                       "kernel": "bf16 matrix cores (default for these latency-bound launches)"}
     return legs
@@ -246,7 +247,7 @@ def main():
 
     def seg_gemv(B):
         def run():
-            f2.fairy2i_gemv_grouped(items[B], algo=f2.GEMV_MFMA)
+            f2.fairy2i_gemv_strided(pool, spool, xs[B], ypool[B], algo=f2.GEMV_MFMA)
         return run
 
     xd1 = f2.XDigits(torch.empty((f2.fairy2i_x_digits_bytes(m, 1),), dtype=torch.uint8, device=dev), 1, m)
@@ -254,10 +255,10 @@ def main():
 
     def seg_decode_i8():               # the batch-1 decode path: digit form, then the GEMV
         f2.fairy2i_x_digits(xs[1], out=xd1)
-        f2.fairy2i_gemv_grouped(items_i8, algo=f2.GEMV_MFMA_I8)
+        f2.fairy2i_gemv_strided(pool, spool, xd1, ypool[1], algo=f2.GEMV_MFMA_I8)
 
-    def seg_gemv_i8():                 # the GEMV launches alone (per-launch kernel time)
-        f2.fairy2i_gemv_grouped(items_i8, algo=f2.GEMV_MFMA_I8)
+    def seg_gemv_i8():                 # the GEMV launch alone (kernel time)
+        f2.fairy2i_gemv_strided(pool, spool, xd1, ypool[1], algo=f2.GEMV_MFMA_I8)
 
     xf1 = f2.XDigits(torch.empty((f2.fairy2i_x_digits_f6_bytes(m, 1),), dtype=torch.uint8, device=dev), 1, m,
                      f2.X_DIGITS_F6)
@@ -265,9 +266,12 @@ def main():
 
     def seg_decode_f4():               # the batch-1 decode path on the fp4 matrix cores
         f2.fairy2i_x_digits_f6(xs[1], out=xf1)
-        f2.fairy2i_gemv_grouped(items_f4, algo=f2.GEMV_MFMA_F4)
+        f2.fairy2i_gemv_strided(pool, spool, xf1, ypool[1], algo=f2.GEMV_MFMA_F4)
 
     def seg_gemv_f4():
+        f2.fairy2i_gemv_strided(pool, spool, xf1, ypool[1], algo=f2.GEMV_MFMA_F4)
+
+    def grouped_f4():                  # the same layers through the grouped call (<= 48 per launch)
         f2.fairy2i_gemv_grouped(items_f4, algo=f2.GEMV_MFMA_F4)
 
     def single_layers():               # one launch per layer (latency-bound small kernels)
@@ -292,8 +296,8 @@ def main():
 
     segments = [seg_quantize, seg_decode_f4, seg_gemv_f4, seg_decode_i8, seg_gemv_i8, seg_gemv(1),
                 seg_gemv(4), seg_gemv(16), seg_act_quant, seg_gemm, seg_dequant, seg_quantize_tensor,
-                single_layers]
-    NSEG = len(segments) - 1
+                grouped_f4, single_layers]
+    NSEG = len(segments) - 2
     for fn in segments:                     # eager warm-up (also loads every kernel)
         fn()
     torch.cuda.synchronize()
@@ -307,6 +311,7 @@ def main():
     torch.cuda.synchronize()
 
     single_graph = graphs.pop()
+    grouped_graph = graphs.pop()
 
     def step():
         e = [ev()]
@@ -333,7 +338,7 @@ def main():
         seg += np.array([e[k].elapsed_time(e[k + 1]) for k in range(NSEG)])   # ms
     seg /= args.steps
     ms_step = float(np.sum(seg))
-    # outside the timed step: the same pool as 128 separate single-layer launches
+    # outside the timed step: the same pool as separate single-layer launches (one per layer)
     single_graph.replay()
     torch.cuda.synchronize()
     e0 = ev()
@@ -342,9 +347,19 @@ def main():
     e1 = ev()
     torch.cuda.synchronize()
     single_us = e0.elapsed_time(e1) * 1e3 / (3 * P)
+    # outside the timed step: the pool through the grouped call (48 layers per launch)
+    for _ in range(5):
+        grouped_graph.replay()
+    torch.cuda.synchronize()
+    e0 = ev()
+    for _ in range(5):
+        grouped_graph.replay()
+    e1 = ev()
+    torch.cuda.synchronize()
+    grouped_us = e0.elapsed_time(e1) * 1e3 / 5
     # outside the timed step: the roofline's kernel time.  One graph holds ROOF_PASSES passes of
-    # the grouped fp4 launches over the pool back to back, so the per-launch time is the kernels'
-    # own (no graph-launch latency between segments).
+    # the strided fp4 launch over the pool back to back, so the launch time is the kernel's own
+    # (no graph-launch latency between segments).
     roof_graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(roof_graph, stream=cap):
         for _ in range(ROOF_PASSES):
@@ -362,10 +377,10 @@ def main():
     bytes_b = {B: gemv_bytes(n, m, T, B) for B in (1, 4, 16)}
     gemv_ms = {1: t_b1, 4: t_b4, 16: t_b16}
     gbs = {B: P * bytes_b[B] / (gemv_ms[B] * 1e-3) / 1e9 for B in (1, 4, 16)}
-    launches = -(-P // 48)                     # grouped launches per segment
+    launches = 1                               # one strided-batch launch per pool pass
     per_launch_us = {B: gemv_ms[B] * 1e3 / launches for B in (1, 4, 16)}
     # batch-1 decode through a digit form of x (made once per x, shared by the pool's layers as
-    # q, k and v share theirs), then the grouped GEMV launches
+    # q, k and v share theirs), then the strided-batch GEMV launch
     bytes_pool = P * bytes_b[1]
     f4_gbs = bytes_pool / (t_decf4 * 1e-3) / 1e9
     f4_launch_us = t_f4 * 1e3 / launches
@@ -396,16 +411,17 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "LLaMA-2 7B attention projection R 4096x4096 -> U,W 2048x2048, T=2; "
-                        "decode GEMV batch 1 (value), 4, 16 over a pool of distinct layer copies; "
+                        "decode GEMV batch 1 (value), 4, 16 over a pool of distinct layer copies "
+                        "stored back to back (one strided-batch launch per pass); "
                         "quantize+pack; prefill act-quant + int8 GEMM over 2048 tokens",
             "rows": 2 * n, "cols": 2 * m, "T": T, "batch": 1, "pool_layers": P,
             "x_dtype": "bf16", "y_dtype": "f32",
             "gemv_kernel": "fp4 x fp6 MFMA (sum/difference sign planes) on the exact fp6 digit form "
-                           "of x, grouped launches",
+                           "of x, one strided-batch launch over the pool",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gemv_f4 (grouped, batch 1)",
+            "kernel": "k_gemv_f4 (strided batch over the pool, batch 1)",
             "achieved": round(roof_gbs, 2),
             "us_per_launch": round(roof_launch_us, 3),
             "peak": HBM_PEAK_GBS,
@@ -427,6 +443,8 @@ def main():
                         "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[4]},
             "gemv_b16": {"GB/s": round(gbs[16], 2), "us_per_launch": round(per_launch_us[16], 3),
                          "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[16]},
+            "gemv_b1_f4_grouped": {"us_per_pass": round(grouped_us, 3), "launches_per_pass": -(-P // 48),
+                                   "GB/s": round(bytes_pool / (grouped_us * 1e-6) / 1e9, 2)},
             "gemv_b1_single_layer_launch": {"us_per_launch": round(single_us, 3),
                                             "GB/s": round(bytes_b[1] / (single_us * 1e-6) / 1e9, 2)},
             "quantize": {"us": round(t_quant * 1e3, 2),

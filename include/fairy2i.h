@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FAIRY2I_ABI_VERSION 4
+#define FAIRY2I_ABI_VERSION 5
 
 typedef enum {
   FAIRY2I_OK = 0,
@@ -234,6 +234,24 @@ typedef struct {
  *           device pointers).  Each item is checked like a fairy2i_gemv call. */
 int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, int T, int x_dtype,
                          int64_t B, int y_dtype, int algo, hipStream_t stream);
+
+/* Strided-batch decode GEMV: `batch` GEMVs of one shape (n, m, T) that share x, with matrix k's
+ * operands at constant strides from matrix 0's (for example q, k and v kept in one buffer, or
+ * the layers of a stack stored back to back).  Same rows as fairy2i_gemv_grouped (ModelScope
+ * card "Method"), but with no limit on the number of matrices per launch: the MFMA kernels run
+ * the whole batch as one grid; VALU runs the matrices one after another.
+ *   packed + k * packed_stride   matrix k's packed form; packed_stride in bytes, >= 0, a
+ *                                multiple of 16.
+ *   scales + k * scales_stride   its scales; scales_stride in floats, >= 0 (0: shared scales).
+ *   y + k * y_stride             its output [B][2n]; y_stride in elements of y_dtype, at least
+ *                                2nB when batch > 1 (outputs must not overlap), and a multiple
+ *                                of 16 bytes.
+ *   x, x_dtype, B, y_dtype, algo as for fairy2i_gemv; 1 <= batch and batch * ceil(n / 16)
+ *   <= 2^30.  Uses no workspace. */
+int fairy2i_gemv_strided(const uint8_t* packed, int64_t packed_stride, const float* scales,
+                         int64_t scales_stride, int64_t n, int64_t m, int T, const void* x,
+                         int x_dtype, int64_t B, void* y, int64_t y_stride, int y_dtype,
+                         int64_t batch, int algo, hipStream_t stream);
 
 /* Per-token int8 activations: delta[tok] = fl32(max_j |x~_j| / 127),
  * q = clamp(round_half_even(fl32(x~ / delta)), -127, 127); delta == 0 gives q = 0.

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert f2.fairy2i_abi_version() == 4
+    assert f2.fairy2i_abi_version() == 5
     for s in range(8):
         assert f2.fairy2i_status_string(s) not in ("", "unknown status")
     assert f2.fairy2i_status_string(99) == "unknown status"
@@ -204,6 +204,33 @@ def test_gemv_grouped_errors(L):
     assert g(badn, 1, 64, 2, f2.BF16, 1, f2.F32, f2.GEMV_MFMA, S) == 2
     odd = (It * 1)(It(FAKE, FAKE, FAKE_ODD, FAKE, 8))
     assert g(odd, 1, 64, 2, f2.BF16, 1, f2.F32, f2.GEMV_MFMA, S) == 5
+
+
+def test_gemv_strided_errors(L):
+    """Every call here fails its argument checks (no kernel is launched on these fake pointers)."""
+    g = L.fairy2i_gemv_strided
+    # (packed, pstride, scales, sstride, n, m, T, x, x_dtype, B, y, ystride, y_dtype, batch, algo, stream)
+    args = [FAKE, 4096, FAKE, 64, 16, 64, 2, FAKE, f2.BF16, 1, FAKE, 64, f2.F32, 3, f2.GEMV_MFMA, S]
+
+    def call(**kw):
+        a = list(args)
+        names = ["packed", "pstride", "scales", "sstride", "n", "m", "T", "x", "x_dtype", "B", "y",
+                 "ystride", "y_dtype", "batch", "algo", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return g(*a)
+
+    assert call(scales=None) == 1
+    assert call(x_dtype=f2.F32) == 4                       # bf16 MFMA kernel takes bf16 x only
+    assert call(T=5) == 3
+    assert call(m=96) == 2
+    assert call(batch=0) == 2 and "batch" in last()
+    assert call(batch=(1 << 29) + 1, n=32) == 2            # batch * ceil(n/16) > 2^30
+    assert call(pstride=-16) == 2
+    assert call(ystride=16) == 2 and "overlap" in last()   # y rows of matrices overlap
+    assert call(pstride=4104) == 5                         # not a multiple of 16
+    assert call(ystride=66) == 5                           # 66 floats = 264 bytes
+    assert call(packed=FAKE_ODD) == 5
 
 
 def test_act_quant_errors(L):

@@ -353,3 +353,60 @@ def test_grouped_large_batch_shared_x(B, m, T):
         codes, scales = host[k]
         want = oracle.gemv_ref(codes, scales, act.values)
         assert rel_l2(down(items[k][3]), want) <= TOL_F32, (k, ns[k])
+
+
+@pytest.mark.parametrize("algo,B,n,m,T,batch,ydt", [
+    ("f4", 1, 2048, 2048, 2, 13, "f32"),     # 1664 tiles: one wave per tile
+    ("f4", 2, 37, 320, 3, 5, "bf16"),        # ragged n and m; a small launch (several waves per tile)
+    ("i8", 1, 200, 512, 2, 9, "f32"),
+    ("i8", 2, 2048, 2048, 1, 13, "f32"),
+    ("bf16", 1, 2048, 2048, 2, 13, "f32"),
+    ("bf16", 4, 2048, 320, 2, 13, "f32"),    # >= 1536 tiles at B >= 3: the shared-x kernel
+    ("bf16", 9, 37, 320, 2, 7, "bf16"),
+    ("valu", 2, 33, 128, 2, 3, "f32"),
+])
+def test_strided_batch_matches_grouped_and_oracle(algo, B, n, m, T, batch, ydt):
+    """A strided batch (matrices back to back in one buffer; scales and outputs at strides, the
+    output rows padded to 16 bytes) gives the grouped call's result on the same matrices bit for
+    bit (same launch shape and order), and the first and last matrix are within tolerance of the
+    oracle.  The first case also checks shared scales (stride 0)."""
+    dev = device()
+    act = workloads.activations(B, 2 * m, seed=90 + B + n)
+    x = x_to_dev(act, dev)
+    if algo in DIGITS:
+        x = DIGITS[algo](x)
+    pb = f2.fairy2i_packed_bytes(n, m, T)
+    packed = torch.empty((batch, pb), dtype=torch.uint8, device=dev)
+    scales = torch.empty((batch, n, T, 2, 2), dtype=torch.float32, device=dev)
+    host = []
+    for k in range(batch):
+        codes = workloads.random_codes(T, n, m, seed=5000 + 31 * k + n)
+        sc = workloads.random_scales(n, T, seed=6000 + k)
+        packed[k] = up(oracle.pack(codes), dev)
+        scales[k] = up(sc, dev)
+        host.append((codes, sc))
+    ydtype = torch.float32 if ydt == "f32" else torch.bfloat16
+    elem = 4 if ydt == "f32" else 2
+    ystride = -(-(B * 2 * n * elem) // 16) * 16 // elem
+    ybuf = torch.full((batch, ystride), float("nan"), dtype=ydtype, device=dev)
+    y = ybuf[:, :B * 2 * n].unflatten(1, (B, 2 * n))
+    announce("strided gemv", algo, B, n, m, T, batch, ydt)
+    f2.fairy2i_gemv_strided(packed, scales, x, y, algo=ALGOS[algo])
+    ygbuf = torch.full_like(ybuf, float("nan"))
+    yg = ygbuf[:, :B * 2 * n].unflatten(1, (B, 2 * n))
+    f2.fairy2i_gemv_grouped([(packed[k], scales[k], x, yg[k]) for k in range(batch)], algo=ALGOS[algo])
+    torch.cuda.synchronize()
+    assert torch.equal(y, yg)
+    for k in (0, batch - 1):
+        codes, sc = host[k]
+        want = oracle.gemv_ref(codes, sc, act.values)
+        if ydt == "f32":
+            assert rel_l2(down(y[k]), want) <= TOL_F32, k
+        else:
+            check_bf16(down(y[k]), want, (algo, k))
+    if algo == "f4" and n == 2048:                      # scales shared by every matrix
+        ys = torch.full_like(y, float("nan"))
+        f2.fairy2i_gemv_strided(packed, scales[0], x, ys, algo=ALGOS[algo])
+        torch.cuda.synchronize()
+        want = oracle.gemv_ref(host[batch - 1][0], host[0][1], act.values)
+        assert rel_l2(down(ys[batch - 1]), want) <= TOL_F32

@@ -60,6 +60,8 @@ class GemvItem(ctypes.Structure):
 
 SIGNATURES["fairy2i_gemv_grouped"] = (_INT, [ctypes.POINTER(GemvItem), _INT, _I64, _INT, _INT, _I64,
                                               _INT, _INT, _P])
+SIGNATURES["fairy2i_gemv_strided"] = (_INT, [_P, _I64, _P, _I64, _I64, _I64, _INT, _P, _INT, _I64, _P, _I64,
+                                              _INT, _I64, _INT, _P])
 
 _lib = None
 
@@ -264,6 +266,21 @@ def fairy2i_gemv_grouped(items, *, algo: int = GEMV_AUTO, stream=None):
     _check(lib().fairy2i_gemv_grouped(arr, len(items), _x_cols(x0), T, xdt, B,
                                       _DTYPE[y0.dtype], algo, _stream(stream)))
     return [it[3] for it in items]
+
+
+def fairy2i_gemv_strided(packed: torch.Tensor, scales: torch.Tensor, x, y: torch.Tensor, *,
+                         algo: int = GEMV_AUTO, stream=None):
+    """A strided batch of GEMVs sharing x: packed [batch][bytes] uint8, scales [batch][n][T][2][2]
+    (or [n][T][2][2], shared by all), y [batch][B][2n] preallocated; the strides are those of the
+    tensors' first dimension (each matrix's slice contiguous).  Returns y."""
+    batch = packed.shape[0]
+    n, T = scales.shape[-4], scales.shape[-3]
+    s_stride = scales.stride(0) if scales.dim() == 5 else 0
+    xp, xdt, B = _x_args(x)
+    _check(lib().fairy2i_gemv_strided(_ptr(packed), packed.stride(0), _ptr(scales), s_stride, n,
+                                      _x_cols(x), T, xp, xdt, B, _ptr(y), y.stride(0), _DTYPE[y.dtype],
+                                      batch, algo, _stream(stream)))
+    return y
 
 
 def fairy2i_act_quant(x: torch.Tensor, q=None, delta=None, stream=None):

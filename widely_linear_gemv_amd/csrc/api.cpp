@@ -302,6 +302,53 @@ int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, i
   return ok();
 }
 
+int fairy2i_gemv_strided(const uint8_t* packed, int64_t packed_stride, const float* scales,
+                         int64_t scales_stride, int64_t n, int64_t m, int T, const void* x,
+                         int x_dtype, int64_t B, void* y, int64_t y_stride, int y_dtype,
+                         int64_t batch, int algo, hipStream_t stream) {
+  if (!packed || !scales || !x || !y) return fail(FAIRY2I_ERR_NULL, "packed, scales, x and y are required");
+  const int kernel = gemv_kernel(x_dtype, y_dtype, algo, B);
+  if (kernel < 0) return -kernel;
+  if (int s = check_stages(T)) return s;
+  if (int s = check_nm(n, m)) return s;
+  if (int s = check_f4_cols(kernel, m)) return s;
+  const int64_t tiles = (n + 15) / 16;
+  if (batch < 1 || batch > (int64_t(1) << 30) / tiles)
+    return fail(FAIRY2I_ERR_SHAPE, "batch = %lld: need 1 <= batch and batch * ceil(n/16) <= 2^30", (long long)batch);
+  const int64_t y_elem = y_dtype == FAIRY2I_BF16 ? 2 : 4;
+  if (packed_stride < 0 || scales_stride < 0 || y_stride < 0)
+    return fail(FAIRY2I_ERR_SHAPE, "strides must be >= 0");
+  if (batch > 1 && y_stride < 2 * n * B)
+    return fail(FAIRY2I_ERR_SHAPE, "y_stride = %lld: outputs of different matrices overlap (need >= 2nB = %lld)",
+                (long long)y_stride, (long long)(2 * n * B));
+  if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(scales, 4) ||
+      packed_stride % 16 != 0 || (y_stride * y_elem) % 16 != 0)
+    return fail(FAIRY2I_ERR_ALIGN, "packed, x and y (and their strides) need 16-byte alignment, scales 4");
+  if (kernel == FAIRY2I_GEMV_VALU) {
+    for (int64_t k = 0; k < batch; ++k) {
+      int s = fairy2i_gemv(packed + k * packed_stride, scales + k * scales_stride, n, m, T, x, x_dtype, B,
+                           static_cast<uint8_t*>(y) + k * y_stride * y_elem, y_dtype, algo, stream);
+      if (s != FAIRY2I_OK) return s;
+    }
+    return ok();
+  }
+  f2i::GemvGroup grp;
+  grp.count = 1;
+  grp.tile_start[0] = 0;
+  grp.tile_start[1] = (int)tiles;
+  grp.items[0] = f2i::GemvItem{packed, scales, x, y, (int)n};
+  grp.batch = (int)batch;
+  grp.tiles_per_item = (int)tiles;
+  grp.packed_stride = packed_stride;
+  grp.scales_stride = scales_stride;
+  grp.y_stride = y_stride;
+  const int ybf = y_dtype == FAIRY2I_BF16;
+  hipError_t e = kernel == FAIRY2I_GEMV_MFMA_F4 ? f2i::launch_gemv_f4_group(grp, (int)m, T, (int)B, ybf, stream)
+               : kernel == FAIRY2I_GEMV_MFMA_I8 ? f2i::launch_gemv_i8_group(grp, (int)m, T, (int)B, ybf, stream)
+               : f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, ybf, stream);
+  return hip_status(e, "gemv (strided batch) launch");
+}
+
 int fairy2i_dequantize(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                        void* R, int R_dtype, hipStream_t stream) {
   if (!packed || !scales || !R) return fail(FAIRY2I_ERR_NULL, "packed, scales and R are required");

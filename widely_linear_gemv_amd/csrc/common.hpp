@@ -69,7 +69,19 @@ struct GemvGroup {
   int count;
   int tile_start[kMaxGroup + 1];   // first 16-row tile of each item; [count] = total tiles
   GemvItem items[kMaxGroup];
+  // Strided batch (batch > 0) instead of the table: items[0] is matrix 0, and matrix k's packed
+  // form, scales and output lie k * packed_stride bytes, k * scales_stride floats and k * y_stride
+  // output elements further on.  Every matrix has tiles_per_item tiles; a launcher sets
+  // units_per_item to its workgroups per matrix.
+  int batch = 0;
+  int tiles_per_item = 0;
+  int units_per_item = 0;
+  int64_t packed_stride = 0, scales_stride = 0, y_stride = 0;
 };
+// 16-row tiles of a launch.
+inline int group_tiles(const GemvGroup& g) {
+  return g.batch > 0 ? g.batch * g.tiles_per_item : g.tile_start[g.count];
+}
 // Buffer resource over [base, base + bytes): loads at offsets past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
   const int nrec = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFF00);
@@ -111,6 +123,24 @@ __device__ __forceinline__ int find_item(const GemvGroup& g, int block) {
     if (g.tile_start[mid] <= block) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Item of workgroup `block` of a grouped or strided-batch launch, and the workgroup's index within
+// that item (`unit`, in the launch's own unit: tiles, or groups of tiles).
+template <typename YT>
+__device__ __forceinline__ GemvItem locate_item(const GemvGroup& g, int block, int& unit) {
+  if (g.batch > 0) {
+    const int k = block / g.units_per_item;
+    unit = block - k * g.units_per_item;
+    GemvItem it = g.items[0];
+    it.packed = static_cast<const uint8_t*>(it.packed) + (int64_t)k * g.packed_stride;
+    it.scales += (int64_t)k * g.scales_stride;
+    it.y = static_cast<YT*>(it.y) + (int64_t)k * g.y_stride;
+    return it;
+  }
+  const int k = find_item(g, block);
+  unit = block - g.tile_start[k];
+  return g.items[k];
 }
 
 hipError_t launch_gemv_mfma_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);

@@ -186,8 +186,8 @@ hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blo
 
 template <int TT, int NW, int BT, typename YT>
 __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_gemv_f4(const GemvGroup grp, int m, int B) {
-  const int item = find_item(grp, blockIdx.x);
-  const GemvItem it = grp.items[item];
+  int tile;
+  const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
   const int n = it.n;
   const uint8_t* __restrict__ packed = static_cast<const uint8_t*>(it.packed);
   const float* __restrict__ scales = it.scales;
@@ -197,7 +197,6 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int r = lane & 15, g = lane >> 4;
-  const int tile = blockIdx.x - grp.tile_start[item];
   const int i0 = tile * 16;
   const int nchunk = (m + kF4Chunk - 1) / kF4Chunk;
   const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
@@ -365,8 +364,10 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
 }
 
 template <int TT, int BT, typename YT>
-static void launch_f4_t(const GemvGroup& grp, int m, int B, hipStream_t s) {
-  const int tiles = grp.tile_start[grp.count];
+static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
+  GemvGroup grp = group;
+  grp.units_per_item = grp.tiles_per_item;        // one workgroup per tile
+  const int tiles = group_tiles(grp);
   const dim3 grid(tiles);
   switch (gemv_waves_per_tile(tiles, m)) {
     case 8: hipLaunchKernelGGL((k_gemv_f4<TT, 8, BT, YT>), grid, dim3(8 * kWave), 0, s, grp, m, B); break;

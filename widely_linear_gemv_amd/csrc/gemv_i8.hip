@@ -120,8 +120,8 @@ hipError_t launch_x_digits(const void* x, int x_bf16, int m, int B, void* blob, 
 
 template <int TT, int NW, typename YT>
 __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int m, int B) {
-  const int item = find_item(grp, blockIdx.x);
-  const GemvItem it = grp.items[item];
+  int tile;
+  const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
   const int n = it.n;
   const uint8_t* __restrict__ packed = static_cast<const uint8_t*>(it.packed);
   const float* __restrict__ scales = it.scales;
@@ -131,7 +131,6 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int r = lane & 15, g = lane >> 4;
-  const int tile = blockIdx.x - grp.tile_start[item];
   const int i0 = tile * 16;
   const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
   // The tile's codes and the digit form through buffer resources: batch entries past B read 0,
@@ -259,8 +258,10 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
 }
 
 template <int TT, typename YT>
-static void launch_i8_t(const GemvGroup& grp, int m, int B, hipStream_t s) {
-  const int tiles = grp.tile_start[grp.count];
+static void launch_i8_t(const GemvGroup& group, int m, int B, hipStream_t s) {
+  GemvGroup grp = group;
+  grp.units_per_item = grp.tiles_per_item;        // one workgroup per tile
+  const int tiles = group_tiles(grp);
   const dim3 grid(tiles);
   switch (gemv_waves_per_tile(tiles, m)) {
     case 8: hipLaunchKernelGGL((k_gemv_i8<TT, 8, YT>), grid, dim3(8 * kWave), 0, s, grp, m, B); break;

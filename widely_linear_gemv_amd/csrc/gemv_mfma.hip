@@ -91,8 +91,8 @@ __device__ __forceinline__ void combine_row(const v4f (&acc)[TT][2][2][CG], cons
 
 template <int TT, int CG, int NW, typename YT>
 __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, int m, int B) {
-  const int item = find_item(grp, blockIdx.x);
-  const GemvItem it = grp.items[item];
+  int tile;
+  const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
   const int n = it.n;
   const uint8_t* __restrict__ packed = static_cast<const uint8_t*>(it.packed);
   const float* __restrict__ scales = it.scales;
@@ -102,7 +102,6 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int r = lane & 15, g = lane >> 4;
-  const int tile = blockIdx.x - grp.tile_start[item];
   const int i0 = tile * 16;
   const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
   // The tile's codes and x through buffer resources: batch entries past B read 0, and so does
@@ -238,9 +237,9 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
 constexpr int kSxWaves = 8;             // tiles (waves) per workgroup of the shared-x kernel
 constexpr int kSxPitch = 2 * kChunk + 16;  // LDS bytes per (batch, component) row of a chunk's x
 
-// Shared-x form for large launches.  grp.tile_start counts workgroups of kSxWaves tiles here, so
-// a workgroup never spans two items (their x differ); tiles past an item's last read no codes and
-// store nothing.  Per chunk the workgroup stages x[b][comp][256 columns] (bf16, permuted per 8
+// Shared-x form for large launches.  grp.tile_start (units_per_item in a strided batch) counts
+// workgroups of kSxWaves tiles here, so a workgroup never spans two items (their x differ); tiles
+// past an item's last read no codes and store nothing.  Per chunk the workgroup stages x[b][comp][256 columns] (bf16, permuted per 8
 // columns) in one of two LDS buffers, one 16-byte unit per thread and column group, and waits
 // once; codes are loaded one chunk ahead as in k_gemv_mfma.
 template <int TT, int CG, typename YT>
@@ -249,8 +248,8 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
   constexpr int kSeg = kXRows * (2 * kChunk / 16) / (kWave * kSxWaves);   // 16-byte units per thread
   static_assert(kSeg * kWave * kSxWaves == kXRows * (2 * kChunk / 16), "whole units per thread");
   __shared__ __align__(16) uint8_t s_x[2][kXRows * kSxPitch];
-  const int item = find_item(grp, blockIdx.x);
-  const GemvItem it = grp.items[item];
+  int unit;
+  const GemvItem it = locate_item<YT>(grp, blockIdx.x, unit);
   const int n = it.n;
   const uint8_t* __restrict__ packed = static_cast<const uint8_t*>(it.packed);
   const float* __restrict__ scales = it.scales;
@@ -263,7 +262,7 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
   const int r = lane & 15, g = lane >> 4;
   const int comp = r & 1;
   const int tiles = (n + 15) / 16;
-  const int tile = kSxWaves * (blockIdx.x - grp.tile_start[item]) + wave;
+  const int tile = kSxWaves * unit + wave;
   const int i0 = tile * 16;
   const int64_t tile_bytes = (int64_t)16 * TT * 2 * (m / 4);
   const __amdgpu_buffer_rsrc_t rsrc_a =
@@ -379,20 +378,26 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
 }
 
 template <int TT, int CG, typename YT>
-static void launch_cg(const GemvGroup& grp, int m, int B, hipStream_t s) {
-  const int tiles = grp.tile_start[grp.count];
+static void launch_cg(const GemvGroup& group, int m, int B, hipStream_t s) {
+  GemvGroup grp = group;
+  const int tiles = group_tiles(grp);
   const int nw = gemv_waves_per_tile(tiles, m);
   if (nw == 1 && B >= 3) {                 // large launch, batch 3-16: shared x
-    GemvGroup sx = grp;
     int blocks = 0;
-    for (int k = 0; k < sx.count; ++k) {
-      sx.tile_start[k] = blocks;
-      blocks += ((sx.items[k].n + 15) / 16 + kSxWaves - 1) / kSxWaves;
+    if (grp.batch > 0) {
+      grp.units_per_item = (grp.tiles_per_item + kSxWaves - 1) / kSxWaves;
+      blocks = grp.batch * grp.units_per_item;
+    } else {
+      for (int k = 0; k < grp.count; ++k) {
+        grp.tile_start[k] = blocks;
+        blocks += ((grp.items[k].n + 15) / 16 + kSxWaves - 1) / kSxWaves;
+      }
+      grp.tile_start[grp.count] = blocks;
     }
-    sx.tile_start[sx.count] = blocks;
-    hipLaunchKernelGGL((k_gemv_mfma_sx<TT, CG, YT>), dim3(blocks), dim3(kSxWaves * kWave), 0, s, sx, m, B);
+    hipLaunchKernelGGL((k_gemv_mfma_sx<TT, CG, YT>), dim3(blocks), dim3(kSxWaves * kWave), 0, s, grp, m, B);
     return;
   }
+  grp.units_per_item = grp.tiles_per_item;        // one workgroup per tile
   const dim3 grid(tiles);
   switch (nw) {
     case 8: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 8, YT>), grid, dim3(8 * kWave), 0, s, grp, m, B); break;
