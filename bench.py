@@ -62,7 +62,7 @@ def parse():
 
 
 ROOF_PASSES = 8           # passes over the pool per roofline graph
-ROOF_WARM = 10            # untimed replays first (~15 ms of the same launches)
+ROOF_WARM = 40            # untimed replays first (~60 ms of the same launches)
 ROOF_REPLAYS = 3
 TRAFFIC_PROFILE = "profiles/gemv_f4_strided_attention4096_T2_hbm_traffic.md"
 
