@@ -90,7 +90,7 @@ def gemv_bytes(n, m, T, B, x_bytes=2, y_bytes=4):
 
 
 def cpu_baseline(R, T, x1, budget_s):
-    """The oracle (float64 NumPy) on the GPU machine's host: the batch-1 GEMV of the same layer,
+    """The oracle (float64 NumPy) on the measuring machine's host cores: the batch-1 GEMV of the same layer,
     repeated until the time budget is spent; plus the quantizer on a row sample."""
     import oracle
     try:

@@ -29,10 +29,12 @@ def bf16_act(values):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_act_quant_bit_exact(dtype):
+@pytest.mark.parametrize("two_m,N", [(4096, 2048), (128, 33), (2112, 17), (11008, 40), (20480, 9)])
+def test_act_quant_bit_exact(dtype, two_m, N):
+    """Token rows held in registers between the two passes (one to eight groups of 2048 values,
+    partial last groups) and the re-reading form (rows longer than 16384)."""
     dev = device()
-    two_m = 4096
-    base = workloads.activations(2048, two_m, workloads.PREFILL_X_SEED, dtype).values
+    base = workloads.activations(N, two_m, workloads.PREFILL_X_SEED + two_m, dtype).values
     vals = np.concatenate([base, edge_tokens(two_m)])
     act = bf16_act(vals) if dtype == "bf16" else workloads.Activations(values=vals, dtype="f32")
     announce("act_quant", dtype, vals.shape)

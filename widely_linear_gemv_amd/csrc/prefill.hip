@@ -41,8 +41,10 @@ template <> struct Load8<uint16_t> {
 };
 
 // One workgroup per token: amax (order-free, exact), delta = amax / 127 (IEEE fp32 divide),
-// q = clamp(rint(x / delta)) with rint rounding half to even.
-template <typename XT>
+// q = clamp(rint(x / delta)) with rint rounding half to even.  KEEP > 0: the token's values stay
+// in registers between the two passes (two_m <= 2048 KEEP, eight per thread and group), so x is
+// read once; KEEP == 0 reads them again in the second pass (from cache).
+template <typename XT, int KEEP>
 __global__ __launch_bounds__(256) void k_act_quant(const XT* __restrict__ x, int two_m,
                                                    int8_t* __restrict__ q,
                                                    float* __restrict__ delta) {
@@ -50,12 +52,29 @@ __global__ __launch_bounds__(256) void k_act_quant(const XT* __restrict__ x, int
   const int tok = blockIdx.x;
   const XT* __restrict__ xr = x + (int64_t)tok * two_m;
   int8_t* __restrict__ qr = q + (int64_t)tok * two_m;
+  constexpr int NK = KEEP > 0 ? KEEP : 1;
+  float keep[NK][8];
   float amax = 0.f;
-  for (int j = threadIdx.x * 8; j < two_m; j += 256 * 8) {
-    float v[8];
-    Load8<XT>::run(xr + j, v);
+  if constexpr (KEEP > 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    for (int c = 0; c < KEEP; ++c) {
+      const int j = (threadIdx.x + 256 * c) * 8;
+      if (j < two_m) {
+        Load8<XT>::run(xr + j, keep[c]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) keep[c][e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(keep[c][e]));
+    }
+  } else {
+    for (int j = threadIdx.x * 8; j < two_m; j += 256 * 8) {
+      float v[8];
+      Load8<XT>::run(xr + j, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
   }
 #pragma unroll
   for (int off = kWave / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
@@ -63,9 +82,7 @@ __global__ __launch_bounds__(256) void k_act_quant(const XT* __restrict__ x, int
   __syncthreads();
   amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
   const float d = amax / 127.0f;
-  for (int j = threadIdx.x * 8; j < two_m; j += 256 * 8) {
-    float v[8];
-    Load8<XT>::run(xr + j, v);
+  auto quantize8 = [&](const float (&v)[8], int j) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -75,18 +92,37 @@ __global__ __launch_bounds__(256) void k_act_quant(const XT* __restrict__ x, int
       if (e < 4) lo |= byte << (8 * e); else hi |= byte << (8 * (e - 4));
     }
     *reinterpret_cast<uint2*>(qr + j) = make_uint2(lo, hi);
+  };
+  if constexpr (KEEP > 0) {
+#pragma unroll
+    for (int c = 0; c < KEEP; ++c) {
+      const int j = (threadIdx.x + 256 * c) * 8;
+      if (j < two_m) quantize8(keep[c], j);
+    }
+  } else {
+    for (int j = threadIdx.x * 8; j < two_m; j += 256 * 8) {
+      float v[8];
+      Load8<XT>::run(xr + j, v);
+      quantize8(v, j);
+    }
   }
   if (threadIdx.x == 0) delta[tok] = d;
 }
 
+template <typename XT>
+static void launch_act_quant_t(const XT* x, int N, int two_m, int8_t* q, float* delta, hipStream_t s) {
+  const dim3 grid(N), block(256);
+  if (two_m <= 2048) hipLaunchKernelGGL((k_act_quant<XT, 1>), grid, block, 0, s, x, two_m, q, delta);
+  else if (two_m <= 4096) hipLaunchKernelGGL((k_act_quant<XT, 2>), grid, block, 0, s, x, two_m, q, delta);
+  else if (two_m <= 8192) hipLaunchKernelGGL((k_act_quant<XT, 4>), grid, block, 0, s, x, two_m, q, delta);
+  else if (two_m <= 16384) hipLaunchKernelGGL((k_act_quant<XT, 8>), grid, block, 0, s, x, two_m, q, delta);
+  else hipLaunchKernelGGL((k_act_quant<XT, 0>), grid, block, 0, s, x, two_m, q, delta);
+}
+
 hipError_t launch_act_quant(const void* x, int x_bf16, int N, int two_m, int8_t* q, float* delta,
                             hipStream_t s) {
-  if (x_bf16)
-    hipLaunchKernelGGL(k_act_quant<uint16_t>, dim3(N), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x), two_m, q, delta);
-  else
-    hipLaunchKernelGGL(k_act_quant<float>, dim3(N), dim3(256), 0, s,
-                       static_cast<const float*>(x), two_m, q, delta);
+  if (x_bf16) launch_act_quant_t(static_cast<const uint16_t*>(x), N, two_m, q, delta, s);
+  else launch_act_quant_t(static_cast<const float*>(x), N, two_m, q, delta, s);
   return hipGetLastError();
 }
 
