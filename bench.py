@@ -373,6 +373,27 @@ def main():
     e1 = ev()
     torch.cuda.synchronize()
 
+    def kernel_us(fn, calls=8, warm=20, replays=3):
+        """Per-call time of fn's launches run back to back: `calls` calls in one graph, replayed
+        after `warm` untimed replays (no graph-launch latency between the calls)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(calls):
+                fn()
+        for _ in range(warm):
+            g.replay()
+        torch.cuda.synchronize()
+        a = ev()
+        for _ in range(replays):
+            g.replay()
+        b = ev()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (replays * calls)
+
+    k_us = {"quantize": kernel_us(seg_quantize), "act_quant": kernel_us(seg_act_quant),
+            "gemm": kernel_us(seg_gemm), "dequantize": kernel_us(seg_dequant),
+            "quantize_per_tensor": kernel_us(seg_quantize_tensor)}
+
     t_quant, t_decf4, t_f4, t_dec, t_i8, t_b1, t_b4, t_b16, t_aq, t_gemm, t_deq, t_qt = seg    # ms
     bytes_b = {B: gemv_bytes(n, m, T, B) for B in (1, 4, 16)}
     gemv_ms = {1: t_b1, 4: t_b4, 16: t_b16}
@@ -449,17 +470,27 @@ def main():
                                             "GB/s": round(bytes_b[1] / (single_us * 1e-6) / 1e9, 2)},
             "quantize": {"us": round(t_quant * 1e3, 2),
                          "real_params_per_s": round(quant_params / (t_quant * 1e-3), 1),
-                         "GB/s": round(quant_read / (t_quant * 1e-3) / 1e9, 2)},
+                         "GB/s": round(quant_read / (t_quant * 1e-3) / 1e9, 2),
+                         "kernel_us": round(k_us["quantize"], 2),
+                         "kernel_GB/s": round(quant_read / (k_us["quantize"] * 1e-6) / 1e9, 2)},
             "quantize_per_tensor": {"us": round(t_qt * 1e3, 2),
-                                    "real_params_per_s": round(quant_params / (t_qt * 1e-3), 1)},
+                                    "real_params_per_s": round(quant_params / (t_qt * 1e-3), 1),
+                                    "kernel_us": round(k_us["quantize_per_tensor"], 2)},
             "act_quant": {"us": round(t_aq * 1e3, 2),
-                          "GB/s": round((Ntok * 2 * m * 3 + Ntok * 4) / (t_aq * 1e-3) / 1e9, 2)},
+                          "GB/s": round((Ntok * 2 * m * 3 + Ntok * 4) / (t_aq * 1e-3) / 1e9, 2),
+                          "kernel_us": round(k_us["act_quant"], 2),
+                          "kernel_GB/s": round((Ntok * 2 * m * 3 + Ntok * 4) / (k_us["act_quant"] * 1e-6) / 1e9, 2)},
             "gemm": {"us": round(t_gemm * 1e3, 2), "issued_TOPS": round(gemm_tops, 2),
                      "useful_TOPS": round(gemm_tops / 2, 2),
                      "frac_of_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "issued_ops": issued_ops},
+                     "issued_ops": issued_ops,
+                     "kernel_us": round(k_us["gemm"], 2),
+                     "kernel_issued_TOPS": round(issued_ops / (k_us["gemm"] * 1e-6) / 1e12, 2),
+                     "kernel_frac_of_int8_peak": round(issued_ops / (k_us["gemm"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)},
             "dequantize": {"us": round(t_deq * 1e3, 2),
-                           "GB/s": round((layer_bytes + n * T * 16 + 4 * n * m * 4) / (t_deq * 1e-3) / 1e9, 2)},
+                           "GB/s": round((layer_bytes + n * T * 16 + 4 * n * m * 4) / (t_deq * 1e-3) / 1e9, 2),
+                           "kernel_us": round(k_us["dequantize"], 2),
+                           "kernel_GB/s": round((layer_bytes + n * T * 16 + 4 * n * m * 4) / (k_us["dequantize"] * 1e-6) / 1e9, 2)},
             "wall_s": round(wall, 3),
         },
     }
