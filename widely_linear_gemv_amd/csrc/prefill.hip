@@ -131,7 +131,6 @@ hipError_t launch_act_quant(const void* x, int x_bf16, int N, int two_m, int8_t*
 enum { kOutF32 = 0, kOutBF16 = 1, kOutRaw = 2 };
 
 constexpr int kGemmWaves = 8;      // waves per workgroup, one 16-row tile each
-constexpr int kActPitch = 256 + 16; // LDS row pitch (bytes) of one (token, component) activation row
 
 // Epilogue of a 16-row x 8*NF-token wave tile: acc[p][f] with plane p = (t*2+M)*2 + re/im and
 // column fragment f (tokens tok0 + 8f + r/2, component r & 1).
@@ -233,18 +232,23 @@ __device__ __forceinline__ void gemm_epilogue(const v4i (&acc)[TT * 4][NF], cons
 }
 
 // Workgroup = 8 tiles of 16 complex rows (wave w takes tile 8 blockIdx.x + w) x 8*NF tokens.  Per
-// 256-column chunk (the chunk of the packed form) the workgroup stages the tokens' activations,
-// [token][component][256 columns] int8 with a padded row pitch, in one of two LDS buffers; every
-// wave then runs the chunk's four 64-column MFMA steps on it: lane (r, g) decodes word s of its
-// row r, 64-column group g for each of the 2T planes (columns 64g + 16s .. +15, the k order of
-// the decode GEMVs) and multiplies both ternary planes with the NF activation fragments it reads
-// from LDS at the same columns.  The next chunk's code words and activations are loaded at the
-// top of a chunk and the activations written to the other LDS buffer at its end, followed by the
-// chunk's one barrier.
+// 256-column chunk (the chunk of the packed form) the workgroup copies into one of two LDS buffers,
+// with direct global-to-LDS buffer loads (no registers on the way): each wave its own tile's 2T
+// code planes (1 KB each, lane l's 16 bytes at 16 l as in the packed form), and all waves together
+// the tokens' activations, [token][component][256 columns] int8, 1 KB (4 rows) per copy.  Within an
+// activation row, 16-byte segment sg sits in slot sg ^ (row % 16), so the 16 lanes that read one
+// fragment (16 rows, same columns) hit 16 different slots and every LDS bank once.  Every wave
+// then runs the chunk's four 64-column MFMA steps: lane (r, g) decodes word s of its row r,
+// 64-column group g for each plane (columns 64g + 16s .. +15, the k order of the decode GEMVs)
+// and multiplies both ternary planes with the NF activation fragments it reads at the same
+// columns.  The next chunk's copies are issued before the current chunk is multiplied; each chunk
+// ends with a wait for this wave's copies and the workgroup's one barrier.
 //
 // No load is predicated: codes and activations are read through buffer resources sized to the
 // tiles and tokens that exist, so reads past n or N return 0 (those outputs are never stored);
 // activation columns past m and code groups past m read as 0 (offset past every range).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 template <int TT, int NF, int MODE>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restrict__ packed,
                                                           const float* __restrict__ scales, int n, int m,
@@ -252,10 +256,11 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
                                                           const float* __restrict__ delta, int N,
                                                           void* __restrict__ yv) {
   constexpr int kPlanes = TT * 4;                  // (t, M, re/im)
-  constexpr int kRows = 8 * NF * 2;                // (token, component) activation rows
-  constexpr int kSeg = kRows * 16 / (64 * kGemmWaves);   // 16-byte staging segments per thread
-  static_assert(kSeg * 64 * kGemmWaves == kRows * 16, "whole segments per thread");
-  __shared__ __align__(16) int8_t s_b[2][kRows * kActPitch];
+  constexpr int kWords = TT * 2;                   // code planes (t, M)
+  constexpr int kActBytes = NF * 4096;             // 16 NF activation rows of 256 bytes
+  constexpr int kCodeBytes = kGemmWaves * kWords * 1024;
+  static_assert(2 * (kCodeBytes + kActBytes) <= 160 * 1024, "two buffers fit in LDS");
+  __shared__ __align__(16) uint8_t s_lds[2][kCodeBytes + kActBytes];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: keeps the buffer resources scalar
@@ -279,75 +284,65 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[p][f] = v4i{0, 0, 0, 0};
 
-  // the wave's 16-row x 256-column block of each plane (t, M): 16 bytes per lane
-  auto load_words = [&](int c, uint4 (&w)[TT * 2]) {
+  // chunk c into buffer b: this wave's planes, then activation blocks wave, wave + 8, ...
+  auto stage = [&](int c, int b) {
+    uint8_t* base = s_lds[b];
     const int groups = min(4, (m - 256 * c) >> 6);
-    const bool ok = g < groups;
+    const bool ok_w = g < groups;
 #pragma unroll
-    for (int tm = 0; tm < TT * 2; ++tm)
-      w[tm] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-          rsrc_w, ok ? (uint32_t)(c * (TT * 2) * 1024 + tm * groups * 256 + lane * 16) : kNoLoad, 0, 0));
-  };
-  // staging segment e = tid + 512 k: activation row e / 16 (token (e/16)/2, component (e/16)&1),
-  // columns 16 (e % 16) .. +15 of the chunk
-  auto load_act = [&](int c, v4i (&st)[kSeg]) {
+    for (int P = 0; P < kWords; ++P)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc_w, (lds_ptr_t)(base + (wave * kWords + P) * 1024), 16,
+          ok_w ? (uint32_t)(c * kWords * 1024 + P * groups * 256 + lane * 16) : kNoLoad, 0, 0, 0);
 #pragma unroll
-    for (int k = 0; k < kSeg; ++k) {
-      const int e = tid + 64 * kGemmWaves * k, row = e >> 4, sg = e & 15;
-      const bool ok = 256 * c + 16 * sg < m;
-      st[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-          rsrc_q, ok ? (uint32_t)((row >> 1) * two_m + (row & 1) * m + 256 * c + 16 * sg) : kNoLoad, 0, 0));
+    for (int k = 0; k < (4 * NF + kGemmWaves - 1) / kGemmWaves; ++k) {
+      const int blk = wave + kGemmWaves * k;        // activation rows 4 blk .. 4 blk + 3
+      if (blk >= 4 * NF) break;
+      const int R = 4 * blk + (lane >> 4), slot = lane & 15, sg = slot ^ (R & 15);
+      const bool ok = 256 * c + 16 * sg < m;        // row R: token R / 2, component R & 1
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc_q, (lds_ptr_t)(base + kCodeBytes + blk * 1024), 16,
+          ok ? (uint32_t)((R >> 1) * two_m + (R & 1) * m + 256 * c + 16 * sg) : kNoLoad, 0, 0, 0);
     }
   };
-  auto store_act = [&](int buf, const v4i (&st)[kSeg]) {
+  constexpr uint32_t lo2 = 0x03030303u;
+  constexpr uint32_t kRe = 0x00FF0001u;   // code 0 -> +1, 1 -> 0, 2 -> -1, 3 -> 0
+  constexpr uint32_t kIm = 0xFF000100u;   // code 0 -> 0, 1 -> +1, 2 -> 0, 3 -> -1
+  auto compute = [&](int b) {
+    const uint8_t* base = s_lds[b];
 #pragma unroll
-    for (int k = 0; k < kSeg; ++k) {
-      const int e = tid + 64 * kGemmWaves * k, row = e >> 4, sg = e & 15;
-      *reinterpret_cast<v4i*>(&s_b[buf][row * kActPitch + 16 * sg]) = st[k];
-    }
-  };
-  auto mfma_step = [&](int buf, const uint4 (&w)[TT * 2], int s) {
-    v4i b[NF];
+    for (int s = 0; s < 4; ++s) {
+      v4i bf[NF];
 #pragma unroll
-    for (int f = 0; f < NF; ++f)      // column r: token 8f + r/2, component r & 1
-      b[f] = *reinterpret_cast<const v4i*>(&s_b[buf][((8 * f + (r >> 1)) * 2 + (r & 1)) * kActPitch + 64 * g + 16 * s]);
-    constexpr uint32_t lo2 = 0x03030303u;
-    constexpr uint32_t kRe = 0x00FF0001u;   // code 0 -> +1, 1 -> 0, 2 -> -1, 3 -> 0
-    constexpr uint32_t kIm = 0xFF000100u;   // code 0 -> 0, 1 -> +1, 2 -> 0, 3 -> -1
+      for (int f = 0; f < NF; ++f) {       // column r: token 8f + r/2, component r & 1 -> row 16 f + r
+        const int R = 16 * f + r;
+        bf[f] = *reinterpret_cast<const v4i*>(base + kCodeBytes + R * 256 + 16 * ((4 * g + s) ^ r));
+      }
 #pragma unroll
-    for (int tm = 0; tm < TT * 2; ++tm) {
-      const uint32_t x = s == 0 ? w[tm].x : s == 1 ? w[tm].y : s == 2 ? w[tm].z : w[tm].w;
-      const uint32_t k0 = x & lo2, k1 = (x >> 2) & lo2, k2 = (x >> 4) & lo2, k3 = (x >> 6) & lo2;
-      const v4i re = v4i{(int)__builtin_amdgcn_perm(0u, kRe, k0), (int)__builtin_amdgcn_perm(0u, kRe, k1),
-                         (int)__builtin_amdgcn_perm(0u, kRe, k2), (int)__builtin_amdgcn_perm(0u, kRe, k3)};
-      const v4i im = v4i{(int)__builtin_amdgcn_perm(0u, kIm, k0), (int)__builtin_amdgcn_perm(0u, kIm, k1),
-                         (int)__builtin_amdgcn_perm(0u, kIm, k2), (int)__builtin_amdgcn_perm(0u, kIm, k3)};
+      for (int tm = 0; tm < kWords; ++tm) {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(base + (wave * kWords + tm) * 1024 + lane * 16 + 4 * s);
+        const uint32_t k0 = x & lo2, k1 = (x >> 2) & lo2, k2 = (x >> 4) & lo2, k3 = (x >> 6) & lo2;
+        const v4i re = v4i{(int)__builtin_amdgcn_perm(0u, kRe, k0), (int)__builtin_amdgcn_perm(0u, kRe, k1),
+                           (int)__builtin_amdgcn_perm(0u, kRe, k2), (int)__builtin_amdgcn_perm(0u, kRe, k3)};
+        const v4i im = v4i{(int)__builtin_amdgcn_perm(0u, kIm, k0), (int)__builtin_amdgcn_perm(0u, kIm, k1),
+                           (int)__builtin_amdgcn_perm(0u, kIm, k2), (int)__builtin_amdgcn_perm(0u, kIm, k3)};
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        acc[tm * 2 + 0][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(re, b[f], acc[tm * 2 + 0][f], 0, 0, 0);
-        acc[tm * 2 + 1][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(im, b[f], acc[tm * 2 + 1][f], 0, 0, 0);
+        for (int f = 0; f < NF; ++f) {
+          acc[tm * 2 + 0][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(re, bf[f], acc[tm * 2 + 0][f], 0, 0, 0);
+          acc[tm * 2 + 1][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(im, bf[f], acc[tm * 2 + 1][f], 0, 0, 0);
+        }
       }
     }
   };
 
-  uint4 w0[TT * 2], w1[TT * 2];
-  v4i st[kSeg];
-  load_words(0, w0);
-  load_act(0, st);
-  store_act(0, st);
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int c = 0; c < nchunk; ++c) {
-    const int buf = c & 1;
-    const int cn = c + 1;   // past the last chunk every load takes the out-of-range offset
-    load_words(cn, w1);
-    load_act(cn, st);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) mfma_step(buf, w0, s);
-    store_act(buf ^ 1, st);                  // its last readers passed the previous barrier
+    if (c + 1 < nchunk) stage(c + 1, (c + 1) & 1);   // its buffer's last readers passed the previous barrier
+    compute(c & 1);
+    __builtin_amdgcn_s_waitcnt(0);                  // this wave's copies of chunk c + 1 have landed
     __syncthreads();
-#pragma unroll
-    for (int tm = 0; tm < TT * 2; ++tm) w0[tm] = w1[tm];
   }
 
   if (tile < tiles) gemm_epilogue<TT, NF, MODE>(acc, scales, n, N, delta, yv, i0, tok0, r, g);
