@@ -28,7 +28,7 @@
 //    integer of magnitude at most 24m < 2^24 (m <= 2^19), so the fp32 accumulation is exact;
 //    Su + Sv is even and below 2^25, so the halving is exact too.  The factor 6 leaves in the
 //    epilogue's digit weight; the only roundings are X itself and the fp32 epilogue.
-//  * Streaming as in the int8 kernel: one wave per 16-row tile of one item of a grouped call
+//  * Streaming as in the int8 kernel: one wave per 16-row tile of one item of a grouped or strided call
 //    (or NW waves splitting the 256-column chunks for small launches), one 1 KB load per plane
 //    and chunk, the next chunk prefetched while the current one is decoded and multiplied.  In
 //    a chunk lane l = 16g + r holds row r, columns 64g..64g+63 (four words); MFMA step s < 2

@@ -23,7 +23,7 @@
 //  * B operand: MFMA column c = 8b + 4comp + l holds digit l of component comp of batch entry
 //    b; lane (c, g) loads the 16 digits of its k-group straight from the digit form.
 //  * K assignment and grouping as in the bf16 kernel: one wave owns a 16-row tile of one item
-//    of a grouped call and streams its 256-column chunks, one 1 KB load per plane, prefetching
+//    of a grouped or strided call and streams its 256-column chunks, one 1 KB load per plane, prefetching
 //    the next chunk's codes and digits while the current one is decoded and multiplied.  In a
 //    chunk lane group g owns columns 64g..64g+63 and at MFMA step s contributes columns
 //    64g+16s..+15.

@@ -27,7 +27,8 @@
 //    64g+8s .. 64g+8s+7.
 //  * Grouped launches: one grid covers the row tiles of several GEMVs of the same m (for
 //    example the q, k and v projections that share x); each workgroup finds its GEMV by binary
-//    search over the first-tile table passed in the kernel arguments.
+//    search over the first-tile table passed in the kernel arguments, or, for a strided batch of
+//    same-shape GEMVs, by one division (operands at fixed strides, no table).
 //  * B operand (32 x 16, bf16): columns are (batch b, component a = Re x or b = Im x); 8 batch
 //    columns per MFMA, two column groups for B > 8.  Each lane loads 8 consecutive bf16 of x and
 //    swaps elements 1,2 and 5,6 with v_perm_b32.
