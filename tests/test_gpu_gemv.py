@@ -410,3 +410,29 @@ def test_strided_batch_matches_grouped_and_oracle(algo, B, n, m, T, batch, ydt):
         torch.cuda.synchronize()
         want = oracle.gemv_ref(host[batch - 1][0], host[0][1], act.values)
         assert rel_l2(down(ys[batch - 1]), want) <= TOL_F32
+
+
+@pytest.mark.parametrize("algo,B", [("f4", 1), ("i8", 1), ("bf16", 4)])
+def test_strided_pool_full_size(algo, B):
+    """The benchmark's own launch: the quantized 4096 x 4096 attention layer repeated 256 times back
+    to back (1 GiB, one strided launch of 32768 workgroups); every copy's output equals the
+    oracle's for that layer within tolerance, and all copies are bit-identical."""
+    dev = device()
+    codes, s32 = attention_layer()
+    P = 256
+    act = workloads.activations(B, 4096, workloads.ATTN_X_SEEDS[B])
+    want = oracle.gemv_ref(codes, s32, act.values)
+    layer = up(oracle.pack(codes), dev)
+    pool = layer.unsqueeze(0).repeat(P, 1).contiguous()
+    spool = up(s32, dev).unsqueeze(0).repeat(P, 1, 1, 1, 1).contiguous()
+    x = x_to_dev(act, dev)
+    if algo in DIGITS:
+        x = DIGITS[algo](x)
+    y = torch.full((P, B, 4096), float("nan"), dtype=torch.float32, device=dev)
+    announce("strided pool", algo, B, P)
+    f2.fairy2i_gemv_strided(pool, spool, x, y, algo=ALGOS[algo])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y[0:1].expand_as(y))
+    assert rel_l2(down(y[P - 1]), want) <= TOL_F32
+    del pool, spool, y
+    torch.cuda.empty_cache()
