@@ -17,14 +17,20 @@
 namespace f2i {
 
 template <typename OT> struct Store4;
+// The real form is written once and not read back by this kernel: non-temporal stores.
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
 template <> struct Store4<float> {
-  __device__ static void run(float* p, const float* v) { *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]); }
+  __device__ static void run(float* p, const float* v) {
+    __builtin_nontemporal_store(v4f_t{v[0], v[1], v[2], v[3]}, reinterpret_cast<v4f_t*>(p));
+  }
 };
 template <> struct Store4<uint16_t> {
   __device__ static void run(uint16_t* p, const float* v) {
-    *reinterpret_cast<uint2*>(p) =
-        make_uint2((uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
-                   (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
+    __builtin_nontemporal_store(
+        v2u_t{(uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+              (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16)},
+        reinterpret_cast<v2u_t*>(p));
   }
 };
 
