@@ -271,3 +271,16 @@ def test_python_binding_raises_with_message(L):
         f2._check(L.fairy2i_pack(NULL, 4, 64, 2, FAKE, S))
     assert "ERR_NULL" in str(e.value) and "required" in str(e.value)
     assert torch is not None
+
+
+def test_strided_binding_rejects_wrong_ranks():
+    import torch
+    packed = torch.zeros(2, 64, dtype=torch.uint8)
+    scales = torch.zeros(2, 16, 2, 2, 2)
+    x = torch.zeros(1, 32)
+    with pytest.raises(ValueError):
+        f2.fairy2i_gemv_strided(packed.flatten(), scales, x, torch.zeros(2, 1, 32))
+    with pytest.raises(ValueError):
+        f2.fairy2i_gemv_strided(packed, scales[0, 0], x, torch.zeros(2, 1, 32))
+    with pytest.raises(ValueError):
+        f2.fairy2i_gemv_strided(packed, scales, x, torch.zeros(2, 32))

@@ -273,6 +273,9 @@ def fairy2i_gemv_strided(packed: torch.Tensor, scales: torch.Tensor, x, y: torch
     """A strided batch of GEMVs sharing x: packed [batch][bytes] uint8, scales [batch][n][T][2][2]
     (or [n][T][2][2], shared by all), y [batch][B][2n] preallocated; the strides are those of the
     tensors' first dimension (each matrix's slice contiguous).  Returns y."""
+    if packed.dim() != 2 or y.dim() != 3 or scales.dim() not in (4, 5):
+        raise ValueError("fairy2i_gemv_strided: packed [batch][bytes], scales [batch][n][T][2][2] or "
+                         "[n][T][2][2], y [batch][B][2n]")
     batch = packed.shape[0]
     n, T = scales.shape[-4], scales.shape[-3]
     s_stride = scales.stride(0) if scales.dim() == 5 else 0
