@@ -133,42 +133,46 @@ enum { kOutF32 = 0, kOutBF16 = 1, kOutRaw = 2 };
 constexpr int kGemmWaves = 8;      // waves per workgroup, one 16-row tile each
 
 // Epilogue of a 16-row x 8*NF-token wave tile: acc[p][f] with plane p = (t*2+M)*2 + re/im and
-// column fragment f (tokens tok0 + 8f + r/2, component r & 1).
+// column fragment f = 2 tg + comp (tokens tok0 + 16 tg + r, component comp: a = Re x, b = Im x).
+// A lane holds both components of its tokens, so it forms Re y and Im y of its four rows alone:
+//   Re y = sum_t  sU_re P_U,re(a) - sU_im P_U,im(b) + sW_re P_W,re(a) + sW_im P_W,im(b)
+//   Im y = sum_t  sU_re P_U,re(b) + sU_im P_U,im(a) + sW_im P_W,im(a) - sW_re P_W,re(b)
+// (U x + W conj(x) with each term's two axis scales), times the token's delta.
 template <int TT, int NF, int MODE>
 __device__ __forceinline__ void gemm_epilogue(const v4i (&acc)[TT * 4][NF], const float* __restrict__ scales,
                                               int n, int N, const float* __restrict__ delta,
                                               void* __restrict__ yv, int i0, int tok0, int r, int g) {
   constexpr int kPlanes = TT * 4;
-  bool b_ok[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) b_ok[f] = tok0 + 8 * f + (r >> 1) < N;
+  constexpr int NT = NF / 2;                 // groups of 16 tokens
 
-  // C layout of a 16x16 tile: lane holds rows 4g..4g+3 of column r.  Plane index p = (t*2+M)*2+re/im.
-  // Each lane stores its four consecutive rows with one 16-byte (8-byte for bf16) store when n is
-  // a multiple of 4, which keeps every store row-aligned; otherwise it stores them one by one.
-  const int comp = r & 1;
+  // C layout of a 16x16 tile: lane holds rows 4g..4g+3 of column r.  Each lane stores its four
+  // consecutive rows with one 16-byte (8-byte for bf16) store when n is a multiple of 4, which
+  // keeps every store row-aligned; otherwise it stores them one by one.
   if (tok0 >= N) return;
   const int ib = i0 + 4 * g;                 // first of this lane's four rows
   const bool vec = (n % 4) == 0;
   if constexpr (MODE == kOutRaw) {
     int* __restrict__ P = static_cast<int*>(yv);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int tok = tok0 + 8 * f + (r >> 1);
-      if (!b_ok[f] || ib >= n) continue;
+    for (int tg = 0; tg < NT; ++tg) {
+      const int tok = tok0 + 16 * tg + r;
+      if (tok >= N || ib >= n) continue;
 #pragma unroll
-      for (int p = 0; p < kPlanes; ++p) {
-        int* dst = P + (((int64_t)p * 2 + comp) * N + tok) * n + ib;
-        if (vec) {
-          *reinterpret_cast<v4i*>(dst) = acc[p][f];
-        } else {
+      for (int comp = 0; comp < 2; ++comp)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (ib + e < n) dst[e] = acc[p][f][e];
+        for (int p = 0; p < kPlanes; ++p) {
+          int* dst = P + (((int64_t)p * 2 + comp) * N + tok) * n + ib;
+          if (vec) {
+            *reinterpret_cast<v4i*>(dst) = acc[p][2 * tg + comp];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (ib + e < n) dst[e] = acc[p][2 * tg + comp][e];
+          }
         }
-      }
     }
   } else {
+#pragma clang fp contract(fast)
     const int64_t ys = 2 * (int64_t)n;
     float s[4][TT][2][2];
 #pragma unroll
@@ -181,50 +185,52 @@ __device__ __forceinline__ void gemm_epilogue(const v4i (&acc)[TT * 4][NF], cons
           for (int ax = 0; ax < 2; ++ax)
             s[e][t][M][ax] = ib + e < n ? scales[(((int64_t)(ib + e) * TT + t) * 2 + M) * 2 + ax] : 0.f;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int tok = tok0 + 8 * f + (r >> 1);
-      const float d = delta[b_ok[f] ? tok : 0];
-      float o[4];
+    for (int tg = 0; tg < NT; ++tg) {
+      const int tok = tok0 + 16 * tg + r;
+      const bool ok = tok < N;
+      const float d = delta[ok ? tok : 0];
+      float ore[4], oim[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float vre = 0.f, vim = 0.f;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-          const float PUr = (float)acc[(t * 2 + 0) * 2 + 0][f][e], PUi = (float)acc[(t * 2 + 0) * 2 + 1][f][e];
-          const float PWr = (float)acc[(t * 2 + 1) * 2 + 0][f][e], PWi = (float)acc[(t * 2 + 1) * 2 + 1][f][e];
-          if (comp == 0) {   // column a = Re x
-            vre += s[e][t][0][0] * PUr + s[e][t][1][0] * PWr;
-            vim += s[e][t][0][1] * PUi + s[e][t][1][1] * PWi;
-          } else {           // column b = Im x
-            vre += s[e][t][1][1] * PWi - s[e][t][0][1] * PUi;
-            vim += s[e][t][0][0] * PUr - s[e][t][1][0] * PWr;
-          }
+          const int u = (t * 2 + 0) * 2, w = (t * 2 + 1) * 2;
+          const float Ura = (float)acc[u][2 * tg][e], Uia = (float)acc[u + 1][2 * tg][e];
+          const float Wra = (float)acc[w][2 * tg][e], Wia = (float)acc[w + 1][2 * tg][e];
+          const float Urb = (float)acc[u][2 * tg + 1][e], Uib = (float)acc[u + 1][2 * tg + 1][e];
+          const float Wrb = (float)acc[w][2 * tg + 1][e], Wib = (float)acc[w + 1][2 * tg + 1][e];
+          vre += s[e][t][0][0] * Ura - s[e][t][0][1] * Uib + s[e][t][1][0] * Wra + s[e][t][1][1] * Wib;
+          vim += s[e][t][0][0] * Urb + s[e][t][0][1] * Uia + s[e][t][1][1] * Wia - s[e][t][1][0] * Wrb;
         }
-        vre += __shfl_xor(vre, 1);   // lanes r and r^1 hold columns a and b of one token
-        vim += __shfl_xor(vim, 1);
-        o[e] = d * (comp == 0 ? vre : vim);   // lane a stores Re y, lane b stores Im y
+        ore[e] = d * vre;
+        oim[e] = d * vim;
       }
-      if (!b_ok[f] || ib >= n) continue;
-      const int64_t off = (int64_t)tok * ys + (comp == 0 ? 0 : n) + ib;
+      if (!ok || ib >= n) continue;
+      const int64_t off = (int64_t)tok * ys + ib;
       if (MODE == kOutF32) {
         float* __restrict__ y = static_cast<float*>(yv) + off;
         if (vec) {
-          *reinterpret_cast<float4*>(y) = make_float4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<float4*>(y) = make_float4(ore[0], ore[1], ore[2], ore[3]);
+          *reinterpret_cast<float4*>(y + n) = make_float4(oim[0], oim[1], oim[2], oim[3]);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (ib + e < n) y[e] = o[e];
+            if (ib + e < n) y[e] = ore[e], y[n + e] = oim[e];
         }
       } else {
         uint16_t* __restrict__ y = static_cast<uint16_t*>(yv) + off;
         if (vec) {
           *reinterpret_cast<uint2*>(y) =
-              make_uint2((uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16),
-                         (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16));
+              make_uint2((uint32_t)f32_to_bf16_rne(ore[0]) | ((uint32_t)f32_to_bf16_rne(ore[1]) << 16),
+                         (uint32_t)f32_to_bf16_rne(ore[2]) | ((uint32_t)f32_to_bf16_rne(ore[3]) << 16));
+          *reinterpret_cast<uint2*>(y + n) =
+              make_uint2((uint32_t)f32_to_bf16_rne(oim[0]) | ((uint32_t)f32_to_bf16_rne(oim[1]) << 16),
+                         (uint32_t)f32_to_bf16_rne(oim[2]) | ((uint32_t)f32_to_bf16_rne(oim[3]) << 16));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (ib + e < n) y[e] = f32_to_bf16_rne(o[e]);
+            if (ib + e < n) y[e] = f32_to_bf16_rne(ore[e]), y[n + e] = f32_to_bf16_rne(oim[e]);
         }
       }
     }
@@ -235,9 +241,11 @@ __device__ __forceinline__ void gemm_epilogue(const v4i (&acc)[TT * 4][NF], cons
 // 256-column chunk (the chunk of the packed form) the workgroup copies into one of two LDS buffers,
 // with direct global-to-LDS buffer loads (no registers on the way): each wave its own tile's 2T
 // code planes (1 KB each, lane l's 16 bytes at 16 l as in the packed form), and all waves together
-// the tokens' activations, [token][component][256 columns] int8, 1 KB (4 rows) per copy.  Within an
-// activation row, 16-byte segment sg sits in slot sg ^ (row % 16), so the 16 lanes that read one
-// fragment (16 rows, same columns) hit 16 different slots and every LDS bank once.  Every wave
+// the tokens' activations, 256 columns of int8 per row, 1 KB (4 rows) per copy.  Row 16 f + r holds
+// column r of token fragment f: token 16 (f/2) + r, component f & 1 (a = Re x, b = Im x), so
+// a lane's accumulators hold both components of its tokens.  Within an activation row, 16-byte
+// segment sg sits in slot sg ^ (row % 16), so the 16 lanes that read one fragment (16 rows, same
+// columns) hit 16 different slots, each its own group of LDS banks.  Every wave
 // then runs the chunk's four 64-column MFMA steps: lane (r, g) decodes word s of its row r,
 // 64-column group g for each plane (columns 64g + 16s .. +15, the k order of the decode GEMVs)
 // and multiplies both ternary planes with the NF activation fragments it reads at the same
@@ -299,10 +307,11 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
       const int blk = wave + kGemmWaves * k;        // activation rows 4 blk .. 4 blk + 3
       if (blk >= 4 * NF) break;
       const int R = 4 * blk + (lane >> 4), slot = lane & 15, sg = slot ^ (R & 15);
-      const bool ok = 256 * c + 16 * sg < m;        // row R: token R / 2, component R & 1
+      const bool ok = 256 * c + 16 * sg < m;        // row R = 16 f + r: fragment f's column r
+      const int tok = 16 * (R >> 5) + (R & 15), comp = (R >> 4) & 1;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsrc_q, (lds_ptr_t)(base + kCodeBytes + blk * 1024), 16,
-          ok ? (uint32_t)((R >> 1) * two_m + (R & 1) * m + 256 * c + 16 * sg) : kNoLoad, 0, 0, 0);
+          ok ? (uint32_t)(tok * two_m + comp * m + 256 * c + 16 * sg) : kNoLoad, 0, 0, 0);
     }
   };
   constexpr uint32_t lo2 = 0x03030303u;
@@ -314,7 +323,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm(const uint8_t* __restr
     for (int s = 0; s < 4; ++s) {
       v4i bf[NF];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {       // column r: token 8f + r/2, component r & 1 -> row 16 f + r
+      for (int f = 0; f < NF; ++f) {       // column r: token 16 (f/2) + r, component f & 1 -> row 16 f + r
         const int R = 16 * f + r;
         bf[f] = *reinterpret_cast<const v4i*>(base + kCodeBytes + R * 256 + 16 * ((4 * g + s) ^ r));
       }
