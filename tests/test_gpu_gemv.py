@@ -436,3 +436,53 @@ def test_strided_pool_full_size(algo, B):
     assert rel_l2(down(y[P - 1]), want) <= TOL_F32
     del pool, spool, y
     torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,m,T,ydt", [
+    (1000, 192, 2, "f32"),      # one chunk per tile: every stream step starts a new tile
+    (1000, 192, 1, "bf16"),
+    (1000, 2112, 2, "f32"),     # nine chunks, the last one of a single 64-column group
+    (1000, 2112, 1, "bf16"),
+])
+def test_large_f4_launch_matches_single_launches(n, m, T, ydt):
+    """A batch-1 fp4 launch of 3780 ragged tiles (one wave per tile, more tiles than the chip keeps
+    resident) against each matrix's own single-matrix launch: bit for bit where that launch also
+    gives one wave per tile (a single chunk), else within 1e-6 relative L2 for fp32 outputs (its
+    waves split the chunks, so its fp32 epilogue adds in another order; bf16 outputs within their
+    own tolerance); the first and last are within tolerance of the oracle."""
+    dev = device()
+    batch = 60
+    act = workloads.activations(1, 2 * m, seed=4242 + m)
+    x = f2.fairy2i_x_digits_f6(x_to_dev(act, dev))
+    pb = f2.fairy2i_packed_bytes(n, m, T)
+    packed = torch.empty((batch, pb), dtype=torch.uint8, device=dev)
+    scales = torch.empty((batch, n, T, 2, 2), dtype=torch.float32, device=dev)
+    host = {}
+    for k in range(batch):
+        codes = workloads.random_codes(T, n, m, seed=7000 + 13 * k + m)
+        sc = workloads.random_scales(n, T, seed=8000 + k)
+        packed[k] = up(oracle.pack(codes), dev)
+        scales[k] = up(sc, dev)
+        if k in (0, batch - 1):
+            host[k] = (codes, sc)
+    ydtype = torch.float32 if ydt == "f32" else torch.bfloat16
+    y = torch.full((batch, 1, 2 * n), float("nan"), dtype=ydtype, device=dev)
+    announce("large f4 launch", n, m, T, batch, ydt)
+    f2.fairy2i_gemv_strided(packed, scales, x, y, algo=f2.GEMV_MFMA_F4)
+    ys = torch.full_like(y, float("nan"))
+    for k in range(batch):
+        f2.fairy2i_gemv(packed[k], scales[k], x, y=ys[k], algo=f2.GEMV_MFMA_F4)
+    torch.cuda.synchronize()
+    if m <= 256:
+        assert torch.equal(y, ys)
+    else:                    # bf16: one rounding step apart at most where the fp32 values differ
+        tol = 1e-6 if ydt == "f32" else 2e-3
+        for k in range(batch):
+            assert rel_l2(down(y[k].float()), down(ys[k].float())) <= tol, k
+    for k, (codes, sc) in host.items():
+        want = oracle.gemv_ref(codes, sc, act.values)
+        if ydt == "f32":
+            assert rel_l2(down(y[k]), want) <= TOL_F32, k
+        else:
+            check_bf16(down(y[k]), want, ("large launch", k))
