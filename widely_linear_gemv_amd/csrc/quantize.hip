@@ -45,13 +45,15 @@ __device__ __forceinline__ void residual_step(double& re2, double& im2, int k, d
 // over s = 1, i, -1, -i, ties to the earlier codeword -- and its share of the stage's axis sums
 // and real-axis count.  In closed form the imaginary axis wins when |im| > |re|, or on a tie when
 // re < 0 <= im (im is then the first maximum); the sign of the winning component picks code 2 or
-// 3.  The winning magnitude is max(|re|, |im|); it reaches its axis's sum through an fma with 1.0
-// or 0.0 (adding +0.0 leaves a non-negative partial sum unchanged).
+// 3.  The winning magnitude is max(|re|, |im|), i.e. the winning axis's (inputs are finite); it
+// reaches its axis's sum through an fma with 1.0 or 0.0 (adding +0.0 leaves a non-negative
+// partial sum unchanged).  The tests combine without short-circuits, so no lane mask is
+// manipulated per entry.
 __device__ __forceinline__ int project_accumulate(double re, double im, double& sre, double& sim, int& nre) {
   const double ar = fabs(re), ai = fabs(im);
-  const bool im_axis = ai > ar || (ai == ar && re < 0.0 && im >= 0.0);
-  const bool neg = im_axis ? im < 0.0 : re < 0.0;
-  const double v = fmax(ar, ai);
+  const bool im_axis = (ai > ar) | ((ai == ar) & (re < 0.0) & (im >= 0.0));
+  const bool neg = (im_axis & (im < 0.0)) | (!im_axis & (re < 0.0));
+  const double v = im_axis ? ai : ar;
   sre = fma(v, im_axis ? 0.0 : 1.0, sre);
   sim = fma(v, im_axis ? 1.0 : 0.0, sim);
   nre += im_axis ? 0 : 1;
@@ -133,6 +135,15 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     }
   }
 
+  // MAXC > 0: the codes of stages 0..2 also stay in registers, two bits per (column, matrix), for
+  // the later stages' residuals (the LDS copy only feeds the packing)
+  constexpr int NCW = MAXC > 0 ? (MAXC * 4 + 31) / 32 : 1;
+  uint32_t creg[3][NCW];
+#pragma unroll
+  for (int tp = 0; tp < 3; ++tp)
+#pragma unroll
+    for (int w = 0; w < NCW; ++w) creg[tp][w] = 0u;
+
   for (int t = 0; t < T; ++t) {
     if constexpr (MAXC > 0) {
       // Keep only the fp32 inputs live across stages: without this the fp64 split of every
@@ -140,6 +151,9 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) asm volatile("" : "+v"(qa[c]), "+v"(qb[c]), "+v"(qc[c]), "+v"(qd[c]));
     }
+    uint32_t cur[NCW];
+#pragma unroll
+    for (int w = 0; w < NCW; ++w) cur[w] = 0u;
     double sre[2] = {0.0, 0.0}, sim[2] = {0.0, 0.0};
     int nre[2] = {0, 0};
     double ps[3][2][2];                                   // doubled scales of the earlier stages
@@ -150,27 +164,40 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
         ps[tp][M][0] = tp < t ? uniform_f64(s_scale[tp][M][0]) : 0.0;
         ps[tp][M][1] = tp < t ? uniform_f64(s_scale[tp][M][1]) : 0.0;
       }
-    auto body = [&](int j, float A, float B, float C, float D) {
+    // column slot c (< MAXC when the codes stay in registers; -1 otherwise), column j
+    auto body = [&](int c, int j, float A, float B, float C, float D) {
 #pragma unroll
       for (int M = 0; M < 2; ++M) {
+        const int bit = (c * 2 + M) * 2;                  // register slot of (c, M)
         double re, im;
         split2(M, A, B, C, D, re, im);
 #pragma unroll
         for (int tp = 0; tp < 3; ++tp)                    // earlier stages, in order
-          if (tp < t) residual_step(re, im, s_codes[(tp * 2 + M) * m + j], ps[tp][M][0], ps[tp][M][1]);
-        s_codes[(t * 2 + M) * m + j] = (uint8_t)project_accumulate(re, im, sre[M], sim[M], nre[M]);
+          if (tp < t) {
+            const int k = c >= 0 ? (int)((creg[tp][bit / 32] >> (bit % 32)) & 3u) : s_codes[(tp * 2 + M) * m + j];
+            residual_step(re, im, k, ps[tp][M][0], ps[tp][M][1]);
+          }
+        const int k = project_accumulate(re, im, sre[M], sim[M], nre[M]);
+        s_codes[(t * 2 + M) * m + j] = (uint8_t)k;
+        if (c >= 0) cur[bit / 32] |= (uint32_t)k << (bit % 32);
       }
     };
     if constexpr (MAXC > 0) {
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
         const int j = l + c * kQThreads;
-        if (j < m) body(j, qa[c], qb[c], qc[c], qd[c]);
+        if (j < m) body(c, j, qa[c], qb[c], qc[c], qd[c]);
+      }
+#pragma unroll
+      for (int w = 0; w < NCW; ++w) {                    // (t is uniform: no register indexing)
+        if (t == 0) creg[0][w] = cur[w];
+        else if (t == 1) creg[1][w] = cur[w];
+        else if (t == 2) creg[2][w] = cur[w];
       }
     } else {
       for (int c = 0; c < nch; ++c) {
         const int j = l + c * kQThreads;
-        if (j < m) body(j, r_value(r0[j]), r_value(r0[m + j]), r_value(r1[j]), r_value(r1[m + j]));
+        if (j < m) body(-1, j, r_value(r0[j]), r_value(r0[m + j]), r_value(r1[j]), r_value(r1[m + j]));
       }
     }
 
