@@ -14,12 +14,22 @@ pytestmark = pytest.mark.gpu
 
 
 def edge_tokens(two_m):
-    """All-zero token, exact half-way ratios (amax = 127 so delta = 1), +-amax, tiny values."""
-    t = np.zeros((4, two_m), dtype=np.float32)
+    """All-zero token, exact half-way ratios (amax = 127 so delta = 1), +-amax, tiny values;
+    ratios within a few fp32 steps of half-integers at a delta other than 1 (the kernel checks
+    those with a true division); a row whose delta is subnormal."""
+    t = np.zeros((6, two_m), dtype=np.float32)
     t[1, :8] = [127, -127, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5]
     t[2, :] = 1e-3
     t[2, 5] = -4.0
     t[3, :] = np.linspace(-3, 3, two_m, dtype=np.float32)
+    d = np.float32(np.float32(100.0) / np.float32(127.0))
+    k = np.arange(two_m) % 253 - 126                          # half-integers k + 1/2, |k| <= 126
+    near = (k + 0.5).astype(np.float32) * d                   # rounded products: x / d next to k + 1/2
+    steps = (np.arange(two_m) % 5 - 2).astype(np.int32)       # -2 .. +2 fp32 steps away
+    near = (near.view(np.int32) + steps).view(np.float32)
+    t[4, :] = np.clip(near, -100.0, 100.0)
+    t[4, 0] = 100.0                                           # amax = 100
+    t[5, :] = np.linspace(-1e-39, 1e-39, two_m, dtype=np.float32)   # delta below 2^-120
     return t
 
 
@@ -108,5 +118,6 @@ def test_prefill_ragged(n, m, T, N):
     scales = workloads.random_scales(n, T, seed=T + N)
     vals = workloads.activations(N, 2 * m, seed=N + 3).values
     if N >= 4:
-        vals[:4] = edge_tokens(2 * m)
+        k = min(N, 6)
+        vals[:k] = edge_tokens(2 * m)[:k]
     gemm_case(dev, codes, scales, bf16_act(vals), np.arange(N), f"n={n} m={m} T={T} N={N}")
