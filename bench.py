@@ -1,6 +1,6 @@
 """Benchmark of the Fairy2i widely-linear hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-s S] [--no-cpu-baseline] [--no-stack]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-s S] [--no-cpu-baseline] [--no-stack] [--no-mlp]
 
 Workload: the LLaMA-2 7B attention projection (R 4096 x 4096 -> U, W 2048 x 2048 complex),
 T = 2 residual stages, bf16 activations, all inputs synthetic and seeded (workloads.py).
@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer stack legs")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the MLP-shape decode legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--prewarm-s", type=float, default=0.3,
                     help="seconds of untimed whole steps before the warm-up steps (clock ramp)")
@@ -182,6 +183,68 @@ def stack_legs(f2, torch, dev, T, reps):
         legs[f"stack_decode_b{B}"] = {"gemvs": 224, "launches": 128, "us": round(t * 1e3, 1),
                                       "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes,
                                       "kernel": "bf16 matrix cores (default for these latency-bound launches)"}
+    return legs
+
+
+MLP_POOL_BYTES = 2 ** 29     # 2x the Infinity Cache per MLP pool
+
+
+def mlp_legs(f2, torch, workloads, dev, reps=5):
+    """The LLaMA-2 7B MLP decode GEMVs: gate/up (11008 x 4096, outlier weights) and down
+    (4096 x 11008) quantized at T = 2 and T = 3, at batch 1 (fp4 matrix cores on the fp6 digit form)
+    and batch 8 (bf16 matrix cores, shared x).  Each case streams a pool of >= 512 MB of copies of
+    its quantized layer as one strided-batch launch per pass, four passes per HIP graph, replayed
+    after warm-up replays.  Runs outside the timed step."""
+    legs = {}
+    for name, layer in (("gate_up", workloads.MLP_GATE_UP), ("down", workloads.MLP_DOWN)):
+        R = torch.from_numpy(layer.weight()).to(dev)
+        n, m = layer.n, layer.m
+        for T in (2, 3):
+            q = f2.fairy2i_quantize(R, T)
+            P = max(1, -(-MLP_POOL_BYTES // q["packed"].numel()))
+            pool = q["packed"].unsqueeze(0).repeat(P, 1).contiguous()
+            spool = q["scales"].unsqueeze(0).repeat(P, 1, 1, 1, 1).contiguous()
+            for B in (1, 8):
+                a = workloads.activations(B, 2 * m, workloads.MLP_X_SEEDS[name])
+                x = torch.from_numpy(a.bf16_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+                y = torch.empty((P, B, 2 * n), dtype=torch.float32, device=dev)
+                if B <= 2:
+                    xd = f2.fairy2i_x_digits_f6(x)
+                    kern = "fp4 matrix cores (fp6 digit form of x, made once)"
+
+                    def fn():
+                        f2.fairy2i_gemv_strided(pool, spool, xd, y, algo=f2.GEMV_MFMA_F4)
+                else:
+                    kern = "bf16 matrix cores (shared x)"
+
+                    def fn():
+                        f2.fairy2i_gemv_strided(pool, spool, x, y, algo=f2.GEMV_MFMA_BF16)
+                fn()
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                    for _ in range(4):
+                        fn()
+                for _ in range(10):
+                    g.replay()
+                torch.cuda.synchronize()
+                stream = torch.cuda.current_stream()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (reps * 4)
+                nbytes = P * gemv_bytes(n, m, T, B)
+                legs[f"mlp_{name}_T{T}_b{B}"] = {
+                    "shape": f"{2 * n}x{2 * m}", "layers_per_launch": P, "us_per_launch": round(us, 2),
+                    "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "kernel": kern}
+            del pool, spool, q
+        del R
+    torch.cuda.empty_cache()
     return legs
 
 
@@ -496,6 +559,8 @@ def main():
     }
     if not args.no_stack:
         out["legs"].update(stack_legs(f2, torch, dev, T, reps=5))
+    if not args.no_mlp:
+        out["legs"].update(mlp_legs(f2, torch, workloads, dev))
     if not args.no_cpu_baseline:
         x1 = workloads.activations(1, 2 * m, workloads.ATTN_X_SEEDS[1]).values
         out["cpu_baseline"] = cpu_baseline(R_np, T, x1, args.cpu_seconds)
