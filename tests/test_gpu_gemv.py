@@ -440,19 +440,22 @@ def test_strided_pool_full_size(algo, B):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("n,m,T,ydt", [
-    (1000, 192, 2, "f32"),      # one chunk per tile: every stream step starts a new tile
+    (1000, 192, 2, "f32"),      # one chunk per tile: the split tiles' extra waves stream nothing
     (1000, 192, 1, "bf16"),
     (1000, 2112, 2, "f32"),     # nine chunks, the last one of a single 64-column group
-    (1000, 2112, 1, "bf16"),
+    (1000, 2112, 3, "bf16"),
 ])
 def test_large_f4_launch_matches_single_launches(n, m, T, ydt):
-    """A batch-1 fp4 launch of 3780 ragged tiles (one wave per tile, more tiles than the chip keeps
-    resident) against each matrix's own single-matrix launch: bit for bit where that launch also
-    gives one wave per tile (a single chunk), else within 1e-6 relative L2 for fp32 outputs (its
-    waves split the chunks, so its fp32 epilogue adds in another order; bf16 outputs within their
-    own tolerance); the first and last are within tolerance of the oracle."""
+    """Batch-1 fp4 launches of 12600 ragged tiles (200 matrices of 63 tiles): the first tiles one
+    wave each, the last 3072 split over four waves whose exact integer sums meet before the
+    epilogue.  Both halves of the batch launched on their own (6300 tiles: one wave per tile
+    throughout) give the same outputs bit for bit; every matrix is within 1e-6 relative L2 (fp32
+    outputs) of its single-matrix launch, whose waves split the chunks and add fp32 partial
+    outputs in another order (bit for bit where that launch also has one wave per tile, a single
+    chunk; bf16 outputs within their own tolerance); the first and last are within tolerance of
+    the oracle."""
     dev = device()
-    batch = 60
+    batch = 200
     act = workloads.activations(1, 2 * m, seed=4242 + m)
     x = f2.fairy2i_x_digits_f6(x_to_dev(act, dev))
     pb = f2.fairy2i_packed_bytes(n, m, T)
@@ -470,13 +473,18 @@ def test_large_f4_launch_matches_single_launches(n, m, T, ydt):
     y = torch.full((batch, 1, 2 * n), float("nan"), dtype=ydtype, device=dev)
     announce("large f4 launch", n, m, T, batch, ydt)
     f2.fairy2i_gemv_strided(packed, scales, x, y, algo=f2.GEMV_MFMA_F4)
+    yh = torch.full_like(y, float("nan"))
+    h = batch // 2
+    f2.fairy2i_gemv_strided(packed[:h], scales[:h], x, yh[:h], algo=f2.GEMV_MFMA_F4)
+    f2.fairy2i_gemv_strided(packed[h:], scales[h:], x, yh[h:], algo=f2.GEMV_MFMA_F4)
     ys = torch.full_like(y, float("nan"))
     for k in range(batch):
         f2.fairy2i_gemv(packed[k], scales[k], x, y=ys[k], algo=f2.GEMV_MFMA_F4)
     torch.cuda.synchronize()
+    assert torch.equal(y, yh)
     if m <= 256:
         assert torch.equal(y, ys)
-    else:                    # bf16: one rounding step apart at most where the fp32 values differ
+    else:
         tol = 1e-6 if ydt == "f32" else 2e-3
         for k in range(batch):
             assert rel_l2(down(y[k].float()), down(ys[k].float())) <= tol, k

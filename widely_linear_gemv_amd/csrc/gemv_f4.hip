@@ -184,10 +184,19 @@ hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blo
 
 // ------------------------------------------------------------------------- GEMV ----
 
-template <int TT, int NW, int BT, typename YT>
-__global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_gemv_f4(const GemvGroup grp, int m, int B) {
+// One unit (a 16-row tile of one item) streamed by NW cooperating waves; `wave` is this wave's
+// index among them, s_scw its own LDS slot for the tile's scales, s_y the NW waves' partial outputs.
+// EXACT (NW = 4, one batch entry): the waves first add their accumulators through LDS (s_acc,
+// 16 T x 64 floats per wave) -- exact, since every partial and total is an integer below 2^24 --
+// and wave w then runs the single-wave epilogue for rows 4g + w, so the outputs are bit-identical
+// to one wave streaming the whole unit.
+template <int TT, int NW, int BT, typename YT, bool EXACT = false>
+__device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B, int unit, int wave,
+                                             float* __restrict__ s_scw, float (*s_y)[BT][2][16],
+                                             float* __restrict__ s_acc = nullptr) {
+  static_assert(!EXACT || (NW == 4 && BT == 1), "the exact split is for four waves and one batch entry");
   int tile;
-  const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
+  const GemvItem it = locate_item<YT>(grp, unit, tile);
   const int n = it.n;
   const uint8_t* __restrict__ packed = static_cast<const uint8_t*>(it.packed);
   const float* __restrict__ scales = it.scales;
@@ -195,7 +204,6 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
   YT* __restrict__ y = static_cast<YT*>(it.y);
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int r = lane & 15, g = lane >> 4;
   const int i0 = tile * 16;
   const int nchunk = (m + kF4Chunk - 1) / kF4Chunk;
@@ -264,7 +272,6 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
   // the compute it overlaps (the scheduler would otherwise sink the loads to their use).  Every
   // prefetch is issued, so every path has the same loads in flight; one past the last chunk has a
   // negative group count and so loads at the out-of-range offset, which reads nothing.
-  __shared__ float s_sc[NW][16 * TT * 4];
   TileScales<TT> tsc;
   tsc.load(scales, i0, n, lane);               // ahead of the first chunk's loads
   if constexpr (BT == 1 && TT <= 2) {
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
     int c = wave;                                  // wave w takes chunks w, w + NW, ...
     load_chunk(c, c0);
     load_chunk(c + NW, c1);
-    tsc.park(s_sc[wave], lane);
+    tsc.park(s_scw, lane);
     for (; c + 2 * NW < nchunk; c += 3 * NW) {
       load_chunk(c + 2 * NW, c2);
       __builtin_amdgcn_sched_barrier(0);
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
     Chunk c0, c1;
     int c = wave;
     load_chunk(c, c0);
-    tsc.park(s_sc[wave], lane);
+    tsc.park(s_scw, lane);
     for (; c + NW < nchunk; c += 2 * NW) {
       load_chunk(c + NW, c1);
       __builtin_amdgcn_sched_barrier(0);
@@ -306,7 +313,29 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
   // P = (Su + Sv) / 2, Q = (Su - Sv) / 2 (exact), then the widely-linear combination with the
   // fp32 scales, the digit weight 2^(3l - S_b) / 6, and the sum over digits (xor 1, 2, 4) and
   // components (xor 8).
-  __shared__ float s_y[NW > 1 ? NW : 1][BT][2][16];     // [wave][batch][re/im][row]
+  if constexpr (EXACT) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int M = 0; M < 2; ++M)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s_acc[((wave * TT * 4 + (t * 2 + M) * 2 + p) * 4 + e) * kWave + lane] = acc[t][M][p][0][e];
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int M = 0; M < 2; ++M)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          float v = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) v += s_acc[((w * TT * 4 + (t * 2 + M) * 2 + p) * 4 + wave) * kWave + lane];
+          acc[t][M][p][0][wave & 3] = v;    // this wave's rows: e = wave
+        }
+  }
   const int comp = r >> 3, l = r & 7;
   const int* hdr = reinterpret_cast<const int*>(blob);
   const int64_t ys = 2 * (int64_t)n;
@@ -316,8 +345,9 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
     const float wdig = ldexpf(1.0f / 6.0f, 3 * l - S);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
+      if (EXACT && e != wave) continue;
       const int i = i0 + 4 * g + e;
-      const float* sc = &s_sc[wave][(4 * g + e) * TT * 4];
+      const float* sc = &s_scw[(4 * g + e) * TT * 4];
       float vre = 0.f, vim = 0.f;
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
@@ -341,7 +371,7 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
         vre += __shfl_xor(vre, off);
         vim += __shfl_xor(vim, off);
       }
-      if (NW > 1) {
+      if (NW > 1 && !EXACT) {
         if (r == 0) { s_y[wave][b][0][4 * g + e] = vre; s_y[wave][b][1][4 * g + e] = vim; }
       } else if (r == 0 && b < B && i < n) {
         store_out(y, (int64_t)b * ys + i, vre);
@@ -349,7 +379,7 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
       }
     }
   }
-  if constexpr (NW > 1) {
+  if constexpr (NW > 1 && !EXACT) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < BT * 2 * 16; idx += kWave * NW) {
       const int row = idx & 15, part = (idx >> 4) & 1, b = idx >> 5;
@@ -363,11 +393,49 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
   }
 }
 
+template <int TT, int NW, int BT, typename YT>
+__global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_gemv_f4(const GemvGroup grp, int m, int B) {
+  __shared__ float s_sc[NW][16 * TT * 4];
+  __shared__ float s_y[NW > 1 ? NW : 1][BT][2][16];     // [wave][batch][re/im][row]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
+  gemv_f4_tile<TT, NW, BT, YT>(grp, m, B, blockIdx.x, wave, s_sc[wave], s_y);
+}
+
+// Large batch-1 launches in two granularities.  The first nA workgroups take four units each,
+// one wave per unit (the fastest form while the chip is full); the rest take one unit each, its
+// chunks split over the four waves.  Workgroups start in index order, so the units that finish a
+// launch are the short-lived ones: the launch's tail, where fewer and fewer waves remain in
+// flight, lasts about a quarter as long.  Both forms give the single-wave kernel's outputs bit for
+// bit (the split one adds its waves' exact integer accumulators before the epilogue).
+template <int TT, typename YT>
+__global__ __launch_bounds__(kWave * 4, 3) void k_gemv_f4_mixed(const GemvGroup grp, int m, int nA) {
+  __shared__ float s_sc[4][16 * TT * 4];
+  __shared__ float s_y[4][1][2][16];
+  __shared__ float s_acc[4 * 16 * TT * kWave];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
+  if ((int)blockIdx.x < nA)
+    gemv_f4_tile<TT, 1, 1, YT>(grp, m, 1, 4 * (int)blockIdx.x + wave, 0, s_sc[wave], s_y);
+  else
+    gemv_f4_tile<TT, 4, 1, YT, true>(grp, m, 1, 4 * nA + ((int)blockIdx.x - nA), wave, s_sc[wave], s_y, s_acc);
+}
+
+// Mixed-granularity launches: units left to the one-unit-per-workgroup form at the end (about one
+// wave lifetime of the whole chip's stream), and the smallest launch that uses them.
+constexpr int kF4TailTiles = 3072;
+constexpr int kF4MixedMinTiles = 4 * kF4TailTiles;
+
 template <int TT, int BT, typename YT>
 static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
   GemvGroup grp = group;
   grp.units_per_item = grp.tiles_per_item;        // one workgroup per tile
   const int tiles = group_tiles(grp);
+  if constexpr (BT == 1 && TT <= 3) {
+    if (gemv_waves_per_tile(tiles, m) == 1 && tiles >= kF4MixedMinTiles) {
+      const int nA = (tiles - kF4TailTiles) / 4;          // four units per workgroup
+      hipLaunchKernelGGL((k_gemv_f4_mixed<TT, YT>), dim3(nA + (tiles - 4 * nA)), dim3(4 * kWave), 0, s, grp, m, nA);
+      return;
+    }
+  }
   const dim3 grid(tiles);
   switch (gemv_waves_per_tile(tiles, m)) {
     case 8: hipLaunchKernelGGL((k_gemv_f4<TT, 8, BT, YT>), grid, dim3(8 * kWave), 0, s, grp, m, B); break;
