@@ -505,7 +505,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gemv_f4_mixed (strided batch over the pool, batch 1; one wave per tile, the last 3072 tiles four waves each)",
+            "kernel": "k_gemv_f4_mixed (strided batch over the pool, batch 1; one wave per tile, the last 1536 tiles four waves each)",
             "achieved": round(roof_gbs, 2),
             "us_per_launch": round(roof_launch_us, 3),
             "peak": HBM_PEAK_GBS,

@@ -447,7 +447,7 @@ def test_strided_pool_full_size(algo, B):
 ])
 def test_large_f4_launch_matches_single_launches(n, m, T, ydt):
     """Batch-1 fp4 launches of 12600 ragged tiles (200 matrices of 63 tiles): the first tiles one
-    wave each, the last 3072 split over four waves whose exact integer sums meet before the
+    wave each, the last 1536 split over four waves whose exact integer sums meet before the
     epilogue.  Both halves of the batch launched on their own (6300 tiles: one wave per tile
     throughout) give the same outputs bit for bit; every matrix is within 1e-6 relative L2 (fp32
     outputs) of its single-matrix launch, whose waves split the chunks and add fp32 partial

@@ -419,10 +419,12 @@ __global__ __launch_bounds__(kWave * 4, 3) void k_gemv_f4_mixed(const GemvGroup 
     gemv_f4_tile<TT, 4, 1, YT, true>(grp, m, 1, 4 * nA + ((int)blockIdx.x - nA), wave, s_sc[wave], s_y, s_acc);
 }
 
-// Mixed-granularity launches: units left to the one-unit-per-workgroup form at the end (about one
-// wave lifetime of the whole chip's stream), and the smallest launch that uses them.
-constexpr int kF4TailTiles = 3072;
-constexpr int kF4MixedMinTiles = 4 * kF4TailTiles;
+// Mixed-granularity launches: units left to the one-unit-per-workgroup form at the end, and the
+// smallest launch that uses them (measured on the 1 GiB pool, 32768 tiles: tails of 256-2048 tiles
+// within 1 % of each other and ~2 % faster than 3072-6144; launches of 6144 tiles ran slower in
+// this form, 16512 unchanged).
+constexpr int kF4TailTiles = 1536;
+constexpr int kF4MixedMinTiles = 12288;
 
 template <int TT, int BT, typename YT>
 static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
