@@ -32,7 +32,9 @@
 //    (or NW waves splitting the 256-column chunks for small launches), one 1 KB load per plane
 //    and chunk, the next chunk prefetched while the current one is decoded and multiplied.  In
 //    a chunk lane l = 16g + r holds row r, columns 64g..64g+63 (four words); MFMA step s < 2
-//    takes words 2s and 2s+1.
+//    takes words 2s and 2s+1.  Large batch-1 launches end on tiles split over four waves, whose
+//    exact integer accumulators are added before the epilogue (k_gemv_f4_mixed): the outputs
+//    are those of one wave per tile, bit for bit, and the launch's tail is short-lived waves.
 #include "common.hpp"
 #include "digits.hpp"
 
