@@ -439,25 +439,27 @@ def test_strided_pool_full_size(algo, B):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("n,m,T,ydt", [
-    (1000, 192, 2, "f32"),      # one chunk per tile: the split tiles' extra waves stream nothing
-    (1000, 192, 1, "bf16"),
-    (1000, 2112, 2, "f32"),     # nine chunks, the last one of a single 64-column group
-    (1000, 2112, 3, "bf16"),
+@pytest.mark.parametrize("algo,n,m,T,ydt", [
+    ("f4", 1000, 192, 2, "f32"),      # one chunk per tile: the split tiles' extra waves stream nothing
+    ("f4", 1000, 192, 1, "bf16"),
+    ("f4", 1000, 2112, 2, "f32"),     # nine chunks, the last one of a single 64-column group
+    ("f4", 1000, 2112, 3, "bf16"),
+    ("i8", 1000, 192, 2, "f32"),
+    ("i8", 1000, 2112, 4, "f32"),
 ])
-def test_large_f4_launch_matches_single_launches(n, m, T, ydt):
-    """Batch-1 fp4 launches of 12600 ragged tiles (200 matrices of 63 tiles): the first tiles one
-    wave each, the last 1536 split over four waves whose exact integer sums meet before the
-    epilogue.  Both halves of the batch launched on their own (6300 tiles: one wave per tile
-    throughout) give the same outputs bit for bit; every matrix is within 1e-6 relative L2 (fp32
-    outputs) of its single-matrix launch, whose waves split the chunks and add fp32 partial
-    outputs in another order (bit for bit where that launch also has one wave per tile, a single
-    chunk; bf16 outputs within their own tolerance); the first and last are within tolerance of
-    the oracle."""
+def test_large_digit_launch_matches_single_launches(algo, n, m, T, ydt):
+    """Batch-1 fp4 and int8 launches of 12600 ragged tiles (200 matrices of 63 tiles).  The fp4
+    launch takes its first tiles one wave each and the last 1536 split over four waves whose exact
+    integer sums meet before the epilogue; the int8 launch takes one wave per tile throughout.
+    Both halves of the batch launched on their own (6300 tiles: one wave per tile) give the same
+    outputs bit for bit; every matrix is within 1e-6 relative L2 (fp32 outputs) of its
+    single-matrix launch, whose waves split the chunks and add fp32 partial outputs in another
+    order (bit for bit where that launch also has one wave per tile, a single chunk; bf16 outputs
+    within their own tolerance); the first and last are within tolerance of the oracle."""
     dev = device()
     batch = 200
     act = workloads.activations(1, 2 * m, seed=4242 + m)
-    x = f2.fairy2i_x_digits_f6(x_to_dev(act, dev))
+    x = DIGITS[algo](x_to_dev(act, dev))
     pb = f2.fairy2i_packed_bytes(n, m, T)
     packed = torch.empty((batch, pb), dtype=torch.uint8, device=dev)
     scales = torch.empty((batch, n, T, 2, 2), dtype=torch.float32, device=dev)
@@ -471,15 +473,15 @@ def test_large_f4_launch_matches_single_launches(n, m, T, ydt):
             host[k] = (codes, sc)
     ydtype = torch.float32 if ydt == "f32" else torch.bfloat16
     y = torch.full((batch, 1, 2 * n), float("nan"), dtype=ydtype, device=dev)
-    announce("large f4 launch", n, m, T, batch, ydt)
-    f2.fairy2i_gemv_strided(packed, scales, x, y, algo=f2.GEMV_MFMA_F4)
+    announce("large launch", algo, n, m, T, batch, ydt)
+    f2.fairy2i_gemv_strided(packed, scales, x, y, algo=ALGOS[algo])
     yh = torch.full_like(y, float("nan"))
     h = batch // 2
-    f2.fairy2i_gemv_strided(packed[:h], scales[:h], x, yh[:h], algo=f2.GEMV_MFMA_F4)
-    f2.fairy2i_gemv_strided(packed[h:], scales[h:], x, yh[h:], algo=f2.GEMV_MFMA_F4)
+    f2.fairy2i_gemv_strided(packed[:h], scales[:h], x, yh[:h], algo=ALGOS[algo])
+    f2.fairy2i_gemv_strided(packed[h:], scales[h:], x, yh[h:], algo=ALGOS[algo])
     ys = torch.full_like(y, float("nan"))
     for k in range(batch):
-        f2.fairy2i_gemv(packed[k], scales[k], x, y=ys[k], algo=f2.GEMV_MFMA_F4)
+        f2.fairy2i_gemv(packed[k], scales[k], x, y=ys[k], algo=ALGOS[algo])
     torch.cuda.synchronize()
     assert torch.equal(y, yh)
     if m <= 256:
