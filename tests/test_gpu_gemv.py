@@ -415,8 +415,9 @@ def test_strided_batch_matches_grouped_and_oracle(algo, B, n, m, T, batch, ydt):
 @pytest.mark.parametrize("algo,B", [("f4", 1), ("i8", 1), ("bf16", 4)])
 def test_strided_pool_full_size(algo, B):
     """The benchmark's own launch: the quantized 4096 x 4096 attention layer repeated 256 times back
-    to back (1 GiB, one strided launch of 32768 workgroups); every copy's output equals the
-    oracle's for that layer within tolerance, and all copies are bit-identical."""
+    to back (1 GiB, 32768 tiles in one strided launch; at batch 1 the fp4 launch splits its last
+    tiles over four waves each); every copy's output equals the oracle's for that layer within
+    tolerance, and all copies are bit-identical."""
     dev = device()
     codes, s32 = attention_layer()
     P = 256
