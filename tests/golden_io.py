@@ -104,3 +104,14 @@ def order_sum_cases():
         entries = {int(a): float(b) for a, b in (e.split(":") for e in f[1:])}
         out.append((m, entries, float(right)))
     return out
+
+
+def tensor_order_cases():
+    """-> [(n, {row: Re U value}, expected per-tensor s_re)] from tensor_order.txt."""
+    out = []
+    for s in lines("tensor_order.txt"):
+        left, right = s.split("->")
+        f = left.split()
+        rows = {int(a): float(int(b)) for a, b in (e.split(":") for e in f[1:])}
+        out.append((int(f[0]), rows, float(int(right))))
+    return out

@@ -474,3 +474,19 @@ def check_per_tensor_scales(quantize, split, seed=21, T=2):
     assert np.all(codes[0, 0] == 0) and s64[0, 0, 0, 0] == 3.0 and s64[1, 0, 0, 0] == 3.0
     codes, _, s64, _ = quantize(Rh, 1)
     assert s64[0, 0, 0, 0] == 2.0 and s64[1, 0, 0, 0] == 4.0
+
+
+def check_per_tensor_order(quantize):
+    """The per-tensor scale combines its row sums in the pinned order (hand-worked cases in
+    tests/golden/tensor_order.txt, where a plain left-to-right or adjacent-pair order gives a
+    different fp64 value)."""
+    for n, rows, want in golden_io.tensor_order_cases():
+        R = np.zeros((2 * n, 2), dtype=np.float32)
+        for i, v in rows.items():
+            R[i, 0] = v            # R11 = Re U + Re W
+            R[n + i, 1] = v        # R22 = Re U - Re W  -> Re U = v, W = 0
+        codes, _, s64, _ = quantize(R, 1, per_tensor=True)
+        assert np.all(codes == 0)
+        assert s64[0, 0, 0, 0] == want, (n, s64[0, 0, 0, 0], want)
+        assert np.all(s64[:, 0, 0, 1] == 0.0) and np.all(s64[:, 0, 1] == 0.0)
+

@@ -209,3 +209,20 @@ def test_tensor_scales_feed_gemv():
     y = down(f2.fairy2i_gemv(out["packed"], out["scales"], xd, algo=f2.GEMV_MFMA_I8))
     codes, s32, _, _ = oracle.quantize(R, T, per_tensor=True)
     assert rel_l2(y, oracle.gemv_ref(codes, s32, act.values)) <= TOL_F32
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_tensor_scales_order_cases(case):
+    """The hand-worked order cases of tests/golden/tensor_order.txt, widened to m = 64 (the
+    value in column 0, zeros elsewhere: the row sums are unchanged and the count is 64 n): the
+    per-tensor fp64 scale must come out in the pinned combining order, bit for bit."""
+    import golden_io
+    dev = device()
+    n, rows, _ = golden_io.tensor_order_cases()[case]
+    m = 64
+    R = np.zeros((2 * n, 2 * m), dtype=np.float32)
+    for i, v in rows.items():
+        R[i, 0] = v
+        R[n + i, m] = v
+    announce("quantize per-tensor order case", case, n)
+    assert_tensor_match(R, 1, gpu_quantize_tensor(R, 1, dev), f"order case {case}")

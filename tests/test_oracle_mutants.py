@@ -219,3 +219,26 @@ def test_per_tensor_mean_of_row_means_caught():
             s32 = s64.astype(np.float32)
         return codes, s32, s64, norms
     fails(pins.check_per_tensor_scales, bad, oracle.split)
+
+
+def test_per_tensor_plain_row_sum_caught(monkeypatch):
+    """Combining the row sums with np.sum (numpy's own order) instead of the pinned order fails
+    the hand-worked order cases."""
+    def bad_mean(row_sums, row_counts):
+        count = int(np.sum(row_counts))
+        return float(np.sum(np.asarray(row_sums, dtype=np.float64))) / count if count > 0 else 0.0
+    monkeypatch.setattr(pq, "_tensor_mean", bad_mean)
+    fails(pins.check_per_tensor_order, oracle.quantize)
+
+
+def test_per_tensor_sequential_row_sum_caught(monkeypatch):
+    """Rows added left to right fail the hand-worked order cases as well."""
+    def bad_mean(row_sums, row_counts):
+        total = 0.0
+        for v in np.asarray(row_sums, dtype=np.float64):
+            total = total + float(v)
+        count = int(np.sum(row_counts))
+        return total / count if count > 0 else 0.0
+    monkeypatch.setattr(pq, "_tensor_mean", bad_mean)
+    fails(pins.check_per_tensor_order, oracle.quantize)
+

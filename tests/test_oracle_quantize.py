@@ -62,3 +62,7 @@ def test_dequantize_real_routes():
 
 def test_per_tensor_scales():
     pins.check_per_tensor_scales(oracle.quantize, oracle.split)
+
+
+def test_per_tensor_order():
+    pins.check_per_tensor_order(oracle.quantize)
