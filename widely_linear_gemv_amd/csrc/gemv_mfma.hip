@@ -49,6 +49,14 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 256;        // columns per chunk of the packed form
+// Long rows (the LONG kernels, rows of more than kFlushChunks chunks): a wave's accumulators take
+// at most kFlushChunks of its chunks (8 MFMA steps each) before their sums are applied to the
+// scales and added to per-lane output partials; the accumulators then restart from zero.  Each
+// fp32 sum so runs over at most 256 MFMA steps plus one output partial per kFlushChunks chunks,
+// instead of m / 32 steps in series, which keeps the rounding of the longest accepted rows (2^22
+// columns) within the fp32 tolerance.  Rows of up to 8192 columns (every LLaMA-2-7B shape) take
+// the plain kernels, whose registers the flush would otherwise crowd.
+constexpr int kFlushChunks = 32;
 
 // Eight codes (h = which half of the word) of one packed word -> A operands of both planes.
 template <int H>
@@ -90,7 +98,32 @@ __device__ __forceinline__ void combine_row(const v4f (&acc)[TT][2][2][CG], cons
   }
 }
 
-template <int TT, int CG, int NW, typename YT>
+// Applies the accumulated sums of every row and column group to the tile's scales, adds them to
+// the output partials and clears the accumulators (long rows; see kFlushChunks).
+template <int TT, int CG>
+__device__ __forceinline__ void flush_partials(v4f (&acc)[TT][2][2][CG], const float* s_scw, int g, int comp,
+                                               float (&ypart)[4][CG][2], bool& flushed) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      float vre, vim;
+      combine_row<TT, CG>(acc, &s_scw[(4 * g + e) * TT * 4], e, cg, comp, vre, vim);
+      ypart[e][cg][0] = flushed ? ypart[e][cg][0] + vre : vre;
+      ypart[e][cg][1] = flushed ? ypart[e][cg][1] + vim : vim;
+    }
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int M = 0; M < 2; ++M)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg) acc[t][M][p][cg] = v4f{0.f, 0.f, 0.f, 0.f};
+  flushed = true;
+}
+
+template <int TT, int CG, int NW, typename YT, bool LONG>
 __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, int m, int B) {
   int tile;
   const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
@@ -179,11 +212,14 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
   // prefetch is unconditional, so every path has the same loads in flight; one past the last
   // chunk has a negative group count and loads at the out-of-range offset (reads nothing).
   __shared__ float s_sc[NW][16 * TT * 4];
+  float ypart[4][CG][2];                         // output partials of long rows
+  bool flushed = false;
   TileScales<TT> tsc;
   tsc.load(scales, i0, n, lane);               // ahead of the first chunk's loads
   {
     Chunk c0, c1;
     int c = wave;                                  // wave w takes chunks w, w + NW, ...
+    int pairs = 0;
     load_chunk(c, c0);
     tsc.park(s_sc[wave], lane);
     for (; c + NW < nchunk; c += 2 * NW) {
@@ -193,6 +229,12 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
       load_chunk(c + 2 * NW, c0);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk(c1);
+      if constexpr (LONG) {
+        if (++pairs == kFlushChunks / 2 && c + 2 * NW < nchunk) {   // wave-uniform
+          pairs = 0;
+          flush_partials<TT, CG>(acc, s_sc[wave], g, comp, ypart, flushed);
+        }
+      }
     }
     if (c < nchunk) compute_chunk(c0);
   }
@@ -210,6 +252,10 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, i
     for (int cg = 0; cg < CG; ++cg) {
       float vre, vim;
       combine_row<TT, CG>(acc, sc, e, cg, comp, vre, vim);
+      if (LONG && flushed) {
+        vre = ypart[e][cg][0] + vre;
+        vim = ypart[e][cg][1] + vim;
+      }
       vre += __shfl_xor(vre, 1);
       vim += __shfl_xor(vim, 1);
       const int b = cg * 8 + (r >> 1);
@@ -243,7 +289,7 @@ constexpr int kSxPitch = 2 * kChunk + 16;  // LDS bytes per (batch, component) r
 // past an item's last read no codes and store nothing.  Per chunk the workgroup stages x[b][comp][256 columns] (bf16, permuted per 8
 // columns) in one of two LDS buffers, one 16-byte unit per thread and column group, and waits
 // once; codes are loaded one chunk ahead as in k_gemv_mfma.
-template <int TT, int CG, typename YT>
+template <int TT, int CG, typename YT, bool LONG>
 __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGroup grp, int m, int B) {
   constexpr int kXRows = 16 * CG;                 // (batch, component) rows of the B operand
   constexpr int kSeg = kXRows * (2 * kChunk / 16) / (kWave * kSxWaves);   // 16-byte units per thread
@@ -336,6 +382,8 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
   };
 
   __shared__ float s_sc[kSxWaves][16 * TT * 4];
+  float ypart[4][CG][2];                         // output partials of long rows
+  bool flushed = false;
   TileScales<TT> tsc;
   tsc.load(scales, i0, n, lane);               // ahead of the first chunk's loads
   uint4 w0[TT][2], w1[TT][2];
@@ -352,6 +400,10 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
     __builtin_amdgcn_sched_barrier(0);
     compute_chunk(c & 1, w0);
     store_x((c & 1) ^ 1, st);                // its last readers passed the previous barrier
+    if constexpr (LONG) {
+      if ((c & (kFlushChunks - 1)) == kFlushChunks - 1 && c + 1 < nchunk)
+        flush_partials<TT, CG>(acc, s_sc[wave], g, comp, ypart, flushed);
+    }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < TT; ++t) { w0[t][0] = w1[t][0]; w0[t][1] = w1[t][1]; }
@@ -367,6 +419,10 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
     for (int cg = 0; cg < CG; ++cg) {
       float vre, vim;
       combine_row<TT, CG>(acc, sc, e, cg, comp, vre, vim);
+      if (LONG && flushed) {
+        vre = ypart[e][cg][0] + vre;
+        vim = ypart[e][cg][1] + vim;
+      }
       vre += __shfl_xor(vre, 1);
       vim += __shfl_xor(vim, 1);
       const int b = cg * 8 + (r >> 1);
@@ -378,11 +434,12 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
   }
 }
 
-template <int TT, int CG, typename YT>
+template <int TT, int CG, typename YT, bool LONG>
 static void launch_cg(const GemvGroup& group, int m, int B, hipStream_t s) {
   GemvGroup grp = group;
   const int tiles = group_tiles(grp);
-  const int nw = gemv_waves_per_tile(tiles, m);
+  int nw = gemv_waves_per_tile(tiles, m);
+  if (LONG && nw > 1) nw = 4;              // long rows have more than 4 chunks
   if (nw == 1 && B >= 3) {                 // large launch, batch 3-16: shared x
     int blocks = 0;
     if (grp.batch > 0) {
@@ -395,23 +452,34 @@ static void launch_cg(const GemvGroup& group, int m, int B, hipStream_t s) {
       }
       grp.tile_start[grp.count] = blocks;
     }
-    hipLaunchKernelGGL((k_gemv_mfma_sx<TT, CG, YT>), dim3(blocks), dim3(kSxWaves * kWave), 0, s, grp, m, B);
+    hipLaunchKernelGGL((k_gemv_mfma_sx<TT, CG, YT, LONG>), dim3(blocks), dim3(kSxWaves * kWave), 0, s, grp, m, B);
     return;
   }
   grp.units_per_item = grp.tiles_per_item;        // one workgroup per tile
   const dim3 grid(tiles);
+  if constexpr (LONG) {
+    if (nw == 4) hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 4, YT, true>), grid, dim3(4 * kWave), 0, s, grp, m, B);
+    else hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 1, YT, true>), grid, dim3(kWave), 0, s, grp, m, B);
+    return;
+  }
   switch (nw) {
-    case 8: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 8, YT>), grid, dim3(8 * kWave), 0, s, grp, m, B); break;
-    case 4: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 4, YT>), grid, dim3(4 * kWave), 0, s, grp, m, B); break;
-    case 2: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 2, YT>), grid, dim3(2 * kWave), 0, s, grp, m, B); break;
-    default: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 1, YT>), grid, dim3(kWave), 0, s, grp, m, B); break;
+    case 8: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 8, YT, false>), grid, dim3(8 * kWave), 0, s, grp, m, B); break;
+    case 4: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 4, YT, false>), grid, dim3(4 * kWave), 0, s, grp, m, B); break;
+    case 2: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 2, YT, false>), grid, dim3(2 * kWave), 0, s, grp, m, B); break;
+    default: hipLaunchKernelGGL((k_gemv_mfma<TT, CG, 1, YT, false>), grid, dim3(kWave), 0, s, grp, m, B); break;
   }
 }
 
 template <int TT, typename YT>
 static void launch_t(const GemvGroup& grp, int m, int B, hipStream_t s) {
-  if (B <= 8) launch_cg<TT, 1, YT>(grp, m, B, s);
-  else launch_cg<TT, 2, YT>(grp, m, B, s);
+  const bool long_rows = (m + kChunk - 1) / kChunk > kFlushChunks;
+  if (B <= 8) {
+    if (long_rows) launch_cg<TT, 1, YT, true>(grp, m, B, s);
+    else launch_cg<TT, 1, YT, false>(grp, m, B, s);
+  } else {
+    if (long_rows) launch_cg<TT, 2, YT, true>(grp, m, B, s);
+    else launch_cg<TT, 2, YT, false>(grp, m, B, s);
+  }
 }
 
 hipError_t launch_gemv_mfma_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s) {

@@ -19,6 +19,8 @@
 
 namespace f2i {
 
+constexpr int kSegWords = 8;      // packed words per lane and row segment (64 * 8 * 16 = 8192 columns)
+
 template <typename XT> struct XLoad;
 template <> struct XLoad<float> {
   __device__ static void load16(const float* p, float* v) {
@@ -61,43 +63,50 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const uint8_t* __restrict__ p
     for (int b = 0; b < NB; ++b) { yr[b] = 0.f; yi[b] = 0.f; }
     for (int t = 0; t < T; ++t) {
       for (int M = 0; M < 2; ++M) {
-        // per-axis sums of +-a and +-b (a = Re x, b = Im x) over this plane's codes
-        float ra[NB], rb[NB], ia[NB], ib[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) { ra[b] = rb[b] = ia[b] = ib[b] = 0.f; }
-        for (int q = lane; q < dw_plane; q += kWave) {
-          const uint32_t w = words[tiled_word(i, t * 2 + M, q, m, T)];
-          const int j0 = q * 16;
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const int bb = b0 + b < B ? b0 + b : B - 1;    // padded columns repeat the last one
-            float xa[16], xb[16];
-            XLoad<XT>::load16(x + bb * xs + j0, xa);
-            XLoad<XT>::load16(x + bb * xs + m + j0, xb);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const uint32_t k = (w >> (8 * (r & 3) + 2 * (r >> 2))) & 3u;   // code j0 + r
-              const uint32_t sgn = (k & 2u) << 30;          // code 2 or 3: negate
-              const float va = __uint_as_float(__float_as_uint(xa[r]) ^ sgn);
-              const float vb = __uint_as_float(__float_as_uint(xb[r]) ^ sgn);
-              const bool on_im = (k & 1u) != 0;              // code 1 or 3: imaginary axis
-              ra[b] += on_im ? 0.f : va;
-              rb[b] += on_im ? 0.f : vb;
-              ia[b] += on_im ? va : 0.f;
-              ib[b] += on_im ? vb : 0.f;
-            }
-          }
-        }
         const int64_t so = (((int64_t)i * T + t) * 2 + M) * 2;
         const float s_re = scales[so], s_im = scales[so + 1];
+        // Segments of kSegWords words per lane (8192 columns): each segment's axis sums are
+        // applied to the scales and added to the outputs, so no fp32 sum of a long row runs over
+        // more than 128 codes or m / 8192 segments in series.  Rows of up to 8192 columns are
+        // one segment.
+        for (int q0 = 0; q0 < dw_plane; q0 += kWave * kSegWords) {
+          const int q1 = min(dw_plane, q0 + kWave * kSegWords);
+          // per-axis sums of +-a and +-b (a = Re x, b = Im x) over this segment's codes
+          float ra[NB], rb[NB], ia[NB], ib[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if (M == 0) {   // U x:       Re = s_re*ra - s_im*ib ; Im = s_re*rb + s_im*ia
-            yr[b] += s_re * ra[b] - s_im * ib[b];
-            yi[b] += s_re * rb[b] + s_im * ia[b];
-          } else {        // W conj(x): Re = s_re*ra + s_im*ib ; Im = s_im*ia - s_re*rb
-            yr[b] += s_re * ra[b] + s_im * ib[b];
-            yi[b] += s_im * ia[b] - s_re * rb[b];
+          for (int b = 0; b < NB; ++b) { ra[b] = rb[b] = ia[b] = ib[b] = 0.f; }
+          for (int q = q0 + lane; q < q1; q += kWave) {
+            const uint32_t w = words[tiled_word(i, t * 2 + M, q, m, T)];
+            const int j0 = q * 16;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const int bb = b0 + b < B ? b0 + b : B - 1;    // padded columns repeat the last one
+              float xa[16], xb[16];
+              XLoad<XT>::load16(x + bb * xs + j0, xa);
+              XLoad<XT>::load16(x + bb * xs + m + j0, xb);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const uint32_t k = (w >> (8 * (r & 3) + 2 * (r >> 2))) & 3u;   // code j0 + r
+                const uint32_t sgn = (k & 2u) << 30;          // code 2 or 3: negate
+                const float va = __uint_as_float(__float_as_uint(xa[r]) ^ sgn);
+                const float vb = __uint_as_float(__float_as_uint(xb[r]) ^ sgn);
+                const bool on_im = (k & 1u) != 0;              // code 1 or 3: imaginary axis
+                ra[b] += on_im ? 0.f : va;
+                rb[b] += on_im ? 0.f : vb;
+                ia[b] += on_im ? va : 0.f;
+                ib[b] += on_im ? vb : 0.f;
+              }
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            if (M == 0) {   // U x:       Re = s_re*ra - s_im*ib ; Im = s_re*rb + s_im*ia
+              yr[b] += s_re * ra[b] - s_im * ib[b];
+              yi[b] += s_re * rb[b] + s_im * ia[b];
+            } else {        // W conj(x): Re = s_re*ra + s_im*ib ; Im = s_im*ia - s_re*rb
+              yr[b] += s_re * ra[b] + s_im * ib[b];
+              yi[b] += s_im * ia[b] - s_re * rb[b];
+            }
           }
         }
       }
