@@ -129,3 +129,68 @@ def test_act_quant_and_gemm_checks():
     raises("bytes", f2.fairy2i_gemm, packed, scales, x, workspace=ws[:-16])
     raises("GPU", f2.fairy2i_gemm, packed, scales, x, workspace=ws)
     raises("GPU", f2.fairy2i_gemm, packed, scales, q, x_scale=torch.zeros(N))
+
+
+class _Recorder:
+    """Stands in for the library: records each compute call's arguments (sizes and helpers go to
+    the real library).  Lets the CPU run every binding function through to its C call."""
+
+    def __init__(self, real):
+        self.real, self.calls = real, []
+
+    def __getattr__(self, name):
+        fn = getattr(self.real, name)
+        if name.endswith("_bytes") or name in ("fairy2i_last_error", "fairy2i_status_string"):
+            return fn
+
+        def record(*args):
+            self.calls.append((name, args))
+            return 0
+        return record
+
+
+@pytest.fixture
+def recorder(monkeypatch):
+    rec = _Recorder(f2.lib())
+    monkeypatch.setattr(f2, "lib", lambda: rec)
+    monkeypatch.setattr(f2, "_gpu", lambda *named: None)       # CPU tensors stand in for GPU ones
+    monkeypatch.setattr(f2, "_stream", lambda stream=None: None)
+    return rec
+
+
+def test_marshalling_reaches_the_c_call(recorder):
+    """Every binding function, given well-formed tensors, computes its C arguments (sizes, dtype
+    codes, strides) without error; the recorded integer arguments are the documented ones."""
+    R = torch.zeros((2 * n, 2 * m), dtype=torch.float32)
+    f2.fairy2i_quantize(R, T, want_scales64=True, want_codes=True)
+    f2.fairy2i_quantize(R.bfloat16(), T)
+    f2.fairy2i_quantize_tensor(R, T)
+    packed, scales = layer()
+    f2.fairy2i_pack(torch.zeros((T, 2, n, m), dtype=torch.uint8))
+    f2.fairy2i_dequantize(packed, scales, m, R_dtype=torch.bfloat16)
+    x = torch.zeros((B, 2 * m), dtype=torch.bfloat16)
+    xd = f2.fairy2i_x_digits_f6(x)
+    f2.fairy2i_x_digits(x)
+    f2.fairy2i_gemv(packed, scales, x)
+    f2.fairy2i_gemv(packed, scales, xd, algo=f2.GEMV_MFMA_F4)
+    f2.fairy2i_gemv_grouped([(packed, scales, x, torch.zeros((B, 2 * n)))] * 2)
+    f2.fairy2i_gemv_strided(packed.unsqueeze(0).expand(3, -1), scales, x, torch.zeros((3, B, 2 * n)))
+    f2.fairy2i_act_quant(x)
+    f2.fairy2i_gemm(packed, scales, x)
+    f2.fairy2i_gemm(packed, scales, x.float(), y_dtype=torch.int32)
+    names = [c[0] for c in recorder.calls]
+    assert names == ["fairy2i_quantize", "fairy2i_quantize_bf16", "fairy2i_quantize_tensor", "fairy2i_pack",
+                     "fairy2i_dequantize", "fairy2i_x_digits_f6", "fairy2i_x_digits", "fairy2i_gemv",
+                     "fairy2i_gemv", "fairy2i_gemv_grouped", "fairy2i_gemv_strided", "fairy2i_act_quant",
+                     "fairy2i_gemm", "fairy2i_gemm"]
+    args = dict((c[0] + str(k), c[1]) for k, c in enumerate(recorder.calls))
+    assert args["fairy2i_quantize0"][1:4] == (2 * n, 2 * m, T)
+    assert args["fairy2i_quantize_tensor2"][1:5] == (f2.F32, 2 * n, 2 * m, T)
+    assert args["fairy2i_pack3"][1:4] == (n, m, T)
+    assert args["fairy2i_dequantize4"][2:5] == (n, m, T) and args["fairy2i_dequantize4"][6] == f2.BF16
+    assert args["fairy2i_gemv7"][2:5] == (n, m, T) and args["fairy2i_gemv7"][6:8] == (f2.BF16, B)
+    assert args["fairy2i_gemv8"][6:8] == (f2.X_DIGITS_F6, B)
+    assert args["fairy2i_gemv_grouped9"][1:6] == (2, m, T, f2.BF16, B)
+    st = args["fairy2i_gemv_strided10"]
+    assert st[1] == 0 and st[3] == 0 and st[4:7] == (n, m, T) and st[11] == 2 * n * B and st[13] == 3
+    assert args["fairy2i_gemm13"][2:5] == (n, m, T) and args["fairy2i_gemm13"][10] == f2.I32

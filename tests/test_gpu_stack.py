@@ -73,3 +73,91 @@ def test_two_layer_stack(B, algo):
         g.replay()
         torch.cuda.synchronize()
         check(host, acts, step.ys, f"graph B={B} replay {rep}")
+
+
+SAMPLE_LAYERS = (0, 31)
+
+
+@pytest.fixture(scope="module")
+def stack_sample():
+    """Layers 0 and 31 of the 32-layer LLaMA-2-7B stack exactly as bench.py draws them (pinned
+    NumPy generator, seed 5000 + 7 L + p), quantized by the oracle at T = 2."""
+    import concurrent.futures
+    import os
+
+    device()                               # skips before the host work when there is no GPU
+
+    def one(key):
+        R = workloads.stack_layer(*key).weight()
+        return key, (R, oracle.quantize(R, T))
+
+    keys = [(L, p) for L in SAMPLE_LAYERS for p in range(len(PROJECTIONS))]
+    announce("oracle: quantizing the sampled stack layers on the host")
+    with concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:   # numpy releases the GIL
+        return dict(ex.map(one, keys))
+
+
+@pytest.mark.parametrize("L", SAMPLE_LAYERS)
+def test_stack_sample_quantize(stack_sample, L):
+    """Every projection of the sampled stack layers: packed bytes and fp64 / fp32 scales bit for
+    bit against the oracle."""
+    dev = device()
+    for p, (name, rows, cols, _) in enumerate(PROJECTIONS):
+        R, (codes, s32, s64, _) = stack_sample[(L, p)]
+        announce("stack quantize layer", L, name, rows, cols)
+        out = f2.fairy2i_quantize(up(R, dev), T, want_scales64=True)
+        assert np.array_equal(down(out["packed"]), oracle.pack(codes)), (L, name)
+        assert np.array_equal(down(out["scales64"]).view(np.uint64), s64.view(np.uint64)), (L, name)
+        assert np.array_equal(down(out["scales"]).view(np.uint32), s32.view(np.uint32)), (L, name)
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_stack_sample_decode_step(stack_sample, B):
+    """One decode step (the default kernels, eager and replayed from a HIP graph) over the two
+    sampled stack layers, quantized on the GPU: every output row of every projection against the
+    oracle GEMV on the oracle's own codes and scales."""
+    dev = device()
+    layers, xs, acts = [], [], []
+    for L in SAMPLE_LAYERS:
+        dl = []
+        for p in range(len(PROJECTIONS)):
+            R, _ = stack_sample[(L, p)]
+            q = f2.fairy2i_quantize(up(R, dev), T)
+            dl.append((q["packed"], q["scales"]))
+        layers.append(dl)
+        lx, la = [], []
+        for g in range(GROUPS):
+            cols = next(c for (_, _, c, grp) in PROJECTIONS if grp == g)
+            a = workloads.activations(B, cols, workloads.stack_x_seed(L, g))
+            la.append(a)
+            lx.append(x_to_dev(a, dev))
+        xs.append(lx)
+        acts.append(la)
+    import concurrent.futures
+    import os
+
+    def ref(kp):
+        k, p = kp
+        _, (codes, s32, _, _) = stack_sample[(SAMPLE_LAYERS[k], p)]
+        return oracle.gemv_ref(codes, s32, acts[k][PROJECTIONS[p][3]].values)
+
+    kps = [(k, p) for k in range(len(SAMPLE_LAYERS)) for p in range(len(PROJECTIONS))]
+    with concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        refs = list(ex.map(ref, kps))
+    want = [[refs[k * len(PROJECTIONS) + p] for p in range(len(PROJECTIONS))] for k in range(len(SAMPLE_LAYERS))]
+    step = DecodeStep(layers, xs)
+    announce("stack sample decode step B =", B, "eager")
+    ys = step.run()
+    for k, L in enumerate(SAMPLE_LAYERS):
+        for p in range(len(PROJECTIONS)):
+            assert rel_l2(down(ys[k][p]), want[k][p]) <= TOL_F32, ("eager", L, PROJECTIONS[p][0])
+    g = step.capture()
+    for row in step.ys:
+        for y in row:
+            y.fill_(float("nan"))
+    announce("stack sample decode step B =", B, "graph replay")
+    g.replay()
+    torch.cuda.synchronize()
+    for k, L in enumerate(SAMPLE_LAYERS):
+        for p in range(len(PROJECTIONS)):
+            assert rel_l2(down(step.ys[k][p]), want[k][p]) <= TOL_F32, ("graph", L, PROJECTIONS[p][0])

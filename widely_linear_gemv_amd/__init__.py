@@ -238,7 +238,7 @@ def fairy2i_quantize(R: torch.Tensor, T: int, *, want_scales64: bool = False,
     codes = torch.empty((T, 2, n, m), dtype=torch.uint8, device=dev) if want_codes else None
     fn = lib().fairy2i_quantize_bf16 if R.dtype == torch.bfloat16 else lib().fairy2i_quantize
     _gpu((R, "R"), (packed, "packed"), (scales, "scales"), (s64, "scales64"), (codes, "codes"))
-    _check(fn(_ptr(R), two_n, two_m, T, _ptr(packed), _ptr(scales), _ptr(s64), _ptr(codes), _stream(stream)))
+    _check(fn(_ptr(R), 2 * n, 2 * m, T, _ptr(packed), _ptr(scales), _ptr(s64), _ptr(codes), _stream(stream)))
     out = {"packed": packed, "scales": scales}
     if s64 is not None:
         out["scales64"] = s64
