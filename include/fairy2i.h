@@ -19,7 +19,7 @@
  *   - Each call checks its arguments on the host, enqueues its kernels on `stream` and
  *     returns; results are valid once the stream has reached that point.  The library never
  *     allocates device memory, keeps no pointer after returning and has no global state
- *     except a thread-local error message.
+ *     except a thread-local error message and the static device array of fairy2i_gemm_noalloc.
  *   - R x~ layout: R is fp32 row-major [2n][2m] (like nn.Linear.weight [out][in]);
  *     x~ = [Re x; Im x] and y~ = [Re y; Im y], i.e. a real vector of length 2m (2n) whose
  *     first half is the real part.  R's four quadrants are the blocks R11, R12, R21, R22.
@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FAIRY2I_ABI_VERSION 5
+#define FAIRY2I_ABI_VERSION 6
 
 typedef enum {
   FAIRY2I_OK = 0,
@@ -278,6 +278,24 @@ int fairy2i_gemm(const uint8_t* packed, const float* scales, int64_t n, int64_t 
                  const void* x, int x_dtype, float* x_scale, int64_t N,
                  void* y, int y_dtype, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
+
+/* fairy2i_gemm for callers that cannot allocate device memory -- code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc -- and so cannot pass a workspace.  Same
+ * arguments, results and checks as fairy2i_gemm without the workspace: when x is BF16 / F32 its
+ * per-token int8 activations and delta are staged in a static device array of the library (one
+ * per GPU, fairy2i_gemm_noalloc_max_bytes() = 32 MiB, held from the first call on that GPU until
+ * the process ends; the entry point and its kernels allocate nothing).  The call uses the array of
+ * the calling thread's current device; `stream` must belong to that device.
+ *   Limit: fairy2i_gemm_workspace_bytes(n, m, T, N, x_dtype) <= fairy2i_gemm_noalloc_max_bytes()
+ *   (for example 2048 tokens of 2m <= 16380 reals); a larger call returns FAIRY2I_ERR_WORKSPACE.
+ *   The array is shared by every call on a GPU and keeps the last call's contents (every byte a
+ *   call reads it has written first): calls that overlap on one GPU -- on different streams or
+ *   host threads without ordering -- race and must not be issued.  With x in I8 the array is not
+ *   used. */
+size_t fairy2i_gemm_noalloc_max_bytes(void);
+int fairy2i_gemm_noalloc(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
+                         const void* x, int x_dtype, float* x_scale, int64_t N,
+                         void* y, int y_dtype, hipStream_t stream);
 
 const char* fairy2i_status_string(int status);
 const char* fairy2i_last_error(void);   /* thread-local detail of the last non-OK return */

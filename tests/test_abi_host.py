@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert f2.fairy2i_abi_version() == 5
+    assert f2.fairy2i_abi_version() == 6
     for s in range(8):
         assert f2.fairy2i_status_string(s) not in ("", "unknown status")
     assert f2.fairy2i_status_string(99) == "unknown status"
@@ -284,3 +284,23 @@ def test_strided_binding_rejects_wrong_ranks():
         f2.fairy2i_gemv_strided(packed, scales[0, 0], x, torch.zeros(2, 1, 32))
     with pytest.raises(ValueError):
         f2.fairy2i_gemv_strided(packed, scales, x, torch.zeros(2, 32))
+
+
+def test_gemm_noalloc_errors(L):
+    """Argument errors of the entry point that allocates nothing, all caught on the host; a call
+    whose activation staging exceeds the static array is refused before any HIP call."""
+    g = L.fairy2i_gemm_noalloc
+    BF, F32, I8 = 1, 0, 2
+    assert g(NULL, FAKE, 64, 256, 2, FAKE, BF, NULL, 8, FAKE, F32, S) == 1
+    assert g(FAKE, FAKE, 64, 256, 2, FAKE, I8, NULL, 8, FAKE, F32, S) == 1     # int8 x needs delta
+    assert g(FAKE, FAKE, 64, 256, 2, FAKE, 9, NULL, 8, FAKE, F32, S) == 4
+    assert g(FAKE, FAKE, 64, 256, 2, FAKE, BF, NULL, 8, FAKE, 7, S) == 4
+    assert g(FAKE, FAKE, 64, 256, 5, FAKE, BF, NULL, 8, FAKE, F32, S) == 3
+    assert g(FAKE, FAKE, 64, 100, 2, FAKE, BF, NULL, 8, FAKE, F32, S) == 2
+    assert g(FAKE, FAKE, 64, 256, 2, FAKE, BF, NULL, 0, FAKE, F32, S) == 2
+    assert g(FAKE, FAKE, 64, 256, 2, FAKE_ODD, BF, NULL, 8, FAKE, F32, S) == 5
+    limit = L.fairy2i_gemm_noalloc_max_bytes()
+    assert limit == 32 << 20
+    N = limit // (2 * 2048) + 1
+    assert g(FAKE, FAKE, 64, 2048, 2, FAKE, BF, NULL, N, FAKE, F32, S) == 6
+    assert "static scratch" in last()

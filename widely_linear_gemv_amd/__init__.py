@@ -46,6 +46,8 @@ SIGNATURES = {
     "fairy2i_act_quant": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P]),
     "fairy2i_gemm_workspace_bytes": (_SZ, [_I64, _I64, _INT, _I64, _INT]),
     "fairy2i_gemm": (_INT, [_P, _P, _I64, _I64, _INT, _P, _INT, _P, _I64, _P, _INT, _P, _SZ, _P]),
+    "fairy2i_gemm_noalloc_max_bytes": (_SZ, []),
+    "fairy2i_gemm_noalloc": (_INT, [_P, _P, _I64, _I64, _INT, _P, _INT, _P, _I64, _P, _INT, _P]),
     "fairy2i_status_string": (ctypes.c_char_p, [_INT]),
     "fairy2i_last_error": (ctypes.c_char_p, []),
     "fairy2i_abi_version": (_INT, []),
@@ -536,3 +538,32 @@ def fairy2i_gemm(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, *,
                               _ptr(x_scale), N, _ptr(y), _DTYPE[y.dtype], _ptr(workspace), ws_bytes,
                               _stream(stream)))
     return y
+
+
+def fairy2i_gemm_noalloc_max_bytes() -> int:
+    return int(lib().fairy2i_gemm_noalloc_max_bytes())
+
+
+def fairy2i_gemm_noalloc(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, *,
+                         x_scale=None, y: torch.Tensor, stream=None):
+    """fairy2i_gemm without a workspace: the activation staging lives in the library's static
+    device array (calls on one GPU must not overlap).  y is preallocated by the caller (no
+    allocation at all here): float32/bfloat16 [N][2n], or int32 [T][2][2][2][N][n]."""
+    dev = _check_x(x, dtypes=(torch.float32, torch.bfloat16, torch.int8))
+    m = x.shape[1] // 2
+    N = x.shape[0]
+    n, T = _check_layer(packed, scales, m, dev)
+    if x_scale is not None or x.dtype == torch.int8:
+        _tensor(x_scale, "x_scale")
+        _dtype(x_scale, "x_scale", torch.float32)
+        _shape(x_scale, "x_scale", (N,))
+        _on_gpu(x_scale, "x_scale", dev)
+    _tensor(y, "y")
+    _dtype(y, "y", torch.float32, torch.bfloat16, torch.int32)
+    _shape(y, "y", (T, 2, 2, 2, N, n) if y.dtype == torch.int32 else (N, 2 * n))
+    _on_gpu(y, "y", dev)
+    _gpu((packed, "packed"), (scales, "scales"), (x, "x"), (x_scale, "x_scale"), (y, "y"))
+    _check(lib().fairy2i_gemm_noalloc(_ptr(packed), _ptr(scales), n, m, T, _ptr(x), _DTYPE[x.dtype],
+                                      _ptr(x_scale), N, _ptr(y), _DTYPE[y.dtype], _stream(stream)))
+    return y
+

@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace {
@@ -383,9 +385,12 @@ size_t fairy2i_gemm_workspace_bytes(int64_t n, int64_t m, int T, int64_t N, int 
   return align16((size_t)N * 2 * (size_t)m) + align16((size_t)N * 4);
 }
 
-int fairy2i_gemm(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
-                 const void* x, int x_dtype, float* x_scale, int64_t N, void* y, int y_dtype,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// Argument checks of the prefill GEMM (null -> dtype -> stages -> shape -> alignment), shared by
+// fairy2i_gemm and fairy2i_gemm_noalloc.
+static int check_gemm(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T, const void* x,
+                      int x_dtype, const float* x_scale, int64_t N, const void* y, int y_dtype) {
   if (!packed || !scales || !x || !y) return fail(FAIRY2I_ERR_NULL, "packed, scales, x and y are required");
   if (x_dtype == FAIRY2I_I8 && !x_scale)
     return fail(FAIRY2I_ERR_NULL, "x_scale (delta) is required with int8 x");
@@ -397,12 +402,15 @@ int fairy2i_gemm(const uint8_t* packed, const float* scales, int64_t n, int64_t 
   if (int s = check_nm(n, m)) return s;
   if (N < 1 || N > kMaxTokens) return fail(FAIRY2I_ERR_SHAPE, "N = %lld out of range", (long long)N);
   if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(scales, 4) ||
-      (x_scale && !aligned(x_scale, 4)) || (workspace && !aligned(workspace, 16)))
+      (x_scale && !aligned(x_scale, 4)))
     return fail(FAIRY2I_ERR_ALIGN, "packed, x, y, workspace need 16-byte alignment; scales, x_scale 4");
-  const size_t need = fairy2i_gemm_workspace_bytes(n, m, T, N, x_dtype);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(FAIRY2I_ERR_WORKSPACE, "GEMM needs %zu workspace bytes, got %zu", need,
-                workspace ? workspace_bytes : size_t(0));
+  return FAIRY2I_OK;
+}
+
+// The prefill GEMM's launches, with the activation workspace (int8 q, then delta) at `workspace`.
+static int gemm_launch(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T, const void* x,
+                       int x_dtype, float* x_scale, int64_t N, void* y, int y_dtype, void* workspace,
+                       hipStream_t stream) {
   const int8_t* q = static_cast<const int8_t*>(x);
   const float* delta = x_scale;
   if (x_dtype != FAIRY2I_I8) {
@@ -418,6 +426,73 @@ int fairy2i_gemm(const uint8_t* packed, const float* scales, int64_t n, int64_t 
   const int mode = y_dtype == FAIRY2I_F32 ? 0 : (y_dtype == FAIRY2I_BF16 ? 1 : 2);
   return hip_status(f2i::launch_gemm(packed, scales, (int)n, (int)m, T, q, delta, (int)N, y, mode, stream),
                     "gemm launch");
+}
+
+// ---- the entry point that allocates nothing: its activation workspace is a static device array ----
+//
+// `scratch` is one array per GPU, reserved when the library's code object is loaded on that GPU and
+// held until the process ends.  In host code its name stands for no device address: the address
+// on the current device comes from hipGetSymbolAddress, taken once per device on the entry point's
+// first call there and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up once per device).
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FAIRY2I_ERR_HIP, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(FAIRY2I_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FAIRY2I_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t fairy2i_gemm_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int fairy2i_gemm_noalloc(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
+                         const void* x, int x_dtype, float* x_scale, int64_t N, void* y, int y_dtype,
+                         hipStream_t stream) {
+  if (int s = check_gemm(packed, scales, n, m, T, x, x_dtype, x_scale, N, y, y_dtype)) return s;
+  const size_t need = fairy2i_gemm_workspace_bytes(n, m, T, N, x_dtype);
+  if (need > kNoAllocScratchBytes)
+    return fail(FAIRY2I_ERR_WORKSPACE,
+                "N = %lld tokens of 2m = %lld need %zu bytes of activation workspace; the static scratch "
+                "holds %zu (use fairy2i_gemm with a caller workspace)",
+                (long long)N, (long long)(2 * m), need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    if (int s = scratch_on_current_device(&ws)) return s;
+  }
+  return gemm_launch(packed, scales, n, m, T, x, x_dtype, x_scale, N, y, y_dtype, ws, stream);
+}
+
+int fairy2i_gemm(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
+                 const void* x, int x_dtype, float* x_scale, int64_t N, void* y, int y_dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int s = check_gemm(packed, scales, n, m, T, x, x_dtype, x_scale, N, y, y_dtype)) return s;
+  if (workspace && !aligned(workspace, 16))
+    return fail(FAIRY2I_ERR_ALIGN, "packed, x, y, workspace need 16-byte alignment; scales, x_scale 4");
+  const size_t need = fairy2i_gemm_workspace_bytes(n, m, T, N, x_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FAIRY2I_ERR_WORKSPACE, "GEMM needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : size_t(0));
+  return gemm_launch(packed, scales, n, m, T, x, x_dtype, x_scale, N, y, y_dtype, workspace, stream);
 }
 
 }  // extern "C"
