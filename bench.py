@@ -90,20 +90,42 @@ def gemv_bytes(n, m, T, B, x_bytes=2, y_bytes=4):
     return T * n * m // 2 + n * T * 2 * 2 * 4 + B * 2 * m * x_bytes + B * 2 * n * y_bytes
 
 
-def cpu_baseline(R, T, x1, budget_s):
-    """The oracle (float64 NumPy) on the measuring machine's host cores: the batch-1 GEMV of the same layer,
-    repeated until the time budget is spent; plus the quantizer on a row sample."""
-    import oracle
+def host_info():
+    """The measuring host's CPU: logical cores, the cores this process may run on, the CPU model
+    and the BLAS thread count NumPy uses."""
+    info = {"cpu_count": os.cpu_count(), "affinity": None, "model": None, "blas_threads": None}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        info["blas_threads"] = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:                                      # pragma: no cover
-        cores = os.cpu_count() or 1
+        pass
+    return info
+
+
+def cpu_baseline(R, T, x1, budget_s, prefill):
+    """The oracle (float64 NumPy) on the measuring machine's host cores, on bounded samples of the
+    same workload: the batch-1 GEMV of the attention layer (repeated until `budget_s` is spent;
+    `value`), the quantizer on a row sample, and the prefill path (activation quantization, the
+    integer GEMM and its epilogue) on a token sample of the 4096 x 4096 prefill layer."""
+    import oracle
+    host = host_info()
+    cores = host["blas_threads"] or host["affinity"] or host["cpu_count"] or 1
     n, m = R.shape[0] // 2, R.shape[1] // 2
     rows = np.arange(128)
     sub = np.concatenate([R[rows], R[n + rows]])
     t0 = time.perf_counter()
-    codes_s, _, _, _ = oracle.quantize(sub, T)
+    oracle.quantize(sub, T)
     tq = time.perf_counter() - t0
     codes, s32, _, _ = oracle.quantize(R, T)               # setup, not timed
     reps, t_gemv = 0, 0.0
@@ -113,31 +135,57 @@ def cpu_baseline(R, T, x1, budget_s):
         t_gemv += time.perf_counter() - t0
         reps += 1
     per = t_gemv / reps
+    Rp, xp = prefill                                       # prefill layer and its activations
+    pc, ps, _, _ = oracle.quantize(Rp, T)                  # setup, not timed
+    ntok = 256
+    t0 = time.perf_counter()
+    q, d = oracle.act_quant_ref(xp[:ntok])
+    P = oracle.gemm_int_ref(pc, q)
+    oracle.gemm_epilogue_ref(P, ps, d)
+    tg = time.perf_counter() - t0
+    pn, pm = Rp.shape[0] // 2, Rp.shape[1] // 2
+    issued = 16 * T * pn * pm * ntok
     return {
         "value": gemv_bytes(n, m, T, 1) / per / 1e9, "unit": "GB/s", "cores": int(cores),
         "kind": "oracle",
         "sample": f"{reps} x oracle gemv_ref of the full {2*n}x{2*m} layer at batch 1 "
                   f"({per*1e3:.1f} ms each); quantizer on {len(rows)} of {n} complex rows "
-                  f"took {tq:.3f} s ({len(rows)*m*4/tq/1e6:.2f} M real params/s)",
+                  f"took {tq:.3f} s ({len(rows)*m*4/tq/1e6:.2f} M real params/s); prefill "
+                  f"(act-quant + integer GEMM + epilogue) of {ntok} of 2048 tokens on the "
+                  f"{2*pn}x{2*pm} layer took {tg:.3f} s",
+        "host": host,
+        "legs": {"gemv_b1": {"GB/s": round(gemv_bytes(n, m, T, 1) / per / 1e9, 5), "s_per_call": round(per, 4)},
+                 "quantize": {"real_params_per_s": round(len(rows) * m * 4 / tq, 1), "s": round(tq, 4)},
+                 "gemm": {"tokens": ntok, "s": round(tg, 4), "issued_TOPS": round(issued / tg / 1e12, 6),
+                          "useful_TOPS": round(issued / 2 / tg / 1e12, 6)}},
     }
 
 
 def stack_legs(f2, torch, dev, T, reps):
     """The LLaMA-2 7B linear stack (32 layers x 7 projections, 6.48e9 real weights): quantize all
     224 matrices, then one decode step (grouped launches per shared input, the stack's default
-    kernel) at batch 1 and batch 8, each captured in a HIP graph.  Weights are drawn on the GPU (torch's
-    generator seeded 5000 + 7 L + p, N(0, 0.02^2)): 25.9 GB of fp32 R is too much for the host
-    generator.  Runs outside the timed step."""
+    kernel) at batch 1 and batch 8, each captured in a HIP graph.  The weights are the pinned
+    generator's (workloads.stack_layer: NumPy, seed 5000 + 7 L + p, N(0, 0.02^2)), drawn on host
+    threads and copied to the GPU (25.9 GB in all), the same matrices the GPU parity test samples;
+    the decode inputs are workloads.activations with seed 6000 + 7 L + g.  Runs outside the timed
+    step."""
+    import concurrent.futures
+    import workloads
     from widely_linear_gemv_amd.stack import DecodeStep, GROUPS, PROJECTIONS
     R, out = [], []
-    for L in range(32):
-        for p, (_, rows, cols, _) in enumerate(PROJECTIONS):
-            g = torch.Generator(device=dev)
-            g.manual_seed(5000 + 7 * L + p)
-            R.append(torch.randn((rows, cols), generator=g, device=dev) * 0.02)
-            n, m = rows // 2, cols // 2
-            out.append({"packed": torch.empty((f2.fairy2i_packed_bytes(n, m, T),), dtype=torch.uint8, device=dev),
-                        "scales": torch.empty((n, T, 2, 2), dtype=torch.float32, device=dev)})
+    keys = [(L, p) for L in range(32) for p in range(len(PROJECTIONS))]
+    workers = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:      # NumPy's generator releases the GIL
+        for k0 in range(0, len(keys), 2 * workers):               # bounded host memory
+            for w in ex.map(lambda key: workloads.stack_layer(*key).weight(), keys[k0:k0 + 2 * workers]):
+                R.append(torch.from_numpy(w).to(dev))
+    gen_s = time.perf_counter() - t0
+    for (L, p) in keys:
+        _, rows, cols, _ = PROJECTIONS[p]
+        n, m = rows // 2, cols // 2
+        out.append({"packed": torch.empty((f2.fairy2i_packed_bytes(n, m, T),), dtype=torch.uint8, device=dev),
+                    "scales": torch.empty((n, T, 2, 2), dtype=torch.float32, device=dev)})
 
     def quantize_all():
         for r, o in zip(R, out):
@@ -165,7 +213,9 @@ def stack_legs(f2, torch, dev, T, reps):
     layers = [[(out[7 * L + p]["packed"], out[7 * L + p]["scales"]) for p in range(7)] for L in range(32)]
     r_bytes = sum(r.numel() * 4 for r in R)
     legs = {"stack_quantize": {"matrices": 224, "ms": round(t_q, 3), "R_GB/s": round(r_bytes / (t_q * 1e-3) / 1e9, 1),
-                               "real_params_per_s": round(sum(r.numel() for r in R) / (t_q * 1e-3), 1)}}
+                               "real_params_per_s": round(sum(r.numel() for r in R) / (t_q * 1e-3), 1),
+                               "weights": f"pinned NumPy generator (seed 5000 + 7 L + p), drawn on {workers} "
+                                          f"host threads in {gen_s:.1f} s"}}
     del R
     for B in (1, 8):
         xs = []
@@ -173,9 +223,8 @@ def stack_legs(f2, torch, dev, T, reps):
             lx = []
             for gi in range(GROUPS):
                 cols = next(c for (_, _, c, grp) in PROJECTIONS if grp == gi)
-                g = torch.Generator(device=dev)
-                g.manual_seed(6000 + 7 * L + gi)
-                lx.append(torch.randn((B, cols), generator=g, device=dev).to(torch.bfloat16))
+                a = workloads.activations(B, cols, workloads.stack_x_seed(L, gi))
+                lx.append(torch.from_numpy(a.bf16_bits.view(np.int16)).to(dev).view(torch.bfloat16))
             xs.append(lx)
         step = DecodeStep(layers, xs)
         t = timed(step.run)
@@ -286,7 +335,10 @@ def main():
     xp = torch.from_numpy(xp_np.bf16_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     qp = torch.empty((Ntok, 2 * m), dtype=torch.int8, device=dev)
     dp = torch.empty((Ntok,), dtype=torch.float32, device=dev)
-    yp = torch.empty((Ntok, 2 * n), dtype=torch.float32, device=dev)
+    # the two prefill layers (4096 x 4096 and 11008 x 4096), quantized once before timing
+    Rp_np = [L.weight() for L in workloads.PREFILL_LAYERS]
+    qpre = [f2.fairy2i_quantize(torch.from_numpy(r).to(dev), T) for r in Rp_np]
+    ypre = [torch.empty((Ntok, L.rows), dtype=torch.float32, device=dev) for L in workloads.PREFILL_LAYERS]
     qout = {"packed": torch.empty_like(q0["packed"]), "scales": torch.empty_like(q0["scales"])}
 
     if args.calib_copy:
@@ -354,8 +406,11 @@ def main():
     def seg_act_quant():
         f2.fairy2i_act_quant(xp, q=qp, delta=dp)
 
-    def seg_gemm():
-        f2.fairy2i_gemm(q0["packed"], q0["scales"], qp, x_scale=dp, y=yp)
+    def seg_gemm():                    # the 4096 x 4096 prefill layer
+        f2.fairy2i_gemm(qpre[0]["packed"], qpre[0]["scales"], qp, x_scale=dp, y=ypre[0])
+
+    def gemm_mlp():                    # the 11008 x 4096 prefill layer (timed outside the step)
+        f2.fairy2i_gemm(qpre[1]["packed"], qpre[1]["scales"], qp, x_scale=dp, y=ypre[1])
 
     segments = [seg_quantize, seg_decode_f4, seg_gemv_f4, seg_decode_i8, seg_gemv_i8, seg_gemv(1),
                 seg_gemv(4), seg_gemv(16), seg_act_quant, seg_gemm, seg_dequant, seg_quantize_tensor,
@@ -455,7 +510,8 @@ def main():
 
     k_us = {"quantize": kernel_us(seg_quantize), "act_quant": kernel_us(seg_act_quant),
             "gemm": kernel_us(seg_gemm), "dequantize": kernel_us(seg_dequant),
-            "quantize_per_tensor": kernel_us(seg_quantize_tensor)}
+            "quantize_per_tensor": kernel_us(seg_quantize_tensor), "gemm_mlp": kernel_us(gemm_mlp)}
+    ops_mlp = 16 * T * workloads.PREFILL_LAYERS[1].n * m * Ntok        # issued int8 ops
 
     t_quant, t_decf4, t_f4, t_dec, t_i8, t_b1, t_b4, t_b16, t_aq, t_gemm, t_deq, t_qt = seg    # ms
     bytes_b = {B: gemv_bytes(n, m, T, B) for B in (1, 4, 16)}
@@ -550,6 +606,11 @@ def main():
                      "kernel_us": round(k_us["gemm"], 2),
                      "kernel_issued_TOPS": round(issued_ops / (k_us["gemm"] * 1e-6) / 1e12, 2),
                      "kernel_frac_of_int8_peak": round(issued_ops / (k_us["gemm"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)},
+            "gemm_11008x4096": {
+                "issued_ops": ops_mlp, "kernel_us": round(k_us["gemm_mlp"], 2),
+                "kernel_issued_TOPS": round(ops_mlp / (k_us["gemm_mlp"] * 1e-6) / 1e12, 2),
+                "kernel_useful_TOPS": round(ops_mlp / 2 / (k_us["gemm_mlp"] * 1e-6) / 1e12, 2),
+                "kernel_frac_of_int8_peak": round(ops_mlp / (k_us["gemm_mlp"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)},
             "dequantize": {"us": round(t_deq * 1e3, 2),
                            "GB/s": round((layer_bytes + n * T * 16 + 4 * n * m * 4) / (t_deq * 1e-3) / 1e9, 2),
                            "kernel_us": round(k_us["dequantize"], 2),
@@ -563,7 +624,7 @@ def main():
         out["legs"].update(mlp_legs(f2, torch, workloads, dev))
     if not args.no_cpu_baseline:
         x1 = workloads.activations(1, 2 * m, workloads.ATTN_X_SEEDS[1]).values
-        out["cpu_baseline"] = cpu_baseline(R_np, T, x1, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(R_np, T, x1, args.cpu_seconds, (Rp_np[0], xp_np.values))
     print(json.dumps(out), flush=True)
 
 
