@@ -235,15 +235,17 @@ def stack_legs(f2, torch, dev, T, reps):
     return legs
 
 
-MLP_POOL_BYTES = 2 ** 29     # 2x the Infinity Cache per MLP pool
+MLP_POOL_BYTES = 2 ** 30     # 4x the Infinity Cache per MLP pool, as for the attention pool
 
 
 def mlp_legs(f2, torch, workloads, dev, reps=5):
     """The LLaMA-2 7B MLP decode GEMVs: gate/up (11008 x 4096, outlier weights) and down
     (4096 x 11008) quantized at T = 2 and T = 3, at batch 1 (fp4 matrix cores on the fp6 digit form)
-    and batch 8 (bf16 matrix cores, shared x).  Each case streams a pool of >= 512 MB of copies of
-    its quantized layer as one strided-batch launch per pass, four passes per HIP graph, replayed
-    after warm-up replays.  Runs outside the timed step."""
+    and batch 8 (bf16 matrix cores, shared x).  Each case streams a pool of >= 1 GiB of copies of
+    its quantized layer (as the attention pool: four times the Infinity Cache, and launches long
+    enough that one launch's ramp and tail are a small part of it) as one strided-batch launch per
+    pass, four passes per HIP graph, replayed for ~50 ms first so the clocks have settled.  Runs
+    outside the timed step."""
     legs = {}
     for name, layer in (("gate_up", workloads.MLP_GATE_UP), ("down", workloads.MLP_DOWN)):
         R = torch.from_numpy(layer.weight()).to(dev)
@@ -274,9 +276,10 @@ def mlp_legs(f2, torch, workloads, dev, reps=5):
                 with torch.cuda.graph(g, stream=torch.cuda.Stream()):
                     for _ in range(4):
                         fn()
-                for _ in range(10):
+                t_w = time.perf_counter()
+                while time.perf_counter() - t_w < 0.05:
                     g.replay()
-                torch.cuda.synchronize()
+                    torch.cuda.synchronize()
                 stream = torch.cuda.current_stream()
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
