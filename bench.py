@@ -511,7 +511,19 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / (replays * calls)
 
+    # the pool through fairy2i_gemv on the bf16 x as it is (AUTO: the fp4 kernel building its
+    # digits on chip for a launch this large), batch 1 and 2
+    x2 = xs[4][:2].contiguous()
+    ypool2 = torch.empty((P, 2, 2 * n), dtype=torch.float32, device=dev)
+
+    def auto_b1():
+        f2.fairy2i_gemv_strided(pool, spool, xs[1], ypool[1])
+
+    def auto_b2():
+        f2.fairy2i_gemv_strided(pool, spool, x2, ypool2)
+
     k_us = {"quantize": kernel_us(seg_quantize), "act_quant": kernel_us(seg_act_quant),
+            "auto_b1": kernel_us(auto_b1, warm=40), "auto_b2": kernel_us(auto_b2, warm=40),
             "gemm": kernel_us(seg_gemm), "dequantize": kernel_us(seg_dequant),
             "quantize_per_tensor": kernel_us(seg_quantize_tensor), "gemm_mlp": kernel_us(gemm_mlp)}
     ops_mlp = 16 * T * workloads.PREFILL_LAYERS[1].n * m * Ntok        # issued int8 ops
@@ -586,6 +598,12 @@ def main():
                         "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[4]},
             "gemv_b16": {"GB/s": round(gbs[16], 2), "us_per_launch": round(per_launch_us[16], 3),
                          "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[16]},
+            "gemv_b1_bf16x_auto": {"us_per_launch": round(k_us["auto_b1"], 3),
+                                   "GB/s": round(bytes_pool / (k_us["auto_b1"] * 1e-6) / 1e9, 2),
+                                   "kernel": "fp4 MFMA, fp6 digit records built on chip from the bf16 x (AUTO)"},
+            "gemv_b2_bf16x_auto": {"us_per_launch": round(k_us["auto_b2"], 3),
+                                   "GB/s": round(P * gemv_bytes(n, m, T, 2) / (k_us["auto_b2"] * 1e-6) / 1e9, 2),
+                                   "kernel": "fp4 MFMA, fp6 digit records built on chip from the bf16 x (AUTO)"},
             "gemv_b1_f4_grouped": {"us_per_pass": round(grouped_us, 3), "launches_per_pass": -(-P // 48),
                                    "GB/s": round(bytes_pool / (grouped_us * 1e-6) / 1e9, 2)},
             "gemv_b1_single_layer_launch": {"us_per_launch": round(single_us, 3),

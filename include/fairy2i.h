@@ -78,7 +78,7 @@ typedef enum {
 } fairy2i_dtype;
 
 /* GEMV kernels.  AUTO picks MFMA_F4 for x in fp6 digit form, MFMA_I8 for x in int8 digit form,
- * MFMA_BF16 for bf16 x and VALU for fp32 x; MFMA means MFMA_BF16.
+ * MFMA_F4 or MFMA_BF16 for bf16 x (below) and VALU for fp32 x; MFMA means MFMA_BF16.
  *   VALU       fp32 add/sub/swap accumulation on the vector ALUs; fp32 or bf16 x.
  *   MFMA_BF16  codes decoded in registers to bf16 planes {+-2, 0}, multiplied with the unchanged
  *              bf16 x on v_mfma_f32_16x16x32_bf16: exact products, fp32 sums.  bf16 x.
@@ -88,10 +88,17 @@ typedef enum {
  *              ~2/3 of the VALU work per code of MFMA_BF16.
  *   MFMA_F4    codes read as fp4 planes of u = B_re + B_im and v = B_re - B_im (both +-1 for
  *              every codeword, eight bit operations per 16 codes), multiplied with x in fp6
- *              digit form (fairy2i_x_digits_f6) on v_mfma_scale_f32_16x16x128_f8f6f4: exact
- *              integer sums in fp32, B_re and B_im sums as (u +- v) / 2, fp32 epilogue.
- *              x_dtype FAIRY2I_X_DIGITS_F6, B <= 2.  The fastest decode kernel on gfx950: half
- *              the MFMA cycles and about half the VALU work per code of MFMA_I8. */
+ *              digit form on v_mfma_scale_f32_16x16x128_f8f6f4: exact integer sums in fp32, B_re
+ *              and B_im sums as (u +- v) / 2, fp32 epilogue.  B <= 2.  x_dtype FAIRY2I_X_DIGITS_F6
+ *              (the digit form made once by fairy2i_x_digits_f6 and shared by every GEMV that
+ *              reads that x) or FAIRY2I_BF16: then each workgroup builds the same digits on chip
+ *              from the bf16 x (outputs identical bit for bit; m * B <= 8192; in a grouped call
+ *              of 1536 tiles or more every item must have the same x).  The fastest decode
+ *              kernel on gfx950: half the MFMA cycles and about half the VALU work per code of
+ *              MFMA_I8.
+ * AUTO with bf16 x takes MFMA_F4 for launches of at least 1536 16-row tiles with B <= 2,
+ * m * B <= 8192 and one x for the launch (there the on-chip digits cost little per tile), and
+ * MFMA_BF16 otherwise (smaller launches would build the digits once per tile). */
 typedef enum {
   FAIRY2I_GEMV_AUTO = 0,
   FAIRY2I_GEMV_VALU = 1,
@@ -209,8 +216,8 @@ int fairy2i_dequantize(const uint8_t* packed, const float* scales, int64_t n, in
  *           1 <= B <= 16.
  *   y       out, [B][2n], y_dtype FAIRY2I_F32 or FAIRY2I_BF16 (round to nearest even).
  *   algo    fairy2i_gemv_algo; MFMA_BF16 requires x_dtype BF16, MFMA_I8 x_dtype X_DIGITS and
- *           B <= 2, MFMA_F4 x_dtype X_DIGITS_F6, B <= 2 and m <= 2^19 (its fp32 sums stay
- *           exact integers); VALU takes F32 or BF16.
+ *           B <= 2, MFMA_F4 x_dtype X_DIGITS_F6 (m <= 2^19: its fp32 sums stay exact integers)
+ *           or BF16 (m * B <= 8192) and B <= 2; VALU takes F32 or BF16.
  * Uses no workspace. */
 int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,

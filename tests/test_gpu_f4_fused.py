@@ -1,0 +1,105 @@
+"""GPU parity of the fp4 decode GEMV on bf16 x (fairy2i_gemv with x_dtype BF16 and MFMA_F4 or
+AUTO): every workgroup builds its fp6 digit records on chip.  The outputs must equal the two-call
+form (fairy2i_x_digits_f6, then the GEMV on the digit form) bit for bit -- same digits, same MFMA
+inputs, same order -- and so match the oracle within the fp32 tolerance.  Cases cover every launch
+form: small launches (a tile's chunks split over 2, 4 or 8 waves), one wave per tile, the
+mixed-granularity large launch (four tiles per workgroup sharing the records, then the split
+tail), batch 1 and 2, T = 1..4, ragged rows and the longest rows the records allow."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL_F32, announce, check_bf16, device, down, rel_l2, up, x_to_dev
+
+import widely_linear_gemv_amd as f2
+
+pytestmark = pytest.mark.gpu
+
+
+def layer(n, m, T, seed):
+    return workloads.random_codes(T, n, m, seed=seed), workloads.random_scales(n, T, seed=seed + 1)
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+@pytest.mark.parametrize("n,m,T,B", [(5, 64, 1, 1), (17, 320, 2, 2), (40, 2048, 2, 1), (33, 1088, 3, 2),
+                                     (100, 5504, 2, 1), (9, 8192, 2, 1), (21, 4096, 4, 2), (300, 2048, 2, 2)])
+def test_fused_matches_two_call_and_oracle(n, m, T, B):
+    dev = device()
+    codes, scales = layer(n, m, T, seed=n * 7 + m + T)
+    act = workloads.activations(B, 2 * m, seed=800 + B + m)
+    packed, s = up(oracle.pack(codes), dev), up(scales, dev)
+    x = x_to_dev(act, dev)
+    for ydt in (torch.float32, torch.bfloat16):
+        announce("gemv fp4 fused", n, m, T, B, ydt)
+        got = down(f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA_F4, y_dtype=ydt))
+        two = down(f2.fairy2i_gemv(packed, s, f2.fairy2i_x_digits_f6(x), algo=f2.GEMV_MFMA_F4, y_dtype=ydt))
+        assert np.array_equal(bits(got), bits(two)), (n, m, T, B, ydt)
+    want = oracle.gemv_ref(codes, scales, act.values)
+    assert rel_l2(down(f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA_F4)), want) <= TOL_F32
+    check_bf16(down(f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA_F4, y_dtype=torch.bfloat16)), want, "fused")
+
+
+@pytest.mark.parametrize("B,T,batch,n", [(1, 2, 128, 256), (1, 3, 48, 256), (2, 2, 100, 256), (1, 1, 200, 256),
+                                         (2, 2, 513, 40), (1, 4, 97, 256), (1, 2, 800, 256), (1, 3, 800, 250)])
+def test_fused_large_strided_launch(B, T, batch, n):
+    """The strided batch (one launch over many layers sharing x) in the large-launch forms: four
+    tiles per workgroup sharing one set of records (the last workgroup partly empty when the tile
+    count is not a multiple of four), and from 12288 tiles at batch 1 and T <= 3 the
+    mixed-granularity form (then the last 1536 tiles split over four waves).  Distinct layers;
+    every output against the two-call form bit for bit, sampled layers against the oracle."""
+    dev = device()
+    m = 2048
+    g = torch.Generator(device=dev)
+    g.manual_seed(batch + T)
+    nb = f2.fairy2i_packed_bytes(n, m, T)
+    pool = torch.randint(0, 256, (batch, nb), dtype=torch.uint8, device=dev, generator=g)
+    spool = (torch.rand((batch, n, T, 2, 2), device=dev, generator=g) * 0.02).contiguous()
+    act = workloads.activations(B, 2 * m, seed=900 + B)
+    x = x_to_dev(act, dev)
+    y1 = torch.empty((batch, B, 2 * n), device=dev)
+    y2 = torch.empty_like(y1)
+    announce("gemv fp4 fused strided", batch, n, m, T, B)
+    f2.fairy2i_gemv_strided(pool, spool, x, y1, algo=f2.GEMV_MFMA_F4)
+    f2.fairy2i_gemv_strided(pool, spool, f2.fairy2i_x_digits_f6(x), y2, algo=f2.GEMV_MFMA_F4)
+    a, b = down(y1), down(y2)
+    assert np.array_equal(bits(a), bits(b))
+    if batch * ((n + 15) // 16) >= 1536:           # AUTO takes the fp4 kernel on bf16 x for large launches
+        y3 = torch.empty_like(y1)
+        f2.fairy2i_gemv_strided(pool, spool, x, y3)
+        assert np.array_equal(bits(down(y3)), bits(a))
+    # the pool's packed bytes are arbitrary: recover codes through the oracle's unpacking
+    for k in (0, batch // 2, batch - 1):
+        codes = oracle.unpack(down(pool[k]), n, m, T)
+        want = oracle.gemv_ref(codes, down(spool[k]), act.values)
+        assert rel_l2(a[k], want) <= TOL_F32, k
+
+
+def test_fused_grouped_and_zero_column():
+    """Grouped call (items of different n sharing x) on bf16 x; an all-zero batch column (S = 0,
+    every digit 0) next to a normal one."""
+    dev = device()
+    m, T, B = 1024, 2, 2
+    act = workloads.activations(B, 2 * m, seed=950)
+    vals = act.values.copy()
+    bits16 = act.bf16_bits.copy()
+    bits16[1] = 0
+    vals[1] = 0.0
+    x = torch.from_numpy(bits16.view(np.int16)).to(dev).view(torch.bfloat16)
+    items, refs = [], []
+    for k, n in enumerate((16, 33, 300)):
+        codes, scales = layer(n, m, T, seed=960 + k)
+        items.append((up(oracle.pack(codes), dev), up(scales, dev), x, torch.empty((B, 2 * n), device=dev)))
+        refs.append(oracle.gemv_ref(codes, scales, vals))
+    announce("gemv fp4 fused grouped")
+    ys = f2.fairy2i_gemv_grouped(items, algo=f2.GEMV_MFMA_F4)
+    xd = f2.fairy2i_x_digits_f6(x)
+    ys2 = f2.fairy2i_gemv_grouped([(p, s, xd, torch.empty_like(y)) for (p, s, _, y) in items], algo=f2.GEMV_MFMA_F4)
+    for y, y2, want in zip(ys, ys2, refs):
+        assert np.array_equal(bits(down(y)), bits(down(y2)))
+        assert np.all(down(y)[1] == 0.0)
+        assert rel_l2(down(y)[0], want[0]) <= TOL_F32

@@ -156,7 +156,16 @@ int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* pac
 
 // Checks the dtype / algorithm / batch combination of a GEMV call and resolves AUTO and MFMA to
 // the kernel that runs.  Returns minus the status (with the message recorded) on a bad combination.
-static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B) {
+// The fp4 GEMV on bf16 x builds each row's fp6 digit records in LDS: at most 32 chunks of 256
+// columns per batch entry (96 KB).  AUTO takes it for launches of at least kF4FusedMinTiles tiles,
+// where four tiles share one workgroup's records (smaller launches build them once per tile, which
+// costs about as much as the bf16 kernel's own work); those workgroups need one x for the launch.
+constexpr int kMaxF4FusedColumns = 8192;
+constexpr int64_t kF4FusedMinTiles = 1536;
+static bool f4_records_fit(int64_t m, int64_t B) { return m * B <= kMaxF4FusedColumns; }
+
+static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B, int64_t m, int64_t tiles = 0,
+                       bool shared_x = true) {
   if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16 && x_dtype != FAIRY2I_X_DIGITS &&
       x_dtype != FAIRY2I_X_DIGITS_F6)
     return -fail(FAIRY2I_ERR_DTYPE, "x_dtype %d: need F32, BF16, X_DIGITS or X_DIGITS_F6", x_dtype);
@@ -169,16 +178,26 @@ static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B) {
   if (kernel == FAIRY2I_GEMV_AUTO)
     kernel = x_dtype == FAIRY2I_X_DIGITS    ? FAIRY2I_GEMV_MFMA_I8
            : x_dtype == FAIRY2I_X_DIGITS_F6 ? FAIRY2I_GEMV_MFMA_F4
-           : x_dtype == FAIRY2I_BF16        ? FAIRY2I_GEMV_MFMA_BF16 : FAIRY2I_GEMV_VALU;
+           : x_dtype == FAIRY2I_BF16        ? (B <= 2 && f4_records_fit(m, B) && shared_x && tiles >= kF4FusedMinTiles
+                                                   ? FAIRY2I_GEMV_MFMA_F4 : FAIRY2I_GEMV_MFMA_BF16)
+                                            : FAIRY2I_GEMV_VALU;
   if (kernel == FAIRY2I_GEMV_MFMA) kernel = FAIRY2I_GEMV_MFMA_BF16;
   if (kernel == FAIRY2I_GEMV_MFMA_I8) {
     if (x_dtype != FAIRY2I_X_DIGITS)
       return -fail(FAIRY2I_ERR_DTYPE, "the int8 MFMA GEMV takes x in digit form (fairy2i_x_digits)");
     if (B > 2) return -fail(FAIRY2I_ERR_SHAPE, "B = %lld: the int8 MFMA GEMV takes B <= 2", (long long)B);
   } else if (kernel == FAIRY2I_GEMV_MFMA_F4) {
-    if (x_dtype != FAIRY2I_X_DIGITS_F6)
-      return -fail(FAIRY2I_ERR_DTYPE, "the fp4 MFMA GEMV takes x in fp6 digit form (fairy2i_x_digits_f6)");
+    if (x_dtype != FAIRY2I_X_DIGITS_F6 && x_dtype != FAIRY2I_BF16)
+      return -fail(FAIRY2I_ERR_DTYPE, "the fp4 MFMA GEMV takes bf16 x or x in fp6 digit form (fairy2i_x_digits_f6)");
     if (B > 2) return -fail(FAIRY2I_ERR_SHAPE, "B = %lld: the fp4 MFMA GEMV takes B <= 2", (long long)B);
+    if (x_dtype == FAIRY2I_BF16 && m > 0 && !f4_records_fit(m, B))
+      return -fail(FAIRY2I_ERR_SHAPE, "m = %lld, B = %lld: the fp4 MFMA GEMV on bf16 x takes m * B <= %d "
+                   "(its digit records are built in LDS); make the digit form with fairy2i_x_digits_f6",
+                   (long long)m, (long long)B, kMaxF4FusedColumns);
+    if (x_dtype == FAIRY2I_BF16 && !shared_x && tiles >= kF4FusedMinTiles)
+      return -fail(FAIRY2I_ERR_SHAPE, "the fp4 MFMA GEMV on bf16 x needs one x for every item of a launch of "
+                   "%lld tiles or more (give the items' x as one digit form, or use the bf16 kernel)",
+                   (long long)kF4FusedMinTiles);
   } else if (x_dtype == FAIRY2I_X_DIGITS) {
     return -fail(FAIRY2I_ERR_DTYPE, "x in digit form needs the int8 MFMA GEMV");
   } else if (x_dtype == FAIRY2I_X_DIGITS_F6) {
@@ -234,7 +253,7 @@ int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t 
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,
                  hipStream_t stream) {
   if (!packed || !scales || !x || !y) return fail(FAIRY2I_ERR_NULL, "packed, scales, x and y are required");
-  const int kernel = gemv_kernel(x_dtype, y_dtype, algo, B);
+  const int kernel = gemv_kernel(x_dtype, y_dtype, algo, B, m, (n + 15) / 16);
   if (kernel < 0) return -kernel;
   if (int s = check_stages(T)) return s;
   if (int s = check_nm(n, m)) return s;
@@ -243,7 +262,7 @@ int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t 
     return fail(FAIRY2I_ERR_ALIGN, "packed, x and y need 16-byte alignment, scales 4");
   if (kernel == FAIRY2I_GEMV_MFMA_F4)
     return hip_status(f2i::launch_gemv_f4(packed, scales, (int)n, (int)m, T, x, (int)B, y,
-                                          y_dtype == FAIRY2I_BF16, stream),
+                                          y_dtype == FAIRY2I_BF16, x_dtype == FAIRY2I_BF16, stream),
                       "gemv (fp4 mfma) launch");
   if (kernel == FAIRY2I_GEMV_MFMA_I8)
     return hip_status(f2i::launch_gemv_i8(packed, scales, (int)n, (int)m, T, x, (int)B, y,
@@ -266,7 +285,13 @@ int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, i
   for (int k = 0; k < count; ++k)
     if (!items[k].packed || !items[k].scales || !items[k].x || !items[k].y)
       return fail(FAIRY2I_ERR_NULL, "item %d: packed, scales, x and y are required", k);
-  const int kernel = gemv_kernel(x_dtype, y_dtype, algo, B);
+  int64_t all_tiles = 0;
+  bool shared_x = true;
+  for (int k = 0; k < count; ++k) {
+    all_tiles += (items[k].n + 15) / 16;
+    shared_x = shared_x && items[k].x == items[0].x;
+  }
+  const int kernel = gemv_kernel(x_dtype, y_dtype, algo, B, m, all_tiles, shared_x);
   if (kernel < 0) return -kernel;
   if (int s = check_stages(T)) return s;
   for (int k = 0; k < count; ++k)
@@ -296,7 +321,8 @@ int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, i
     }
     grp.tile_start[grp.count] = tiles;
     const int ybf = y_dtype == FAIRY2I_BF16;
-    hipError_t e = kernel == FAIRY2I_GEMV_MFMA_F4 ? f2i::launch_gemv_f4_group(grp, (int)m, T, (int)B, ybf, stream)
+    hipError_t e = kernel == FAIRY2I_GEMV_MFMA_F4
+                       ? f2i::launch_gemv_f4_group(grp, (int)m, T, (int)B, ybf, x_dtype == FAIRY2I_BF16, stream)
                  : kernel == FAIRY2I_GEMV_MFMA_I8 ? f2i::launch_gemv_i8_group(grp, (int)m, T, (int)B, ybf, stream)
                  : f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, ybf, stream);
     if (e != hipSuccess) return hip_status(e, "gemv (grouped mfma) launch");
@@ -309,7 +335,7 @@ int fairy2i_gemv_strided(const uint8_t* packed, int64_t packed_stride, const flo
                          int x_dtype, int64_t B, void* y, int64_t y_stride, int y_dtype,
                          int64_t batch, int algo, hipStream_t stream) {
   if (!packed || !scales || !x || !y) return fail(FAIRY2I_ERR_NULL, "packed, scales, x and y are required");
-  const int kernel = gemv_kernel(x_dtype, y_dtype, algo, B);
+  const int kernel = gemv_kernel(x_dtype, y_dtype, algo, B, m, batch > 0 && n > 0 ? batch * ((n + 15) / 16) : 0);
   if (kernel < 0) return -kernel;
   if (int s = check_stages(T)) return s;
   if (int s = check_nm(n, m)) return s;
@@ -345,7 +371,8 @@ int fairy2i_gemv_strided(const uint8_t* packed, int64_t packed_stride, const flo
   grp.scales_stride = scales_stride;
   grp.y_stride = y_stride;
   const int ybf = y_dtype == FAIRY2I_BF16;
-  hipError_t e = kernel == FAIRY2I_GEMV_MFMA_F4 ? f2i::launch_gemv_f4_group(grp, (int)m, T, (int)B, ybf, stream)
+  hipError_t e = kernel == FAIRY2I_GEMV_MFMA_F4
+                     ? f2i::launch_gemv_f4_group(grp, (int)m, T, (int)B, ybf, x_dtype == FAIRY2I_BF16, stream)
                : kernel == FAIRY2I_GEMV_MFMA_I8 ? f2i::launch_gemv_i8_group(grp, (int)m, T, (int)B, ybf, stream)
                : f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, ybf, stream);
   return hip_status(e, "gemv (strided batch) launch");

@@ -81,7 +81,7 @@ struct GemvGroup {
   int64_t packed_stride = 0, scales_stride = 0, y_stride = 0;
 };
 // 16-row tiles of a launch.
-inline int group_tiles(const GemvGroup& g) {
+__host__ __device__ inline int group_tiles(const GemvGroup& g) {
   return g.batch > 0 ? g.batch * g.tiles_per_item : g.tile_start[g.count];
 }
 // Buffer resource over [base, base + bytes): loads at offsets past the end return 0.
@@ -159,9 +159,12 @@ hipError_t launch_gemv_mfma(const uint8_t* packed, const float* scales, int n, i
 hipError_t launch_gemv_i8(const uint8_t* packed, const float* scales, int n, int m, int T,
                           const void* digits, int B, void* y, int y_bf16, hipStream_t s);
 hipError_t launch_gemv_i8_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
+// x_bf16: x is bf16 [B][2m] and each workgroup builds its fp6 digit records on chip; otherwise x
+// is the digit form made by launch_x_digits_f6.
 hipError_t launch_gemv_f4(const uint8_t* packed, const float* scales, int n, int m, int T,
-                          const void* digits, int B, void* y, int y_bf16, hipStream_t s);
-hipError_t launch_gemv_f4_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
+                          const void* x, int B, void* y, int y_bf16, int x_bf16, hipStream_t s);
+hipError_t launch_gemv_f4_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, int x_bf16, hipStream_t s);
+int gemv_f4_record_bytes(int m, int B);     // LDS bytes of the on-chip records (x_bf16 launches)
 size_t x_digits_f6_bytes(int64_t m, int64_t B);
 hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blob, hipStream_t s);
 size_t x_digits_bytes(int64_t m, int64_t B);

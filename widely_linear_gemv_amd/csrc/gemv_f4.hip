@@ -28,6 +28,10 @@
 //    integer of magnitude at most 24m < 2^24 (m <= 2^19), so the fp32 accumulation is exact;
 //    Su + Sv is even and below 2^25, so the halving is exact too.  The factor 6 leaves in the
 //    epilogue's digit weight; the only roundings are X itself and the fp32 epilogue.
+//  * bf16 x without a digit-form buffer: each workgroup builds the records it multiplies in LDS
+//    (build_f6_records: same S, X and digits as k_x_digits_f6, so the outputs equal the two-call
+//    form bit for bit).  Large launches keep their workgroups resident (k_gemv_f4_persist), so a
+//    workgroup builds once and then streams many tiles; small launches build once per tile.
 //  * Streaming as in the int8 kernel: one wave per 16-row tile of one item of a grouped or strided call
 //    (or NW waves splitting the 256-column chunks for small launches), one 1 KB load per plane
 //    and chunk, the next chunk prefetched while the current one is decoded and multiplied.  In
@@ -35,6 +39,8 @@
 //    takes words 2s and 2s+1.  Large batch-1 launches end on tiles split over four waves, whose
 //    exact integer accumulators are added before the epilogue (k_gemv_f4_mixed): the outputs
 //    are those of one wave per tile, bit for bit, and the launch's tail is short-lived waves.
+#include <algorithm>
+
 #include "common.hpp"
 #include "digits.hpp"
 
@@ -184,6 +190,121 @@ hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blo
   return hipGetLastError();
 }
 
+// ------------------------------------------- fp6 digit records built on chip (bf16 x) ----
+//
+// The fp4 GEMV on bf16 x without a digit-form buffer: each workgroup makes the records its waves
+// multiply -- the same X = rne(x 2^S) with the same S and digits as k_x_digits_f6, so the outputs
+// are those of the two-call form bit for bit -- in LDS, once, and its waves read their B operands
+// from there.  Records are compact (24 bytes: the 32 six-bit values, no padding), ordered
+// [chunk][step][b][lane] as in the digit form.  The digits come from Y = X + kDigitBias, whose
+// plain base-8 digits are the balanced digits plus 4 (X is within +-2^22, so 0 <= Y < 8^8); a
+// v_perm_b32 maps four such digits at once to their fp6 e2m3 codes.
+constexpr int kRecBytes = 24;
+constexpr int kDigitBias = 9586980;                 // 4 (8^8 - 1) / 7
+constexpr uint32_t kF6CodesLo = 0x28303438u;       // fp6 e2m3 of the digits -4, -3, -2, -1
+constexpr uint32_t kF6CodesHi = 0x14100800u;       // and of 0, 1, 2, 3
+
+// LDS bytes of the records of a row of m columns and B batch entries.
+__host__ __device__ inline int f4_record_bytes(int m, int B) {
+  return ((m + kF4Chunk - 1) / kF4Chunk) * 2 * B * kWave * kRecBytes;
+}
+
+// LDS bytes of the staged bf16 x of B batch entries (2m values each).
+__host__ __device__ inline int f4_xstage_bytes(int m, int B) { return 4 * m * B; }
+
+// Workgroup-collective: copies x (bf16 [B][2m]) into s_x (its loads all issued before any is
+// waited on), takes S_b of every batch entry into s_S[b], then builds every record into s_rec from
+// the staged copy.  Ends with a barrier.  s_red holds one float per wave and batch entry.
+__device__ void build_f6_records(const uint16_t* __restrict__ x, int m, int B, uint8_t* __restrict__ s_rec,
+                                 uint16_t* __restrict__ s_x, int* __restrict__ s_S, float* __restrict__ s_red) {
+  const int tid = threadIdx.x, nthr = blockDim.x, nwave = nthr / kWave;
+  const int units = (2 * m * B) / 8;                  // 16-byte units of x (8 values each)
+  const int per_b = (2 * m) / 8;
+  float amax[2] = {0.f, 0.f};
+  constexpr int kBatch = 8;                           // units in flight per thread
+  for (int u0 = tid; u0 < units; u0 += kBatch * nthr) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int u = u0 + k * nthr;
+      v[k] = u < units ? reinterpret_cast<const uint4*>(x)[u] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int u = u0 + k * nthr;
+      if (u < units) {
+        reinterpret_cast<uint4*>(s_x)[u] = v[k];
+        const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(wd[e])), fabsf(bf16_hi(wd[e]))));
+        if (u < per_b) amax[0] = fmaxf(amax[0], mx); else amax[1] = fmaxf(amax[1], mx);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) amax[b] = fmaxf(amax[b], __shfl_xor(amax[b], off));
+  }
+  if ((tid & (kWave - 1)) == 0) {
+    s_red[tid / kWave] = amax[0];
+    s_red[nwave + tid / kWave] = amax[1];
+  }
+  __syncthreads();
+  if (tid < B) {                                      // max |x_b| is order-free, so exact
+    float mx = 0.f;
+    for (int w = 0; w < nwave; ++w) mx = fmaxf(mx, s_red[tid * nwave + w]);
+    s_S[tid] = digit_exponent(mx);
+  }
+  __syncthreads();
+  const int nrec = ((m + kF4Chunk - 1) / kF4Chunk) * 2 * B * kWave;
+  for (int rec = tid; rec < nrec; rec += nthr) {
+    const int lane = rec & (kWave - 1), blk = rec / kWave;
+    const int b = blk % B, cs = blk / B, s = cs & 1, c = cs >> 1;
+    const int g = lane >> 4, comp = (lane >> 3) & 1, l = lane & 7;
+    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+    if (kF4Chunk * c + 64 * g < m) {
+      const int S = s_S[b];
+      const float f1 = ldexpf(1.0f, S / 2), f2 = ldexpf(1.0f, S - S / 2);   // 2^S, exact in two steps
+      const uint4* src = reinterpret_cast<const uint4*>(s_x + (int64_t)b * 2 * m + (int64_t)comp * m +
+                                                       kF4Chunk * c + 64 * g + 32 * s);
+      int fld[32];                                    // base-8 digit l of Y, columns 0..31
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint4 u = src[h];
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = bf16_lo(wd[e]), hi = bf16_hi(wd[e]);
+          const int Ylo = (int)rintf((lo * f1) * f2) + kDigitBias;
+          const int Yhi = (int)rintf((hi * f1) * f2) + kDigitBias;
+          fld[8 * h + 2 * e] = (Ylo >> (3 * l)) & 7;
+          fld[8 * h + 2 * e + 1] = (Yhi >> (3 * l)) & 7;
+        }
+      }
+      // element q = 4a + i of the operand is column f4_column(0, 0, q) (+16 for q >= 16)
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        uint32_t sel = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sel |= (uint32_t)fld[f4_column(0, 0, 4 * a + i)] << (8 * i);
+        const uint32_t codes = __builtin_amdgcn_perm(kF6CodesHi, kF6CodesLo, sel);
+        const uint32_t p24 = (codes & 0x3Fu) | ((codes >> 2) & 0xFC0u) | ((codes >> 4) & 0x3F000u) |
+                             ((codes >> 6) & 0xFC0000u);
+        const int bit = 24 * a;                       // bits 24a .. 24a + 23 of the 192-bit operand
+        w[bit >> 5] |= p24 << (bit & 31);
+        if ((bit & 31) > 8) w[(bit >> 5) + 1] |= p24 >> (32 - (bit & 31));
+      }
+    }
+    uint2* dst = reinterpret_cast<uint2*>(s_rec + rec * kRecBytes);
+    dst[0] = make_uint2(w[0], w[1]);
+    dst[1] = make_uint2(w[2], w[3]);
+    dst[2] = make_uint2(w[4], w[5]);
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------------- GEMV ----
 
 // One unit (a 16-row tile of one item) streamed by NW cooperating waves; `wave` is this wave's
@@ -192,10 +313,14 @@ hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blo
 // 16 T x 64 floats per wave) -- exact, since every partial and total is an integer below 2^24 --
 // and wave w then runs the single-wave epilogue for rows 4g + w, so the outputs are bit-identical
 // to one wave streaming the whole unit.
-template <int TT, int NW, int BT, typename YT, bool EXACT = false>
+// FUSED: x is bf16 [B][2m] (not its digit form) and the workgroup has built its records in s_rec
+// and S_b in s_S (build_f6_records) before its waves call this function.
+template <int TT, int NW, int BT, typename YT, bool EXACT = false, bool FUSED = false>
 __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B, int unit, int wave,
                                              float* __restrict__ s_scw, float (*s_y)[BT][2][16],
-                                             float* __restrict__ s_acc = nullptr) {
+                                             float* __restrict__ s_acc = nullptr,
+                                             const uint8_t* __restrict__ s_rec = nullptr,
+                                             const int* __restrict__ s_S = nullptr) {
   static_assert(!EXACT || (NW == 4 && BT == 1), "the exact split is for four waves and one batch entry");
   int tile;
   const GemvItem it = locate_item<YT>(grp, unit, tile);
@@ -224,17 +349,20 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
 #pragma unroll
         for (int b = 0; b < BT; ++b) acc[t][M][p][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  struct Chunk { uint4 w[TT][2]; v8i x[2][BT]; };     // codes; fp6 digit operands per step
+  // codes; fp6 digit operands per step (from the digit form; FUSED reads them from LDS instead)
+  struct Chunk { uint4 w[TT][2]; v8i x[FUSED ? 1 : 2][FUSED ? 1 : BT]; int c; };
   auto load_chunk = [&](int c, Chunk& ch) {
     const int groups = min(4, (m - kF4Chunk * c) >> 6);
     const bool k_ok = g < groups;
     const uint32_t cbase = (uint32_t)c * (TT * 2) * 1024;
+    ch.c = c;
 #pragma unroll
     for (int t = 0; t < TT; ++t)
 #pragma unroll
       for (int M = 0; M < 2; ++M)
         ch.w[t][M] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
             rsrc_a, k_ok ? cbase + (uint32_t)((t * 2 + M) * groups * 256 + lane * 16) : kNoLoad, 0, kStreamLoad));
+    if constexpr (FUSED) return;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -245,12 +373,27 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
             rsrc_x, ok ? off : kNoLoad, 0, 0));
         const v2i hi = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(
             rsrc_x, ok ? off + 16 : kNoLoad, 0, 0));
-        ch.x[s][b] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, 0, 0};
+        ch.x[FUSED ? 0 : s][FUSED ? 0 : b] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, 0, 0};
       }
   };
   auto compute_chunk = [&](const Chunk& ch) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      v8i xs[BT];                          // this step's B operands
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        if constexpr (FUSED) {
+          if (b < B) {
+            const uint2* rp = reinterpret_cast<const uint2*>(s_rec + (((ch.c * 2 + s) * B + b) * kWave + lane) * kRecBytes);
+            const uint2 r0 = rp[0], r1 = rp[1], r2 = rp[2];
+            xs[b] = v8i{(int)r0.x, (int)r0.y, (int)r1.x, (int)r1.y, (int)r2.x, (int)r2.y, 0, 0};
+          } else {
+            xs[b] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          }
+        } else {
+          xs[b] = ch.x[FUSED ? 0 : s][FUSED ? 0 : b];
+        }
+      }
 #pragma unroll
       for (int t = 0; t < TT; ++t)
 #pragma unroll
@@ -261,9 +404,9 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
 #pragma unroll
           for (int b = 0; b < BT; ++b) {
             acc[t][M][0][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pu, ch.x[s][b], acc[t][M][0][b], 4, 2, 0, 127, 0, 127);   // A fp4, B fp6 e2m3, scales 2^0
+                pu, xs[b], acc[t][M][0][b], 4, 2, 0, 127, 0, 127);   // A fp4, B fp6 e2m3, scales 2^0
             acc[t][M][1][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pv, ch.x[s][b], acc[t][M][1][b], 4, 2, 0, 127, 0, 127);
+                pv, xs[b], acc[t][M][1][b], 4, 2, 0, 127, 0, 127);
           }
         }
     }
@@ -316,6 +459,7 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
   // fp32 scales, the digit weight 2^(3l - S_b) / 6, and the sum over digits (xor 1, 2, 4) and
   // components (xor 8).
   if constexpr (EXACT) {
+    if constexpr (FUSED) __syncthreads();        // s_acc shares LDS with the records: all waves are past them
 #pragma unroll
     for (int t = 0; t < TT; ++t)
 #pragma unroll
@@ -343,7 +487,7 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
   const int64_t ys = 2 * (int64_t)n;
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
-    const int S = b < B ? hdr[2 + b] : 0;
+    const int S = b < B ? (FUSED ? s_S[b] : hdr[2 + b]) : 0;
     const float wdig = ldexpf(1.0f / 6.0f, 3 * l - S);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -395,12 +539,21 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
   }
 }
 
-template <int TT, int NW, int BT, typename YT>
+template <int TT, int NW, int BT, typename YT, bool FUSED>
 __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_gemv_f4(const GemvGroup grp, int m, int B) {
   __shared__ float s_sc[NW][16 * TT * 4];
   __shared__ float s_y[NW > 1 ? NW : 1][BT][2][16];     // [wave][batch][re/im][row]
+  __shared__ int s_S[2];
+  __shared__ float s_red[2 * NW];
+  extern __shared__ __align__(16) uint8_t s_dyn[];       // FUSED: records, then the staged x
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
-  gemv_f4_tile<TT, NW, BT, YT>(grp, m, B, blockIdx.x, wave, s_sc[wave], s_y);
+  if constexpr (FUSED) {
+    int tile;
+    const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
+    build_f6_records(static_cast<const uint16_t*>(it.x), m, B, s_dyn,
+                     reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)), s_S, s_red);
+  }
+  gemv_f4_tile<TT, NW, BT, YT, false, FUSED>(grp, m, B, blockIdx.x, wave, s_sc[wave], s_y, nullptr, s_dyn, s_S);
 }
 
 // Large batch-1 launches in two granularities.  The first nA workgroups take four units each,
@@ -408,17 +561,47 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
 // chunks split over the four waves.  Workgroups start in index order, so the units that finish a
 // launch are the short-lived ones: the launch's tail, where fewer and fewer waves remain in
 // flight, lasts about a quarter as long.  Both forms give the single-wave kernel's outputs bit for
-// bit (the split one adds its waves' exact integer accumulators before the epilogue).
-template <int TT, typename YT>
+// bit (the split one adds its waves' exact integer accumulators before the epilogue).  FUSED: the
+// four tiles of a workgroup share one set of records; the split form's accumulator exchange reuses
+// their LDS once every wave is past its last chunk.  (Every item of a launch shares x.)
+template <int TT, typename YT, bool FUSED>
 __global__ __launch_bounds__(kWave * 4, 3) void k_gemv_f4_mixed(const GemvGroup grp, int m, int nA) {
   __shared__ float s_sc[4][16 * TT * 4];
   __shared__ float s_y[4][1][2][16];
-  __shared__ float s_acc[4 * 16 * TT * kWave];
+  __shared__ float s_acc_own[FUSED ? 1 : 4 * 16 * TT * kWave];
+  __shared__ int s_S[2];
+  __shared__ float s_red[8];
+  extern __shared__ __align__(16) uint8_t s_dyn[];       // FUSED: records and staged x; then s_acc
+  float* s_acc = FUSED ? reinterpret_cast<float*>(s_dyn) : s_acc_own;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
+  if constexpr (FUSED)
+    build_f6_records(static_cast<const uint16_t*>(grp.items[0].x), m, 1, s_dyn,
+                     reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, 1)), s_S, s_red);
   if ((int)blockIdx.x < nA)
-    gemv_f4_tile<TT, 1, 1, YT>(grp, m, 1, 4 * (int)blockIdx.x + wave, 0, s_sc[wave], s_y);
+    gemv_f4_tile<TT, 1, 1, YT, false, FUSED>(grp, m, 1, 4 * (int)blockIdx.x + wave, 0, s_sc[wave], s_y, nullptr,
+                                             s_dyn, s_S);
   else
-    gemv_f4_tile<TT, 4, 1, YT, true>(grp, m, 1, 4 * nA + ((int)blockIdx.x - nA), wave, s_sc[wave], s_y, s_acc);
+    gemv_f4_tile<TT, 4, 1, YT, true, FUSED>(grp, m, 1, 4 * nA + ((int)blockIdx.x - nA), wave, s_sc[wave], s_y,
+                                            s_acc, s_dyn, s_S);
+}
+
+// FUSED launches of one wave per tile (at least 1536 tiles): workgroups of four waves stay resident
+// for the whole launch, build one set of records, and each wave then streams tiles
+// 4 blockIdx + wave, then 4 gridDim more, ... (the grid is the number of workgroups the chip holds
+// at once), so the records are built once per resident workgroup rather than once per four tiles.
+template <int TT, int BT, typename YT>
+__global__ __launch_bounds__(kWave * 4, (BT == 1 && TT <= 3) ? 3 : 1) void k_gemv_f4_persist(const GemvGroup grp, int m, int B) {
+  __shared__ float s_sc[4][16 * TT * 4];
+  __shared__ float s_y[1][BT][2][16];
+  __shared__ int s_S[2];
+  __shared__ float s_red[8];
+  extern __shared__ __align__(16) uint8_t s_dyn[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
+  build_f6_records(static_cast<const uint16_t*>(grp.items[0].x), m, B, s_dyn,
+                   reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)), s_S, s_red);
+  const int tiles = group_tiles(grp);
+  for (int unit = 4 * (int)blockIdx.x + wave; unit < tiles; unit += 4 * (int)gridDim.x)
+    gemv_f4_tile<TT, 1, BT, YT, false, true>(grp, m, B, unit, 0, s_sc[wave], s_y, nullptr, s_dyn, s_S);
 }
 
 // Mixed-granularity launches: units left to the one-unit-per-workgroup form at the end, and the
@@ -428,57 +611,107 @@ __global__ __launch_bounds__(kWave * 4, 3) void k_gemv_f4_mixed(const GemvGroup 
 constexpr int kF4TailTiles = 1536;
 constexpr int kF4MixedMinTiles = 12288;
 
-template <int TT, int BT, typename YT>
+// Dynamic LDS of a launch; the attribute that allows more than 64 KB is set once per kernel.
+template <typename K>
+static void lds_launch_prepare(K kernel, size_t bytes, bool& done) {
+  if (bytes > 65536 && !done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)bytes);
+    done = true;
+  }
+}
+
+template <int TT, int BT, typename YT, bool FUSED>
 static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
   GemvGroup grp = group;
   grp.units_per_item = grp.tiles_per_item;        // one workgroup per tile
   const int tiles = group_tiles(grp);
+  const size_t rec = FUSED ? (size_t)f4_record_bytes(m, B) + f4_xstage_bytes(m, B) : 0;
+  if constexpr (FUSED) {
+    if (gemv_waves_per_tile(tiles, m) == 1) {             // resident workgroups, four tiles at a time
+      static bool attr = false;
+      static int resident = 0;                            // workgroups the chip holds at once
+      lds_launch_prepare(k_gemv_f4_persist<TT, BT, YT>, rec, attr);
+      if (resident == 0) {
+        int per_cu = 0, dev = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_gemv_f4_persist<TT, BT, YT>),
+                                                         4 * kWave, rec) != hipSuccess || per_cu < 1)
+          per_cu = 1;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+          cus = 256;
+        resident = per_cu * cus;
+      }
+      const int grid = std::min((tiles + 3) / 4, resident);
+      hipLaunchKernelGGL((k_gemv_f4_persist<TT, BT, YT>), dim3(grid), dim3(4 * kWave), rec, s, grp, m, B);
+      return;
+    }
+  }
   if constexpr (BT == 1 && TT <= 3) {
     if (gemv_waves_per_tile(tiles, m) == 1 && tiles >= kF4MixedMinTiles) {
       const int nA = (tiles - kF4TailTiles) / 4;          // four units per workgroup
-      hipLaunchKernelGGL((k_gemv_f4_mixed<TT, YT>), dim3(nA + (tiles - 4 * nA)), dim3(4 * kWave), 0, s, grp, m, nA);
+      const size_t lds = FUSED ? std::max(rec, (size_t)4 * 16 * TT * kWave * sizeof(float)) : 0;
+      static bool attr = false;
+      lds_launch_prepare(k_gemv_f4_mixed<TT, YT, FUSED>, lds, attr);
+      hipLaunchKernelGGL((k_gemv_f4_mixed<TT, YT, FUSED>), dim3(nA + (tiles - 4 * nA)), dim3(4 * kWave), lds, s, grp,
+                         m, nA);
       return;
     }
   }
   const dim3 grid(tiles);
   switch (gemv_waves_per_tile(tiles, m)) {
-    case 8: hipLaunchKernelGGL((k_gemv_f4<TT, 8, BT, YT>), grid, dim3(8 * kWave), 0, s, grp, m, B); break;
-    case 4: hipLaunchKernelGGL((k_gemv_f4<TT, 4, BT, YT>), grid, dim3(4 * kWave), 0, s, grp, m, B); break;
-    case 2: hipLaunchKernelGGL((k_gemv_f4<TT, 2, BT, YT>), grid, dim3(2 * kWave), 0, s, grp, m, B); break;
-    default: hipLaunchKernelGGL((k_gemv_f4<TT, 1, BT, YT>), grid, dim3(kWave), 0, s, grp, m, B); break;
+#define F2I_F4_CASE(NWV)                                                                               \
+    {                                                                                                    \
+      static bool attr = false;                                                                          \
+      lds_launch_prepare(k_gemv_f4<TT, NWV, BT, YT, FUSED>, rec, attr);                                 \
+      hipLaunchKernelGGL((k_gemv_f4<TT, NWV, BT, YT, FUSED>), grid, dim3(NWV * kWave), rec, s, grp, m, B); \
+    }                                                                                                    \
+    break;
+    case 8: F2I_F4_CASE(8)
+    case 4: F2I_F4_CASE(4)
+    case 2: F2I_F4_CASE(2)
+    default: F2I_F4_CASE(1)
+#undef F2I_F4_CASE
   }
 }
 
-template <int TT, typename YT>
+template <int TT, typename YT, bool FUSED>
 static void launch_f4_b(const GemvGroup& grp, int m, int B, hipStream_t s) {
-  if (B == 1) launch_f4_t<TT, 1, YT>(grp, m, B, s);
-  else launch_f4_t<TT, 2, YT>(grp, m, B, s);
+  if (B == 1) launch_f4_t<TT, 1, YT, FUSED>(grp, m, B, s);
+  else launch_f4_t<TT, 2, YT, FUSED>(grp, m, B, s);
 }
 
-template <typename YT>
+template <typename YT, bool FUSED>
 static void launch_f4_y(const GemvGroup& grp, int m, int T, int B, hipStream_t s) {
   switch (T) {
-    case 1: launch_f4_b<1, YT>(grp, m, B, s); break;
-    case 2: launch_f4_b<2, YT>(grp, m, B, s); break;
-    case 3: launch_f4_b<3, YT>(grp, m, B, s); break;
-    default: launch_f4_b<4, YT>(grp, m, B, s); break;
+    case 1: launch_f4_b<1, YT, FUSED>(grp, m, B, s); break;
+    case 2: launch_f4_b<2, YT, FUSED>(grp, m, B, s); break;
+    case 3: launch_f4_b<3, YT, FUSED>(grp, m, B, s); break;
+    default: launch_f4_b<4, YT, FUSED>(grp, m, B, s); break;
   }
 }
 
-hipError_t launch_gemv_f4_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s) {
-  if (y_bf16) launch_f4_y<uint16_t>(grp, m, T, B, s);
-  else launch_f4_y<float>(grp, m, T, B, s);
+hipError_t launch_gemv_f4_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, int x_bf16, hipStream_t s) {
+  if (x_bf16) {
+    if (y_bf16) launch_f4_y<uint16_t, true>(grp, m, T, B, s);
+    else launch_f4_y<float, true>(grp, m, T, B, s);
+  } else {
+    if (y_bf16) launch_f4_y<uint16_t, false>(grp, m, T, B, s);
+    else launch_f4_y<float, false>(grp, m, T, B, s);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_f4(const uint8_t* packed, const float* scales, int n, int m, int T,
-                          const void* digits, int B, void* y, int y_bf16, hipStream_t s) {
+                          const void* x, int B, void* y, int y_bf16, int x_bf16, hipStream_t s) {
   GemvGroup grp;
   grp.count = 1;
   grp.tile_start[0] = 0;
   grp.tile_start[1] = (n + 15) / 16;
-  grp.items[0] = GemvItem{packed, scales, digits, y, n};
-  return launch_gemv_f4_group(grp, m, T, B, y_bf16, s);
+  grp.items[0] = GemvItem{packed, scales, x, y, n};
+  return launch_gemv_f4_group(grp, m, T, B, y_bf16, x_bf16, s);
 }
+
+int gemv_f4_record_bytes(int m, int B) { return f4_record_bytes(m, B); }
 
 }  // namespace f2i
