@@ -15,7 +15,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfairy2i.so")
+# FAIRY2I_LIB selects another build of the same library (the host-sanitized one, for instance).
+LIB_PATH = os.environ.get("FAIRY2I_LIB") or os.path.join(_HERE, "libfairy2i.so")
 
 FAIRY2I_OK = 0
 STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_STAGES", 4: "ERR_DTYPE",

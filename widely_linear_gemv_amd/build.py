@@ -1,9 +1,17 @@
 """Build libfairy2i.so in-tree with hipcc for gfx950.
 
-    python -m widely_linear_gemv_amd.build        # or: python widely_linear_gemv_amd/build.py
+    python -m widely_linear_gemv_amd.build              # or: python widely_linear_gemv_amd/build.py
+    python -m widely_linear_gemv_amd.build --host-san   # host-sanitized variant (see below)
 
 Each HIP source compiles to an object in _build/, then one shared library is linked next
 to this file.  Always recompiles (it is the "does it build" check as well as the build).
+
+The host-sanitized variant instruments the host half of every source (the C ABI's argument
+checks, size arithmetic and launch set-up) with AddressSanitizer and UndefinedBehaviorSanitizer;
+device code is compiled exactly as in the normal build.  It is linked to
+_build/host-san/libfairy2i.so without a sanitizer runtime: load it into a process that has the
+runtime preloaded (LD_PRELOAD=<clang>/lib/linux/libclang_rt.asan-x86_64.so) and point the
+binding at it with FAIRY2I_LIB.
 """
 from __future__ import annotations
 
@@ -19,6 +27,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfairy2i.so")
+SAN_BUILD = os.path.join(BUILD, "host-san")
+SAN_LIB = os.path.join(SAN_BUILD, "libfairy2i.so")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -44,30 +54,56 @@ SOURCES = {
 }
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-only instrumentation: each flag goes to the host compilation alone.
+HOST_SAN = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+
+
+def _compile(src: str, extra: list[str], out_dir: str = BUILD, host_flags: tuple = ()) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *host_flags, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, host_san: bool = False) -> str:
+    out_dir, lib_path = (SAN_BUILD, SAN_LIB) if host_san else (BUILD, LIB)
+    flags = tuple(HOST_SAN) if host_san else ()
+    os.makedirs(out_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], out_dir, flags), SOURCES.items()))
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
+
+
+def asan_runtime() -> str:
+    """Path of the AddressSanitizer runtime that the host-sanitized library needs preloaded."""
+    res = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+        return path
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(clang)) if os.path.isdir(clang) else []:
+        cand = os.path.join(clang, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(cand):
+            return os.path.realpath(cand)
+    raise RuntimeError("AddressSanitizer runtime libclang_rt.asan-x86_64.so not found")
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, host_san="--host-san" in sys.argv[1:])
     sys.exit(0)
