@@ -73,8 +73,10 @@ typedef enum {
   FAIRY2I_BF16 = 1,
   FAIRY2I_I8 = 2,
   FAIRY2I_I32 = 3,
-  FAIRY2I_X_DIGITS = 4,     /* decode-GEMV x in exact int8 digit form (fairy2i_x_digits) */
-  FAIRY2I_X_DIGITS_F6 = 5   /* decode-GEMV x in exact fp6 digit form (fairy2i_x_digits_f6) */
+  FAIRY2I_X_DIGITS = 4,     /* decode-GEMV x as 22-bit integers in int8 digits (fairy2i_x_digits):
+                             * each element off by at most 2^-22 of its column's max |x|, exact
+                             * for bf16 values within 2^14 of that maximum */
+  FAIRY2I_X_DIGITS_F6 = 5   /* the same integers in fp6 digits (fairy2i_x_digits_f6), same bound */
 } fairy2i_dtype;
 
 /* GEMV kernels.  AUTO picks MFMA_F4 for x in fp6 digit form, MFMA_I8 for x in int8 digit form,
@@ -171,7 +173,8 @@ int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* pac
  * W conj(x), with x held exactly as integers).  For each batch column b < B: one power of two
  * 2^S_b with max_j |x_b,j| 2^S_b in [2^21, 2^22) (S_b = 0 for an all-zero column), X =
  * round_half_even(x 2^S_b) -- exact for every bf16 value no more than 2^14 below the column
- * maximum, relative error below 2^-22 of the maximum otherwise -- and X = d0 + 2^8 d1 + 2^16 d2
+ * maximum; otherwise (smaller bf16 values, most fp32 values) off by at most 2^-22 of the column
+ * maximum, so an output moves by at most that times the sum of |R^| over its row -- and X = d0 + 2^8 d1 + 2^16 d2
  * with signed int8 digits.
  *   x        [B][2m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16, 16-byte aligned.  1 <= B <= 2.
  *   digits   out, fairy2i_x_digits_bytes(m, B) bytes, 16-byte aligned: int32 header
@@ -182,7 +185,7 @@ size_t fairy2i_x_digits_bytes(int64_t m, int64_t B);
 int fairy2i_x_digits(const void* x, int x_dtype, int64_t m, int64_t B, void* digits, hipStream_t stream);
 
 /* fp6 digit form of decode-GEMV activations, the input of the MFMA_F4 kernel.  The same X_b =
- * round_half_even(x_b 2^S_b) as fairy2i_x_digits (same S_b, same exactness), written with eight
+ * round_half_even(x_b 2^S_b) as fairy2i_x_digits (same S_b, same rounding), written with eight
  * balanced base-8 digits X = sum_l 8^l d_l, d_l in [-4, 3], each stored as fp6 e2m3 (exact).
  *   x        [B][2m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16, 16-byte aligned.  1 <= B <= 2.
  *   digits   out, fairy2i_x_digits_f6_bytes(m, B) = 64 + ceil(m / 256) * 4096 * B bytes,
