@@ -46,6 +46,11 @@ METRIC = "packed 2-bit widely-linear GEMV HBM GB/s (% peak) + prefill GEMM int8 
 POOL_BYTES = 2 ** 30     # 4x the 256 MB Infinity Cache: every pass streams from HBM
 
 
+def progress(msg: str) -> None:
+    """A progress line on stderr (stdout carries only the result line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -65,7 +70,7 @@ def parse():
 ROOF_PASSES = 8           # passes over the pool per roofline graph
 ROOF_WARM = 40            # untimed replays first (~60 ms of the same launches)
 ROOF_REPLAYS = 3
-TRAFFIC_PROFILE = "profiles/gemv_f4_strided_attention4096_T2_hbm_traffic.md"
+TRAFFIC_PROFILE = "profiles/gemv_strided_pool_attention4096_T2_hbm_traffic.md"
 
 
 def measured_traffic_per_layer():
@@ -452,6 +457,7 @@ def main():
     torch.cuda.synchronize()
     seg = np.zeros(NSEG)
     t0 = time.perf_counter()
+    progress(f"warm-up done; timing {args.steps} steps")
     all_events = [step() for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -654,11 +660,15 @@ def main():
             "wall_s": round(wall, 3),
         },
     }
+    progress("steps and kernel legs done")
     if not args.no_stack:
+        progress("32-layer stack legs")
         out["legs"].update(stack_legs(f2, torch, dev, T, reps=5))
     if not args.no_mlp:
+        progress("MLP-shape decode legs")
         out["legs"].update(mlp_legs(f2, torch, workloads, dev))
     if not args.no_cpu_baseline:
+        progress("CPU oracle baseline")
         x1 = workloads.activations(1, 2 * m, workloads.ATTN_X_SEEDS[1]).values
         out["cpu_baseline"] = cpu_baseline(R_np, T, x1, args.cpu_seconds, (Rp_np[0], xp_np.values))
     print(json.dumps(out), flush=True)
