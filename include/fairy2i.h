@@ -210,9 +210,12 @@ int fairy2i_x_digits_f6(const void* x, int x_dtype, int64_t m, int64_t B, void* 
 int fairy2i_dequantize(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                        void* R, int R_dtype, hipStream_t stream);
 
-/* Decode GEMV: y~[b] = sum_t U~(t) x[b] + W~(t) conj(x[b]) for b < B, every code an add,
- * subtract or real/imaginary swap with sign; one accumulator per (stage, matrix, axis) so each
- * scale multiplies an accumulated sum, not a weight.
+/* Decode GEMV: y~[b] = sum_t U~(t) x[b] + W~(t) conj(x[b]) for b < B (ModelScope card "Method":
+ * the widely-linear form y = U x + W conj(x), each matrix the sum of its T quantized terms;
+ * zhichai.net note "Industry implications": with codes in {+-1, +-i} every product is an add,
+ * subtract or real/imaginary swap with sign; 36Kr article: the stage terms are independent and
+ * summed).  One accumulator per (stage, matrix, axis), so each scale multiplies an accumulated
+ * sum, not a weight.
  *   packed, scales  as produced by fairy2i_quantize.
  *   x       [B][2m] with x_dtype FAIRY2I_F32 or FAIRY2I_BF16, or a digit form of such an x
  *           (x_dtype FAIRY2I_X_DIGITS or FAIRY2I_X_DIGITS_F6, made with the same m and B).
@@ -263,7 +266,9 @@ int fairy2i_gemv_strided(const uint8_t* packed, int64_t packed_stride, const flo
                          int x_dtype, int64_t B, void* y, int64_t y_stride, int y_dtype,
                          int64_t batch, int algo, hipStream_t stream);
 
-/* Per-token int8 activations: delta[tok] = fl32(max_j |x~_j| / 127),
+/* Per-token int8 activations for the prefill GEMM (the pages fix no activation format; this is
+ * the plainest integer form that lets the int8 matrix cores run the multiplication-free product
+ * of the zhichai.net note, "Industry implications"): delta[tok] = fl32(max_j |x~_j| / 127),
  * q = clamp(round_half_even(fl32(x~ / delta)), -127, 127); delta == 0 gives q = 0.
  *   x      [N][two_m], x_dtype FAIRY2I_F32 or FAIRY2I_BF16.  q out int8 [N][two_m],
  *   delta  out fp32 [N]. */
