@@ -27,6 +27,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfairy2i.so")
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi", "driver.c")
+C_DRIVER = os.path.join(ROOT, "tests", "c_abi", "fairy2i_c_driver")
 SAN_BUILD = os.path.join(BUILD, "host-san")
 SAN_LIB = os.path.join(SAN_BUILD, "libfairy2i.so")
 
@@ -90,6 +92,24 @@ def build(verbose: bool = False, host_san: bool = False) -> str:
     return lib_path
 
 
+def build_c_driver(verbose: bool = False) -> str:
+    """The plain-C driver of the ABI used by the tests (host code only, built with gcc against
+    include/fairy2i.h and the in-tree library)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    cc = shutil.which("gcc") or shutil.which("cc") or "gcc"
+    cmd = [cc, "-O2", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", os.path.join(rocm, "include"), C_DRIVER_SRC, "-L", PKG, "-lfairy2i",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../widely_linear_gemv_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", C_DRIVER]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C driver build failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {C_DRIVER}")
+    return C_DRIVER
+
+
 def asan_runtime() -> str:
     """Path of the AddressSanitizer runtime that the host-sanitized library needs preloaded."""
     res = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
@@ -105,5 +125,8 @@ def asan_runtime() -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True, host_san="--host-san" in sys.argv[1:])
+    san = "--host-san" in sys.argv[1:]
+    build(verbose=True, host_san=san)
+    if not san:
+        build_c_driver(verbose=True)
     sys.exit(0)
