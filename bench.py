@@ -237,6 +237,17 @@ def stack_legs(f2, torch, dev, T, reps):
         legs[f"stack_decode_b{B}"] = {"gemvs": 224, "launches": 128, "us": round(t * 1e3, 1),
                                       "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes,
                                       "kernel": "bf16 matrix cores (default for these latency-bound launches)"}
+        if B == 1:
+            # the fp4 kernel: with its digit pass in the step (256 launches), and on x already
+            # in digit form (the 128 GEMV launches alone, for inputs a producer writes in that form)
+            for given, key, note in ((False, "stack_decode_b1_f4", "fp4 matrix cores, fp6 digit pass per group"),
+                                     (True, "stack_decode_b1_f4_digits_given",
+                                      "fp4 matrix cores on x already in fp6 digit form (digit passes outside the step)")):
+                fstep = DecodeStep(layers, xs, algo=f2.GEMV_MFMA_F4, digits_given=given)
+                tf = timed(fstep.run)
+                legs[key] = {"gemvs": 224, "launches": 128 if given else 256, "us": round(tf * 1e3, 1),
+                             "GB/s": round(nbytes / (tf * 1e-3) / 1e9, 1), "kernel": note}
+                del fstep
     return legs
 
 

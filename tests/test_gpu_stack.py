@@ -53,14 +53,16 @@ def check(host, acts, ys, label):
             assert rel_l2(got, want) <= TOL_F32, (label, L, PROJECTIONS[p][0])
 
 
-@pytest.mark.parametrize("B,algo", [(1, None), (1, f2.GEMV_MFMA_F4), (2, f2.GEMV_MFMA_F4),
-                                    (2, f2.GEMV_MFMA_I8), (8, None)],
-                         ids=["b1-default", "b1-f4", "b2-f4", "b2-i8", "b8-default"])
-def test_two_layer_stack(B, algo):
-    """Default kernel (bf16 matrix cores on the bf16 x) and the digit-form kernels."""
+@pytest.mark.parametrize("B,algo,given", [(1, None, False), (1, f2.GEMV_MFMA_F4, False), (2, f2.GEMV_MFMA_F4, False),
+                                          (2, f2.GEMV_MFMA_I8, False), (8, None, False), (1, f2.GEMV_MFMA_F4, True),
+                                          (1, f2.GEMV_MFMA_I8, True)],
+                         ids=["b1-default", "b1-f4", "b2-f4", "b2-i8", "b8-default", "b1-f4-given", "b1-i8-given"])
+def test_two_layer_stack(B, algo, given):
+    """Default kernel (bf16 matrix cores on the bf16 x), the digit-form kernels with the digit
+    passes in the step, and with the digit forms made once beforehand."""
     dev = device()
     host, dev_layers, xs, acts = build(dev, 2, B)
-    step = DecodeStep(dev_layers, xs, algo=algo)
+    step = DecodeStep(dev_layers, xs, algo=algo, digits_given=given)
     announce("stack decode step B =", B, "algo", step.algo, "eager")
     check(host, acts, step.run(), f"eager B={B}")
     torch.cuda.synchronize()

@@ -10,7 +10,9 @@ a 32-layer stack is 128 launches, captured once in a HIP graph and replayed.  By
 launches take the bf16 x as it is (bf16 matrix cores): these launches are small (4-23 MB) and
 latency-bound, and a digit-form pass per group (needed by the fp4 and int8 kernels, which are
 faster per launch) costs more than it saves.  With algo=GEMV_MFMA_F4 or GEMV_MFMA_I8 each group
-first makes the digit form of its x.  This module only sequences
+first makes the digit form of its x; with digits_given=True the digit forms are made once when the
+step is built and the step runs the GEMVs alone (for inputs that arrive in digit form, from a
+producer that writes it).  This module only sequences
 calls of the C ABI (through the binding); all arithmetic runs in the library's kernels.
 """
 from __future__ import annotations
@@ -33,9 +35,11 @@ GROUPS = 4
 
 class DecodeStep:
     """layers[L][p] = (packed, scales) for projection p of layer L (shapes as PROJECTIONS);
-    xs[L][g] = bf16 input [B][2m] of group g of layer L.  Outputs: self.ys[L][p] fp32 [B][2n]."""
+    xs[L][g] = bf16 input [B][2m] of group g of layer L.  Outputs: self.ys[L][p] fp32 [B][2n].
+    digits_given (digit-form algos only): make each x's digit form once, here, instead of in
+    every run()."""
 
-    def __init__(self, layers, xs, *, algo: int | None = None):
+    def __init__(self, layers, xs, *, algo: int | None = None, digits_given: bool = False):
         self.layers, self.xs = layers, xs
         B = xs[0][0].shape[0]
         self.B = B
@@ -44,17 +48,26 @@ class DecodeStep:
         self.ys = [[torch.empty((B, rows), dtype=torch.float32, device=dev)
                     for (_, rows, _, _) in PROJECTIONS] for _ in layers]
         self.digits = None
+        if digits_given and self.algo not in _DIGIT_FORMS:
+            raise ValueError("digits_given needs a digit-form algo (GEMV_MFMA_F4 or GEMV_MFMA_I8)")
+        self.digits_given = digits_given
         if self.algo in _DIGIT_FORMS:
             nbytes, self._convert, code = _DIGIT_FORMS[self.algo]
             self.digits = [[XDigits(torch.empty((nbytes(x.shape[1] // 2, B),), dtype=torch.uint8, device=dev),
                                     B, x.shape[1] // 2, code)
                             for x in layer_xs] for layer_xs in xs]
+            if digits_given:
+                for layer_xs, layer_digits in zip(xs, self.digits):
+                    for x, d in zip(layer_xs, layer_digits):
+                        self._convert(x, out=d)
 
     def run(self, stream=None):
         for L, projs in enumerate(self.layers):
             for g in range(GROUPS):
                 x = self.xs[L][g]
-                if self.digits is not None:
+                if self.digits_given:
+                    x = self.digits[L][g]
+                elif self.digits is not None:
                     x = self._convert(x, out=self.digits[L][g], stream=stream)
                 items = [(projs[p][0], projs[p][1], x, self.ys[L][p])
                          for p, (_, _, _, grp) in enumerate(PROJECTIONS) if grp == g]
