@@ -27,8 +27,11 @@ form + fp4 GEMV launch) divided by its time (GB/s).  The JSON line also carries 
 of that GEMV kernel -- its launches timed, after the steps, in one graph of 8 back-to-back passes
 over the pool, so that graph-launch latency between segments does not count as kernel time --
 the other legs (GB/s, TOPS, params/s; the same pool through the grouped call, 48 layers per
-launch; one launch per layer) and the CPU oracle timed on a bounded sample of the same
-workload.
+launch; one launch per layer; fairy2i_gemv on the bf16 x as given, AUTO, at batch 1 and 2; the
+prefill GEMM on the 11008 x 4096 layer and on zero-valued data; the 32-layer stack's quantizer
+and decode step, the latter also on the fp4 kernel with and without its digit passes; the MLP
+shapes at T = 2 and 3) and the CPU oracle timed on a bounded sample of the same workload.
+Progress lines go to stderr; stdout carries the one JSON line.
 """
 from __future__ import annotations
 
