@@ -5,6 +5,8 @@ inputs, same order -- and so match the oracle within the fp32 tolerance.  Cases 
 form: small launches (a tile's chunks split over 2, 4 or 8 waves), one wave per tile, the
 mixed-granularity large launch (four tiles per workgroup sharing the records, then the split
 tail), batch 1 and 2, T = 1..4, ragged rows and the longest rows the records allow."""
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -103,3 +105,66 @@ def test_fused_grouped_and_zero_column():
         assert np.array_equal(bits(down(y)), bits(down(y2)))
         assert np.all(down(y)[1] == 0.0)
         assert rel_l2(down(y)[0], want[0]) <= TOL_F32
+
+
+@pytest.mark.parametrize("B,m,T", [(1, 8192, 2), (2, 4096, 2), (2, 64, 1), (1, 5504, 3), (2, 2048, 4)])
+def test_fused_persistent_row_lengths(B, m, T):
+    """The resident-workgroup form (launches of at least 1536 tiles) up to the longest rows whose
+    records fit: batch 2 builds its records from x in global memory (no staged copy), batch 1 from
+    the copy in LDS.  One-tile layers, so the launch's tile count is the layer count; every output
+    against the two-call form bit for bit, sampled layers against the oracle."""
+    dev = device()
+    n, batch = 16, 1540
+    g = torch.Generator(device=dev)
+    g.manual_seed(m + 10 * B + T)
+    nb = f2.fairy2i_packed_bytes(n, m, T)
+    pool = torch.randint(0, 256, (batch, nb), dtype=torch.uint8, device=dev, generator=g)
+    spool = (torch.rand((batch, n, T, 2, 2), device=dev, generator=g) * 0.02).contiguous()
+    act = workloads.activations(B, 2 * m, seed=970 + B + m)
+    x = x_to_dev(act, dev)
+    y1 = torch.empty((batch, B, 2 * n), device=dev)
+    y2 = torch.empty_like(y1)
+    announce("gemv fp4 fused persistent", B, m, T)
+    f2.fairy2i_gemv_strided(pool, spool, x, y1, algo=f2.GEMV_MFMA_F4)
+    f2.fairy2i_gemv_strided(pool, spool, f2.fairy2i_x_digits_f6(x), y2, algo=f2.GEMV_MFMA_F4)
+    a = down(y1)
+    assert np.array_equal(bits(a), bits(down(y2)))
+    for k in (0, batch - 1):
+        codes = oracle.unpack(down(pool[k]), n, m, T)
+        assert rel_l2(a[k], oracle.gemv_ref(codes, down(spool[k]), act.values)) <= TOL_F32, k
+
+
+_LDS_ORDER = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import widely_linear_gemv_amd as f2
+dev = torch.device("cuda:0")
+g = torch.Generator(device=dev)
+g.manual_seed(5)
+for n, batch in ((40, 1), (16, 1540)):          # small launches, then the resident-workgroup form
+    for m in (4160, 8192):                       # 67 KB of LDS first, then 128 KB
+        nb = f2.fairy2i_packed_bytes(n, m, 2)
+        pool = torch.randint(0, 256, (batch, nb), dtype=torch.uint8, device=dev, generator=g)
+        sc = (torch.rand((batch, n, 2, 2, 2), device=dev, generator=g) * 0.02).contiguous()
+        x = torch.randn((1, 2 * m), device=dev, generator=g).to(torch.bfloat16)
+        y1 = torch.empty((batch, 1, 2 * n), device=dev)
+        y2 = torch.empty_like(y1)
+        f2.fairy2i_gemv_strided(pool, sc, x, y1, algo=f2.GEMV_MFMA_F4)
+        f2.fairy2i_gemv_strided(pool, sc, f2.fairy2i_x_digits_f6(x), y2, algo=f2.GEMV_MFMA_F4)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), (n, batch, m)
+print("lds order ok")
+"""
+
+
+def test_fused_lds_limit_grows_within_a_process():
+    """A fresh process whose first launches on bf16 x need just over 64 KB of LDS and whose later
+    ones need 128 KB: the kernels' LDS limit is set for the largest launch the API accepts, so
+    the later launches run too (they used to fail with the limit of the first)."""
+    import os
+    import subprocess
+    device()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    announce("gemv fp4 fused LDS limit in a fresh process")
+    res = subprocess.run([sys.executable, "-c", _LDS_ORDER, root], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0 and "lds order ok" in res.stdout, res.stdout[-2000:] + res.stderr[-2000:]

@@ -212,9 +212,13 @@ __host__ __device__ inline int f4_record_bytes(int m, int B) {
 // LDS bytes of the staged bf16 x of B batch entries (2m values each).
 __host__ __device__ inline int f4_xstage_bytes(int m, int B) { return 4 * m * B; }
 
-// Workgroup-collective: copies x (bf16 [B][2m]) into s_x (its loads all issued before any is
-// waited on), takes S_b of every batch entry into s_S[b], then builds every record into s_rec from
-// the staged copy.  Ends with a barrier.  s_red holds one float per wave and batch entry.
+// Workgroup-collective: reads x (bf16 [B][2m]; its loads all issued before any is waited on),
+// takes S_b of every batch entry into s_S[b], then builds every record into s_rec.  kStage: x is
+// copied into s_x on the first pass and the records are built from that copy; otherwise they read
+// x again from global memory (from L2: every workgroup of the launch reads the same x), which
+// leaves the workgroup only the records' LDS.  Ends with a barrier.  s_red holds one float per
+// wave and batch entry.
+template <bool kStage>
 __device__ void build_f6_records(const uint16_t* __restrict__ x, int m, int B, uint8_t* __restrict__ s_rec,
                                  uint16_t* __restrict__ s_x, int* __restrict__ s_S, float* __restrict__ s_red) {
   const int tid = threadIdx.x, nthr = blockDim.x, nwave = nthr / kWave;
@@ -233,7 +237,7 @@ __device__ void build_f6_records(const uint16_t* __restrict__ x, int m, int B, u
     for (int k = 0; k < kBatch; ++k) {
       const int u = u0 + k * nthr;
       if (u < units) {
-        reinterpret_cast<uint4*>(s_x)[u] = v[k];
+        if constexpr (kStage) reinterpret_cast<uint4*>(s_x)[u] = v[k];
         const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
         float mx = 0.f;
 #pragma unroll
@@ -267,7 +271,7 @@ __device__ void build_f6_records(const uint16_t* __restrict__ x, int m, int B, u
     if (kF4Chunk * c + 64 * g < m) {
       const int S = s_S[b];
       const float f1 = ldexpf(1.0f, S / 2), f2 = ldexpf(1.0f, S - S / 2);   // 2^S, exact in two steps
-      const uint4* src = reinterpret_cast<const uint4*>(s_x + (int64_t)b * 2 * m + (int64_t)comp * m +
+      const uint4* src = reinterpret_cast<const uint4*>((kStage ? s_x : x) + (int64_t)b * 2 * m + (int64_t)comp * m +
                                                        kF4Chunk * c + 64 * g + 32 * s);
       int fld[32];                                    // base-8 digit l of Y, columns 0..31
 #pragma unroll
@@ -438,6 +442,22 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
     }
     if (c < nchunk) compute_chunk(c0);
     if (c + NW < nchunk) compute_chunk(c1);
+  } else if constexpr (BT == 2 || FUSED) {
+    // One chunk per iteration, the prefetched set copied into place at its end (16 moves per
+    // chunk).  With the loop unrolled over two sets instead, the register allocator moves the
+    // accumulators between register ranges every iteration (64-192 accumulator moves per 32-96
+    // MFMAs at batch 2), which also raised the batch-2 kernels from 164-168 to 212-228 registers
+    // (two waves per SIMD instead of three).
+    Chunk cur, nxt;
+    int c = wave;
+    load_chunk(c, cur);
+    tsc.park(s_scw, lane);
+    for (; c < nchunk; c += NW) {
+      load_chunk(c + NW, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk(cur);
+      cur = nxt;
+    }
   } else {
     Chunk c0, c1;
     int c = wave;
@@ -735,8 +755,8 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
   if constexpr (FUSED) {
     int tile;
     const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
-    build_f6_records(static_cast<const uint16_t*>(it.x), m, B, s_dyn,
-                     reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)), s_S, s_red);
+    build_f6_records<true>(static_cast<const uint16_t*>(it.x), m, B, s_dyn,
+                           reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)), s_S, s_red);
   }
   gemv_f4_tile<TT, NW, BT, YT, false, FUSED>(grp, m, B, blockIdx.x, wave, s_sc[wave], s_y, nullptr, s_dyn, s_S);
 }
@@ -760,8 +780,8 @@ __global__ __launch_bounds__(kWave * 4, 3) void k_gemv_f4_mixed(const GemvGroup 
   float* s_acc = FUSED ? reinterpret_cast<float*>(s_dyn) : s_acc_own;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   if constexpr (FUSED)
-    build_f6_records(static_cast<const uint16_t*>(grp.items[0].x), m, 1, s_dyn,
-                     reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, 1)), s_S, s_red);
+    build_f6_records<true>(static_cast<const uint16_t*>(grp.items[0].x), m, 1, s_dyn,
+                           reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, 1)), s_S, s_red);
   if ((int)blockIdx.x < nA)
     gemv_f4_tile<TT, 1, 1, YT, false, FUSED>(grp, m, 1, 4 * (int)blockIdx.x + wave, 0, s_sc[wave], s_y, nullptr,
                                              s_dyn, s_S);
@@ -782,8 +802,9 @@ __global__ __launch_bounds__(kWave * 4, (BT == 1 && TT <= 3) ? 3 : 1) void k_gem
   __shared__ float s_red[8];
   extern __shared__ __align__(16) uint8_t s_dyn[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
-  build_f6_records(static_cast<const uint16_t*>(grp.items[0].x), m, B, s_dyn,
-                   reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)), s_S, s_red);
+  // batch 2 builds without the staged copy of x: the records alone let three workgroups share a CU
+  build_f6_records<BT == 1>(static_cast<const uint16_t*>(grp.items[0].x), m, B, s_dyn,
+                            BT == 1 ? reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)) : nullptr, s_S, s_red);
   const int tiles = group_tiles(grp);
   if constexpr (BT == 1) {
     gemv_f4_stream<TT, BT, YT>(grp, m, B, 4 * (int)blockIdx.x + wave, 4 * (int)gridDim.x, tiles, s_sc[wave], s_dyn, s_S);
@@ -802,12 +823,20 @@ __global__ __launch_bounds__(kWave * 4, (BT == 1 && TT <= 3) ? 3 : 1) void k_gem
 constexpr int kF4TailTiles = 1536;
 constexpr int kF4MixedMinTiles = 12288;
 
-// Dynamic LDS of a launch; the attribute that allows more than 64 KB is set once per kernel.
+// Most dynamic LDS a launch on bf16 x can take with BT batch entries per tile: records (and the
+// staged x, if kept) of m B <= 8192 columns, the most the C ABI accepts on this path.
+static size_t f4_fused_lds_max(int BT, bool stage) {
+  const int m = 8192 / BT;
+  return (size_t)f4_record_bytes(m, BT) + (stage ? (size_t)f4_xstage_bytes(m, BT) : 0);
+}
+
+// Dynamic LDS above 64 KB needs a kernel attribute; it is set once per kernel, to the most any of
+// its launches can take, so later launches with larger rows are covered too.
 template <typename K>
-static void lds_launch_prepare(K kernel, size_t bytes, bool& done) {
-  if (bytes > 65536 && !done) {
+static void lds_launch_prepare(K kernel, size_t max_bytes, bool& done) {
+  if (max_bytes > 65536 && !done) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)bytes);
+                              (int)max_bytes);
     done = true;
   }
 }
@@ -820,21 +849,24 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
   const size_t rec = FUSED ? (size_t)f4_record_bytes(m, B) + f4_xstage_bytes(m, B) : 0;
   if constexpr (FUSED) {
     if (gemv_waves_per_tile(tiles, m) == 1) {             // resident workgroups, four tiles at a time
+      const size_t lds = BT == 1 ? rec : (size_t)f4_record_bytes(m, B);
       static bool attr = false;
-      static int resident = 0;                            // workgroups the chip holds at once
-      lds_launch_prepare(k_gemv_f4_persist<TT, BT, YT>, rec, attr);
-      if (resident == 0) {
+      static size_t resident_lds = 0;
+      static int resident = 0;                            // workgroups the chip holds at once with that LDS
+      lds_launch_prepare(k_gemv_f4_persist<TT, BT, YT>, f4_fused_lds_max(BT, BT == 1), attr);
+      if (resident == 0 || resident_lds != lds) {
         int per_cu = 0, dev = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_gemv_f4_persist<TT, BT, YT>),
-                                                         4 * kWave, rec) != hipSuccess || per_cu < 1)
+                                                         4 * kWave, lds) != hipSuccess || per_cu < 1)
           per_cu = 1;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
           cus = 256;
         resident = per_cu * cus;
+        resident_lds = lds;
       }
       const int grid = std::min((tiles + 3) / 4, resident);
-      hipLaunchKernelGGL((k_gemv_f4_persist<TT, BT, YT>), dim3(grid), dim3(4 * kWave), rec, s, grp, m, B);
+      hipLaunchKernelGGL((k_gemv_f4_persist<TT, BT, YT>), dim3(grid), dim3(4 * kWave), lds, s, grp, m, B);
       return;
     }
   }
@@ -843,7 +875,9 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
       const int nA = (tiles - kF4TailTiles) / 4;          // four units per workgroup
       const size_t lds = FUSED ? std::max(rec, (size_t)4 * 16 * TT * kWave * sizeof(float)) : 0;
       static bool attr = false;
-      lds_launch_prepare(k_gemv_f4_mixed<TT, YT, FUSED>, lds, attr);
+      lds_launch_prepare(k_gemv_f4_mixed<TT, YT, FUSED>,
+                         FUSED ? std::max(f4_fused_lds_max(1, true), (size_t)4 * 16 * TT * kWave * sizeof(float)) : 0,
+                         attr);
       hipLaunchKernelGGL((k_gemv_f4_mixed<TT, YT, FUSED>), dim3(nA + (tiles - 4 * nA)), dim3(4 * kWave), lds, s, grp,
                          m, nA);
       return;
@@ -854,7 +888,7 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
 #define F2I_F4_CASE(NWV)                                                                               \
     {                                                                                                    \
       static bool attr = false;                                                                          \
-      lds_launch_prepare(k_gemv_f4<TT, NWV, BT, YT, FUSED>, rec, attr);                                 \
+      lds_launch_prepare(k_gemv_f4<TT, NWV, BT, YT, FUSED>, FUSED ? f4_fused_lds_max(BT, true) : 0, attr);  \
       hipLaunchKernelGGL((k_gemv_f4<TT, NWV, BT, YT, FUSED>), grid, dim3(NWV * kWave), rec, s, grp, m, B); \
     }                                                                                                    \
     break;
