@@ -123,8 +123,12 @@ __device__ __forceinline__ void flush_partials(v4f (&acc)[TT][2][2][CG], const f
   flushed = true;
 }
 
+// At most eight batch columns (CG = 1) the hint of two waves per SIMD keeps every accumulator in
+// the arch registers: without it the allocator placed some of them in the accumulation registers
+// and moved them back and forth every iteration (12-80 moves per 64-130 MFMAs at T = 2), taking
+// 240 registers where 148 do (three waves per SIMD); with two column groups the same hint spills.
 template <int TT, int CG, int NW, typename YT, bool LONG>
-__global__ __launch_bounds__(kWave * NW) void k_gemv_mfma(const GemvGroup grp, int m, int B) {
+__global__ __launch_bounds__(kWave * NW, CG == 1 ? 2 : 1) void k_gemv_mfma(const GemvGroup grp, int m, int B) {
   int tile;
   const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
   const int n = it.n;
