@@ -171,7 +171,8 @@ def cpu_baseline(R, T, x1, budget_s, prefill):
 
 def stack_legs(f2, torch, dev, T, reps):
     """The LLaMA-2 7B linear stack (32 layers x 7 projections, 6.48e9 real weights): quantize all
-    224 matrices, then one decode step (grouped launches per shared input, the stack's default
+    224 matrices (grouped calls, the matrices of one shape sharing launches; and, for comparison,
+    one call per matrix), then one decode step (grouped launches per shared input, the stack's default
     kernel) at batch 1 and batch 8, each captured in a HIP graph.  The weights are the pinned
     generator's (workloads.stack_layer: NumPy, seed 5000 + 7 L + p, N(0, 0.02^2)), drawn on host
     threads and copied to the GPU (25.9 GB in all), the same matrices the GPU parity test samples;
@@ -195,7 +196,16 @@ def stack_legs(f2, torch, dev, T, reps):
         out.append({"packed": torch.empty((f2.fairy2i_packed_bytes(n, m, T),), dtype=torch.uint8, device=dev),
                     "scales": torch.empty((n, T, 2, 2), dtype=torch.float32, device=dev)})
 
+    by_shape = {}                   # grouped calls: the matrices of one shape share launches
+    for r, o in zip(R, out):
+        by_shape.setdefault(tuple(r.shape), []).append((r, o))
+
     def quantize_all():
+        for items in by_shape.values():
+            f2.fairy2i_quantize_grouped([r for r, _ in items], T, packed=[o["packed"] for _, o in items],
+                                        scales=[o["scales"] for _, o in items])
+
+    def quantize_each():
         for r, o in zip(R, out):
             f2.fairy2i_quantize(r, T, packed=o["packed"], scales=o["scales"])
 
@@ -218,9 +228,12 @@ def stack_legs(f2, torch, dev, T, reps):
         return e0.elapsed_time(e1) / reps          # ms
 
     t_q = timed(quantize_all)
+    t_q1 = timed(quantize_each)
     layers = [[(out[7 * L + p]["packed"], out[7 * L + p]["scales"]) for p in range(7)] for L in range(32)]
     r_bytes = sum(r.numel() * 4 for r in R)
-    legs = {"stack_quantize": {"matrices": 224, "ms": round(t_q, 3), "R_GB/s": round(r_bytes / (t_q * 1e-3) / 1e9, 1),
+    legs = {"stack_quantize": {"matrices": 224, "launches": sum((len(v) + 31) // 32 for v in by_shape.values()),
+                               "ms": round(t_q, 3), "R_GB/s": round(r_bytes / (t_q * 1e-3) / 1e9, 1),
+                               "one_call_per_matrix_ms": round(t_q1, 3),
                                "real_params_per_s": round(sum(r.numel() for r in R) / (t_q * 1e-3), 1),
                                "weights": f"pinned NumPy generator (seed 5000 + 7 L + p), drawn on {workers} "
                                           f"host threads in {gen_s:.1f} s"}}

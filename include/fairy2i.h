@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FAIRY2I_ABI_VERSION 6
+#define FAIRY2I_ABI_VERSION 7
 
 typedef enum {
   FAIRY2I_OK = 0,
@@ -125,7 +125,8 @@ size_t fairy2i_packed_bytes(int64_t n, int64_t m, int T);
  *   scales   out, fp32 [n][T][2][2] (round-to-nearest-even of the fp64 scales).
  *   scales64 optional out (NULL skips), fp64 [n][T][2][2].
  *   codes    optional out (NULL skips), uint8 [T][2][n][m], one code per byte.
- * Extra requirement: 2*T*m <= 65536 (codes of one row are staged on chip). */
+ * Extra requirements: 2*T*m <= 65536 (codes of one row are staged on chip); ceil(n / 16) * 16
+ * < 2^24 (one workgroup per row, one launch). */
 int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T,
                      uint8_t* packed, float* scales, double* scales64, uint8_t* codes,
                      hipStream_t stream);
@@ -136,6 +137,26 @@ int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T,
 int fairy2i_quantize_bf16(const uint16_t* R, int64_t two_n, int64_t two_m, int T,
                           uint8_t* packed, float* scales, double* scales64, uint8_t* codes,
                           hipStream_t stream);
+
+/* fairy2i_quantize on count layers of one shape, in as few launches as the per-launch table
+ * allows (32 layers each): every layer is quantized exactly as by its own fairy2i_quantize call
+ * (same codes, packed bytes and scales, bit for bit), but the layers' rows share launches, so a
+ * stack of small layers fills the device instead of ending every launch on a partial round of
+ * workgroups.  Arguments are host arrays of count device pointers:
+ *   R         [count] layers [two_n][two_m], R_dtype FAIRY2I_F32 (4-byte aligned) or
+ *             FAIRY2I_BF16 (raw bits, 2-byte aligned, widened exactly); read only.
+ *   packed    [count] out, each fairy2i_packed_bytes(n, m, T) bytes, 16-byte aligned.
+ *   scales    [count] out, each fp32 [n][T][2][2].
+ *   scales64  NULL, or [count] optional outs (entries may be NULL), each fp64 [n][T][2][2].
+ *   codes     NULL, or [count] optional outs (entries may be NULL), each uint8 [T][2][n][m],
+ *             16-byte aligned.
+ * count = 0 does nothing; count < 0 or more rows than one launch can address
+ * (min(count, 32) * ceil(n / 16) * 16 >= 2^24) is FAIRY2I_ERR_SHAPE; a NULL array or R,
+ * packed or scales entry is FAIRY2I_ERR_NULL.  Nothing is launched unless every argument
+ * passes.  Extra requirement as fairy2i_quantize: 2*T*m <= 65536. */
+int fairy2i_quantize_grouped(int count, const void* const* R, int R_dtype, int64_t two_n, int64_t two_m, int T,
+                             uint8_t* const* packed, float* const* scales, double* const* scales64,
+                             uint8_t* const* codes, hipStream_t stream);
 
 /* Device workspace bytes of fairy2i_quantize_tensor for n complex rows: 40 n rounded up to a
  * multiple of 16, plus 128 (0 when n is out of range; m and T do not enter). */
@@ -155,7 +176,8 @@ size_t fairy2i_quantize_tensor_workspace_bytes(int64_t n, int64_t m, int T);
  *               and undefined on return.  Calls that share one workspace must not overlap.
  *   packed, scales, scales64, codes  as fairy2i_quantize; every row of scales (scales64) holds
  *               the same pairs, so every consumer of fairy2i_quantize's output takes them as is.
- * Runs as 2T + 1 launches on stream.  Extra requirement: m <= 32768.  Error codes as
+ * Runs as 2T + 1 launches on stream.  Extra requirements: m <= 32768, and n as for
+ * fairy2i_quantize.  Error codes as
  * fairy2i_quantize, plus FAIRY2I_ERR_WORKSPACE for a short workspace and FAIRY2I_ERR_DTYPE
  * for another R_dtype. */
 int fairy2i_quantize_tensor(const void* R, int R_dtype, int64_t two_n, int64_t two_m, int T,
@@ -206,7 +228,8 @@ int fairy2i_x_digits_f6(const void* x, int x_dtype, int64_t m, int64_t B, void* 
  * The stage sums run over t in order in fp32.
  *   packed, scales  as produced by fairy2i_quantize.
  *   R       out, [2n][2m] row-major, R_dtype FAIRY2I_F32 or FAIRY2I_BF16 (round to nearest even),
- *           16-byte aligned. */
+ *           16-byte aligned.
+ * Extra requirement: n as for fairy2i_quantize (one workgroup per row). */
 int fairy2i_dequantize(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                        void* R, int R_dtype, hipStream_t stream);
 

@@ -70,6 +70,21 @@ static void fetch(const char* dir, const char* name, const void* dev, size_t byt
   free(h);
 }
 
+/* two device buffers hold the same bytes */
+static void same_bytes(const void* a, const void* b, size_t bytes, const char* what) {
+  void* ha = malloc(bytes);
+  void* hb = malloc(bytes);
+  if (!ha || !hb) exit(2);
+  CHECK_HIP(hipMemcpy(ha, a, bytes, hipMemcpyDeviceToHost));
+  CHECK_HIP(hipMemcpy(hb, b, bytes, hipMemcpyDeviceToHost));
+  if (memcmp(ha, hb, bytes) != 0) {
+    fprintf(stderr, "%s: bytes differ\n", what);
+    failed = 1;
+  }
+  free(ha);
+  free(hb);
+}
+
 int main(int argc, char** argv) {
   if (argc != 7) {
     fprintf(stderr, "usage: %s DIR two_n two_m T B N\n", argv[0]);
@@ -80,7 +95,7 @@ int main(int argc, char** argv) {
   const int T = atoi(argv[4]);
   const int64_t B = atoll(argv[5]), N = atoll(argv[6]);
   const int64_t n = two_n / 2, m = two_m / 2;
-  if (fairy2i_abi_version() != 6) { fprintf(stderr, "ABI version %d\n", fairy2i_abi_version()); return 2; }
+  if (fairy2i_abi_version() != 7) { fprintf(stderr, "ABI version %d\n", fairy2i_abi_version()); return 2; }
 
   const size_t r_bytes = (size_t)(two_n * two_m) * sizeof(float);
   const size_t x_bytes = (size_t)(B * two_m) * sizeof(float);
@@ -112,6 +127,13 @@ int main(int argc, char** argv) {
 
   expect(fairy2i_quantize((const float*)R, two_n, two_m, T, (uint8_t*)packed, (float*)scales, (double*)scales64,
                           NULL, s), FAIRY2I_OK, "fairy2i_quantize");
+  /* the same layer twice through the grouped call: both copies equal the single call */
+  const void* g_R[2] = {R, R};
+  uint8_t* g_packed[2] = {(uint8_t*)to_device(NULL, packed_bytes), (uint8_t*)to_device(NULL, packed_bytes)};
+  float* g_scales[2] = {(float*)to_device(NULL, nscale * sizeof(float)), (float*)to_device(NULL, nscale * sizeof(float))};
+  double* g_scales64[2] = {(double*)to_device(NULL, nscale * sizeof(double)), NULL};
+  expect(fairy2i_quantize_grouped(2, g_R, FAIRY2I_F32, two_n, two_m, T, g_packed, g_scales, g_scales64, NULL, s),
+         FAIRY2I_OK, "fairy2i_quantize_grouped");
   expect(fairy2i_gemv((const uint8_t*)packed, (const float*)scales, n, m, T, x, FAIRY2I_F32, B, y_valu, FAIRY2I_F32,
                       FAIRY2I_GEMV_VALU, s), FAIRY2I_OK, "fairy2i_gemv (VALU)");
   if (B <= 2) {
@@ -133,6 +155,11 @@ int main(int argc, char** argv) {
                       FAIRY2I_GEMV_MFMA_BF16, s), FAIRY2I_ERR_DTYPE, "bf16 kernel on fp32 x");
 
   CHECK_HIP(hipStreamSynchronize(s));
+  for (int k = 0; k < 2; ++k) {
+    same_bytes(g_packed[k], packed, packed_bytes, "grouped quantize: packed");
+    same_bytes(g_scales[k], scales, nscale * sizeof(float), "grouped quantize: scales");
+  }
+  same_bytes(g_scales64[0], scales64, nscale * sizeof(double), "grouped quantize: scales64");
   fetch(dir, "packed.u8", packed, packed_bytes);
   fetch(dir, "scales.f32", scales, nscale * sizeof(float));
   fetch(dir, "scales64.f64", scales64, nscale * sizeof(double));
@@ -145,6 +172,8 @@ int main(int argc, char** argv) {
   hipFree(R); hipFree(x); hipFree(xp); hipFree(packed); hipFree(scales); hipFree(scales64);
   hipFree(y_valu); hipFree(y_f4); hipFree(digits); hipFree(p); hipFree(delta);
   if (ws) hipFree(ws);
+  for (int k = 0; k < 2; ++k) { hipFree(g_packed[k]); hipFree(g_scales[k]); }
+  hipFree(g_scales64[0]);
   free(hR); free(hx); free(hxp);
   if (failed) return 1;
   printf("ok\n");

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert f2.fairy2i_abi_version() == 6
+    assert f2.fairy2i_abi_version() == 7
     for s in range(8):
         assert f2.fairy2i_status_string(s) not in ("", "unknown status")
     assert f2.fairy2i_status_string(99) == "unknown status"
@@ -75,6 +75,38 @@ def test_quantize_bf16_errors(L):
     assert q(FAKE, 256, 256, 5, FAKE, FAKE, NULL, NULL, S) == 3
     assert q(FAKE, 255, 256, 2, FAKE, FAKE, NULL, NULL, S) == 2
     assert q(FAKE + 1, 256, 256, 2, FAKE, FAKE, NULL, NULL, S) == 5
+
+
+def test_quantize_row_launch_bound(L):
+    # one workgroup per row: more than 2^24 - 16 rows is a shape error for every row kernel
+    big = 2 * ((1 << 24) + 16)
+    assert L.fairy2i_quantize(FAKE, big, 256, 2, FAKE, FAKE, NULL, NULL, S) == 2
+    assert "at most" in last()
+    assert L.fairy2i_dequantize(FAKE, FAKE, big // 2, 128, 2, FAKE, 0, S) == 2
+
+
+def _ptrs(*vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def test_quantize_grouped_errors(L):
+    q = L.fairy2i_quantize_grouped
+    R, P, Sc = _ptrs(FAKE, FAKE), _ptrs(FAKE, FAKE), _ptrs(FAKE, FAKE)
+    assert q(0, NULL, 0, 256, 256, 2, NULL, NULL, NULL, NULL, S) == 0            # nothing to do
+    assert q(-1, R, 0, 256, 256, 2, P, Sc, NULL, NULL, S) == 2
+    assert q(2, NULL, 0, 256, 256, 2, P, Sc, NULL, NULL, S) == 1
+    assert q(2, R, 7, 256, 256, 2, P, Sc, NULL, NULL, S) == 4                     # R dtype
+    assert q(2, R, 0, 256, 256, 5, P, Sc, NULL, NULL, S) == 3
+    assert q(2, R, 0, 255, 256, 2, P, Sc, NULL, NULL, S) == 2
+    assert q(2, R, 0, 256, 2 * 16384 + 128, 2, P, Sc, NULL, NULL, S) == 2          # 2*T*m too big
+    assert q(2, R, 0, 2 * (1 << 23), 256, 2, P, Sc, NULL, NULL, S) == 2            # 2 x 2^23 rows >= 2^24
+    assert "workgroups" in last()
+    assert q(2, _ptrs(FAKE, NULL), 0, 256, 256, 2, P, Sc, NULL, NULL, S) == 1      # a NULL entry
+    assert "layer 1" in last()
+    assert q(2, R, 0, 256, 256, 2, _ptrs(FAKE, FAKE_ODD), Sc, NULL, NULL, S) == 5
+    assert q(2, _ptrs(FAKE, FAKE + 2), 0, 256, 256, 2, P, Sc, NULL, NULL, S) == 5  # fp32 R needs 4
+    assert q(2, R, 0, 256, 256, 2, P, Sc, _ptrs(NULL, FAKE + 4), NULL, S) == 5     # scales64 needs 8
+    assert q(2, R, 0, 256, 256, 2, P, Sc, NULL, _ptrs(FAKE + 8, NULL), S) == 5     # codes need 16
 
 
 def test_quantize_tensor_workspace_bytes(L):

@@ -41,6 +41,19 @@ def test_quantize_checks():
     raises("GPU", f2.fairy2i_quantize, R, T)                       # everything else right
 
 
+def test_quantize_grouped_checks():
+    R = torch.zeros((2 * n, 2 * m), dtype=torch.float32)
+    assert f2.fairy2i_quantize_grouped([], T) == []
+    raises("group", f2.fairy2i_quantize_grouped, [R, R[:, :-2].contiguous()], T)     # another shape
+    raises("group", f2.fairy2i_quantize_grouped, [R, R.bfloat16()], T)              # another dtype
+    raises("dtype", f2.fairy2i_quantize_grouped, [R.double()], T)
+    raises("contiguous", f2.fairy2i_quantize_grouped, [R, R.t()], T)
+    packed, scales = layer()
+    raises("outputs", f2.fairy2i_quantize_grouped, [R, R], T, packed=[packed])
+    raises("bytes", f2.fairy2i_quantize_grouped, [R], T, packed=[packed[:-16]], scales=[scales])
+    raises("GPU", f2.fairy2i_quantize_grouped, [R, R], T)                            # everything else right
+
+
 def test_quantize_tensor_checks():
     R = torch.zeros((2 * n, 2 * m), dtype=torch.bfloat16)
     ws = torch.zeros(f2.fairy2i_quantize_tensor_workspace_bytes(n, m, T), dtype=torch.uint8)

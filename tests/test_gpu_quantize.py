@@ -226,3 +226,30 @@ def test_tensor_scales_order_cases(case):
         R[n + i, m] = v
     announce("quantize per-tensor order case", case, n)
     assert_tensor_match(R, 1, gpu_quantize_tensor(R, 1, dev), f"order case {case}")
+
+
+@pytest.mark.parametrize("count,n,m,T,dtype", [(3, 40, 128, 2, torch.float32),      # ragged tiles, MAXC 1
+                                               (5, 16, 2048, 3, torch.float32),     # MAXC 8
+                                               (2, 33, 5504, 2, torch.bfloat16),    # MAXC 24
+                                               (2, 17, 8192, 1, torch.float32),     # re-read form
+                                               (35, 24, 256, 4, torch.float32)])    # two launches (32 + 3)
+def test_grouped_matches_single(count, n, m, T, dtype):
+    """fairy2i_quantize_grouped: every layer's codes, packed bytes (padding rows included) and
+    fp32/fp64 scales equal its own fairy2i_quantize call bit for bit; the first and last layers
+    also against the oracle."""
+    dev = device()
+    rng = np.random.default_rng(count * 1000 + n + m + T)
+    Rs = [torch.from_numpy((rng.standard_normal((2 * n, 2 * m)) * 0.02).astype(np.float32)).to(dev).to(dtype)
+          for _ in range(count)]
+    announce("quantize grouped", count, n, m, T, dtype)
+    got = f2.fairy2i_quantize_grouped(Rs, T, want_scales64=True, want_codes=True)
+    assert len(got) == count
+    for k, R in enumerate(Rs):
+        one = f2.fairy2i_quantize(R, T, want_scales64=True, want_codes=True)
+        for key in ("packed", "codes"):
+            assert torch.equal(got[k][key], one[key]), (k, key)
+        assert torch.equal(got[k]["scales"].view(torch.int32), one["scales"].view(torch.int32)), k
+        assert torch.equal(got[k]["scales64"].view(torch.int64), one["scales64"].view(torch.int64)), k
+    for k in (0, count - 1):
+        Rk = down(Rs[k].float()).astype(np.float32)
+        assert_rows_match(Rk, T, np.arange(n), {kk: down(v) for kk, v in got[k].items()}, f"grouped layer {k}")

@@ -61,6 +61,10 @@ class GemvItem(ctypes.Structure):
                 ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
+SIGNATURES["fairy2i_quantize_grouped"] = (_INT, [_INT, ctypes.POINTER(ctypes.c_void_p), _INT, _I64, _I64, _INT,
+                                                  ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                                  ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                                  _P])
 SIGNATURES["fairy2i_gemv_grouped"] = (_INT, [ctypes.POINTER(GemvItem), _INT, _I64, _INT, _INT, _I64,
                                               _INT, _INT, _P])
 SIGNATURES["fairy2i_gemv_strided"] = (_INT, [_P, _I64, _P, _I64, _I64, _I64, _INT, _P, _INT, _I64, _P, _I64,
@@ -248,6 +252,47 @@ def fairy2i_quantize(R: torch.Tensor, T: int, *, want_scales64: bool = False,
     if codes is not None:
         out["codes"] = codes
     return out
+
+
+def fairy2i_quantize_grouped(Rs, T: int, *, want_scales64: bool = False, want_codes: bool = False,
+                             packed=None, scales=None, stream=None):
+    """fairy2i_quantize on a list of layers of one shape and dtype (fp32 or bf16 [2n][2m] on one
+    GPU), in shared launches; each layer's result equals its own fairy2i_quantize call.  packed and
+    scales: None (allocated) or lists of one output per layer.  Returns a list of dicts like
+    fairy2i_quantize."""
+    Rs = list(Rs)
+    if not Rs:
+        return []
+    n, m, dev = _check_weight(Rs[0], "R[0]")
+    for k, R in enumerate(Rs):
+        nk, mk, _ = _check_weight(R, f"R[{k}]")
+        if (nk, mk) != (n, m) or R.dtype != Rs[0].dtype:
+            raise ValueError(f"R[{k}]: {R.dtype} [{2 * nk}][{2 * mk}], the group is {Rs[0].dtype} [{2 * n}][{2 * m}]")
+    count = len(Rs)
+    for name, given in (("packed", packed), ("scales", scales)):
+        if given is not None and len(given) != count:
+            raise ValueError(f"{name}: {len(given)} outputs for {count} layers")
+    outs = [_quant_outputs(None if packed is None else packed[k], None if scales is None else scales[k], n, m, T, dev)
+            for k in range(count)]
+    s64 = [torch.empty((n, T, 2, 2), dtype=torch.float64, device=dev) for _ in range(count)] if want_scales64 else None
+    codes = [torch.empty((T, 2, n, m), dtype=torch.uint8, device=dev) for _ in range(count)] if want_codes else None
+    named = [(R, f"R[{k}]") for k, R in enumerate(Rs)]
+    named += [(t, f"{name}[{k}]") for k, (pk, sc) in enumerate(outs) for t, name in ((pk, "packed"), (sc, "scales"))]
+    named += [(t, f"scales64[{k}]") for k, t in enumerate(s64 or [])] + [(t, f"codes[{k}]") for k, t in enumerate(codes or [])]
+    _gpu(*named)
+    arr = lambda ts: (ctypes.c_void_p * count)(*[t.data_ptr() for t in ts])
+    _check(lib().fairy2i_quantize_grouped(count, arr(Rs), _DTYPE[Rs[0].dtype], 2 * n, 2 * m, T,
+                                          arr([o[0] for o in outs]), arr([o[1] for o in outs]),
+                                          arr(s64) if s64 else None, arr(codes) if codes else None, _stream(stream)))
+    res = []
+    for k, (pk, sc) in enumerate(outs):
+        d = {"packed": pk, "scales": sc}
+        if s64:
+            d["scales64"] = s64[k]
+        if codes:
+            d["codes"] = codes[k]
+        res.append(d)
+    return res
 
 
 def fairy2i_quantize_tensor(R: torch.Tensor, T: int, *, want_scales64: bool = False,

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "common.hpp"
@@ -61,6 +62,16 @@ int check_nm(int64_t n, int64_t m) {
 
 size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
 
+// Kernels with one 256-thread workgroup per row (quantizers, dequantize) address at most
+// 2^24 - 1 workgroups per launch (2^32 work-items).
+constexpr int64_t kMaxRowLaunch = (int64_t(1) << 24) - 1;
+int check_row_launch(int64_t n) {
+  if ((n + 15) / 16 * 16 > kMaxRowLaunch)
+    return fail(FAIRY2I_ERR_SHAPE, "n = %lld: one launch covers at most %lld rows", (long long)n,
+                (long long)(kMaxRowLaunch / 16 * 16));
+  return FAIRY2I_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +103,7 @@ static int quantize_any(const void* R, int r_bf16, int64_t two_n, int64_t two_m,
                 (long long)two_n, (long long)two_m);
   const int64_t n = two_n / 2, m = two_m / 2;
   if (int s = check_nm(n, m)) return s;
+  if (int s = check_row_launch(n)) return s;
   if (2 * T * m > 65536)
     return fail(FAIRY2I_ERR_SHAPE, "2*T*m = %lld exceeds 65536", (long long)(2 * T * m));
   if (!aligned(R, r_bf16 ? 2 : 4) || !aligned(packed, 16) || !aligned(scales, 4) ||
@@ -109,6 +121,47 @@ int fairy2i_quantize(const float* R, int64_t two_n, int64_t two_m, int T, uint8_
 int fairy2i_quantize_bf16(const uint16_t* R, int64_t two_n, int64_t two_m, int T, uint8_t* packed,
                           float* scales, double* scales64, uint8_t* codes, hipStream_t stream) {
   return quantize_any(R, 1, two_n, two_m, T, packed, scales, scales64, codes, stream);
+}
+
+int fairy2i_quantize_grouped(int count, const void* const* R, int R_dtype, int64_t two_n, int64_t two_m, int T,
+                             uint8_t* const* packed, float* const* scales, double* const* scales64,
+                             uint8_t* const* codes, hipStream_t stream) {
+  if (count < 0) return fail(FAIRY2I_ERR_SHAPE, "count = %d", count);
+  if (count > 0 && (!R || !packed || !scales)) return fail(FAIRY2I_ERR_NULL, "R, packed and scales arrays are required");
+  if (R_dtype != FAIRY2I_F32 && R_dtype != FAIRY2I_BF16)
+    return fail(FAIRY2I_ERR_DTYPE, "R_dtype %d: need F32 or BF16", R_dtype);
+  if (int s = check_stages(T)) return s;
+  if (two_n < 2 || two_n % 2 || two_m < 2 || two_m % 2)
+    return fail(FAIRY2I_ERR_SHAPE, "R is %lld x %lld; both sizes must be even",
+                (long long)two_n, (long long)two_m);
+  const int64_t n = two_n / 2, m = two_m / 2;
+  if (int s = check_nm(n, m)) return s;
+  if (2 * T * m > 65536)
+    return fail(FAIRY2I_ERR_SHAPE, "2*T*m = %lld exceeds 65536", (long long)(2 * T * m));
+  const int64_t rows = (n + 15) / 16 * 16;
+  if (std::min(count, f2i::kMaxQuantItems) * rows > kMaxRowLaunch)
+    return fail(FAIRY2I_ERR_SHAPE, "%d layers of %lld rows exceed one launch's %lld workgroups",
+                std::min(count, f2i::kMaxQuantItems), (long long)rows, (long long)kMaxRowLaunch);
+  const int bf16 = R_dtype == FAIRY2I_BF16;
+  for (int k = 0; k < count; ++k) {
+    if (!R[k] || !packed[k] || !scales[k]) return fail(FAIRY2I_ERR_NULL, "layer %d: R, packed and scales are required", k);
+    const double* s64 = scales64 ? scales64[k] : nullptr;
+    const uint8_t* cd = codes ? codes[k] : nullptr;
+    if (!aligned(R[k], bf16 ? 2 : 4) || !aligned(packed[k], 16) || !aligned(scales[k], 4) ||
+        (s64 && !aligned(s64, 8)) || (cd && !aligned(cd, 16)))
+      return fail(FAIRY2I_ERR_ALIGN, "layer %d: R needs 4 (fp32) or 2 (bf16), scales 4, scales64 8, "
+                  "packed/codes 16-byte alignment", k);
+  }
+  for (int k0 = 0; k0 < count; k0 += f2i::kMaxQuantItems) {
+    f2i::QuantGroup grp;
+    grp.count = std::min(count - k0, f2i::kMaxQuantItems);
+    for (int k = 0; k < grp.count; ++k)
+      grp.items[k] = f2i::QuantItem{R[k0 + k], packed[k0 + k], scales[k0 + k],
+                                    scales64 ? scales64[k0 + k] : nullptr, codes ? codes[k0 + k] : nullptr};
+    if (int s = hip_status(f2i::launch_quantize_group(grp, bf16, (int)n, (int)m, T, stream), "grouped quantize launch"))
+      return s;
+  }
+  return ok();
 }
 
 size_t fairy2i_quantize_tensor_workspace_bytes(int64_t n, int64_t m, int T) {
@@ -131,6 +184,7 @@ int fairy2i_quantize_tensor(const void* R, int R_dtype, int64_t two_n, int64_t t
                 (long long)two_n, (long long)two_m);
   const int64_t n = two_n / 2, m = two_m / 2;
   if (int s = check_nm(n, m)) return s;
+  if (int s = check_row_launch(n)) return s;
   if (2 * m > 65536) return fail(FAIRY2I_ERR_SHAPE, "m = %lld exceeds 32768", (long long)m);
   const size_t need = f2i::quantize_tensor_workspace_bytes(n);
   if (workspace_bytes < need)
@@ -385,6 +439,7 @@ int fairy2i_dequantize(const uint8_t* packed, const float* scales, int64_t n, in
     return fail(FAIRY2I_ERR_DTYPE, "R_dtype %d: need F32 or BF16", R_dtype);
   if (int s = check_stages(T)) return s;
   if (int s = check_nm(n, m)) return s;
+  if (int s = check_row_launch(n)) return s;
   if (!aligned(packed, 16) || !aligned(R, 16) || !aligned(scales, 4))
     return fail(FAIRY2I_ERR_ALIGN, "packed and R need 16-byte alignment, scales 4");
   return hip_status(f2i::launch_dequant(packed, scales, (int)n, (int)m, T, R, R_dtype == FAIRY2I_BF16, stream),

@@ -148,6 +148,20 @@ __device__ __forceinline__ GemvItem locate_item(const GemvGroup& g, int block, i
 hipError_t launch_gemv_mfma_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
 hipError_t launch_quantize(const void* R, int r_bf16, int n, int m, int T, uint8_t* packed, float* scales,
                            double* scales64, uint8_t* codes, hipStream_t s);
+// One matrix of a grouped quantize launch (every item has the same n, m, T and R dtype).
+struct QuantItem {
+  const void* R;
+  uint8_t* packed;
+  float* scales;
+  double* scales64;    // may be null
+  uint8_t* codes;      // may be null
+};
+constexpr int kMaxQuantItems = 32;   // items per launch; the table travels in the kernel arguments
+struct QuantGroup {
+  int count;
+  QuantItem items[kMaxQuantItems];
+};
+hipError_t launch_quantize_group(const QuantGroup& grp, int r_bf16, int n, int m, int T, hipStream_t s);
 size_t quantize_tensor_workspace_bytes(int64_t n);
 hipError_t launch_quantize_tensor(const void* R, int r_bf16, int n, int m, int T, void* ws, uint8_t* packed,
                                   float* scales, double* scales64, uint8_t* codes, hipStream_t s);

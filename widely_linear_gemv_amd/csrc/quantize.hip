@@ -101,23 +101,31 @@ __device__ __forceinline__ float r_value(float v) { return v; }
 __device__ __forceinline__ float r_value(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 // MAXC > 0: the row's inputs stay in registers (m <= 256 * MAXC).  MAXC == 0: they are re-read
-// from memory each stage (any m).  RT: fp32 or bf16 (raw bits) weights.
+// from memory each stage (any m).  RT: fp32 or bf16 (raw bits) weights.  A launch covers the
+// matrices of a group one after another, padded_rows(n) workgroups each (one matrix: a group of
+// one); every matrix is quantized exactly as on its own.
 template <int MAXC, typename RT>
-__global__ __launch_bounds__(kQThreads) void k_quantize(
-    const RT* __restrict__ R, int n, int m, int T, uint8_t* __restrict__ packed,
-    float* __restrict__ scales, double* __restrict__ scales64, uint8_t* __restrict__ codes_out) {
+__global__ __launch_bounds__(kQThreads) void k_quantize(const QuantGroup grp, int n, int m, int T) {
   extern __shared__ __align__(16) uint8_t s_codes[];        // [T][2][m], one code per byte
   __shared__ double s_part[4][kQThreads];                   // [U re, U im, W re, W im][thread]
   __shared__ int s_cnt[2][kQThreads / kWave];               // real-axis counts per wave
   __shared__ double s_scale[4][2][2];                       // doubled fp64 scales [t][M][axis]
-  if ((int)blockIdx.x >= n) {                                // padding row of the last tile
+  const int rows = padded_rows(n);
+  const int item = (int)blockIdx.x / rows;                  // workgroup-uniform
+  const int i = (int)blockIdx.x - item * rows;              // this workgroup's row
+  const QuantItem& it = grp.items[item];
+  const RT* __restrict__ R = static_cast<const RT*>(it.R);
+  uint8_t* __restrict__ packed = it.packed;
+  float* __restrict__ scales = it.scales;
+  double* __restrict__ scales64 = it.scales64;
+  uint8_t* __restrict__ codes_out = it.codes;
+  if (i >= n) {                                              // padding row of the last tile
     uint32_t* __restrict__ pw = reinterpret_cast<uint32_t*>(packed);
     for (int q = threadIdx.x; q < 2 * T * (m / 16); q += kQThreads)
-      pw[tiled_word(blockIdx.x, q / (m / 16), q % (m / 16), m, T)] = 0u;
+      pw[tiled_word(i, q / (m / 16), q % (m / 16), m, T)] = 0u;
     return;
   }
 
-  const int i = blockIdx.x;
   const int l = threadIdx.x;
   const int64_t ld = 2 * (int64_t)m;
   const RT* __restrict__ r0 = R + (int64_t)i * ld;             // row i of R
@@ -483,28 +491,34 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ codes,
 }
 
 template <typename RT>
-static void launch_quantize_t(const RT* R, int n, int m, int T, uint8_t* packed, float* scales,
-                              double* scales64, uint8_t* codes, hipStream_t s) {
+static void launch_quantize_t(const QuantGroup& grp, int n, int m, int T, hipStream_t s) {
   const size_t lds = (size_t)2 * T * m;
   const int nch = (m + kQThreads - 1) / kQThreads;
-  const dim3 grid(padded_rows(n)), block(kQThreads);
+  const dim3 grid((unsigned)(grp.count * padded_rows(n))), block(kQThreads);
   if (nch <= 1)
-    hipLaunchKernelGGL((k_quantize<1, RT>), grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+    hipLaunchKernelGGL((k_quantize<1, RT>), grid, block, lds, s, grp, n, m, T);
   else if (nch <= 8)
-    hipLaunchKernelGGL((k_quantize<8, RT>), grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+    hipLaunchKernelGGL((k_quantize<8, RT>), grid, block, lds, s, grp, n, m, T);
   else if (nch <= 24)
-    hipLaunchKernelGGL((k_quantize<24, RT>), grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+    hipLaunchKernelGGL((k_quantize<24, RT>), grid, block, lds, s, grp, n, m, T);
   else
-    hipLaunchKernelGGL((k_quantize<0, RT>), grid, block, lds, s, R, n, m, T, packed, scales, scales64, codes);
+    hipLaunchKernelGGL((k_quantize<0, RT>), grid, block, lds, s, grp, n, m, T);
+}
+
+hipError_t launch_quantize_group(const QuantGroup& grp, int r_bf16, int n, int m, int T, hipStream_t s) {
+  if (r_bf16)
+    launch_quantize_t<uint16_t>(grp, n, m, T, s);
+  else
+    launch_quantize_t<float>(grp, n, m, T, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const void* R, int r_bf16, int n, int m, int T, uint8_t* packed, float* scales,
                            double* scales64, uint8_t* codes, hipStream_t s) {
-  if (r_bf16)
-    launch_quantize_t(static_cast<const uint16_t*>(R), n, m, T, packed, scales, scales64, codes, s);
-  else
-    launch_quantize_t(static_cast<const float*>(R), n, m, T, packed, scales, scales64, codes, s);
-  return hipGetLastError();
+  QuantGroup grp;
+  grp.count = 1;
+  grp.items[0] = QuantItem{R, packed, scales, scales64, codes};
+  return launch_quantize_group(grp, r_bf16, n, m, T, s);
 }
 
 hipError_t launch_pack(const uint8_t* codes, int n, int m, int T, uint8_t* packed, hipStream_t s) {
