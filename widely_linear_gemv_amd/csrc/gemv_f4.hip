@@ -40,6 +40,7 @@
 //    exact integer accumulators are added before the epilogue (k_gemv_f4_mixed): the outputs
 //    are those of one wave per tile, bit for bit, and the launch's tail is short-lived waves.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "digits.hpp"
@@ -830,15 +831,53 @@ static size_t f4_fused_lds_max(int BT, bool stage) {
   return (size_t)f4_record_bytes(m, BT) + (stage ? (size_t)f4_xstage_bytes(m, BT) : 0);
 }
 
-// Dynamic LDS above 64 KB needs a kernel attribute; it is set once per kernel, to the most any of
-// its launches can take, so later launches with larger rows are covered too.
+// Host-side launch state of one kernel, per device and guarded by a mutex (callers may launch
+// from several threads or devices): whether its dynamic-LDS limit has been raised there, and how
+// many of its workgroups the device holds at once with a given dynamic LDS.
+constexpr int kMaxLaunchDevices = 64;
+struct KernelLaunchState {
+  std::mutex mu;
+  bool lds_set[kMaxLaunchDevices] = {};
+  size_t resident_lds[kMaxLaunchDevices] = {};
+  int resident[kMaxLaunchDevices] = {};
+};
+
+static int current_device() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess ? dev : 0;
+}
+
+// Dynamic LDS above 64 KB needs a kernel attribute; it is set once per kernel and device, to the
+// most any of its launches can take, so later launches with larger rows are covered too.
 template <typename K>
-static void lds_launch_prepare(K kernel, size_t max_bytes, bool& done) {
-  if (max_bytes > 65536 && !done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)max_bytes);
-    done = true;
+static void lds_launch_prepare(K kernel, size_t max_bytes, KernelLaunchState& st) {
+  if (max_bytes <= 65536) return;
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lock(st.mu);
+  if (dev >= 0 && dev < kMaxLaunchDevices && st.lds_set[dev]) return;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)max_bytes);
+  if (dev >= 0 && dev < kMaxLaunchDevices) st.lds_set[dev] = true;
+}
+
+// Workgroups of `threads` threads and `lds` bytes of dynamic LDS that the current device holds at
+// once (at least one per CU).
+template <typename K>
+static int resident_workgroups(K kernel, int threads, size_t lds, KernelLaunchState& st) {
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lock(st.mu);
+  const bool cached = dev >= 0 && dev < kMaxLaunchDevices;
+  if (cached && st.resident[dev] > 0 && st.resident_lds[dev] == lds) return st.resident[dev];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), threads, lds) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  if (cached) {
+    st.resident[dev] = per_cu * cus;
+    st.resident_lds[dev] = lds;
   }
+  return per_cu * cus;
 }
 
 template <int TT, int BT, typename YT, bool FUSED>
@@ -850,22 +889,9 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
   if constexpr (FUSED) {
     if (gemv_waves_per_tile(tiles, m) == 1) {             // resident workgroups, four tiles at a time
       const size_t lds = BT == 1 ? rec : (size_t)f4_record_bytes(m, B);
-      static bool attr = false;
-      static size_t resident_lds = 0;
-      static int resident = 0;                            // workgroups the chip holds at once with that LDS
-      lds_launch_prepare(k_gemv_f4_persist<TT, BT, YT>, f4_fused_lds_max(BT, BT == 1), attr);
-      if (resident == 0 || resident_lds != lds) {
-        int per_cu = 0, dev = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_gemv_f4_persist<TT, BT, YT>),
-                                                         4 * kWave, lds) != hipSuccess || per_cu < 1)
-          per_cu = 1;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-          cus = 256;
-        resident = per_cu * cus;
-        resident_lds = lds;
-      }
-      const int grid = std::min((tiles + 3) / 4, resident);
+      static KernelLaunchState st;
+      lds_launch_prepare(k_gemv_f4_persist<TT, BT, YT>, f4_fused_lds_max(BT, BT == 1), st);
+      const int grid = std::min((tiles + 3) / 4, resident_workgroups(k_gemv_f4_persist<TT, BT, YT>, 4 * kWave, lds, st));
       hipLaunchKernelGGL((k_gemv_f4_persist<TT, BT, YT>), dim3(grid), dim3(4 * kWave), lds, s, grp, m, B);
       return;
     }
@@ -874,10 +900,10 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
     if (gemv_waves_per_tile(tiles, m) == 1 && tiles >= kF4MixedMinTiles) {
       const int nA = (tiles - kF4TailTiles) / 4;          // four units per workgroup
       const size_t lds = FUSED ? std::max(rec, (size_t)4 * 16 * TT * kWave * sizeof(float)) : 0;
-      static bool attr = false;
+      static KernelLaunchState st;
       lds_launch_prepare(k_gemv_f4_mixed<TT, YT, FUSED>,
                          FUSED ? std::max(f4_fused_lds_max(1, true), (size_t)4 * 16 * TT * kWave * sizeof(float)) : 0,
-                         attr);
+                         st);
       hipLaunchKernelGGL((k_gemv_f4_mixed<TT, YT, FUSED>), dim3(nA + (tiles - 4 * nA)), dim3(4 * kWave), lds, s, grp,
                          m, nA);
       return;
@@ -887,8 +913,8 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
   switch (gemv_waves_per_tile(tiles, m)) {
 #define F2I_F4_CASE(NWV)                                                                               \
     {                                                                                                    \
-      static bool attr = false;                                                                          \
-      lds_launch_prepare(k_gemv_f4<TT, NWV, BT, YT, FUSED>, FUSED ? f4_fused_lds_max(BT, true) : 0, attr);  \
+      static KernelLaunchState st;                                                                       \
+      lds_launch_prepare(k_gemv_f4<TT, NWV, BT, YT, FUSED>, FUSED ? f4_fused_lds_max(BT, true) : 0, st);    \
       hipLaunchKernelGGL((k_gemv_f4<TT, NWV, BT, YT, FUSED>), grid, dim3(NWV * kWave), rec, s, grp, m, B); \
     }                                                                                                    \
     break;
