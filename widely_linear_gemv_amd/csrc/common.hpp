@@ -27,6 +27,30 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// Sum of v over aligned groups of N lanes (N = 2, 4, 8 or 16, within a 16-lane row), every lane
+// of a group ending with the total, on DPP lane permutes (a VALU operand modifier: no LDS
+// traffic).  The steps pair lanes as an xor butterfly over offsets 1, 2, 4, 8 does -- quad
+// permutes for 1 and 2; then, with the values already uniform across each quad (half-row),
+// the half-row mirror (lane 7 - i) and the row mirror (lane 15 - i) meet the same partner groups
+// as offsets 4 and 8 -- and IEEE addition is commutative, so the sums are the butterfly's bit
+// for bit and equal in every lane of the group.
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  // No contraction into these adds: fusing a caller's multiply into the first one would leave
+  // the two lanes of a pair with differently rounded sums.
+#pragma clang fp contract(off)
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "groups of 2, 4, 8 or 16 lanes");
+  v += dpp_read<0xB1>(v);                          // quad_perm [1, 0, 3, 2]: lane ^ 1
+  if constexpr (N >= 4) v += dpp_read<0x4E>(v);    // quad_perm [2, 3, 0, 1]: lane ^ 2
+  if constexpr (N >= 8) v += dpp_read<0x141>(v);   // row_half_mirror: quad 0 <-> 1, 2 <-> 3
+  if constexpr (N >= 16) v += dpp_read<0x140>(v);  // row_mirror: half-row 0 <-> 1
+  return v;
+}
+
 // Stores one fp32 value as the output dtype.
 __device__ __forceinline__ void store_out(float* y, int64_t idx, float v) { y[idx] = v; }
 __device__ __forceinline__ void store_out(uint16_t* y, int64_t idx, float v) { y[idx] = f32_to_bf16_rne(v); }

@@ -477,8 +477,8 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
 
   // Epilogue.  Lane holds rows 4g..4g+3 of column r = 8 comp + l.  Axis sums (times 6)
   // P = (Su + Sv) / 2, Q = (Su - Sv) / 2 (exact), then the widely-linear combination with the
-  // fp32 scales, the digit weight 2^(3l - S_b) / 6, and the sum over digits (xor 1, 2, 4) and
-  // components (xor 8).
+  // fp32 scales, the digit weight 2^(3l - S_b) / 6, and the sum over digits and components: the
+  // 16 lanes of a row, on DPP lane permutes (group_sum).
   if constexpr (EXACT) {
     if constexpr (FUSED) __syncthreads();        // s_acc shares LDS with the records: all waves are past them
 #pragma unroll
@@ -533,11 +533,8 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
       }
       vre *= wdig;
       vim *= wdig;
-#pragma unroll
-      for (int off = 1; off <= 8; off <<= 1) {
-        vre += __shfl_xor(vre, off);
-        vim += __shfl_xor(vim, off);
-      }
+      vre = group_sum<16>(vre);
+      vim = group_sum<16>(vim);
       if (NW > 1 && !EXACT) {
         if (r == 0) { s_y[wave][b][0][4 * g + e] = vre; s_y[wave][b][1][4 * g + e] = vim; }
       } else if (r == 0 && b < B && i < n) {
@@ -657,11 +654,8 @@ __device__ __forceinline__ void gemv_f4_stream(const GemvGroup& grp, int m, int 
         }
         vre *= wdig;
         vim *= wdig;
-#pragma unroll
-        for (int off = 1; off <= 8; off <<= 1) {
-          vre += __shfl_xor(vre, off);
-          vim += __shfl_xor(vim, off);
-        }
+        vre = group_sum<16>(vre);
+        vim = group_sum<16>(vim);
         if (r == 0 && b < B && i < n) {
           store_out(y, (int64_t)b * ys + i, vre);
           store_out(y, (int64_t)b * ys + n + i, vim);

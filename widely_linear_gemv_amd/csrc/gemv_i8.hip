@@ -28,7 +28,8 @@
 //    chunk lane group g owns columns 64g..64g+63 and at MFMA step s contributes columns
 //    64g+16s..+15.
 //  * Epilogue: each lane scales its int32 sums by 2^(8l - S_b) and the fp32 axis scales, and
-//    the digits and components of a batch entry are summed across lanes (xor 1, 2, 4).
+//    the digits and components of a batch entry are summed across its 8 lanes on DPP lane
+//    permutes (group_sum).
 #include "common.hpp"
 #include "digits.hpp"
 
@@ -231,11 +232,8 @@ __global__ __launch_bounds__(kWave * NW) void k_gemv_i8(const GemvGroup grp, int
     }
     vre *= wdig;
     vim *= wdig;
-#pragma unroll
-    for (int off = 1; off <= 4; off <<= 1) {   // digits (1, 2) and components (4)
-      vre += __shfl_xor(vre, off);
-      vim += __shfl_xor(vim, off);
-    }
+    vre = group_sum<8>(vre);                    // digits (lanes ^ 1, ^ 2) and components (^ 4)
+    vim = group_sum<8>(vim);
     if (NW > 1) {
       if ((r & 7) == 0) { s_y[wave][bl][0][4 * g + e] = vre; s_y[wave][bl][1][4 * g + e] = vim; }
     } else if ((r & 7) == 0 && bl < B && i < n) {

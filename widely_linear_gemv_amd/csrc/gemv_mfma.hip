@@ -260,8 +260,8 @@ __global__ __launch_bounds__(kWave * NW, CG == 1 ? 2 : 1) void k_gemv_mfma(const
         vre = ypart[e][cg][0] + vre;
         vim = ypart[e][cg][1] + vim;
       }
-      vre += __shfl_xor(vre, 1);
-      vim += __shfl_xor(vim, 1);
+      vre = group_sum<2>(vre);
+      vim = group_sum<2>(vim);
       const int b = cg * 8 + (r >> 1);
       if (NW > 1) {
         if (comp == 0) { s_y[wave][b][0][4 * g + e] = vre; s_y[wave][b][1][4 * g + e] = vim; }
@@ -427,8 +427,8 @@ __global__ __launch_bounds__(kWave * kSxWaves) void k_gemv_mfma_sx(const GemvGro
         vre = ypart[e][cg][0] + vre;
         vim = ypart[e][cg][1] + vim;
       }
-      vre += __shfl_xor(vre, 1);
-      vim += __shfl_xor(vim, 1);
+      vre = group_sum<2>(vre);
+      vim = group_sum<2>(vim);
       const int b = cg * 8 + (r >> 1);
       if (comp == 0 && b < B && i < n) {
         store_out(y, (int64_t)b * ys + i, vre);
