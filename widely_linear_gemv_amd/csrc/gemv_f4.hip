@@ -263,54 +263,79 @@ __device__ void build_f6_records(const uint16_t* __restrict__ x, int m, int B, u
     s_S[tid] = digit_exponent(mx);
   }
   __syncthreads();
-  const int nrec = ((m + kF4Chunk - 1) / kF4Chunk) * 2 * B * kWave;
-  for (int rec = tid; rec < nrec; rec += nthr) {
-    const int lane = rec & (kWave - 1), blk = rec / kWave;
+  // Records in halves: an item is 16 consecutive columns of one (chunk, step, batch entry, lane
+  // group, component) -- elements 16h .. 16h + 15 of that record -- and all eight of its digits,
+  // so each column's Y is formed once; element q = 16h + 4a + i is column f4_column(0, 0, 4a + i)
+  // of the half, and the half of digit l's record is the 96 bits 3h .. 3h + 2 (in dwords).
+  const int nitem = ((m + kF4Chunk - 1) / kF4Chunk) * 2 * B * 16;
+  for (int item = tid; item < nitem; item += nthr) {
+    const int h = item & 1, comp = (item >> 1) & 1, g = (item >> 2) & 3, blk = item >> 4;
     const int b = blk % B, cs = blk / B, s = cs & 1, c = cs >> 1;
-    const int g = lane >> 4, comp = (lane >> 3) & 1, l = lane & 7;
-    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+    uint32_t* dst0 = reinterpret_cast<uint32_t*>(s_rec + (((c * 2 + s) * B + b) * kWave + 16 * g + 8 * comp) * kRecBytes) + 3 * h;
     if (kF4Chunk * c + 64 * g < m) {
       const int S = s_S[b];
       const float f1 = ldexpf(1.0f, S / 2), f2 = ldexpf(1.0f, S - S / 2);   // 2^S, exact in two steps
       const uint4* src = reinterpret_cast<const uint4*>((kStage ? s_x : x) + (int64_t)b * 2 * m + (int64_t)comp * m +
-                                                       kF4Chunk * c + 64 * g + 32 * s);
-      int fld[32];                                    // base-8 digit l of Y, columns 0..31
+                                                       kF4Chunk * c + 64 * g + 32 * s + 16 * h);
+      int Y[16];                                      // X + kDigitBias of the half's 16 columns
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const uint4 u = src[h];
+      for (int k = 0; k < 2; ++k) {
+        const uint4 u = src[k];
         const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float lo = bf16_lo(wd[e]), hi = bf16_hi(wd[e]);
-          const int Ylo = (int)rintf((lo * f1) * f2) + kDigitBias;
-          const int Yhi = (int)rintf((hi * f1) * f2) + kDigitBias;
-          fld[8 * h + 2 * e] = (Ylo >> (3 * l)) & 7;
-          fld[8 * h + 2 * e + 1] = (Yhi >> (3 * l)) & 7;
+          Y[8 * k + 2 * e] = (int)rintf((bf16_lo(wd[e]) * f1) * f2) + kDigitBias;
+          Y[8 * k + 2 * e + 1] = (int)rintf((bf16_hi(wd[e]) * f1) * f2) + kDigitBias;
         }
       }
-      // element q = 4a + i of the operand is column f4_column(0, 0, q) (+16 for q >= 16)
+#pragma unroll 2
+      for (int l = 0; l < 8; ++l) {
+        uint32_t p24[4];
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        uint32_t sel = 0;
+        for (int a = 0; a < 4; ++a) {
+          uint32_t sel = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sel |= (uint32_t)fld[f4_column(0, 0, 4 * a + i)] << (8 * i);
-        const uint32_t codes = __builtin_amdgcn_perm(kF6CodesHi, kF6CodesLo, sel);
-        const uint32_t p24 = (codes & 0x3Fu) | ((codes >> 2) & 0xFC0u) | ((codes >> 4) & 0x3F000u) |
-                             ((codes >> 6) & 0xFC0000u);
-        const int bit = 24 * a;                       // bits 24a .. 24a + 23 of the 192-bit operand
-        w[bit >> 5] |= p24 << (bit & 31);
-        if ((bit & 31) > 8) w[(bit >> 5) + 1] |= p24 >> (32 - (bit & 31));
+          for (int i = 0; i < 4; ++i) sel |= (uint32_t)((Y[f4_column(0, 0, 4 * a + i)] >> (3 * l)) & 7) << (8 * i);
+          const uint32_t codes = __builtin_amdgcn_perm(kF6CodesHi, kF6CodesLo, sel);
+          p24[a] = (codes & 0x3Fu) | ((codes >> 2) & 0xFC0u) | ((codes >> 4) & 0x3F000u) | ((codes >> 6) & 0xFC0000u);
+        }
+        uint32_t* dst = dst0 + l * (kRecBytes / 4);
+        dst[0] = p24[0] | (p24[1] << 24);
+        dst[1] = (p24[1] >> 8) | (p24[2] << 16);
+        dst[2] = (p24[2] >> 16) | (p24[3] << 8);
+      }
+    } else {
+#pragma unroll
+      for (int l = 0; l < 8; ++l) {
+        uint32_t* dst = dst0 + l * (kRecBytes / 4);
+        dst[0] = 0u;
+        dst[1] = 0u;
+        dst[2] = 0u;
       }
     }
-    uint2* dst = reinterpret_cast<uint2*>(s_rec + rec * kRecBytes);
-    dst[0] = make_uint2(w[0], w[1]);
-    dst[1] = make_uint2(w[2], w[3]);
-    dst[2] = make_uint2(w[4], w[5]);
   }
   __syncthreads();
 }
 
 // ------------------------------------------------------------------------- GEMV ----
+
+// The epilogue's sum over a row's 16 lanes (digits and components).  One batch entry per tile:
+// DPP permutes (group_sum).  Two: lane shuffles, whose LDS round trips the compiler schedules
+// with fewer live registers here (with DPP the batch-2 kernels took 8-80 more registers, which
+// cost a wave per SIMD at T = 2 on small launches and at T = 3).
+template <int BT>
+__device__ __forceinline__ void row_sums(float& vre, float& vim) {
+  if constexpr (BT == 1) {
+    vre = group_sum<16>(vre);
+    vim = group_sum<16>(vim);
+  } else {
+#pragma unroll
+    for (int off = 1; off <= 8; off <<= 1) {
+      vre += __shfl_xor(vre, off);
+      vim += __shfl_xor(vim, off);
+    }
+  }
+}
 
 // One unit (a 16-row tile of one item) streamed by NW cooperating waves; `wave` is this wave's
 // index among them, s_scw its own LDS slot for the tile's scales, s_y the NW waves' partial outputs.
@@ -533,8 +558,7 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
       }
       vre *= wdig;
       vim *= wdig;
-      vre = group_sum<16>(vre);
-      vim = group_sum<16>(vim);
+      row_sums<BT>(vre, vim);
       if (NW > 1 && !EXACT) {
         if (r == 0) { s_y[wave][b][0][4 * g + e] = vre; s_y[wave][b][1][4 * g + e] = vim; }
       } else if (r == 0 && b < B && i < n) {
@@ -654,8 +678,7 @@ __device__ __forceinline__ void gemv_f4_stream(const GemvGroup& grp, int m, int 
         }
         vre *= wdig;
         vim *= wdig;
-        vre = group_sum<16>(vre);
-        vim = group_sum<16>(vim);
+        row_sums<BT>(vre, vim);
         if (r == 0 && b < B && i < n) {
           store_out(y, (int64_t)b * ys + i, vre);
           store_out(y, (int64_t)b * ys + n + i, vim);
