@@ -252,7 +252,8 @@ def stack_legs(f2, torch, dev, T, reps):
         nbytes = sum(gemv_bytes(rows // 2, cols // 2, T, B) for L in range(32) for (_, rows, cols, _) in PROJECTIONS)
         legs[f"stack_decode_b{B}"] = {"gemvs": 224, "launches": 128, "us": round(t * 1e3, 1),
                                       "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes,
-                                      "kernel": "bf16 matrix cores (default for these latency-bound launches)"}
+                                      "kernel": "AUTO: fp4 matrix cores with the digits of x built on chip per tile"
+                                                if B == 1 else "AUTO: bf16 matrix cores"}
         if B == 1:
             # the fp4 kernel: with its digit pass in the step (256 launches), and on x already
             # in digit form (the 128 GEMV launches alone, for inputs a producer writes in that form)
@@ -643,10 +644,10 @@ def main():
                          "layers_per_launch": P / launches, "bytes_per_layer": bytes_b[16]},
             "gemv_b1_bf16x_auto": {"us_per_launch": round(k_us["auto_b1"], 3),
                                    "GB/s": round(bytes_pool / (k_us["auto_b1"] * 1e-6) / 1e9, 2),
-                                   "kernel": "fp4 MFMA, fp6 digit records built on chip from the bf16 x (AUTO)"},
+                                   "kernel": "fp4 MFMA, digit records built on chip from the bf16 x (AUTO)"},
             "gemv_b2_bf16x_auto": {"us_per_launch": round(k_us["auto_b2"], 3),
                                    "GB/s": round(P * gemv_bytes(n, m, T, 2) / (k_us["auto_b2"] * 1e-6) / 1e9, 2),
-                                   "kernel": "fp4 MFMA, fp6 digit records built on chip from the bf16 x (AUTO)"},
+                                   "kernel": "fp4 MFMA, digit records built on chip from the bf16 x (AUTO)"},
             "gemv_b1_f4_grouped": {"us_per_pass": round(grouped_us, 3), "launches_per_pass": -(-P // 48),
                                    "GB/s": round(bytes_pool / (grouped_us * 1e-6) / 1e9, 2)},
             "gemv_b1_single_layer_launch": {"us_per_launch": round(single_us, 3),

@@ -99,8 +99,10 @@ typedef enum {
  *              kernel on gfx950: half the MFMA cycles and about half the VALU work per code of
  *              MFMA_I8.
  * AUTO with bf16 x takes MFMA_F4 for launches of at least 1536 16-row tiles with B <= 2,
- * m * B <= 8192 and one x for the launch (there the on-chip digits cost little per tile), and
- * MFMA_BF16 otherwise (smaller launches would build the digits once per tile). */
+ * m * B <= 8192 and one x for the launch (resident workgroups build the digits once for many
+ * tiles); for smaller launches at B = 1 with 2048 <= m <= 6144, or with m up to 8192 in launches
+ * of at most 256 tiles (each workgroup builds the digits for its own tile, which there still costs
+ * less than MFMA_BF16's work); and MFMA_BF16 otherwise. */
 typedef enum {
   FAIRY2I_GEMV_AUTO = 0,
   FAIRY2I_GEMV_VALU = 1,

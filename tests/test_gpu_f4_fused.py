@@ -1,5 +1,5 @@
 """GPU parity of the fp4 decode GEMV on bf16 x (fairy2i_gemv with x_dtype BF16 and MFMA_F4 or
-AUTO): every workgroup builds its fp6 digit records on chip.  The outputs must equal the two-call
+AUTO): every workgroup builds its digit records on chip (fp4).  The outputs must equal the two-call
 form (fairy2i_x_digits_f6, then the GEMV on the digit form) bit for bit -- same digits, same MFMA
 inputs, same order -- and so match the oracle within the fp32 tolerance.  Cases cover every launch
 form: small launches (a tile's chunks split over 2, 4 or 8 waves), one wave per tile, the
@@ -29,7 +29,8 @@ def bits(a):
 
 
 @pytest.mark.parametrize("n,m,T,B", [(5, 64, 1, 1), (17, 320, 2, 2), (40, 2048, 2, 1), (33, 1088, 3, 2),
-                                     (100, 5504, 2, 1), (9, 8192, 2, 1), (21, 4096, 4, 2), (300, 2048, 2, 2)])
+                                     (100, 5504, 2, 1), (9, 8192, 2, 1), (21, 4096, 4, 2), (300, 2048, 2, 2),
+                                     (1030, 5504, 2, 1), (1040, 4096, 3, 2)])
 def test_fused_matches_two_call_and_oracle(n, m, T, B):
     dev = device()
     codes, scales = layer(n, m, T, seed=n * 7 + m + T)
@@ -44,6 +45,42 @@ def test_fused_matches_two_call_and_oracle(n, m, T, B):
     want = oracle.gemv_ref(codes, scales, act.values)
     assert rel_l2(down(f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA_F4)), want) <= TOL_F32
     check_bf16(down(f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA_F4, y_dtype=torch.bfloat16)), want, "fused")
+
+
+@pytest.mark.parametrize("B,m,T", [(1, 1088, 2), (2, 320, 3), (2, 2048, 1)])
+def test_fused_rounding_matches_two_call(B, m, T):
+    """x over 2^-20 .. 2^6 with zeros, and a quarter of its entries exactly half-way for
+    X = x 2^S (odd multiples of 2^-(S+1) beside a maximum of 1, S = 21, or of 3, S = 20): the
+    records built on chip round to nearest even exactly as the digit form does, whose X the
+    digit-form test holds to np.rint, so the outputs are bit-identical to the two-call form."""
+    dev = device()
+    n = 48
+    rng = np.random.default_rng(90 + B + m + T)
+    v = rng.standard_normal((B, 2 * m)).astype(np.float32)
+    v *= np.float32(2.0) ** rng.integers(-20, 6, size=v.shape).astype(np.float32)
+    v[rng.random(v.shape) < 0.05] = 0.0
+    for b, amax, S in ((0, 1.0, 21), (1, 3.0, 20)):
+        if b >= B:
+            break
+        v[b] *= np.float32(amax) / np.abs(v[b]).max()
+        v[b, int(np.argmax(np.abs(v[b])))] = amax
+        ties = rng.random(2 * m) < 0.25
+        odd = (2 * rng.integers(0, 128, size=2 * m) + 1).astype(np.float32)
+        sign = np.where(rng.random(2 * m) < 0.5, -1.0, 1.0).astype(np.float32)
+        v[b] = np.where(ties, sign * odd * np.float32(2.0) ** -(S + 1), v[b])
+        v[b, int(np.argmax(np.abs(v[b])))] = amax          # the maximum survives the ties
+    bits_ = workloads.f32_to_bf16_bits(v)
+    act = workloads.Activations(values=workloads.bf16_bits_to_f32(bits_), dtype="bf16", bf16_bits=bits_)
+    codes, scales = layer(n, m, T, seed=700 + m)
+    packed, s = up(oracle.pack(codes), dev), up(scales, dev)
+    x = x_to_dev(act, dev)
+    announce("gemv fp4 fused rounding", n, m, T, B)
+    for ydt in (torch.float32, torch.bfloat16):
+        got = down(f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA_F4, y_dtype=ydt))
+        two = down(f2.fairy2i_gemv(packed, s, f2.fairy2i_x_digits_f6(x), algo=f2.GEMV_MFMA_F4, y_dtype=ydt))
+        assert np.array_equal(bits(got), bits(two)), (m, T, B, ydt)
+    assert rel_l2(down(f2.fairy2i_gemv(packed, s, x, algo=f2.GEMV_MFMA_F4)),
+                  oracle.gemv_ref(codes, scales, act.values)) <= TOL_F32
 
 
 @pytest.mark.parametrize("B,T,batch,n", [(1, 2, 128, 256), (1, 3, 48, 256), (2, 2, 100, 256), (1, 1, 200, 256),
@@ -79,6 +116,25 @@ def test_fused_large_strided_launch(B, T, batch, n):
         codes = oracle.unpack(down(pool[k]), n, m, T)
         want = oracle.gemv_ref(codes, down(spool[k]), act.values)
         assert rel_l2(a[k], want) <= TOL_F32, k
+
+
+@pytest.mark.parametrize("B,m,tiles,fused", [(1, 2048, 24, True), (1, 5504, 8, True), (1, 8192, 16, True),
+                                              (1, 8192, 260, False), (1, 1024, 40, False), (2, 2048, 24, False)])
+def test_auto_on_bf16_x_small_launches(B, m, tiles, fused):
+    """AUTO on bf16 x below 1536 tiles: the fp4 kernel with on-chip digits at batch 1 for
+    2048 <= m <= 6144, and up to m = 8192 in launches of at most 256 tiles; the bf16 kernel
+    otherwise.  Checked bit for bit against the kernel that should run, and against the oracle."""
+    dev = device()
+    n, T = 16 * tiles, 2
+    codes, scales = layer(n, m, T, seed=40 + m + tiles)
+    act = workloads.activations(B, 2 * m, seed=60 + B + m)
+    packed, s = up(oracle.pack(codes), dev), up(scales, dev)
+    x = x_to_dev(act, dev)
+    announce("gemv auto bf16 x", n, m, T, B, fused)
+    got = down(f2.fairy2i_gemv(packed, s, x))
+    want_algo = f2.GEMV_MFMA_F4 if fused else f2.GEMV_MFMA_BF16
+    assert np.array_equal(bits(got), bits(down(f2.fairy2i_gemv(packed, s, x, algo=want_algo)))), (B, m, tiles)
+    assert rel_l2(got, oracle.gemv_ref(codes, scales, act.values)) <= TOL_F32
 
 
 def test_fused_grouped_and_zero_column():

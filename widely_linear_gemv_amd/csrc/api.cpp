@@ -210,13 +210,26 @@ int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* pac
 
 // Checks the dtype / algorithm / batch combination of a GEMV call and resolves AUTO and MFMA to
 // the kernel that runs.  Returns minus the status (with the message recorded) on a bad combination.
-// The fp4 GEMV on bf16 x builds each row's fp6 digit records in LDS: at most 32 chunks of 256
-// columns per batch entry (96 KB).  AUTO takes it for launches of at least kF4FusedMinTiles tiles,
-// where four tiles share one workgroup's records (smaller launches build them once per tile, which
-// costs about as much as the bf16 kernel's own work); those workgroups need one x for the launch.
+// The fp4 GEMV on bf16 x builds each row's digit records in LDS (fp4, 16 bytes per record): at
+// most 32 chunks of 256 columns over the batch entries (64 KB).  AUTO takes it for launches of at
+// least kF4FusedMinTiles tiles, whose workgroups stay resident and build the records once for many
+// tiles (those workgroups need one x for the launch).  Smaller launches build them once per tile;
+// at batch 1 that still beats the bf16 kernel from m = 2048 (per launch, 32 distinct T = 2 layers
+// in a graph, bf16 / fp4 us: m = 2048, 256 tiles 5.85 / 5.48, 688 tiles 11.13 / 9.76, 1535 tiles
+// 18.85 / 16.54; m = 4096 and 5504 faster at every size from 16 tiles; m = 1024 slower at every
+// size), as long as two workgroups' records and staged x (12 m bytes) fit in a CU's LDS: at
+// m = 8192 (96 KB) only launches of up to 256 tiles gain (384 tiles 20.42 / 23.24).  At batch 2
+// the per-tile build and the second batch entry's operands make it slower than bf16 at every
+// small size measured (m = 512 to 4096, 16 to 1535 tiles).
 constexpr int kMaxF4FusedColumns = 8192;
 constexpr int64_t kF4FusedMinTiles = 1536;
+constexpr int64_t kF4FusedSmallMinM = 2048;
+constexpr int64_t kF4FusedSmallMaxM = 6144;          // 72 KB of LDS: two workgroups per CU
+constexpr int64_t kF4FusedSmallMaxTilesWide = 256;   // beyond kF4FusedSmallMaxM: one round of workgroups
 static bool f4_records_fit(int64_t m, int64_t B) { return m * B <= kMaxF4FusedColumns; }
+static bool f4_fused_small_wins(int64_t B, int64_t m, int64_t tiles) {
+  return B == 1 && m >= kF4FusedSmallMinM && (m <= kF4FusedSmallMaxM || tiles <= kF4FusedSmallMaxTilesWide);
+}
 
 static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B, int64_t m, int64_t tiles = 0,
                        bool shared_x = true) {
@@ -232,7 +245,9 @@ static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B, int64_t m,
   if (kernel == FAIRY2I_GEMV_AUTO)
     kernel = x_dtype == FAIRY2I_X_DIGITS    ? FAIRY2I_GEMV_MFMA_I8
            : x_dtype == FAIRY2I_X_DIGITS_F6 ? FAIRY2I_GEMV_MFMA_F4
-           : x_dtype == FAIRY2I_BF16        ? (B <= 2 && f4_records_fit(m, B) && shared_x && tiles >= kF4FusedMinTiles
+           : x_dtype == FAIRY2I_BF16        ? (B <= 2 && f4_records_fit(m, B) &&
+                                                       (tiles >= kF4FusedMinTiles ? shared_x
+                                                                                  : f4_fused_small_wins(B, m, tiles))
                                                    ? FAIRY2I_GEMV_MFMA_F4 : FAIRY2I_GEMV_MFMA_BF16)
                                             : FAIRY2I_GEMV_VALU;
   if (kernel == FAIRY2I_GEMV_MFMA) kernel = FAIRY2I_GEMV_MFMA_BF16;

@@ -197,7 +197,7 @@ hipError_t launch_gemv_mfma(const uint8_t* packed, const float* scales, int n, i
 hipError_t launch_gemv_i8(const uint8_t* packed, const float* scales, int n, int m, int T,
                           const void* digits, int B, void* y, int y_bf16, hipStream_t s);
 hipError_t launch_gemv_i8_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
-// x_bf16: x is bf16 [B][2m] and each workgroup builds its fp6 digit records on chip; otherwise x
+// x_bf16: x is bf16 [B][2m] and each workgroup builds its digit records on chip; otherwise x
 // is the digit form made by launch_x_digits_f6.
 hipError_t launch_gemv_f4(const uint8_t* packed, const float* scales, int n, int m, int T,
                           const void* x, int B, void* y, int y_bf16, int x_bf16, hipStream_t s);

@@ -29,8 +29,8 @@
 //    Su + Sv is even and below 2^25, so the halving is exact too.  The factor 6 leaves in the
 //    epilogue's digit weight; the only roundings are X itself and the fp32 epilogue.
 //  * bf16 x without a digit-form buffer: each workgroup builds the records it multiplies in LDS
-//    (build_f6_records: same S, X and digits as k_x_digits_f6, so the outputs equal the two-call
-//    form bit for bit).  Large launches keep their workgroups resident (k_gemv_f4_persist), so a
+//    (build_f4_records: same S, X and digits as k_x_digits_f6, held as fp4, which represents
+//    every digit exactly, so the outputs equal the two-call form bit for bit).  Large launches keep their workgroups resident (k_gemv_f4_persist), so a
 //    workgroup builds once and then streams many tiles; small launches build once per tile.
 //  * Streaming as in the int8 kernel: one wave per 16-row tile of one item of a grouped or strided call
 //    (or NW waves splitting the 256-column chunks for small launches), one 1 KB load per plane
@@ -191,19 +191,22 @@ hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blo
   return hipGetLastError();
 }
 
-// ------------------------------------------- fp6 digit records built on chip (bf16 x) ----
+// ------------------------------------------- fp4 digit records built on chip (bf16 x) ----
 //
 // The fp4 GEMV on bf16 x without a digit-form buffer: each workgroup makes the records its waves
-// multiply -- the same X = rne(x 2^S) with the same S and digits as k_x_digits_f6, so the outputs
-// are those of the two-call form bit for bit -- in LDS, once, and its waves read their B operands
-// from there.  Records are compact (24 bytes: the 32 six-bit values, no padding), ordered
-// [chunk][step][b][lane] as in the digit form.  The digits come from Y = X + kDigitBias, whose
-// plain base-8 digits are the balanced digits plus 4 (X is within +-2^22, so 0 <= Y < 8^8); a
-// v_perm_b32 maps four such digits at once to their fp6 e2m3 codes.
-constexpr int kRecBytes = 24;
+// multiply -- the same X = rne(x 2^S), with the same S and digits as k_x_digits_f6 -- in LDS, once,
+// and its waves read their B operands from there.  The digits d in [-4, 3] are exact in fp4 e2m1
+// too (0, +-1, +-2, +-3, -4), so these records hold them as fp4: 16 bytes (the 32 values, element
+// q in bits 4q..4q+3), ordered [chunk][step][b][lane] as in the digit form, and the MFMAs that
+// read them take B as fp4.  Every product +-6d and every sum are the integers of the fp6 form, so
+// the outputs equal the two-call form's bit for bit.  The digits come from Y = X + kDigitBias,
+// whose plain base-8 digits are the balanced digits plus 4 (X is within +-2^22, so
+// 0 <= Y < 8^8); a v_perm_b32 maps four such digits at once to their fp4 codes (one per byte),
+// and two such words interleave into a word of eight nibbles.
+constexpr int kRecBytes = 16;
 constexpr int kDigitBias = 9586980;                 // 4 (8^8 - 1) / 7
-constexpr uint32_t kF6CodesLo = 0x28303438u;       // fp6 e2m3 of the digits -4, -3, -2, -1
-constexpr uint32_t kF6CodesHi = 0x14100800u;       // and of 0, 1, 2, 3
+constexpr uint32_t kF4CodesLo = 0x0A0C0D0Eu;       // fp4 e2m1 of the digits -4, -3, -2, -1
+constexpr uint32_t kF4CodesHi = 0x05040200u;       // and of 0, 1, 2, 3
 
 // LDS bytes of the records of a row of m columns and B batch entries.
 __host__ __device__ inline int f4_record_bytes(int m, int B) {
@@ -213,31 +216,94 @@ __host__ __device__ inline int f4_record_bytes(int m, int B) {
 // LDS bytes of the staged bf16 x of B batch entries (2m values each).
 __host__ __device__ inline int f4_xstage_bytes(int m, int B) { return 4 * m * B; }
 
-// Workgroup-collective: reads x (bf16 [B][2m]; its loads all issued before any is waited on),
-// takes S_b of every batch entry into s_S[b], then builds every record into s_rec.  kStage: x is
-// copied into s_x on the first pass and the records are built from that copy; otherwise they read
-// x again from global memory (from L2: every workgroup of the launch reads the same x), which
-// leaves the workgroup only the records' LDS.  Ends with a barrier.  s_red holds one float per
-// wave and batch entry.
+// Maximum over the 64 lanes of a wave (exact, so the order is free): DPP within each row of 16
+// lanes, then the four rows' results.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_read<0xB1>(v));                 // lane ^ 1
+  v = fmaxf(v, dpp_read<0x4E>(v));                 // lane ^ 2
+  v = fmaxf(v, dpp_read<0x141>(v));                // row_half_mirror
+  v = fmaxf(v, dpp_read<0x140>(v));                // row_mirror: every lane holds its row's maximum
+  const int iv = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// The four 3-bit digits of a 12-bit value, one per byte (digit i in the low bits of byte i).
+__device__ __forceinline__ uint32_t spread_digits(uint32_t v) {
+  v = (v | (v << 10)) & 0x003F003Fu;                // digits 0-1 in bits 0-5, digits 2-3 in bits 16-21
+  return (v | (v << 5)) & 0x07070707u;              // each digit at the bottom of its own byte
+}
+
+// 4 x 4 byte transpose: byte t of out[i] is byte i of in[t].
+__device__ __forceinline__ void transpose_bytes(const uint32_t in[4], uint32_t out[4]) {
+  const uint32_t u0 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);   // in0.0 in1.0 in0.1 in1.1
+  const uint32_t u1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);   // in0.2 in1.2 in0.3 in1.3
+  const uint32_t u2 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+  const uint32_t u3 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(u2, u0, 0x05040100u);                     // u0.0 u0.1 u2.0 u2.1
+  out[1] = __builtin_amdgcn_perm(u2, u0, 0x07060302u);                     // u0.2 u0.3 u2.2 u2.3
+  out[2] = __builtin_amdgcn_perm(u3, u1, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(u3, u1, 0x07060302u);
+}
+
+// Workgroup-collective: reads x (bf16 [B][2m]), takes S_b of every batch entry (each thread
+// computes it; s_S[b] keeps a copy for the epilogue), then builds every record into s_rec.
+// kStage: x is copied into s_x on the first pass and the records are built from that copy;
+// otherwise they read x again from global memory (from L2: every workgroup of the launch reads the
+// same x), which leaves the workgroup only the records' LDS.  s_red holds one float per wave and
+// batch entry.  In two parts: load_x() issues the loads of the first (usually the only) batch of x
+// into registers, build() does the rest and ends with a barrier.  Every wave of the workgroup calls
+// both, once each, in that order; a wave may issue its first code loads between them, and since a
+// wave's loads complete in issue order, build()'s wait for x then does not wait for those code
+// loads, which stream while the records are built.
 template <bool kStage>
-__device__ void build_f6_records(const uint16_t* __restrict__ x, int m, int B, uint8_t* __restrict__ s_rec,
-                                 uint16_t* __restrict__ s_x, int* __restrict__ s_S, float* __restrict__ s_red) {
+struct F4RecordBuild {
+  static constexpr int kBatch = 8;                    // 16-byte units of x in flight per thread
+  const uint16_t* x;
+  int m, B;
+  uint8_t* s_rec;
+  uint16_t* s_x;
+  int* s_S;
+  float* s_red;
+  uint4 v[kBatch];
+
+  __device__ __forceinline__ int units() const { return (2 * m * B) / 8; }   // 16-byte units of x (8 values each)
+  __device__ __forceinline__ void load_batch(int u0) {
+    const int nthr = blockDim.x, nu = units();
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int u = u0 + k * nthr;
+      v[k] = u < nu ? reinterpret_cast<const uint4*>(x)[u] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void load_x() {
+    load_batch(threadIdx.x);
+    __builtin_amdgcn_sched_barrier(0);                // issued before the caller's next loads
+  }
+  __device__ __forceinline__ void build();
+};
+
+// No record build (the operands come from the digit form, or the records are already built).
+struct NoRecordBuild {
+  __device__ __forceinline__ void load_x() {}
+  __device__ __forceinline__ void build() {}
+};
+
+template <bool kStage>
+__device__ __forceinline__ void F4RecordBuild<kStage>::build() {
+  __builtin_amdgcn_sched_barrier(0);                  // the caller's loads stay ahead of the build
   const int tid = threadIdx.x, nthr = blockDim.x, nwave = nthr / kWave;
-  const int units = (2 * m * B) / 8;                  // 16-byte units of x (8 values each)
+  const int nu = units();
   const int per_b = (2 * m) / 8;
   float amax[2] = {0.f, 0.f};
-  constexpr int kBatch = 8;                           // units in flight per thread
-  for (int u0 = tid; u0 < units; u0 += kBatch * nthr) {
-    uint4 v[kBatch];
+  auto take = [&](int u0) {                           // stage and take the maxima of a loaded batch
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int u = u0 + k * nthr;
-      v[k] = u < units ? reinterpret_cast<const uint4*>(x)[u] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int u = u0 + k * nthr;
-      if (u < units) {
+      if (u < nu) {
         if constexpr (kStage) reinterpret_cast<uint4*>(s_x)[u] = v[k];
         const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
         float mx = 0.f;
@@ -246,75 +312,94 @@ __device__ void build_f6_records(const uint16_t* __restrict__ x, int m, int B, u
         if (u < per_b) amax[0] = fmaxf(amax[0], mx); else amax[1] = fmaxf(amax[1], mx);
       }
     }
+  };
+  take(tid);                                          // the batch load_x issued: outside the loop, so
+  for (int u0 = tid + kBatch * nthr; u0 < nu; u0 += kBatch * nthr) {   // its waits count x alone
+    load_batch(u0);
+    take(u0);
   }
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) amax[b] = fmaxf(amax[b], __shfl_xor(amax[b], off));
-  }
+  amax[0] = wave_max(amax[0]);
+  if (B > 1) amax[1] = wave_max(amax[1]);
   if ((tid & (kWave - 1)) == 0) {
     s_red[tid / kWave] = amax[0];
     s_red[nwave + tid / kWave] = amax[1];
   }
   __syncthreads();
-  if (tid < B) {                                      // max |x_b| is order-free, so exact
-    float mx = 0.f;
-    for (int w = 0; w < nwave; ++w) mx = fmaxf(mx, s_red[tid * nwave + w]);
-    s_S[tid] = digit_exponent(mx);
+  int S[2] = {0, 0};                                  // max |x_b| is order-free, so exact
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    if (b < B) {
+      float mx = 0.f;
+      for (int w = 0; w < nwave; ++w) mx = fmaxf(mx, s_red[b * nwave + w]);
+      S[b] = digit_exponent(mx);
+    }
   }
-  __syncthreads();
+  if (tid < B) s_S[tid] = tid == 0 ? S[0] : S[1];     // read by the epilogue, after the last barrier
   // Records in halves: an item is 16 consecutive columns of one (chunk, step, batch entry, lane
   // group, component) -- elements 16h .. 16h + 15 of that record -- and all eight of its digits,
-  // so each column's Y is formed once; element q = 16h + 4a + i is column f4_column(0, 0, 4a + i)
-  // of the half, and the half of digit l's record is the 96 bits 3h .. 3h + 2 (in dwords).
+  // so each column's Y is formed once; element q = 16h + e is column f4_column(0, 0, e) of the
+  // half, and the half of digit l's record is its dwords 2h and 2h + 1 (elements 8j .. 8j + 7 of
+  // the half in dword 2h + j).
   const int nitem = ((m + kF4Chunk - 1) / kF4Chunk) * 2 * B * 16;
   for (int item = tid; item < nitem; item += nthr) {
     const int h = item & 1, comp = (item >> 1) & 1, g = (item >> 2) & 3, blk = item >> 4;
     const int b = blk % B, cs = blk / B, s = cs & 1, c = cs >> 1;
-    uint32_t* dst0 = reinterpret_cast<uint32_t*>(s_rec + (((c * 2 + s) * B + b) * kWave + 16 * g + 8 * comp) * kRecBytes) + 3 * h;
+    uint8_t* dst0 = s_rec + (((c * 2 + s) * B + b) * kWave + 16 * g + 8 * comp) * kRecBytes + 8 * h;
     if (kF4Chunk * c + 64 * g < m) {
-      const int S = s_S[b];
-      const float f1 = ldexpf(1.0f, S / 2), f2 = ldexpf(1.0f, S - S / 2);   // 2^S, exact in two steps
+      const int Sb = b == 0 ? S[0] : S[1];
+      const float f1 = ldexpf(1.0f, Sb / 2), f2 = ldexpf(1.0f, Sb - Sb / 2);   // 2^S, exact in two steps
       const uint4* src = reinterpret_cast<const uint4*>((kStage ? s_x : x) + (int64_t)b * 2 * m + (int64_t)comp * m +
                                                        kF4Chunk * c + 64 * g + 32 * s + 16 * h);
-      int Y[16];                                      // X + kDigitBias of the half's 16 columns
+      // Y of each of the half's 16 columns, then its digits 0-3 and 4-7 as fp4 codes, one per byte.
+      // X = rne(x 2^S): x f1 f2 is exact and below 2^22 in magnitude, so adding 1.5 2^23 in the
+      // same fma rounds it to the integer in the sum's low bits (ties to even, as rintf).
+      uint32_t cl[16], ch[16];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const uint4 u = src[k];
         const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Y[8 * k + 2 * e] = (int)rintf((bf16_lo(wd[e]) * f1) * f2) + kDigitBias;
-          Y[8 * k + 2 * e + 1] = (int)rintf((bf16_hi(wd[e]) * f1) * f2) + kDigitBias;
+        for (int e = 0; e < 8; ++e) {
+          const float xv = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+          const uint32_t y = __float_as_uint(__builtin_fmaf(xv * f1, f2, 12582912.0f)) -
+                             (0x4B400000u - (uint32_t)kDigitBias);
+          cl[8 * k + e] = __builtin_amdgcn_perm(kF4CodesHi, kF4CodesLo, spread_digits(y & 0xFFFu));
+          ch[8 * k + e] = __builtin_amdgcn_perm(kF4CodesHi, kF4CodesLo, spread_digits(y >> 12));
         }
       }
-#pragma unroll 2
-      for (int l = 0; l < 8; ++l) {
-        uint32_t p24[4];
+      // Dword j of digit l's half: nibble k is element 8j + k, so byte t pairs elements 8j + 2t
+      // and 8j + 2t + 1; the pairs of all four digits of a word, transposed, give four digits'
+      // dwords at once.
+      uint32_t dw[2][8];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          uint32_t sel = 0;
+      for (int j = 0; j < 2; ++j) {
+        uint32_t pl[4], ph[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sel |= (uint32_t)((Y[f4_column(0, 0, 4 * a + i)] >> (3 * l)) & 7) << (8 * i);
-          const uint32_t codes = __builtin_amdgcn_perm(kF6CodesHi, kF6CodesLo, sel);
-          p24[a] = (codes & 0x3Fu) | ((codes >> 2) & 0xFC0u) | ((codes >> 4) & 0x3F000u) | ((codes >> 6) & 0xFC0000u);
+        for (int t = 0; t < 4; ++t) {
+          const int c0 = f4_column(0, 0, 8 * j + 2 * t), c1 = f4_column(0, 0, 8 * j + 2 * t + 1);
+          pl[t] = cl[c0] | (cl[c1] << 4);
+          ph[t] = ch[c0] | (ch[c1] << 4);
         }
-        uint32_t* dst = dst0 + l * (kRecBytes / 4);
-        dst[0] = p24[0] | (p24[1] << 24);
-        dst[1] = (p24[1] >> 8) | (p24[2] << 16);
-        dst[2] = (p24[2] >> 16) | (p24[3] << 8);
+        transpose_bytes(pl, &dw[j][0]);
+        transpose_bytes(ph, &dw[j][4]);
       }
+#pragma unroll
+      for (int l = 0; l < 8; ++l) *reinterpret_cast<uint2*>(dst0 + l * kRecBytes) = make_uint2(dw[0][l], dw[1][l]);
     } else {
 #pragma unroll
-      for (int l = 0; l < 8; ++l) {
-        uint32_t* dst = dst0 + l * (kRecBytes / 4);
-        dst[0] = 0u;
-        dst[1] = 0u;
-        dst[2] = 0u;
-      }
+      for (int l = 0; l < 8; ++l) *reinterpret_cast<uint2*>(dst0 + l * kRecBytes) = make_uint2(0u, 0u);
     }
   }
   __syncthreads();
+}
+
+// The whole build at once (for callers with no loads to put between its parts).
+template <bool kStage>
+__device__ __forceinline__ void build_f4_records(const uint16_t* x, int m, int B, uint8_t* s_rec, uint16_t* s_x,
+                                                 int* s_S, float* s_red) {
+  F4RecordBuild<kStage> bld{x, m, B, s_rec, s_x, s_S, s_red, {}};
+  bld.load_x();
+  bld.build();
 }
 
 // ------------------------------------------------------------------------- GEMV ----
@@ -343,14 +428,16 @@ __device__ __forceinline__ void row_sums(float& vre, float& vim) {
 // 16 T x 64 floats per wave) -- exact, since every partial and total is an integer below 2^24 --
 // and wave w then runs the single-wave epilogue for rows 4g + w, so the outputs are bit-identical
 // to one wave streaming the whole unit.
-// FUSED: x is bf16 [B][2m] (not its digit form) and the workgroup has built its records in s_rec
-// and S_b in s_S (build_f6_records) before its waves call this function.
-template <int TT, int NW, int BT, typename YT, bool EXACT = false, bool FUSED = false>
+// FUSED: x is bf16 [B][2m] (not its digit form); the operands are the workgroup's records in s_rec
+// and S_b in s_S, built either before the waves call this function or by bld, which the function
+// calls (every wave, once) with the tile's scale and first code loads between its two parts.
+template <int TT, int NW, int BT, typename YT, bool EXACT = false, bool FUSED = false,
+          typename Build = NoRecordBuild>
 __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B, int unit, int wave,
                                              float* __restrict__ s_scw, float (*s_y)[BT][2][16],
                                              float* __restrict__ s_acc = nullptr,
                                              const uint8_t* __restrict__ s_rec = nullptr,
-                                             const int* __restrict__ s_S = nullptr) {
+                                             const int* __restrict__ s_S = nullptr, Build bld = {}) {
   static_assert(!EXACT || (NW == 4 && BT == 1), "the exact split is for four waves and one batch entry");
   int tile;
   const GemvItem it = locate_item<YT>(grp, unit, tile);
@@ -414,9 +501,8 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
       for (int b = 0; b < BT; ++b) {
         if constexpr (FUSED) {
           if (b < B) {
-            const uint2* rp = reinterpret_cast<const uint2*>(s_rec + (((ch.c * 2 + s) * B + b) * kWave + lane) * kRecBytes);
-            const uint2 r0 = rp[0], r1 = rp[1], r2 = rp[2];
-            xs[b] = v8i{(int)r0.x, (int)r0.y, (int)r1.x, (int)r1.y, (int)r2.x, (int)r2.y, 0, 0};
+            const uint4 rr = *reinterpret_cast<const uint4*>(s_rec + (((ch.c * 2 + s) * B + b) * kWave + lane) * kRecBytes);
+            xs[b] = v8i{(int)rr.x, (int)rr.y, (int)rr.z, (int)rr.w, 0, 0, 0, 0};
           } else {
             xs[b] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
           }
@@ -433,10 +519,11 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
           decode_f4(s == 0 ? q.x : q.z, s == 0 ? q.y : q.w, pu, pv);
 #pragma unroll
           for (int b = 0; b < BT; ++b) {
+            // A fp4; B fp6 e2m3 (digit form) or fp4 (records in LDS); scales 2^0
             acc[t][M][0][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pu, xs[b], acc[t][M][0][b], 4, 2, 0, 127, 0, 127);   // A fp4, B fp6 e2m3, scales 2^0
+                pu, xs[b], acc[t][M][0][b], 4, FUSED ? 4 : 2, 0, 127, 0, 127);
             acc[t][M][1][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pv, xs[b], acc[t][M][1][b], 4, 2, 0, 127, 0, 127);
+                pv, xs[b], acc[t][M][1][b], 4, FUSED ? 4 : 2, 0, 127, 0, 127);
           }
         }
     }
@@ -448,12 +535,14 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
   // prefetch is issued, so every path has the same loads in flight; one past the last chunk has a
   // negative group count and so loads at the out-of-range offset, which reads nothing.
   TileScales<TT> tsc;
+  bld.load_x();
   tsc.load(scales, i0, n, lane);               // ahead of the first chunk's loads
   if constexpr (BT == 1 && TT <= 2) {
     Chunk c0, c1, c2;
     int c = wave;                                  // wave w takes chunks w, w + NW, ...
     load_chunk(c, c0);
     load_chunk(c + NW, c1);
+    bld.build();
     tsc.park(s_scw, lane);
     for (; c + 2 * NW < nchunk; c += 3 * NW) {
       load_chunk(c + 2 * NW, c2);
@@ -477,6 +566,7 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
     Chunk cur, nxt;
     int c = wave;
     load_chunk(c, cur);
+    bld.build();
     tsc.park(s_scw, lane);
     for (; c < nchunk; c += NW) {
       load_chunk(c + NW, nxt);
@@ -488,6 +578,7 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
     Chunk c0, c1;
     int c = wave;
     load_chunk(c, c0);
+    bld.build();
     tsc.park(s_scw, lane);
     for (; c + NW < nchunk; c += 2 * NW) {
       load_chunk(c + NW, c1);
@@ -587,11 +678,17 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
 // chunk it runs that unit's epilogue.  B operands come from the workgroup's records in LDS; each
 // unit's scales are loaded while the unit streams and parked in s_scw before its epilogue.  The
 // arithmetic per unit is that of gemv_f4_tile with one wave, so the outputs are identical.
-template <int TT, int BT, typename YT>
+// bld builds the records (every wave calls it once), with the first unit's scale and code loads
+// issued between its two parts.
+template <int TT, int BT, typename YT, typename Build>
 __device__ __forceinline__ void gemv_f4_stream(const GemvGroup& grp, int m, int B, int first, int stride, int tiles,
                                                float* __restrict__ s_scw, const uint8_t* __restrict__ s_rec,
-                                               const int* __restrict__ s_S) {
-  if (first >= tiles) return;
+                                               const int* __restrict__ s_S, Build bld) {
+  if (first >= tiles) {
+    bld.load_x();
+    bld.build();
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane & 15, g = lane >> 4;
   const int nchunk = (m + kF4Chunk - 1) / kF4Chunk;
@@ -697,9 +794,8 @@ __device__ __forceinline__ void gemv_f4_stream(const GemvGroup& grp, int m, int 
 #pragma unroll
       for (int b = 0; b < BT; ++b) {
         if (b < B) {
-          const uint2* rp = reinterpret_cast<const uint2*>(s_rec + (((cc * 2 + s) * B + b) * kWave + lane) * kRecBytes);
-          const uint2 r0 = rp[0], r1 = rp[1], r2 = rp[2];
-          xs[b] = v8i{(int)r0.x, (int)r0.y, (int)r1.x, (int)r1.y, (int)r2.x, (int)r2.y, 0, 0};
+          const uint4 rr = *reinterpret_cast<const uint4*>(s_rec + (((cc * 2 + s) * B + b) * kWave + lane) * kRecBytes);
+          xs[b] = v8i{(int)rr.x, (int)rr.y, (int)rr.z, (int)rr.w, 0, 0, 0, 0};
         } else {
           xs[b] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         }
@@ -714,9 +810,9 @@ __device__ __forceinline__ void gemv_f4_stream(const GemvGroup& grp, int m, int 
 #pragma unroll
           for (int b = 0; b < BT; ++b) {
             acc[t][M][0][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pu, xs[b], acc[t][M][0][b], 4, 2, 0, 127, 0, 127);   // A fp4, B fp6 e2m3, scales 2^0
+                pu, xs[b], acc[t][M][0][b], 4, 4, 0, 127, 0, 127);   // A and B fp4, scales 2^0
             acc[t][M][1][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pv, xs[b], acc[t][M][1][b], 4, 2, 0, 127, 0, 127);
+                pv, xs[b], acc[t][M][1][b], 4, 4, 0, 127, 0, 127);
           }
         }
     }
@@ -727,11 +823,13 @@ __device__ __forceinline__ void gemv_f4_stream(const GemvGroup& grp, int m, int 
     }
   };
 
+  bld.load_x();
   load_scales(0);
   if constexpr (BT == 1 && TT <= 2) {                  // three operand sets in flight
     Chunk c0, c1, c2;
     load_next(c0);
     load_next(c1);
+    bld.build();
     int st = 0;
     for (; st + 2 < total; st += 3) {
       load_next(c2);
@@ -749,6 +847,7 @@ __device__ __forceinline__ void gemv_f4_stream(const GemvGroup& grp, int m, int 
   } else {                                            // two
     Chunk c0, c1;
     load_next(c0);
+    bld.build();
     int st = 0;
     for (; st + 1 < total; st += 2) {
       load_next(c1);
@@ -773,10 +872,12 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
   if constexpr (FUSED) {
     int tile;
     const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
-    build_f6_records<true>(static_cast<const uint16_t*>(it.x), m, B, s_dyn,
-                           reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)), s_S, s_red);
+    const F4RecordBuild<true> bld{static_cast<const uint16_t*>(it.x), m, B, s_dyn,
+                                  reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)), s_S, s_red, {}};
+    gemv_f4_tile<TT, NW, BT, YT, false, true>(grp, m, B, blockIdx.x, wave, s_sc[wave], s_y, nullptr, s_dyn, s_S, bld);
+  } else {
+    gemv_f4_tile<TT, NW, BT, YT, false, false>(grp, m, B, blockIdx.x, wave, s_sc[wave], s_y);
   }
-  gemv_f4_tile<TT, NW, BT, YT, false, FUSED>(grp, m, B, blockIdx.x, wave, s_sc[wave], s_y, nullptr, s_dyn, s_S);
 }
 
 // Large batch-1 launches in two granularities.  The first nA workgroups take four units each,
@@ -798,7 +899,7 @@ __global__ __launch_bounds__(kWave * 4, 3) void k_gemv_f4_mixed(const GemvGroup 
   float* s_acc = FUSED ? reinterpret_cast<float*>(s_dyn) : s_acc_own;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   if constexpr (FUSED)
-    build_f6_records<true>(static_cast<const uint16_t*>(grp.items[0].x), m, 1, s_dyn,
+    build_f4_records<true>(static_cast<const uint16_t*>(grp.items[0].x), m, 1, s_dyn,
                            reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, 1)), s_S, s_red);
   if ((int)blockIdx.x < nA)
     gemv_f4_tile<TT, 1, 1, YT, false, FUSED>(grp, m, 1, 4 * (int)blockIdx.x + wave, 0, s_sc[wave], s_y, nullptr,
@@ -820,13 +921,17 @@ __global__ __launch_bounds__(kWave * 4, (BT == 1 && TT <= 3) ? 3 : 1) void k_gem
   __shared__ float s_red[8];
   extern __shared__ __align__(16) uint8_t s_dyn[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
-  // batch 2 builds without the staged copy of x: the records alone let three workgroups share a CU
-  build_f6_records<BT == 1>(static_cast<const uint16_t*>(grp.items[0].x), m, B, s_dyn,
-                            BT == 1 ? reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)) : nullptr, s_S, s_red);
+  const uint16_t* x = static_cast<const uint16_t*>(grp.items[0].x);
   const int tiles = group_tiles(grp);
   if constexpr (BT == 1) {
-    gemv_f4_stream<TT, BT, YT>(grp, m, B, 4 * (int)blockIdx.x + wave, 4 * (int)gridDim.x, tiles, s_sc[wave], s_dyn, s_S);
+    const F4RecordBuild<true> bld{x, m, B, s_dyn, reinterpret_cast<uint16_t*>(s_dyn + f4_record_bytes(m, B)), s_S,
+                                  s_red, {}};
+    gemv_f4_stream<TT, BT, YT>(grp, m, B, 4 * (int)blockIdx.x + wave, 4 * (int)gridDim.x, tiles, s_sc[wave], s_dyn, s_S,
+                               bld);
   } else {
+    // batch 2 builds without the staged copy of x (the records alone let three workgroups share a
+    // CU), before its tile loop
+    build_f4_records<false>(x, m, B, s_dyn, nullptr, s_S, s_red);
     // batch 2: one tile at a time (the streaming form's registers would halve its occupancy;
     // measured 5139 against 4832 GB/s on the 1 GiB attention pool)
     for (int unit = 4 * (int)blockIdx.x + wave; unit < tiles; unit += 4 * (int)gridDim.x)
