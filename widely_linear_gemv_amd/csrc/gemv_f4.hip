@@ -404,13 +404,14 @@ __device__ __forceinline__ void build_f4_records(const uint16_t* x, int m, int B
 
 // ------------------------------------------------------------------------- GEMV ----
 
-// The epilogue's sum over a row's 16 lanes (digits and components).  One batch entry per tile:
-// DPP permutes (group_sum).  Two: lane shuffles, whose LDS round trips the compiler schedules
-// with fewer live registers here (with DPP the batch-2 kernels took 8-80 more registers, which
-// cost a wave per SIMD at T = 2 on small launches and at T = 3).
-template <int BT>
+// The epilogue's sum over a row's 16 lanes (digits and components): DPP permutes (group_sum) for
+// one batch entry per tile, and for two at T <= 2 (there they cost no registers, and against lane
+// shuffles through LDS they saved ~1 us per small batch-2 launch: 32-layer decode step on the
+// digit form 1220 -> 1092 us).  Two entries at T > 2: lane shuffles, which the compiler schedules
+// with fewer live registers there (with DPP those kernels took 16-48 more and lost a wave per SIMD).
+template <int BT, int TT>
 __device__ __forceinline__ void row_sums(float& vre, float& vim) {
-  if constexpr (BT == 1) {
+  if constexpr (BT == 1 || TT <= 2) {
     vre = group_sum<16>(vre);
     vim = group_sum<16>(vim);
   } else {
@@ -649,7 +650,7 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
       }
       vre *= wdig;
       vim *= wdig;
-      row_sums<BT>(vre, vim);
+      row_sums<BT, TT>(vre, vim);
       if (NW > 1 && !EXACT) {
         if (r == 0) { s_y[wave][b][0][4 * g + e] = vre; s_y[wave][b][1][4 * g + e] = vim; }
       } else if (r == 0 && b < B && i < n) {
@@ -775,7 +776,7 @@ __device__ __forceinline__ void gemv_f4_stream(const GemvGroup& grp, int m, int 
         }
         vre *= wdig;
         vim *= wdig;
-        row_sums<BT>(vre, vim);
+        row_sums<BT, TT>(vre, vim);
         if (r == 0 && b < B && i < n) {
           store_out(y, (int64_t)b * ys + i, vre);
           store_out(y, (int64_t)b * ys + n + i, vim);
