@@ -93,16 +93,23 @@ typedef enum {
  *              digit form on v_mfma_scale_f32_16x16x128_f8f6f4: exact integer sums in fp32, B_re
  *              and B_im sums as (u +- v) / 2, fp32 epilogue.  B <= 2.  x_dtype FAIRY2I_X_DIGITS_F6
  *              (the digit form made once by fairy2i_x_digits_f6 and shared by every GEMV that
- *              reads that x) or FAIRY2I_BF16: then each workgroup builds the same digits on chip
- *              from the bf16 x (outputs identical bit for bit; m * B <= 8192; in a grouped call
- *              of 1536 tiles or more every item must have the same x).  The fastest decode
+ *              reads that x) or FAIRY2I_BF16: then the digits are built on chip from the bf16 x
+ *              (m * B <= 8192; in a grouped call of 1536 tiles or more every item must have the
+ *              same x).  In launches of 1536 tiles or more, at B = 2, and for m <= 256 each
+ *              workgroup builds the same digits as fairy2i_x_digits_f6 (outputs identical bit for
+ *              bit to the two-call form).  Smaller launches at B = 1 digitize each 256-column
+ *              chunk at its own exponent (max over the chunk's 512 values of |x| 2^S_c in
+ *              [2^21, 2^22)), each wave for the chunks it multiplies, and pass 2^-S_c to the
+ *              MFMAs as block scales: every element is off by at most 2^-22 of its chunk's
+ *              maximum (never more than the per-row form), the chunks' sums are added in fp32,
+ *              and the outputs are not bit-identical to the two-call form.  The fastest decode
  *              kernel on gfx950: half the MFMA cycles and about half the VALU work per code of
  *              MFMA_I8.
  * AUTO with bf16 x takes MFMA_F4 for launches of at least 1536 16-row tiles with B <= 2,
  * m * B <= 8192 and one x for the launch (resident workgroups build the digits once for many
  * tiles); for smaller launches at B = 1 with 2048 <= m <= 6144, or with m up to 8192 in launches
- * of at most 256 tiles (each workgroup builds the digits for its own tile, which there still costs
- * less than MFMA_BF16's work); and MFMA_BF16 otherwise. */
+ * of at most 256 tiles (each wave builds the digits of its own chunks, which there costs less than
+ * MFMA_BF16's work); and MFMA_BF16 otherwise. */
 typedef enum {
   FAIRY2I_GEMV_AUTO = 0,
   FAIRY2I_GEMV_VALU = 1,

@@ -213,6 +213,9 @@ __host__ __device__ inline int f4_record_bytes(int m, int B) {
   return ((m + kF4Chunk - 1) / kF4Chunk) * 2 * B * kWave * kRecBytes;
 }
 
+// LDS bytes of the per-chunk exponents of the per-wave records (16-byte aligned).
+__host__ __device__ inline int f4_local_exp_bytes(int m) { return (((m + kF4Chunk - 1) / kF4Chunk) * 4 + 15) & ~15; }
+
 // LDS bytes of the staged bf16 x of B batch entries (2m values each).
 __host__ __device__ inline int f4_xstage_bytes(int m, int B) { return 4 * m * B; }
 
@@ -249,6 +252,46 @@ __device__ __forceinline__ void transpose_bytes(const uint32_t in[4], uint32_t o
   out[3] = __builtin_amdgcn_perm(u3, u1, 0x07060302u);
 }
 
+// Half of the eight digit records of one (chunk, step, batch entry, lane group, component): its
+// 16 columns' bf16 values u (in column order, elements 16h .. 16h + 15 of the records) at exponent
+// S; writes 8 bytes of digit l's record at dst0 + l kRecBytes for every l.  Each column's Y is
+// formed once, then its digits 0-3 and 4-7 as fp4 codes, one per byte.  X = rne(x 2^S): x f1 f2 is
+// exact and below 2^22 in magnitude, so adding 1.5 2^23 in the same fma rounds it to the integer in
+// the sum's low bits (ties to even, as rintf).
+__device__ __forceinline__ void build_record_half(const uint4 u[2], int S, uint8_t* dst0) {
+  const float f1 = ldexpf(1.0f, S / 2), f2 = ldexpf(1.0f, S - S / 2);   // 2^S, exact in two steps
+  uint32_t cl[16], ch[16];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t wd[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xv = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+      const uint32_t y = __float_as_uint(__builtin_fmaf(xv * f1, f2, 12582912.0f)) -
+                         (0x4B400000u - (uint32_t)kDigitBias);
+      cl[8 * k + e] = __builtin_amdgcn_perm(kF4CodesHi, kF4CodesLo, spread_digits(y & 0xFFFu));
+      ch[8 * k + e] = __builtin_amdgcn_perm(kF4CodesHi, kF4CodesLo, spread_digits(y >> 12));
+    }
+  }
+  // Dword j of digit l's half: nibble k is element 8j + k, so byte t pairs elements 8j + 2t and
+  // 8j + 2t + 1; the pairs of all four digits of a word, transposed, give four digits' dwords at once.
+  uint32_t dw[2][8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t pl[4], ph[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c0 = f4_column(0, 0, 8 * j + 2 * t), c1 = f4_column(0, 0, 8 * j + 2 * t + 1);
+      pl[t] = cl[c0] | (cl[c1] << 4);
+      ph[t] = ch[c0] | (ch[c1] << 4);
+    }
+    transpose_bytes(pl, &dw[j][0]);
+    transpose_bytes(ph, &dw[j][4]);
+  }
+#pragma unroll
+  for (int l = 0; l < 8; ++l) *reinterpret_cast<uint2*>(dst0 + l * kRecBytes) = make_uint2(dw[0][l], dw[1][l]);
+}
+
 // Workgroup-collective: reads x (bf16 [B][2m]), takes S_b of every batch entry (each thread
 // computes it; s_S[b] keeps a copy for the epilogue), then builds every record into s_rec.
 // kStage: x is copied into s_x on the first pass and the records are built from that copy;
@@ -261,6 +304,7 @@ __device__ __forceinline__ void transpose_bytes(const uint32_t in[4], uint32_t o
 // loads, which stream while the records are built.
 template <bool kStage>
 struct F4RecordBuild {
+  static constexpr bool kLocal = false;               // one exponent S_b per batch entry
   static constexpr int kBatch = 8;                    // 16-byte units of x in flight per thread
   const uint16_t* x;
   int m, B;
@@ -288,6 +332,7 @@ struct F4RecordBuild {
 
 // No record build (the operands come from the digit form, or the records are already built).
 struct NoRecordBuild {
+  static constexpr bool kLocal = false;
   __device__ __forceinline__ void load_x() {}
   __device__ __forceinline__ void build() {}
 };
@@ -346,45 +391,10 @@ __device__ __forceinline__ void F4RecordBuild<kStage>::build() {
     const int b = blk % B, cs = blk / B, s = cs & 1, c = cs >> 1;
     uint8_t* dst0 = s_rec + (((c * 2 + s) * B + b) * kWave + 16 * g + 8 * comp) * kRecBytes + 8 * h;
     if (kF4Chunk * c + 64 * g < m) {
-      const int Sb = b == 0 ? S[0] : S[1];
-      const float f1 = ldexpf(1.0f, Sb / 2), f2 = ldexpf(1.0f, Sb - Sb / 2);   // 2^S, exact in two steps
       const uint4* src = reinterpret_cast<const uint4*>((kStage ? s_x : x) + (int64_t)b * 2 * m + (int64_t)comp * m +
                                                        kF4Chunk * c + 64 * g + 32 * s + 16 * h);
-      // Y of each of the half's 16 columns, then its digits 0-3 and 4-7 as fp4 codes, one per byte.
-      // X = rne(x 2^S): x f1 f2 is exact and below 2^22 in magnitude, so adding 1.5 2^23 in the
-      // same fma rounds it to the integer in the sum's low bits (ties to even, as rintf).
-      uint32_t cl[16], ch[16];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint4 u = src[k];
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xv = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
-          const uint32_t y = __float_as_uint(__builtin_fmaf(xv * f1, f2, 12582912.0f)) -
-                             (0x4B400000u - (uint32_t)kDigitBias);
-          cl[8 * k + e] = __builtin_amdgcn_perm(kF4CodesHi, kF4CodesLo, spread_digits(y & 0xFFFu));
-          ch[8 * k + e] = __builtin_amdgcn_perm(kF4CodesHi, kF4CodesLo, spread_digits(y >> 12));
-        }
-      }
-      // Dword j of digit l's half: nibble k is element 8j + k, so byte t pairs elements 8j + 2t
-      // and 8j + 2t + 1; the pairs of all four digits of a word, transposed, give four digits'
-      // dwords at once.
-      uint32_t dw[2][8];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint32_t pl[4], ph[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int c0 = f4_column(0, 0, 8 * j + 2 * t), c1 = f4_column(0, 0, 8 * j + 2 * t + 1);
-          pl[t] = cl[c0] | (cl[c1] << 4);
-          ph[t] = ch[c0] | (ch[c1] << 4);
-        }
-        transpose_bytes(pl, &dw[j][0]);
-        transpose_bytes(ph, &dw[j][4]);
-      }
-#pragma unroll
-      for (int l = 0; l < 8; ++l) *reinterpret_cast<uint2*>(dst0 + l * kRecBytes) = make_uint2(dw[0][l], dw[1][l]);
+      const uint4 u[2] = {src[0], src[1]};
+      build_record_half(u, b == 0 ? S[0] : S[1], dst0);
     } else {
 #pragma unroll
       for (int l = 0; l < 8; ++l) *reinterpret_cast<uint2*>(dst0 + l * kRecBytes) = make_uint2(0u, 0u);
@@ -401,6 +411,87 @@ __device__ __forceinline__ void build_f4_records(const uint16_t* x, int m, int B
   bld.load_x();
   bld.build();
 }
+
+// Per-wave records with one exponent per chunk (batch 1, bf16 x): wave w of the NW waves that
+// split a tile builds the records of its own chunks c = w, w + NW, ... and nothing else, each at
+// its chunk's own exponent S_c (max over the chunk's 512 values of |x| 2^S_c in [2^21, 2^22)).
+// There is no workgroup-wide step: the wave reads only its chunks of x, reduces their maxima on
+// DPP and writes records that only it reads (LDS accesses of one wave complete in order).  The
+// chunk's MFMAs then take 2^-S_c as their block scales (2^-floor(S_c/2) on A, the rest on B; S_c
+// lies in [-106, 147], so both fit E8M0), so the digit sums of every chunk enter the fp32
+// accumulators at one common scale and the epilogue applies only the digit weight.  Against one
+// exponent per row, each chunk's X keeps 22 bits below its own maximum (never fewer), and the sums
+// across chunks round in fp32.  A pass covers two of the wave's chunks, 32 items (the halves of a
+// chunk's records) each, one item per lane.
+struct F4LocalBuild {
+  static constexpr bool kLocal = true;
+  const uint16_t* x;                                  // bf16 [2m] (one batch entry)
+  int m, nw, wave;
+  uint8_t* s_rec;
+  int* s_Sc;                                          // one exponent per chunk
+  uint4 v[2];                                         // this lane's item: 16 columns of x
+  __device__ __forceinline__ int nchunk() const { return (m + kF4Chunk - 1) / kF4Chunk; }
+  __device__ __forceinline__ int lane() const { return threadIdx.x & (kWave - 1); }
+  __device__ __forceinline__ int chunk_of(int pass) const { return wave + nw * (2 * pass + (lane() >> 5)); }
+  __device__ __forceinline__ bool present(int c, int g) const { return c < nchunk() && kF4Chunk * c + 64 * g < m; }
+  __device__ __forceinline__ const uint4* src(int c) const {
+    const int item = lane() & 31, h = item & 1, comp = (item >> 1) & 1, g = (item >> 2) & 3, s = item >> 4;
+    return reinterpret_cast<const uint4*>(x + (int64_t)comp * m + kF4Chunk * c + 64 * g + 32 * s + 16 * h);
+  }
+  __device__ __forceinline__ void load_pass(int pass) {
+    const int c = chunk_of(pass), g = ((lane() & 31) >> 2) & 3;
+    if (present(c, g)) {
+      const uint4* p = src(c);
+      v[0] = p[0];
+      v[1] = p[1];
+    } else {
+      v[0] = v[1] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void load_x() {
+    load_pass(0);
+    __builtin_amdgcn_sched_barrier(0);                // issued before the caller's next loads
+  }
+  __device__ __forceinline__ void build() {
+    __builtin_amdgcn_sched_barrier(0);                // the caller's loads stay ahead of the build
+    const int cpw = wave < nchunk() ? (nchunk() - wave + nw - 1) / nw : 0;   // chunks of this wave
+    const int item = lane() & 31, h = item & 1, comp = (item >> 1) & 1, g = (item >> 2) & 3, s = item >> 4;
+    for (int pass = 0; 2 * pass < cpw; ++pass) {
+      if (pass > 0) load_pass(pass);
+      float mx = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(wd[e])), fabsf(bf16_hi(wd[e]))));
+      }
+      mx = fmaxf(mx, dpp_read<0xB1>(mx));             // lane ^ 1
+      mx = fmaxf(mx, dpp_read<0x4E>(mx));             // lane ^ 2
+      mx = fmaxf(mx, dpp_read<0x141>(mx));            // row_half_mirror
+      mx = fmaxf(mx, dpp_read<0x140>(mx));            // row_mirror: every lane holds its row's maximum
+      const int iv = __builtin_bit_cast(int, mx);
+      const float m0 = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)),
+                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16)));
+      const float m1 = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)),
+                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
+      const int S0 = digit_exponent(m0), S1 = digit_exponent(m1);
+      const int c = chunk_of(pass);
+      if (c < nchunk()) {
+        uint8_t* dst0 = s_rec + ((c * 2 + s) * kWave + 16 * g + 8 * comp) * kRecBytes + 8 * h;
+        if (present(c, g)) {
+          build_record_half(v, lane() < 32 ? S0 : S1, dst0);
+        } else {
+#pragma unroll
+          for (int l = 0; l < 8; ++l) *reinterpret_cast<uint2*>(dst0 + l * kRecBytes) = make_uint2(0u, 0u);
+        }
+      }
+      if (lane() == 0) {
+        s_Sc[wave + nw * 2 * pass] = S0;
+        if (wave + nw * (2 * pass + 1) < nchunk()) s_Sc[wave + nw * (2 * pass + 1)] = S1;
+      }
+    }
+  }
+};
 
 // ------------------------------------------------------------------------- GEMV ----
 
@@ -495,6 +586,13 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
       }
   };
   auto compute_chunk = [&](const Chunk& ch) {
+    // block scales (E8M0, 127 = 2^0): 2^-S_c for per-chunk records (Build::kLocal), else 2^0
+    int sca = 127, scb = 127;
+    if constexpr (Build::kLocal) {
+      const int S = __builtin_amdgcn_readfirstlane(bld.s_Sc[ch.c]);
+      sca = 127 - (S >> 1);
+      scb = 127 - (S - (S >> 1));
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       v8i xs[BT];                          // this step's B operands
@@ -520,11 +618,11 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
           decode_f4(s == 0 ? q.x : q.z, s == 0 ? q.y : q.w, pu, pv);
 #pragma unroll
           for (int b = 0; b < BT; ++b) {
-            // A fp4; B fp6 e2m3 (digit form) or fp4 (records in LDS); scales 2^0
+            // A fp4; B fp6 e2m3 (digit form) or fp4 (records in LDS)
             acc[t][M][0][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pu, xs[b], acc[t][M][0][b], 4, FUSED ? 4 : 2, 0, 127, 0, 127);
+                pu, xs[b], acc[t][M][0][b], 4, FUSED ? 4 : 2, 0, sca, 0, scb);
             acc[t][M][1][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pv, xs[b], acc[t][M][1][b], 4, FUSED ? 4 : 2, 0, 127, 0, 127);
+                pv, xs[b], acc[t][M][1][b], 4, FUSED ? 4 : 2, 0, sca, 0, scb);
           }
         }
     }
@@ -625,7 +723,7 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
   const int64_t ys = 2 * (int64_t)n;
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
-    const int S = b < B ? (FUSED ? s_S[b] : hdr[2 + b]) : 0;
+    const int S = Build::kLocal || b >= B ? 0 : (FUSED ? s_S[b] : hdr[2 + b]);   // kLocal: in the MFMA scales
     const float wdig = ldexpf(1.0f / 6.0f, 3 * l - S);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -881,6 +979,23 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
   }
 }
 
+// Small batch-1 launches on bf16 x (NW > 1 waves per tile): each wave builds the records of its
+// own chunks at per-chunk exponents (F4LocalBuild), so no wave waits on another before its first
+// MFMA; the waves meet once, to add their partial outputs.
+template <int TT, int NW, typename YT>
+__global__ __launch_bounds__(kWave * NW, TT <= 3 ? 3 : 1) void k_gemv_f4_local(const GemvGroup grp, int m) {
+  static_assert(NW > 1, "the waves of a tile split its chunks");
+  __shared__ float s_sc[NW][16 * TT * 4];
+  __shared__ float s_y[NW][1][2][16];                   // [wave][batch][re/im][row]
+  extern __shared__ __align__(16) uint8_t s_dyn[];       // records, then one exponent per chunk
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
+  int tile;
+  const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
+  const F4LocalBuild bld{static_cast<const uint16_t*>(it.x), m, NW, wave, s_dyn,
+                         reinterpret_cast<int*>(s_dyn + f4_record_bytes(m, 1)), {}};
+  gemv_f4_tile<TT, NW, 1, YT, false, true>(grp, m, 1, blockIdx.x, wave, s_sc[wave], s_y, nullptr, s_dyn, nullptr, bld);
+}
+
 // Large batch-1 launches in two granularities.  The first nA workgroups take four units each,
 // one wave per unit (the fastest form while the chip is full); the rest take one unit each, its
 // chunks split over the four waves.  Workgroups start in index order, so the units that finish a
@@ -949,8 +1064,9 @@ constexpr int kF4MixedMinTiles = 12288;
 
 // Most dynamic LDS a launch on bf16 x can take with BT batch entries per tile: records (and the
 // staged x, if kept) of m B <= 8192 columns, the most the C ABI accepts on this path.
+constexpr int kF4FusedMaxCols = 8192;
 static size_t f4_fused_lds_max(int BT, bool stage) {
-  const int m = 8192 / BT;
+  const int m = kF4FusedMaxCols / BT;
   return (size_t)f4_record_bytes(m, BT) + (stage ? (size_t)f4_xstage_bytes(m, BT) : 0);
 }
 
@@ -1033,6 +1149,23 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
     }
   }
   const dim3 grid(tiles);
+  if constexpr (FUSED && BT == 1) {                       // small launches: per-wave records
+    const size_t lds = (size_t)f4_record_bytes(m, 1) + f4_local_exp_bytes(m);
+    const size_t lds_max = (size_t)f4_record_bytes(kF4FusedMaxCols, 1) + f4_local_exp_bytes(kF4FusedMaxCols);
+    switch (gemv_waves_per_tile(tiles, m)) {
+#define F2I_F4_LOCAL_CASE(NWV)                                                                        \
+      {                                                                                                 \
+        static KernelLaunchState st;                                                                    \
+        lds_launch_prepare(k_gemv_f4_local<TT, NWV, YT>, lds_max, st);                                  \
+        hipLaunchKernelGGL((k_gemv_f4_local<TT, NWV, YT>), grid, dim3(NWV * kWave), lds, s, grp, m);    \
+      }                                                                                                 \
+      return;
+      case 8: F2I_F4_LOCAL_CASE(8)
+      case 4: F2I_F4_LOCAL_CASE(4)
+      default: F2I_F4_LOCAL_CASE(2)
+#undef F2I_F4_LOCAL_CASE
+    }
+  } else {
   switch (gemv_waves_per_tile(tiles, m)) {
 #define F2I_F4_CASE(NWV)                                                                               \
     {                                                                                                    \
@@ -1046,6 +1179,7 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
     case 2: F2I_F4_CASE(2)
     default: F2I_F4_CASE(1)
 #undef F2I_F4_CASE
+  }
   }
 }
 
