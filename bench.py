@@ -252,7 +252,7 @@ def stack_legs(f2, torch, dev, T, reps):
         nbytes = sum(gemv_bytes(rows // 2, cols // 2, T, B) for L in range(32) for (_, rows, cols, _) in PROJECTIONS)
         legs[f"stack_decode_b{B}"] = {"gemvs": 224, "launches": 128, "us": round(t * 1e3, 1),
                                       "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes,
-                                      "kernel": "AUTO: fp4 matrix cores with the digits of x built on chip per tile"
+                                      "kernel": "AUTO: fp4 matrix cores, each wave digitizing its own chunks of x on chip"
                                                 if B == 1 else "AUTO: bf16 matrix cores"}
         if B == 1:
             # the fp4 kernel: with its digit pass in the step (256 launches), and on x already

@@ -107,9 +107,9 @@ typedef enum {
  *              MFMA_I8.
  * AUTO with bf16 x takes MFMA_F4 for launches of at least 1536 16-row tiles with B <= 2,
  * m * B <= 8192 and one x for the launch (resident workgroups build the digits once for many
- * tiles); for smaller launches at B = 1 with 2048 <= m <= 6144, or with m up to 8192 in launches
- * of at most 256 tiles (each wave builds the digits of its own chunks, which there costs less than
- * MFMA_BF16's work); and MFMA_BF16 otherwise. */
+ * tiles); for smaller launches at B = 1 with 2048 <= m <= 8192, or 1024 <= m < 2048 in launches
+ * of at least 128 tiles (each wave builds the digits of its own chunks, which there costs less
+ * than MFMA_BF16's work); and MFMA_BF16 otherwise. */
 typedef enum {
   FAIRY2I_GEMV_AUTO = 0,
   FAIRY2I_GEMV_VALU = 1,

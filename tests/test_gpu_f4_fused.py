@@ -151,11 +151,13 @@ def test_fused_large_strided_launch(B, T, batch, n):
 
 
 @pytest.mark.parametrize("B,m,tiles,fused", [(1, 2048, 24, True), (1, 5504, 8, True), (1, 8192, 16, True),
-                                              (1, 8192, 260, False), (1, 1024, 40, False), (2, 2048, 24, False)])
+                                              (1, 8192, 260, True), (1, 1024, 40, False), (1, 1024, 130, True),
+                                              (1, 960, 300, False), (2, 2048, 24, False)])
 def test_auto_on_bf16_x_small_launches(B, m, tiles, fused):
     """AUTO on bf16 x below 1536 tiles: the fp4 kernel with on-chip digits at batch 1 for
-    2048 <= m <= 6144, and up to m = 8192 in launches of at most 256 tiles; the bf16 kernel
-    otherwise.  Checked bit for bit against the kernel that should run, and against the oracle."""
+    2048 <= m <= 8192, and for 1024 <= m < 2048 in launches of at least 128 tiles; the bf16
+    kernel otherwise.  Checked bit for bit against the kernel that should run, and against the
+    oracle."""
     dev = device()
     n, T = 16 * tiles, 2
     codes, scales = layer(n, m, T, seed=40 + m + tiles)

@@ -213,22 +213,22 @@ int fairy2i_pack(const uint8_t* codes, int64_t n, int64_t m, int T, uint8_t* pac
 // The fp4 GEMV on bf16 x builds each row's digit records in LDS (fp4, 16 bytes per record): at
 // most 32 chunks of 256 columns over the batch entries (64 KB).  AUTO takes it for launches of at
 // least kF4FusedMinTiles tiles, whose workgroups stay resident and build the records once for many
-// tiles (those workgroups need one x for the launch).  Smaller launches build them once per tile;
-// at batch 1 that still beats the bf16 kernel from m = 2048 (per launch, 32 distinct T = 2 layers
-// in a graph, bf16 / fp4 us: m = 2048, 256 tiles 5.85 / 5.48, 688 tiles 11.13 / 9.76, 1535 tiles
-// 18.85 / 16.54; m = 4096 and 5504 faster at every size from 16 tiles; m = 1024 slower at every
-// size), as long as two workgroups' records and staged x (12 m bytes) fit in a CU's LDS: at
-// m = 8192 (96 KB) only launches of up to 256 tiles gain (384 tiles 20.42 / 23.24).  At batch 2
-// the per-tile build and the second batch entry's operands make it slower than bf16 at every
-// small size measured (m = 512 to 4096, 16 to 1535 tiles).
+// tiles (those workgroups need one x for the launch).  In smaller launches at batch 1 each wave
+// builds the records of its own chunks only; per launch, 32 distinct T = 2 layers in a graph,
+// bf16 / fp4 us: m = 2048 16 tiles 5.08 / 5.00, 256 tiles 5.94 / 4.77, 1535 tiles 21.06 / 14.76;
+// m = 4096, 5504 and 8192 faster at every size (8192, 1535 tiles: 58.76 / 44.35); m = 1024 16 tiles
+// 3.85 / 4.09, 64 tiles 4.11 / 4.11, 128 tiles 4.23 / 4.18, 1535 tiles 12.56 / 10.84; m = 512
+// slower up to 128 tiles and at 1535.  At batch 2 the per-tile build and the second batch entry's
+// operands make it slower than bf16 at every small size measured (m = 512 to 4096, 16 to 1535
+// tiles).
 constexpr int kMaxF4FusedColumns = 8192;
 constexpr int64_t kF4FusedMinTiles = 1536;
-constexpr int64_t kF4FusedSmallMinM = 2048;
-constexpr int64_t kF4FusedSmallMaxM = 6144;          // 72 KB of LDS: two workgroups per CU
-constexpr int64_t kF4FusedSmallMaxTilesWide = 256;   // beyond kF4FusedSmallMaxM: one round of workgroups
+constexpr int64_t kF4FusedSmallMinM = 2048;          // any launch size from here
+constexpr int64_t kF4FusedShortMinM = 1024;          // and from kF4FusedShortMinTiles tiles from here
+constexpr int64_t kF4FusedShortMinTiles = 128;
 static bool f4_records_fit(int64_t m, int64_t B) { return m * B <= kMaxF4FusedColumns; }
 static bool f4_fused_small_wins(int64_t B, int64_t m, int64_t tiles) {
-  return B == 1 && m >= kF4FusedSmallMinM && (m <= kF4FusedSmallMaxM || tiles <= kF4FusedSmallMaxTilesWide);
+  return B == 1 && (m >= kF4FusedSmallMinM || (m >= kF4FusedShortMinM && tiles >= kF4FusedShortMinTiles));
 }
 
 static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B, int64_t m, int64_t tiles = 0,

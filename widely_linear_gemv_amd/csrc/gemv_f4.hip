@@ -425,70 +425,83 @@ __device__ __forceinline__ void build_f4_records(const uint16_t* x, int m, int B
 // chunk's records) each, one item per lane.
 struct F4LocalBuild {
   static constexpr bool kLocal = true;
+  static constexpr int kPre = 4;                      // passes whose x loads are issued up front
   const uint16_t* x;                                  // bf16 [2m] (one batch entry)
   int m, nw, wave;
   uint8_t* s_rec;
   int* s_Sc;                                          // one exponent per chunk
-  uint4 v[2];                                         // this lane's item: 16 columns of x
+  uint4 v[kPre][2];                                   // this lane's items: 16 columns of x per pass
   __device__ __forceinline__ int nchunk() const { return (m + kF4Chunk - 1) / kF4Chunk; }
+  __device__ __forceinline__ int passes() const {     // two of the wave's chunks per pass
+    const int cpw = wave < nchunk() ? (nchunk() - wave + nw - 1) / nw : 0;
+    return (cpw + 1) / 2;
+  }
   __device__ __forceinline__ int lane() const { return threadIdx.x & (kWave - 1); }
   __device__ __forceinline__ int chunk_of(int pass) const { return wave + nw * (2 * pass + (lane() >> 5)); }
   __device__ __forceinline__ bool present(int c, int g) const { return c < nchunk() && kF4Chunk * c + 64 * g < m; }
-  __device__ __forceinline__ const uint4* src(int c) const {
+  // Range-checked buffer loads (absent columns read the out-of-range offset, which returns 0):
+  // no branch, so the passes' loads issue back to back with no wait between them.
+  __device__ __forceinline__ void load_pass(int pass, uint4 (&u)[2]) const {
+    const __amdgpu_buffer_rsrc_t rs = range_rsrc(x, (int64_t)4 * m);
+    const int c = chunk_of(pass);
     const int item = lane() & 31, h = item & 1, comp = (item >> 1) & 1, g = (item >> 2) & 3, s = item >> 4;
-    return reinterpret_cast<const uint4*>(x + (int64_t)comp * m + kF4Chunk * c + 64 * g + 32 * s + 16 * h);
+    const uint32_t off = present(c, g) ? (uint32_t)(2 * (comp * m + kF4Chunk * c + 64 * g + 32 * s + 16 * h)) : kNoLoad;
+    u[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    u[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off == kNoLoad ? kNoLoad : off + 16, 0, 0));
   }
-  __device__ __forceinline__ void load_pass(int pass) {
-    const int c = chunk_of(pass), g = ((lane() & 31) >> 2) & 3;
-    if (present(c, g)) {
-      const uint4* p = src(c);
-      v[0] = p[0];
-      v[1] = p[1];
-    } else {
-      v[0] = v[1] = make_uint4(0, 0, 0, 0);
-    }
-  }
+  // The x loads of the first kPre passes (all of them for rows of up to 8192 columns split over
+  // four or more waves), so that later passes do not wait for a load of their own.
   __device__ __forceinline__ void load_x() {
-    load_pass(0);
+    const int np = passes();
+#pragma unroll
+    for (int p = 0; p < kPre; ++p)
+      if (p < np) load_pass(p, v[p]);
     __builtin_amdgcn_sched_barrier(0);                // issued before the caller's next loads
+  }
+  __device__ __forceinline__ void build_pass(int pass, const uint4 (&u)[2]) {
+    const int item = lane() & 31, h = item & 1, comp = (item >> 1) & 1, g = (item >> 2) & 3, s = item >> 4;
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t wd[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(wd[e])), fabsf(bf16_hi(wd[e]))));
+    }
+    mx = fmaxf(mx, dpp_read<0xB1>(mx));               // lane ^ 1
+    mx = fmaxf(mx, dpp_read<0x4E>(mx));               // lane ^ 2
+    mx = fmaxf(mx, dpp_read<0x141>(mx));              // row_half_mirror
+    mx = fmaxf(mx, dpp_read<0x140>(mx));              // row_mirror: every lane holds its row's maximum
+    const int iv = __builtin_bit_cast(int, mx);
+    const float m0 = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)),
+                           __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16)));
+    const float m1 = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)),
+                           __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
+    const int S0 = digit_exponent(m0), S1 = digit_exponent(m1);
+    const int c = chunk_of(pass);
+    if (c < nchunk()) {
+      uint8_t* dst0 = s_rec + ((c * 2 + s) * kWave + 16 * g + 8 * comp) * kRecBytes + 8 * h;
+      if (present(c, g)) {
+        build_record_half(u, lane() < 32 ? S0 : S1, dst0);
+      } else {
+#pragma unroll
+        for (int l = 0; l < 8; ++l) *reinterpret_cast<uint2*>(dst0 + l * kRecBytes) = make_uint2(0u, 0u);
+      }
+    }
+    if (lane() == 0) {
+      s_Sc[wave + nw * 2 * pass] = S0;
+      if (wave + nw * (2 * pass + 1) < nchunk()) s_Sc[wave + nw * (2 * pass + 1)] = S1;
+    }
   }
   __device__ __forceinline__ void build() {
     __builtin_amdgcn_sched_barrier(0);                // the caller's loads stay ahead of the build
-    const int cpw = wave < nchunk() ? (nchunk() - wave + nw - 1) / nw : 0;   // chunks of this wave
-    const int item = lane() & 31, h = item & 1, comp = (item >> 1) & 1, g = (item >> 2) & 3, s = item >> 4;
-    for (int pass = 0; 2 * pass < cpw; ++pass) {
-      if (pass > 0) load_pass(pass);
-      float mx = 0.f;
+    const int np = passes();
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(wd[e])), fabsf(bf16_hi(wd[e]))));
-      }
-      mx = fmaxf(mx, dpp_read<0xB1>(mx));             // lane ^ 1
-      mx = fmaxf(mx, dpp_read<0x4E>(mx));             // lane ^ 2
-      mx = fmaxf(mx, dpp_read<0x141>(mx));            // row_half_mirror
-      mx = fmaxf(mx, dpp_read<0x140>(mx));            // row_mirror: every lane holds its row's maximum
-      const int iv = __builtin_bit_cast(int, mx);
-      const float m0 = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)),
-                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16)));
-      const float m1 = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)),
-                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
-      const int S0 = digit_exponent(m0), S1 = digit_exponent(m1);
-      const int c = chunk_of(pass);
-      if (c < nchunk()) {
-        uint8_t* dst0 = s_rec + ((c * 2 + s) * kWave + 16 * g + 8 * comp) * kRecBytes + 8 * h;
-        if (present(c, g)) {
-          build_record_half(v, lane() < 32 ? S0 : S1, dst0);
-        } else {
-#pragma unroll
-          for (int l = 0; l < 8; ++l) *reinterpret_cast<uint2*>(dst0 + l * kRecBytes) = make_uint2(0u, 0u);
-        }
-      }
-      if (lane() == 0) {
-        s_Sc[wave + nw * 2 * pass] = S0;
-        if (wave + nw * (2 * pass + 1) < nchunk()) s_Sc[wave + nw * (2 * pass + 1)] = S1;
-      }
+    for (int p = 0; p < kPre; ++p)
+      if (p < np) build_pass(p, v[p]);
+    for (int p = kPre; p < np; ++p) {                 // rows longer than the up-front loads cover
+      uint4 u[2];
+      load_pass(p, u);
+      build_pass(p, u);
     }
   }
 };
@@ -1119,6 +1132,15 @@ static int resident_workgroups(K kernel, int threads, size_t lds, KernelLaunchSt
   return per_cu * cus;
 }
 
+// Waves per tile of the per-wave-record launches: as the other small launches, except that long
+// rows (16 chunks or more) in launches of at most 256 tiles split over eight waves, so each wave
+// builds fewer records before its first MFMA (32-layer step, 4096 x 11008 projection: 8.2 ->
+// 7.9 us per launch; at 2048 columns eight waves were slower, 4.46 -> 5.0 us).
+static int f4_local_waves_per_tile(int tiles, int m) {
+  const int nchunk = (m + kF4Chunk - 1) / kF4Chunk;
+  return nchunk >= 16 && tiles <= 256 ? 8 : gemv_waves_per_tile(tiles, m);
+}
+
 template <int TT, int BT, typename YT, bool FUSED>
 static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
   GemvGroup grp = group;
@@ -1152,7 +1174,7 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
   if constexpr (FUSED && BT == 1) {                       // small launches: per-wave records
     const size_t lds = (size_t)f4_record_bytes(m, 1) + f4_local_exp_bytes(m);
     const size_t lds_max = (size_t)f4_record_bytes(kF4FusedMaxCols, 1) + f4_local_exp_bytes(kF4FusedMaxCols);
-    switch (gemv_waves_per_tile(tiles, m)) {
+    switch (f4_local_waves_per_tile(tiles, m)) {
 #define F2I_F4_LOCAL_CASE(NWV)                                                                        \
       {                                                                                                 \
         static KernelLaunchState st;                                                                    \

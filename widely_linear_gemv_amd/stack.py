@@ -7,9 +7,9 @@ the projections that read the same input, are independent).
 Per transformer layer the seven projections form four groups by their input: q, k and v share x;
 o reads its own; gate and up share x; down reads its own.  A group is one grouped GEMV launch, so
 a 32-layer stack is 128 launches, captured once in a HIP graph and replayed.  By default (AUTO)
-the launches take the bf16 x as it is: at batch 1 the fp4 kernel builds the digits of x on chip
-in every workgroup (these launches are small, 4-23 MB, and a separate digit-form launch per group
-would cost more than it saves), at larger batches the bf16 kernel runs.  With algo=GEMV_MFMA_F4
+the launches take the bf16 x as it is: at batch 1 the fp4 kernel digitizes x on chip, each wave
+the chunks it multiplies (these launches are small, 4-23 MB, and a separate digit-form launch per
+group would cost more than it saves), at larger batches the bf16 kernel runs.  With algo=GEMV_MFMA_F4
 or GEMV_MFMA_I8 each group first makes the digit form of its x in a launch of its own; with
 digits_given=True the digit forms are made once when the step is built and the step runs the
 GEMVs alone (for inputs that arrive in digit form, from a producer that writes it).  This module only sequences
