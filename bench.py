@@ -556,6 +556,9 @@ def main():
     def auto_b2():
         f2.fairy2i_gemv_strided(pool, spool, x2, ypool2)
 
+    def auto_b4():                     # AUTO at batch 4: fp4 code planes on x split into fp8 parts
+        f2.fairy2i_gemv_strided(pool, spool, xs[4], ypool[4])
+
     # the same GEMM launch on all-zero activations and codes 0x55 (one plane all zero, the other +1):
     # the same instructions and memory traffic with little switching, so the chip holds a higher clock
     q_zero = torch.zeros_like(qp)
@@ -568,6 +571,7 @@ def main():
     k_us = {"quantize": kernel_us(seg_quantize), "act_quant": kernel_us(seg_act_quant),
             "gemm_zero_data": kernel_us(gemm_zero_data),
             "auto_b1": kernel_us(auto_b1, warm=40), "auto_b2": kernel_us(auto_b2, warm=40),
+            "auto_b4": kernel_us(auto_b4, warm=40),
             "gemm": kernel_us(seg_gemm), "dequantize": kernel_us(seg_dequant),
             "quantize_per_tensor": kernel_us(seg_quantize_tensor), "gemm_mlp": kernel_us(gemm_mlp)}
     ops_mlp = 16 * T * workloads.PREFILL_LAYERS[1].n * m * Ntok        # issued int8 ops
@@ -648,6 +652,9 @@ def main():
             "gemv_b2_bf16x_auto": {"us_per_launch": round(k_us["auto_b2"], 3),
                                    "GB/s": round(P * gemv_bytes(n, m, T, 2) / (k_us["auto_b2"] * 1e-6) / 1e9, 2),
                                    "kernel": "fp4 MFMA, digit records built on chip from the bf16 x (AUTO)"},
+            "gemv_b4_bf16x_auto": {"us_per_launch": round(k_us["auto_b4"], 3),
+                                   "GB/s": round(P * bytes_b[4] / (k_us["auto_b4"] * 1e-6) / 1e9, 2),
+                                   "kernel": "fp4 MFMA on x split into two fp8 parts with per-block scales (AUTO)"},
             "gemv_b1_f4_grouped": {"us_per_pass": round(grouped_us, 3), "launches_per_pass": -(-P // 48),
                                    "GB/s": round(bytes_pool / (grouped_us * 1e-6) / 1e9, 2)},
             "gemv_b1_single_layer_launch": {"us_per_launch": round(single_us, 3),

@@ -104,8 +104,14 @@ typedef enum {
  *              maximum (never more than the per-row form), the chunks' sums are added in fp32,
  *              and the outputs are not bit-identical to the two-call form.  The fastest decode
  *              kernel on gfx950: half the MFMA cycles and about half the VALU work per code of
- *              MFMA_I8.
- * AUTO with bf16 x takes MFMA_F4 for launches of at least 1536 16-row tiles with B <= 2,
+ *              MFMA_I8.  At 3 <= B <= 16 (bf16 x only) the same fp4 planes multiply x split into
+ *              two fp8 e4m3 parts, hi = rne(x 2^-E) and lo = rne(x 2^-E - hi), under one E8M0
+ *              scale 2^E per 32 columns (the columns one fp4 lane holds at one MFMA step) with
+ *              E = floor(log2 M) - 7 for the block's max |x| = M: every product exact, fp32 sums;
+ *              each x entry is exact when |x| >= 2^-10 M and otherwise off by at most 2^-17 M
+ *              (m <= 2^19).
+ * AUTO with bf16 x takes MFMA_F4 at 3 <= B <= 4 for launches of at least 1536 16-row tiles (the
+ * fp8 split above); and for launches of at least 1536 16-row tiles with B <= 2,
  * m * B <= 8192 and one x for the launch (resident workgroups build the digits once for many
  * tiles); for smaller launches at B = 1 with 2048 <= m <= 8192, or 1024 <= m < 2048 in launches
  * of at least 128 tiles (each wave builds the digits of its own chunks, which there costs less
@@ -255,7 +261,8 @@ int fairy2i_dequantize(const uint8_t* packed, const float* scales, int64_t n, in
  *   y       out, [B][2n], y_dtype FAIRY2I_F32 or FAIRY2I_BF16 (round to nearest even).
  *   algo    fairy2i_gemv_algo; MFMA_BF16 requires x_dtype BF16, MFMA_I8 x_dtype X_DIGITS and
  *           B <= 2, MFMA_F4 x_dtype X_DIGITS_F6 (m <= 2^19: its fp32 sums stay exact integers)
- *           or BF16 (m * B <= 8192) and B <= 2; VALU takes F32 or BF16.
+ *           and B <= 2, or BF16 (B <= 2: m * B <= 8192; B > 2: m <= 2^19); VALU takes F32 or
+ *           BF16.
  * Uses no workspace. */
 int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,

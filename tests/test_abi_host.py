@@ -166,7 +166,7 @@ def test_gemv_errors(L):
     assert call(algo=f2.GEMV_MFMA_BF16, xd=f2.X_DIGITS) == 4
     assert call(algo=f2.GEMV_MFMA_F4, xd=f2.X_DIGITS) == 4          # needs the fp6 form
     assert call(algo=f2.GEMV_MFMA_F4, xd=f2.F32) == 4               # bf16 x or the fp6 form
-    assert call(algo=f2.GEMV_MFMA_F4, xd=f2.BF16, B=3) == 2
+    assert call(algo=f2.GEMV_MFMA_F4, xd=f2.BF16, B=3, m=(1 << 19) + 64) == 2   # fp8 split: fp32 sums
     assert call(algo=f2.GEMV_MFMA_F4, xd=f2.BF16, m=8192 + 64) == 2    # records built in LDS
     assert call(algo=f2.GEMV_MFMA_F4, xd=f2.BF16, m=4096 + 64, B=2) == 2
     assert "fairy2i_x_digits_f6" in last()

@@ -39,6 +39,8 @@ def kernels(B):
     if B <= 2:
         ks += [("i8", f2.GEMV_MFMA_I8, f2.fairy2i_x_digits), ("f4", f2.GEMV_MFMA_F4, f2.fairy2i_x_digits_f6),
                ("f4 on bf16 x", f2.GEMV_MFMA_F4, None)]
+    else:
+        ks += [("f4 on bf16 x split into fp8", f2.GEMV_MFMA_F4, None)]
     return ks
 
 

@@ -50,6 +50,7 @@ SOURCES = {
     "gemv_mfma.hip": [],
     "gemv_i8.hip": [],
     "gemv_f4.hip": [],
+    "gemv_f8x.hip": [],
     "prefill.hip": ["-ffp-contract=off"],
     "dequant.hip": ["-ffp-contract=off"],
     "api.cpp": ["-x", "hip"],

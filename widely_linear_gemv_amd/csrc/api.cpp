@@ -231,6 +231,18 @@ static bool f4_fused_small_wins(int64_t B, int64_t m, int64_t tiles) {
   return B == 1 && (m >= kF4FusedSmallMinM || (m >= kF4FusedShortMinM && tiles >= kF4FusedShortMinTiles));
 }
 
+// At batch 3-4 the fp4 kernel on x split into two fp8 parts beats the bf16 kernel on large
+// launches (1 GiB pools, bf16 / fp4 x fp8 us: 4096 x 4096 at B = 3 337.7 / 262.9, B = 4 316.4 /
+// 247.2; 11008 x 4096 B = 4 301.6 / 252.4; 4096 x 11008 B = 4 289.1 / 250.5); at B = 8 the two are
+// within 3 % either way and at B = 16 it takes twice as long (its four column groups need four-wave
+// workgroups); in the decode step's small launches (4-23 MB) its eight-tile workgroups leave most
+// of the chip idle (B = 8: 18.9 against 11.4 us per q/k/v launch).
+constexpr int64_t kF4x8MinTiles = 1536;
+constexpr int64_t kF4x8MaxM = int64_t(1) << 19;
+static bool f4x8_wins(int64_t B, int64_t m, int64_t tiles) {
+  return B >= 3 && B <= 4 && tiles >= kF4x8MinTiles && m <= kF4x8MaxM;
+}
+
 static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B, int64_t m, int64_t tiles = 0,
                        bool shared_x = true) {
   if (x_dtype != FAIRY2I_F32 && x_dtype != FAIRY2I_BF16 && x_dtype != FAIRY2I_X_DIGITS &&
@@ -245,9 +257,10 @@ static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B, int64_t m,
   if (kernel == FAIRY2I_GEMV_AUTO)
     kernel = x_dtype == FAIRY2I_X_DIGITS    ? FAIRY2I_GEMV_MFMA_I8
            : x_dtype == FAIRY2I_X_DIGITS_F6 ? FAIRY2I_GEMV_MFMA_F4
-           : x_dtype == FAIRY2I_BF16        ? (B <= 2 && f4_records_fit(m, B) &&
-                                                       (tiles >= kF4FusedMinTiles ? shared_x
-                                                                                  : f4_fused_small_wins(B, m, tiles))
+           : x_dtype == FAIRY2I_BF16        ? ((B <= 2 && f4_records_fit(m, B) &&
+                                                        (tiles >= kF4FusedMinTiles ? shared_x
+                                                                                   : f4_fused_small_wins(B, m, tiles))) ||
+                                                       f4x8_wins(B, m, tiles)
                                                    ? FAIRY2I_GEMV_MFMA_F4 : FAIRY2I_GEMV_MFMA_BF16)
                                             : FAIRY2I_GEMV_VALU;
   if (kernel == FAIRY2I_GEMV_MFMA) kernel = FAIRY2I_GEMV_MFMA_BF16;
@@ -258,12 +271,14 @@ static int gemv_kernel(int x_dtype, int y_dtype, int algo, int64_t B, int64_t m,
   } else if (kernel == FAIRY2I_GEMV_MFMA_F4) {
     if (x_dtype != FAIRY2I_X_DIGITS_F6 && x_dtype != FAIRY2I_BF16)
       return -fail(FAIRY2I_ERR_DTYPE, "the fp4 MFMA GEMV takes bf16 x or x in fp6 digit form (fairy2i_x_digits_f6)");
-    if (B > 2) return -fail(FAIRY2I_ERR_SHAPE, "B = %lld: the fp4 MFMA GEMV takes B <= 2", (long long)B);
-    if (x_dtype == FAIRY2I_BF16 && m > 0 && !f4_records_fit(m, B))
+    if (B > 2 && x_dtype != FAIRY2I_BF16)
+      return -fail(FAIRY2I_ERR_SHAPE, "B = %lld: the fp4 MFMA GEMV on a digit form takes B <= 2 (bf16 x: B <= 16)",
+                   (long long)B);
+    if (x_dtype == FAIRY2I_BF16 && B <= 2 && m > 0 && !f4_records_fit(m, B))
       return -fail(FAIRY2I_ERR_SHAPE, "m = %lld, B = %lld: the fp4 MFMA GEMV on bf16 x takes m * B <= %d "
                    "(its digit records are built in LDS); make the digit form with fairy2i_x_digits_f6",
                    (long long)m, (long long)B, kMaxF4FusedColumns);
-    if (x_dtype == FAIRY2I_BF16 && !shared_x && tiles >= kF4FusedMinTiles)
+    if (x_dtype == FAIRY2I_BF16 && B <= 2 && !shared_x && tiles >= kF4FusedMinTiles)
       return -fail(FAIRY2I_ERR_SHAPE, "the fp4 MFMA GEMV on bf16 x needs one x for every item of a launch of "
                    "%lld tiles or more (give the items' x as one digit form, or use the bf16 kernel)",
                    (long long)kF4FusedMinTiles);
@@ -318,6 +333,14 @@ int fairy2i_x_digits_f6(const void* x, int x_dtype, int64_t m, int64_t B, void* 
                     "x fp6 digits launch");
 }
 
+// The fp4 matrix-core GEMVs: batch 1-2 on a digit form or bf16 x (launch_gemv_f4_group); batch 3-16
+// on bf16 x split into fp8 parts (launch_gemv_f8x_group).
+static hipError_t launch_f4_family(const f2i::GemvGroup& grp, int64_t m, int T, int64_t B, int ybf, int x_dtype,
+                                   hipStream_t stream) {
+  if (B > 2) return f2i::launch_gemv_f8x_group(grp, (int)m, T, (int)B, ybf, stream);
+  return f2i::launch_gemv_f4_group(grp, (int)m, T, (int)B, ybf, x_dtype == FAIRY2I_BF16, stream);
+}
+
 int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t m, int T,
                  const void* x, int x_dtype, int64_t B, void* y, int y_dtype, int algo,
                  hipStream_t stream) {
@@ -329,6 +352,15 @@ int fairy2i_gemv(const uint8_t* packed, const float* scales, int64_t n, int64_t 
   if (int s = check_f4_cols(kernel, m)) return s;
   if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(scales, 4))
     return fail(FAIRY2I_ERR_ALIGN, "packed, x and y need 16-byte alignment, scales 4");
+  if (kernel == FAIRY2I_GEMV_MFMA_F4 && B > 2) {
+    f2i::GemvGroup grp;
+    grp.count = 1;
+    grp.tile_start[0] = 0;
+    grp.tile_start[1] = (int)((n + 15) / 16);
+    grp.items[0] = f2i::GemvItem{packed, scales, x, y, (int)n};
+    return hip_status(launch_f4_family(grp, m, T, B, y_dtype == FAIRY2I_BF16, x_dtype, stream),
+                      "gemv (fp4 x fp8 mfma) launch");
+  }
   if (kernel == FAIRY2I_GEMV_MFMA_F4)
     return hip_status(f2i::launch_gemv_f4(packed, scales, (int)n, (int)m, T, x, (int)B, y,
                                           y_dtype == FAIRY2I_BF16, x_dtype == FAIRY2I_BF16, stream),
@@ -391,7 +423,7 @@ int fairy2i_gemv_grouped(const fairy2i_gemv_item* items, int count, int64_t m, i
     grp.tile_start[grp.count] = tiles;
     const int ybf = y_dtype == FAIRY2I_BF16;
     hipError_t e = kernel == FAIRY2I_GEMV_MFMA_F4
-                       ? f2i::launch_gemv_f4_group(grp, (int)m, T, (int)B, ybf, x_dtype == FAIRY2I_BF16, stream)
+                       ? launch_f4_family(grp, m, T, B, ybf, x_dtype, stream)
                  : kernel == FAIRY2I_GEMV_MFMA_I8 ? f2i::launch_gemv_i8_group(grp, (int)m, T, (int)B, ybf, stream)
                  : f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, ybf, stream);
     if (e != hipSuccess) return hip_status(e, "gemv (grouped mfma) launch");
@@ -441,7 +473,7 @@ int fairy2i_gemv_strided(const uint8_t* packed, int64_t packed_stride, const flo
   grp.y_stride = y_stride;
   const int ybf = y_dtype == FAIRY2I_BF16;
   hipError_t e = kernel == FAIRY2I_GEMV_MFMA_F4
-                     ? f2i::launch_gemv_f4_group(grp, (int)m, T, (int)B, ybf, x_dtype == FAIRY2I_BF16, stream)
+                     ? launch_f4_family(grp, m, T, B, ybf, x_dtype, stream)
                : kernel == FAIRY2I_GEMV_MFMA_I8 ? f2i::launch_gemv_i8_group(grp, (int)m, T, (int)B, ybf, stream)
                : f2i::launch_gemv_mfma_group(grp, (int)m, T, (int)B, ybf, stream);
   return hip_status(e, "gemv (strided batch) launch");

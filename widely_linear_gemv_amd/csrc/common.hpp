@@ -202,6 +202,8 @@ hipError_t launch_gemv_i8_group(const GemvGroup& grp, int m, int T, int B, int y
 hipError_t launch_gemv_f4(const uint8_t* packed, const float* scales, int n, int m, int T,
                           const void* x, int B, void* y, int y_bf16, int x_bf16, hipStream_t s);
 hipError_t launch_gemv_f4_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, int x_bf16, hipStream_t s);
+// Batch 3-16 on bf16 x: fp4 code planes times x split into two fp8 parts under per-block scales.
+hipError_t launch_gemv_f8x_group(const GemvGroup& grp, int m, int T, int B, int y_bf16, hipStream_t s);
 int gemv_f4_record_bytes(int m, int B);     // LDS bytes of the on-chip records (x_bf16 launches)
 size_t x_digits_f6_bytes(int64_t m, int64_t B);
 hipError_t launch_x_digits_f6(const void* x, int x_bf16, int m, int B, void* blob, hipStream_t s);
