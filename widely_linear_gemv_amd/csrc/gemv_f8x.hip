@@ -55,8 +55,9 @@ __device__ __forceinline__ void keep_live_after(const V& v, const v4f& after) {
 
 template <int CG, int NWV>
 struct F8Stage {
-  // LDS of one chunk: records [step s][column group][lane] of 32 bytes, then the block-scale bytes
-  // [s][column group][lane].
+  // LDS of one chunk: records [step s][column group][half][lane] of 16 bytes (a lane's 32 bytes as
+  // two planes, so the lanes of a 16-byte read are consecutive: conflict-free), then the
+  // block-scale bytes [s][column group][lane].
   static constexpr int kRecBytes = 2 * CG * kWave * kF8Rec;
   static constexpr int kBytes = kRecBytes + 2 * CG * kWave;
   // Work items per chunk: (batch entry, component, block, quarter), 4 CG * 2 * 8 * 4 of them.
@@ -166,9 +167,9 @@ __global__ __launch_bounds__((kWave * f8_waves<TT, CG>())) void k_gemv_f8x(const
         const int cg = b >> 2, nh = 4 * (b & 3) + 2 * comp;      // column of hi; lo is nh + 1
         const int l_rec = 16 * (2 * (g & 1) + (k >> 1)) + nh;     // B lane holding this quarter
         const int at = 16 * (g >> 1) + 8 * (k & 1);               // its byte offset in that record
-        uint8_t* base = rec + ((s * CG + cg) * kWave) * kF8Rec;
-        *reinterpret_cast<uint2*>(base + l_rec * kF8Rec + at) = make_uint2(hi[0], hi[1]);
-        *reinterpret_cast<uint2*>(base + (l_rec + 1) * kF8Rec + at) = make_uint2(lo[0], lo[1]);
+        uint8_t* base = rec + ((s * CG + cg) * kWave) * kF8Rec + (at >> 4) * (kWave * 16) + (at & 15);
+        *reinterpret_cast<uint2*>(base + l_rec * 16) = make_uint2(hi[0], hi[1]);
+        *reinterpret_cast<uint2*>(base + (l_rec + 1) * 16) = make_uint2(lo[0], lo[1]);
         if (k == 0) {
           const uint32_t sb = (uint32_t)(127 + E);
           *reinterpret_cast<uint16_t*>(scb + (s * CG + cg) * kWave + 16 * g + nh) = (uint16_t)(sb | (sb << 8));
@@ -196,8 +197,9 @@ __global__ __launch_bounds__((kWave * f8_waves<TT, CG>())) void k_gemv_f8x(const
       int sb[CG];
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg) {
-        const uint4* p = reinterpret_cast<const uint4*>(rec + ((s * CG + cg) * kWave + lane) * kF8Rec);
-        const uint4 lo = p[0], hi = p[1];
+        const uint8_t* p = rec + ((s * CG + cg) * kWave) * kF8Rec + lane * 16;
+        const uint4 lo = *reinterpret_cast<const uint4*>(p);
+        const uint4 hi = *reinterpret_cast<const uint4*>(p + kWave * 16);
         xb[cg] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         sb[cg] = scb[(s * CG + cg) * kWave + lane];
       }
