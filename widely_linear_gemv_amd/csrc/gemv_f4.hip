@@ -184,8 +184,8 @@ __host__ __device__ inline int f4_record_bytes(int m, int B) {
   return ((m + kF4Chunk - 1) / kF4Chunk) * 2 * B * kWave * kRecBytes;
 }
 
-// LDS bytes of the per-chunk exponents of the per-wave records (16-byte aligned).
-__host__ __device__ inline int f4_local_exp_bytes(int m) { return (((m + kF4Chunk - 1) / kF4Chunk) * 4 + 15) & ~15; }
+// LDS bytes of the per-chunk, per-batch-entry exponents of the per-wave records (16-byte aligned).
+__host__ __device__ inline int f4_local_exp_bytes(int m, int B) { return (((m + kF4Chunk - 1) / kF4Chunk) * B * 4 + 15) & ~15; }
 
 // LDS bytes of the staged bf16 x of B batch entries (2m values each).
 __host__ __device__ inline int f4_xstage_bytes(int m, int B) { return 4 * m * B; }
@@ -383,7 +383,7 @@ __device__ __forceinline__ void build_f4_records(const uint16_t* x, int m, int B
   bld.build();
 }
 
-// Per-wave records with one exponent per chunk (batch 1, bf16 x): wave w of the NW waves that
+// Per-wave records with one exponent per chunk and batch entry (bf16 x): wave w of the NW waves that
 // split a tile builds the records of its own chunks c = w, w + NW, ... and nothing else, each at
 // its chunk's own exponent S_c (max over the chunk's 512 values of |x| 2^S_c in [2^21, 2^22)).
 // There is no workgroup-wide step: the wave reads only its chunks of x, reduces their maxima on
@@ -392,28 +392,34 @@ __device__ __forceinline__ void build_f4_records(const uint16_t* x, int m, int B
 // lies in [-106, 147], so both fit E8M0), so the digit sums of every chunk enter the fp32
 // accumulators at one common scale and the epilogue applies only the digit weight.  Against one
 // exponent per row, each chunk's X keeps 22 bits below its own maximum (never fewer), and the sums
-// across chunks round in fp32.  A pass covers two of the wave's chunks, 32 items (the halves of a
-// chunk's records) each, one item per lane.
+// across chunks round in fp32.  A pass covers 64 items (halves of a chunk's records), one per lane:
+// two of the wave's chunks at batch 1, one chunk's two batch entries at batch 2.
+template <int BT>
 struct F4LocalBuild {
   static constexpr bool kLocal = true;
   static constexpr int kPre = 4;                      // passes whose x loads are issued up front
-  const uint16_t* x;                                  // bf16 [2m] (one batch entry)
+  const uint16_t* x;                                  // bf16 [BT][2m]
   int m, nw, wave;
   uint8_t* s_rec;
-  int* s_Sc;                                          // one exponent per chunk
+  int* s_Sc;                                          // one exponent per chunk and batch entry
   uint4 v[kPre][2];                                   // this lane's items: 16 columns of x per pass
   __device__ __forceinline__ int nchunk() const { return (m + kF4Chunk - 1) / kF4Chunk; }
-  __device__ __forceinline__ int passes() const {     // two of the wave's chunks per pass
+  // A pass covers 64 half-records: two of the wave's chunks at batch 1, one chunk's two batch
+  // entries at batch 2 (lanes 32-63 take the second).
+  __device__ __forceinline__ int passes() const {
     const int cpw = wave < nchunk() ? (nchunk() - wave + nw - 1) / nw : 0;
-    return (cpw + 1) / 2;
+    return BT == 1 ? (cpw + 1) / 2 : cpw;
   }
   __device__ __forceinline__ int lane() const { return threadIdx.x & (kWave - 1); }
-  __device__ __forceinline__ int chunk_of(int pass) const { return wave + nw * (2 * pass + (lane() >> 5)); }
+  __device__ __forceinline__ int chunk_of(int pass) const {
+    return BT == 1 ? wave + nw * (2 * pass + (lane() >> 5)) : wave + nw * pass;
+  }
+  __device__ __forceinline__ int batch_of() const { return BT == 1 ? 0 : lane() >> 5; }
   __device__ __forceinline__ bool present(int c, int g) const { return c < nchunk() && kF4Chunk * c + 64 * g < m; }
   // Range-checked buffer loads (absent columns read the out-of-range offset, which returns 0):
   // no branch, so the passes' loads issue back to back with no wait between them.
   __device__ __forceinline__ void load_pass(int pass, uint4 (&u)[2]) const {
-    const __amdgpu_buffer_rsrc_t rs = range_rsrc(x, (int64_t)4 * m);
+    const __amdgpu_buffer_rsrc_t rs = range_rsrc(x + (int64_t)batch_of() * 2 * m, (int64_t)4 * m);
     const int c = chunk_of(pass);
     const int item = lane() & 31, h = item & 1, comp = (item >> 1) & 1, g = (item >> 2) & 3, s = item >> 4;
     const uint32_t off = present(c, g) ? (uint32_t)(2 * (comp * m + kF4Chunk * c + 64 * g + 32 * s + 16 * h)) : kNoLoad;
@@ -450,7 +456,7 @@ struct F4LocalBuild {
     const int S0 = digit_exponent(m0), S1 = digit_exponent(m1);
     const int c = chunk_of(pass);
     if (c < nchunk()) {
-      uint8_t* dst0 = s_rec + ((c * 2 + s) * kWave + 16 * g + 8 * comp) * kRecBytes + 8 * h;
+      uint8_t* dst0 = s_rec + (((c * 2 + s) * BT + batch_of()) * kWave + 16 * g + 8 * comp) * kRecBytes + 8 * h;
       if (present(c, g)) {
         build_record_half(u, lane() < 32 ? S0 : S1, dst0);
       } else {
@@ -459,8 +465,13 @@ struct F4LocalBuild {
       }
     }
     if (lane() == 0) {
-      s_Sc[wave + nw * 2 * pass] = S0;
-      if (wave + nw * (2 * pass + 1) < nchunk()) s_Sc[wave + nw * (2 * pass + 1)] = S1;
+      if constexpr (BT == 1) {
+        s_Sc[wave + nw * 2 * pass] = S0;
+        if (wave + nw * (2 * pass + 1) < nchunk()) s_Sc[wave + nw * (2 * pass + 1)] = S1;
+      } else {
+        s_Sc[2 * (wave + nw * pass)] = S0;             // [chunk][batch entry]
+        s_Sc[2 * (wave + nw * pass) + 1] = S1;
+      }
     }
   }
   __device__ __forceinline__ void build() {
@@ -570,12 +581,18 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
       }
   };
   auto compute_chunk = [&](const Chunk& ch) {
-    // block scales (E8M0, 127 = 2^0): 2^-S_c for per-chunk records (Build::kLocal), else 2^0
-    int sca = 127, scb = 127;
-    if constexpr (Build::kLocal) {
-      const int S = __builtin_amdgcn_readfirstlane(bld.s_Sc[ch.c]);
-      sca = 127 - (S >> 1);
-      scb = 127 - (S - (S >> 1));
+    // block scales (E8M0, 127 = 2^0): 2^-S for per-chunk records (Build::kLocal; one S per chunk
+    // and batch entry), else 2^0
+    int sca[BT], scb[BT];
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      sca[b] = 127;
+      scb[b] = 127;
+      if constexpr (Build::kLocal) {
+        const int S = __builtin_amdgcn_readfirstlane(bld.s_Sc[ch.c * BT + b]);
+        sca[b] = 127 - (S >> 1);
+        scb[b] = 127 - (S - (S >> 1));
+      }
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -604,9 +621,9 @@ __device__ __forceinline__ void gemv_f4_tile(const GemvGroup& grp, int m, int B,
           for (int b = 0; b < BT; ++b) {
             // A fp4; B fp6 e2m3 (digit form) or fp4 (records in LDS)
             acc[t][M][0][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pu, xs[b], acc[t][M][0][b], 4, FUSED ? 4 : 2, 0, sca, 0, scb);
+                pu, xs[b], acc[t][M][0][b], 4, FUSED ? 4 : 2, 0, sca[b], 0, scb[b]);
             acc[t][M][1][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                pv, xs[b], acc[t][M][1][b], 4, FUSED ? 4 : 2, 0, sca, 0, scb);
+                pv, xs[b], acc[t][M][1][b], 4, FUSED ? 4 : 2, 0, sca[b], 0, scb[b]);
           }
         }
     }
@@ -963,21 +980,21 @@ __global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_ge
   }
 }
 
-// Small batch-1 launches on bf16 x (NW > 1 waves per tile): each wave builds the records of its
+// Small launches on bf16 x (NW > 1 waves per tile, batch 1-2): each wave builds the records of its
 // own chunks at per-chunk exponents (F4LocalBuild), so no wave waits on another before its first
 // MFMA; the waves meet once, to add their partial outputs.
-template <int TT, int NW, typename YT>
-__global__ __launch_bounds__(kWave * NW, TT <= 3 ? 3 : 1) void k_gemv_f4_local(const GemvGroup grp, int m) {
+template <int TT, int NW, int BT, typename YT>
+__global__ __launch_bounds__(kWave * NW, (BT == 1 && TT <= 3) ? 3 : 1) void k_gemv_f4_local(const GemvGroup grp, int m) {
   static_assert(NW > 1, "the waves of a tile split its chunks");
   __shared__ float s_sc[NW][16 * TT * 4];
-  __shared__ float s_y[NW][1][2][16];                   // [wave][batch][re/im][row]
+  __shared__ float s_y[NW][BT][2][16];                  // [wave][batch][re/im][row]
   extern __shared__ __align__(16) uint8_t s_dyn[];       // records, then one exponent per chunk
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   int tile;
   const GemvItem it = locate_item<YT>(grp, blockIdx.x, tile);
-  const F4LocalBuild bld{static_cast<const uint16_t*>(it.x), m, NW, wave, s_dyn,
-                         reinterpret_cast<int*>(s_dyn + f4_record_bytes(m, 1)), {}};
-  gemv_f4_tile<TT, NW, 1, YT, false, true>(grp, m, 1, blockIdx.x, wave, s_sc[wave], s_y, nullptr, s_dyn, nullptr, bld);
+  const F4LocalBuild<BT> bld{static_cast<const uint16_t*>(it.x), m, NW, wave, s_dyn,
+                             reinterpret_cast<int*>(s_dyn + f4_record_bytes(m, BT)), {}};
+  gemv_f4_tile<TT, NW, BT, YT, false, true>(grp, m, BT, blockIdx.x, wave, s_sc[wave], s_y, nullptr, s_dyn, nullptr, bld);
 }
 
 // Large batch-1 launches in two granularities.  The first nA workgroups take four units each,
@@ -1142,15 +1159,15 @@ static void launch_f4_t(const GemvGroup& group, int m, int B, hipStream_t s) {
     }
   }
   const dim3 grid(tiles);
-  if constexpr (FUSED && BT == 1) {                       // small launches: per-wave records
-    const size_t lds = (size_t)f4_record_bytes(m, 1) + f4_local_exp_bytes(m);
-    const size_t lds_max = (size_t)f4_record_bytes(kF4FusedMaxCols, 1) + f4_local_exp_bytes(kF4FusedMaxCols);
+  if constexpr (FUSED) {                                  // small launches: per-wave records
+    const size_t lds = (size_t)f4_record_bytes(m, BT) + f4_local_exp_bytes(m, BT);
+    const size_t lds_max = (size_t)f4_record_bytes(kF4FusedMaxCols / BT, BT) + f4_local_exp_bytes(kF4FusedMaxCols / BT, BT);
     switch (f4_local_waves_per_tile(tiles, m)) {
 #define F2I_F4_LOCAL_CASE(NWV)                                                                        \
       {                                                                                                 \
         static KernelLaunchState st;                                                                    \
-        lds_launch_prepare(k_gemv_f4_local<TT, NWV, YT>, lds_max, st);                                  \
-        hipLaunchKernelGGL((k_gemv_f4_local<TT, NWV, YT>), grid, dim3(NWV * kWave), lds, s, grp, m);    \
+        lds_launch_prepare(k_gemv_f4_local<TT, NWV, BT, YT>, lds_max, st);                              \
+        hipLaunchKernelGGL((k_gemv_f4_local<TT, NWV, BT, YT>), grid, dim3(NWV * kWave), lds, s, grp, m); \
       }                                                                                                 \
       return;
       case 8: F2I_F4_LOCAL_CASE(8)
