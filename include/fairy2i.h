@@ -95,10 +95,10 @@ typedef enum {
  *              (the digit form made once by fairy2i_x_digits_f6 and shared by every GEMV that
  *              reads that x) or FAIRY2I_BF16: then the digits are built on chip from the bf16 x
  *              (m * B <= 8192; in a grouped call of 1536 tiles or more every item must have the
- *              same x).  In launches of 1536 tiles or more, at B = 2, and for m <= 256 each
- *              workgroup builds the same digits as fairy2i_x_digits_f6 (outputs identical bit for
- *              bit to the two-call form).  Smaller launches at B = 1 digitize each 256-column
- *              chunk at its own exponent (max over the chunk's 512 values of |x| 2^S_c in
+ *              same x).  In launches of 1536 tiles or more, and for m <= 256, each workgroup
+ *              builds the same digits as fairy2i_x_digits_f6 (outputs identical bit for bit to
+ *              the two-call form).  Smaller launches digitize each 256-column chunk of each batch
+ *              entry at its own exponent (max over the chunk's 512 values of |x| 2^S_c in
  *              [2^21, 2^22)), each wave for the chunks it multiplies, and pass 2^-S_c to the
  *              MFMAs as block scales: every element is off by at most 2^-22 of its chunk's
  *              maximum (never more than the per-row form), the chunks' sums are added in fp32,
